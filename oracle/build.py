@@ -1,0 +1,28 @@
+"""Build the CPU oracle shared library (test infrastructure; plain g++ with OpenMP).
+
+``python oracle/build.py`` writes ``oracle/liboracle.so``.  Strict IEEE fp64: no
+fast-math and no contraction of multiply-add, so the oracle's sums are the textbook
+left-to-right ones.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.cpp")
+OUT = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["g++", "-std=c++17", "-O2", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", SRC, "-o", OUT + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)
