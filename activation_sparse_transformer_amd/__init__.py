@@ -1,0 +1,11 @@
+"""Activation-sparse ReLU FFN layer in TwELL form for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libsparse_ffn.so`` (hand-written HIP kernels behind a C ABI, see
+``include/sparse_ffn.h``); ``sparse_ffn`` is a thin ctypes binding to it.
+"""
+from .sparse_ffn import (  # noqa: F401
+    Config, SparseFFN, TwellBuffers, SffnError, twell_pack, twell_stats, check, buffer_sizes,
+    profile_enable, profile_reset, profile_read, lib, LIB_PATH,
+    SFFN_OK, SFFN_ERR_INVALID_ARGUMENT, SFFN_ERR_UNSUPPORTED, SFFN_ERR_BACKUP_OVERFLOW,
+    SFFN_ERR_DEVICE,
+)

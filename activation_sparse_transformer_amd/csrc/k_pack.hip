@@ -1,0 +1,330 @@
+// TwELL packing kernels for gfx950: the standalone pack of a dense fp32 hidden tensor,
+// the fp32 fused up-projection + ReLU + pack (small fp32 layers), the canonical ordering
+// of backup entries, and the statistics reduction.
+//
+// Format (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom CUDA
+// kernels solve"): the hidden columns are split into tiles of K columns; inside a tile
+// every token row keeps its nonzeros ELL-style (values plus local column indices, W slots);
+// the nonzeros that do not fit the W slots go to a small dense backup (the "sparse main
+// plus a few dense backups" hybrid of the same section), one K-wide slice per
+// overflowing tile-row.
+//
+// Work decomposition: one wave64 owns one (tile, 32-token group).  Each lane holds K/64
+// columns of every token of the group in registers; a token's tile-row is compacted with
+// ballot + mbcnt: the rank of a nonzero is the number of nonzeros at lower columns, so
+// slots come out in ascending column order with no shared-memory traffic.
+#include "sffn_common.hpp"
+
+namespace sffn {
+
+__global__ void zero_claim_kernel(int32_t* claim) {
+  if (threadIdx.x == 0) *claim = 0;
+}
+
+hipError_t launch_zero_claim(const Workspace& ws, hipStream_t s) {
+  hipLaunchKernelGGL(zero_claim_kernel, dim3(1), dim3(64), 0, s, ws.claim);
+  return hipGetLastError();
+}
+
+// Store one value of the TwELL value array in the layer dtype.
+template <bool BF16>
+__device__ __forceinline__ void store_val(void* base, size_t idx, float v) {
+  if constexpr (BF16) {
+    static_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
+  } else {
+    static_cast<float*>(base)[idx] = v;
+  }
+}
+
+// Values source of the pack: MODE_H reads a dense fp32 hidden tensor; MODE_UP computes
+// h = ReLU(x W_up^T + b) in fp32 on the fly (the fused forward of fp32 layers).
+enum { MODE_H = 0, MODE_UP = 1 };
+
+// One wave per (tile k, token group g).  4 waves per workgroup.
+template <int K, bool BF16, int MODE>
+__global__ __launch_bounds__(256) void pack_kernel(Dims d, const float* __restrict__ h,
+                                                   const float* __restrict__ x,
+                                                   const float* __restrict__ Wu,
+                                                   const float* __restrict__ bu,
+                                                   twell_buffers_t b, Workspace ws,
+                                                   float* __restrict__ zdump) {
+  constexpr int C = K / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= d.nt * d.ng) return;  // uniform per wave
+  const int k = wave / d.ng;
+  const int g = wave - k * d.ng;
+  const int t0 = g * GROUP;
+  const int T = d.T, W = d.W;
+
+  float v[GROUP][C];
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    const int t = t0 + i;
+    const bool valid = t < T;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int64_t n = (int64_t)k * K + c * 64 + lane;
+      float val = 0.0f;
+      if (valid) {
+        if constexpr (MODE == MODE_H) {
+          val = h[(int64_t)t * d.F + n];
+        } else {
+          const float* xr = x + (int64_t)t * d.D;
+          const float* wr = Wu + n * d.D;
+          float acc = 0.0f;
+          for (int i2 = 0; i2 < d.D; ++i2) acc = fmaf(xr[i2], wr[i2], acc);
+          acc += bu[n];
+          if (zdump) zdump[(int64_t)t * d.F + n] = acc;
+          val = acc > 0.0f ? acc : 0.0f;
+        }
+      }
+      v[i][c] = val;
+    }
+  }
+
+  // Phase 1: true count of every tile-row of the group; lane i keeps token i's count.
+  int cnt_lane = 0;
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) cnt += __popcll(ballot64(v[i][c] != 0.0f));
+    if (lane == i) cnt_lane = cnt;
+  }
+  // One staging claim for all of the group's overflowing tile-rows.
+  const uint64_t om = ballot64(lane < GROUP && cnt_lane > W);
+  const int n_ov = __popcll(om);
+  int base = 0;
+  if (n_ov > 0) {
+    if (lane == 0) base = atomicAdd(ws.claim, n_ov);
+    base = __shfl(base, 0);
+  }
+  if (lane == 0) ws.ov_grp[(int64_t)k * d.ng + g] = n_ov;
+
+  // Phase 2: write slots, padding, counts and the staged remainder.
+  int lr = 0;  // rank of the next overflowing tile-row inside the group
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    const int t = t0 + i;
+    if (t >= T) break;
+    const int cnt = __builtin_amdgcn_readlane(cnt_lane, i);
+    const bool over = cnt > W;
+    const int slot = base + lr;
+    const bool stage = over && slot < d.cap;
+    const size_t row = ((size_t)k * T + t) * (size_t)W;
+    int prefix = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bool nz = v[i][c] != 0.0f;
+      const uint64_t m = ballot64(nz);
+      const int r = prefix + mbcnt64(m);
+      prefix += __popcll(m);
+      const int col = c * 64 + lane;
+      if (nz && r < W) {
+        store_val<BF16>(b.vals, row + r, v[i][c]);
+        b.cols[row + r] = (uint8_t)col;
+      }
+      if (stage) store_val<BF16>(ws.stage_vals, (size_t)slot * K + col, (nz && r >= W) ? v[i][c] : 0.0f);
+    }
+    const int used = cnt < W ? cnt : W;
+    for (int s = used + lane; s < W; s += 64) {
+      store_val<BF16>(b.vals, row + s, 0.0f);
+      b.cols[row + s] = 0;
+    }
+    if (lane == 0) {
+      b.counts[(size_t)k * T + t] = (uint16_t)cnt;
+      if (stage) {
+        ws.stage_key[2 * slot] = k;
+        ws.stage_key[2 * slot + 1] = t | (lr << 24);
+      }
+    }
+    if (over) ++lr;
+  }
+}
+
+template <int K, bool BF16, int MODE>
+static hipError_t launch_pack_t(const Dims& d, const float* h, const float* x, const float* Wu,
+                                const float* bu, const twell_buffers_t& b, const Workspace& ws,
+                                float* zdump, hipStream_t s) {
+  const int waves = d.nt * d.ng;
+  const int blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((pack_kernel<K, BF16, MODE>), dim3(blocks), dim3(256), 0, s, d, h, x, Wu,
+                     bu, b, ws, zdump);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_pack_dispatch(const Dims& d, const float* h, const float* x,
+                                       const float* Wu, const float* bu,
+                                       const twell_buffers_t& b, const Workspace& ws,
+                                       float* zdump, hipStream_t s) {
+  if (d.bf16) {
+    switch (d.K) {
+      case 64: return launch_pack_t<64, true, MODE>(d, h, x, Wu, bu, b, ws, zdump, s);
+      case 128: return launch_pack_t<128, true, MODE>(d, h, x, Wu, bu, b, ws, zdump, s);
+      case 256: return launch_pack_t<256, true, MODE>(d, h, x, Wu, bu, b, ws, zdump, s);
+    }
+  } else {
+    switch (d.K) {
+      case 64: return launch_pack_t<64, false, MODE>(d, h, x, Wu, bu, b, ws, zdump, s);
+      case 128: return launch_pack_t<128, false, MODE>(d, h, x, Wu, bu, b, ws, zdump, s);
+      case 256: return launch_pack_t<256, false, MODE>(d, h, x, Wu, bu, b, ws, zdump, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack(const Dims& d, const float* h, const twell_buffers_t& b,
+                       const Workspace& ws, hipStream_t s) {
+  return launch_pack_dispatch<MODE_H>(d, h, nullptr, nullptr, nullptr, b, ws, nullptr, s);
+}
+
+hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, const float* bu,
+                              const twell_buffers_t& b, const Workspace& ws, float* zdump,
+                              hipStream_t s) {
+  return launch_pack_dispatch<MODE_UP>(d, nullptr, x, Wu, bu, b, ws, zdump, s);
+}
+
+// ---------------------------------------------------------------------------------------
+// Canonical backup order.  Producers stage overflowing tile-rows in claim order and
+// record, per (tile, group), how many overflowed and each entry's rank in its group.  The
+// final position of an entry of (k, t) is the exclusive prefix over (k, group) of those
+// counts, plus its rank: ascending (tile, token), the same for every run.
+//
+// Every workgroup scans the (small) counter array redundantly, then copies its share of
+// staged entries; workgroup 0 also writes bk_tile_ptr, bk_n and the status word.
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(1024) void order_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+  __shared__ int part[1024];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int N = d.nt * d.ng;
+  const int chunk = (N + 1023) / 1024;
+  int s = 0;
+  for (int q = tid * chunk, e = min(N, (tid + 1) * chunk); q < e; ++q) s += ws.ov_grp[q];
+  const int incl = wave_incl_scan(s);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int woff = 0;
+  for (int w = 0; w < wv; ++w) woff += wsum[w];
+  part[tid] = woff + incl - s;  // exclusive prefix of this thread's chunk
+  __syncthreads();
+  int total = 0;
+  for (int w = 0; w < 16; ++w) total += wsum[w];
+
+  auto prefix = [&](int p) -> int {  // sum of ov_grp[0 .. p)
+    if (p >= N) return total;
+    const int c = p / chunk;
+    int r = part[c];
+    for (int q = c * chunk; q < p; ++q) r += ws.ov_grp[q];
+    return r;
+  };
+
+  if (blockIdx.x == 0) {
+    for (int kk = tid; kk <= d.nt; kk += 1024) b.bk_tile_ptr[kk] = prefix(kk * d.ng);
+    if (tid == 0) {
+      *b.bk_n = total;
+      *b.status = total > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+    }
+  }
+
+  const int n_staged = min(*ws.claim, d.cap);
+  const int gw = blockIdx.x * 16 + wv;
+  const int nw = gridDim.x * 16;
+  constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;  // 32-bit words per slice
+  for (int e = gw; e < n_staged; e += nw) {
+    const int kk = ws.stage_key[2 * e];
+    const int tw = ws.stage_key[2 * e + 1];
+    const int t = tw & 0xFFFFFF, lr = tw >> 24;
+    const int fin = prefix(kk * d.ng + t / GROUP) + lr;
+    if (fin >= d.cap) continue;  // capacity exceeded: the status word reports it
+    const uint32_t* src = static_cast<const uint32_t*>(ws.stage_vals) + (size_t)e * WORDS;
+    uint32_t* dst = static_cast<uint32_t*>(b.bk_vals) + (size_t)fin * WORDS;
+    for (int q = lane; q < WORDS; q += 64) dst[q] = src[q];
+    if (lane == 0) {
+      b.bk_tile[fin] = kk;
+      b.bk_tok[fin] = t;
+    }
+  }
+}
+
+hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                        hipStream_t s) {
+  int blocks = (d.cap + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 64 ? 64 : blocks);
+#define SFFN_ORDER(KK, BB) \
+  hipLaunchKernelGGL((order_kernel<KK, BB>), dim3(blocks), dim3(1024), 0, s, d, b, ws)
+  if (d.bf16) {
+    if (d.K == 64) SFFN_ORDER(64, true);
+    else if (d.K == 128) SFFN_ORDER(128, true);
+    else SFFN_ORDER(256, true);
+  } else {
+    if (d.K == 64) SFFN_ORDER(64, false);
+    else if (d.K == 128) SFFN_ORDER(128, false);
+    else SFFN_ORDER(256, false);
+  }
+#undef SFFN_ORDER
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Statistics: one workgroup reduces the counts array.
+__global__ __launch_bounds__(1024) void stats_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+  __shared__ long long red[5][16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const size_t n = (size_t)d.nt * d.T;
+  long long nnz = 0, slots = 0, over = 0, bnz = 0, mx = 0;
+  for (size_t q = tid; q < n; q += 1024) {
+    const long long c = b.counts[q];
+    nnz += c;
+    slots += c < d.W ? c : d.W;
+    over += c > d.W ? 1 : 0;
+    bnz += c > d.W ? c - d.W : 0;
+    mx = c > mx ? c : mx;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    nnz += __shfl_xor(nnz, o);
+    slots += __shfl_xor(slots, o);
+    over += __shfl_xor(over, o);
+    bnz += __shfl_xor(bnz, o);
+    const long long m2 = __shfl_xor(mx, o);
+    mx = m2 > mx ? m2 : mx;
+  }
+  if (lane == 0) {
+    red[0][wv] = nnz; red[1][wv] = slots; red[2][wv] = over; red[3][wv] = bnz; red[4][wv] = mx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long a[5] = {0, 0, 0, 0, 0};
+    for (int w = 0; w < 16; ++w) {
+      for (int j = 0; j < 4; ++j) a[j] += red[j][w];
+      a[4] = red[4][w] > a[4] ? red[4][w] : a[4];
+    }
+    for (int j = 0; j < 5; ++j) ws.stats[j] = a[j];
+    ws.stats[5] = *b.bk_n;
+    ws.stats[6] = *b.status;
+    ws.stats[7] = 0;
+  }
+}
+
+hipError_t launch_stats(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, s, d, b, ws);
+  return hipGetLastError();
+}
+
+}  // namespace sffn

@@ -1,0 +1,385 @@
+// Fused up-projection + bias + ReLU + TwELL pack, bf16 MFMA on gfx950.
+//
+// z = x W_up^T + b (fp32 accumulation), h = z if z > 0 else 0, and h goes straight into
+// TwELL: the dense hidden tensor is never written to device memory (upppp.jp TwELL article
+// of 2026-05-11, section "What TwELL and the custom CUDA kernels solve": the inference
+// kernel builds the TwELL form on the fly; innovatopia.jp article, "Editor's commentary":
+// no extra memory traffic or kernel launches for the sparse format).
+//
+// Main loop (dense contraction, MFMA-bound):
+//   * workgroup tile 256 neurons x BM tokens (BM = 64*NB), 4 waves; wave (wn, wt) owns
+//     neurons [128*wn, 128*wn+128) x tokens [wt*BM/2, (wt+1)*BM/2) of the tile.
+//   * v_mfma_f32_32x32x16_bf16 with A = W_up rows (neurons) and B = x rows (tokens): both
+//     operands are contiguous along d_model, so both are read from LDS as 16-byte rows.
+//   * BK = 64; global -> register prefetch of the next k-slice while the current one is
+//     multiplied; LDS double buffer; 16-byte chunks XOR-swizzled by row so the 32 rows a
+//     wave reads at one column land in distinct banks.
+//   * workgroups are ordered in groups of 8 token blocks and dispatched so that the
+//     workgroups sharing an XCD's L2 cover a compact patch of the output.
+//
+// Epilogue (the TwELL pack, done on the accumulator registers):
+//   The 32x32 accumulator layout puts token n = lane%32 of a block in lanes n and n+32,
+//   each holding 16 of the block's 32 neurons (lane half h holds the neurons 8q+4h+i).
+//   Over the wave's 4 neuron blocks the lane pair holds all 128 neurons of the token,
+//   i.e. a whole 128-column tile-row.  Each lane builds a 64-bit mask of its positive
+//   pre-activations, swaps masks with its partner (lane ^ 32), and gets the rank of every
+//   nonzero - the number of nonzeros at lower columns - from popcounts.  No transpose of
+//   the hidden tile through LDS is needed.  Ranks < W are scattered into an LDS staging
+//   block that is then written out as contiguous TwELL rows; ranks >= W go to the staged
+//   backup slice of the tile-row.  Tiles of 64 columns are handled as two tiles per wave,
+//   tiles of 256 columns span the two waves with the same tokens (counts exchanged in LDS).
+#include "sffn_common.hpp"
+
+namespace sffn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int UP_BN = 256;  // neurons per workgroup
+constexpr int UP_BK = 64;   // d_model slice per LDS stage
+constexpr int UP_GM = 8;    // token blocks per ordering group
+
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+template <int K, int NB, bool DUMP>
+__global__ __launch_bounds__(256) void up_pack_bf16_kernel(
+    Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
+    const uint16_t* __restrict__ bu, twell_buffers_t b, Workspace ws, float* __restrict__ zdump) {
+  constexpr int BM = 64 * NB;            // tokens per workgroup
+  constexpr int HM = BM / 2;             // tokens per wave
+  constexpr int ALD = UP_BN * 8 / 256;   // 16-byte A pieces per thread per stage (8)
+  constexpr int BLD = BM * 8 / 256;      // 16-byte B pieces per thread per stage
+  constexpr int TPW = (K == 64) ? 2 : 1; // tile parts per wave
+  constexpr int NTWG = UP_BN / K;        // tiles per workgroup (4, 2, 1)
+
+  // LDS: the main loop's double buffer, reused after the loop for the TwELL staging.
+  constexpr int MAIN_BYTES = 2 * (UP_BN + BM) * 128;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN_BYTES];
+  __shared__ int part_cnt[2][32][2];   // K=256: per (wt, token) count of each wave half
+  __shared__ int claim_base[NTWG][2];  // staged-backup base per (tile, wt)
+  uint4* sA = reinterpret_cast<uint4*>(smem);                  // [2][UP_BN*8]
+  uint4* sB = reinterpret_cast<uint4*>(smem) + 2 * UP_BN * 8;  // [2][BM*8]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wt = wave >> 1;
+  const int T = d.T, D = d.D, W = d.W;
+
+  // ---- tile ordering (XCD-aware, grouped along tokens)
+  const int nN = d.F / UP_BN;
+  const int nM = (T + BM - 1) / BM;
+  const int total = nN * nM;
+  const int per_xcd = (total + 7) / 8;
+  const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (P >= total) return;
+  const int grp = P / (UP_GM * nN);
+  const int first_m = grp * UP_GM;
+  const int gsz = min(nM - first_m, UP_GM);
+  const int pin = P - grp * UP_GM * nN;
+  const int mb = first_m + pin % gsz;
+  const int nb = pin / gsz;
+  const int n0 = nb * UP_BN, m0 = mb * BM;
+
+  // ---- main loop
+  const size_t rowA = (size_t)D;  // elements per W_up / x row
+  const int pc = tid & 7;         // 16-byte piece within a 128-byte k-slice row
+  uint4 ra[ALD], rb[BLD];
+  auto gload = [&](int kt) {
+    const int k0 = kt * UP_BK + pc * 8;
+#pragma unroll
+    for (int q = 0; q < ALD; ++q) {
+      const int r = (q * 256 + tid) >> 3;
+      ra[q] = *reinterpret_cast<const uint4*>(Wu + (size_t)(n0 + r) * rowA + k0);
+    }
+#pragma unroll
+    for (int q = 0; q < BLD; ++q) {
+      const int r = (q * 256 + tid) >> 3;
+      int tok = m0 + r;
+      tok = tok < T ? tok : T - 1;
+      rb[q] = *reinterpret_cast<const uint4*>(x + (size_t)tok * rowA + k0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < ALD; ++q) {
+      const int r = (q * 256 + tid) >> 3;
+      sA[buf * UP_BN * 8 + r * 8 + (pc ^ (r & 7))] = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < BLD; ++q) {
+      const int r = (q * 256 + tid) >> 3;
+      sB[buf * BM * 8 + r * 8 + (pc ^ (r & 7))] = rb[q];
+    }
+  };
+
+  floatx16 acc[4][NB];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][bb][r] = 0.0f;
+
+  const int nk = D / UP_BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int l32 = lane & 31, lh = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint4* A = sA + buf * UP_BN * 8;
+    const uint4* B = sB + buf * BM * 8;
+#pragma unroll
+    for (int kk = 0; kk < UP_BK / 16; ++kk) {
+      const int ch = kk * 2 + lh;
+      bf16x8_t fa[4], fb[NB];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r = wn * 128 + a * 32 + l32;
+        fa[a] = __builtin_bit_cast(bf16x8_t, A[r * 8 + (ch ^ (r & 7))]);
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const int r = wt * HM + bb * 32 + l32;
+        fb[bb] = __builtin_bit_cast(bf16x8_t, B[r * 8 + (ch ^ (r & 7))]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[bb], acc[a][bb], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  // Own element e = a*16 + r holds wave-local neuron nl = a*32 + 8*(r>>2) + 4*lh + (r&3);
+  // e ascending <=> nl ascending among this lane's elements.
+  float bias[4][16];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = a * 32 + 8 * q + 4 * lh;
+      const uint2 bw = *reinterpret_cast<const uint2*>(bu + n0 + wn * 128 + nl);
+      bias[a][4 * q + 0] = __uint_as_float(bw.x << 16);
+      bias[a][4 * q + 1] = __uint_as_float(bw.x & 0xFFFF0000u);
+      bias[a][4 * q + 2] = __uint_as_float(bw.y << 16);
+      bias[a][4 * q + 3] = __uint_as_float(bw.y & 0xFFFF0000u);
+    }
+
+  // staging: vals [NTWG][2 wt][32 tok][W] bf16, cols [NTWG][2][32][W] u8
+  uint16_t* st_vals = reinterpret_cast<uint16_t*>(smem);
+  uint8_t* st_cols = smem + (size_t)NTWG * 2 * 32 * W * 2;
+  const int st_words = NTWG * 2 * 32 * W * 3 / 4;  // W*3*64*NTWG bytes, multiple of 4
+
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const int tokblk = m0 + wt * HM + bb * 32;  // first token of this 32-token block
+    const int tok = tokblk + l32;
+    const bool valid = tok < T;
+    const int g = tokblk / GROUP;
+
+    // (1) clear the staging block
+    __syncthreads();
+    for (int q = tid; q < st_words; q += 256) reinterpret_cast<uint32_t*>(smem)[q] = 0u;
+
+    // (2) positive mask of this lane's 64 elements
+    uint64_t own = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float z = acc[a][bb][r] + bias[a][r];
+        if (DUMP && valid)
+          zdump[(size_t)tok * d.F + n0 + wn * 128 + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = z;
+        own |= (uint64_t)(valid && z > 0.0f) << (a * 16 + r);
+      }
+    const uint32_t pm_lo = __shfl_xor((uint32_t)own, 32);
+    const uint32_t pm_hi = __shfl_xor((uint32_t)(own >> 32), 32);
+    const uint64_t pm = ((uint64_t)pm_hi << 32) | pm_lo;
+
+    // (3) per tile part: count, rank base, overflow
+    // tile part j of this wave covers own/partner bits tmask[j]
+    uint64_t tmask[TPW];
+    if constexpr (TPW == 2) {
+      tmask[0] = 0x00000000FFFFFFFFull;
+      tmask[1] = 0xFFFFFFFF00000000ull;
+    } else {
+      tmask[0] = ~0ull;
+    }
+    int part[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) part[j] = popc64(own & tmask[j]) + popc64(pm & tmask[j]);
+    if constexpr (K == 256) {
+      if (lh == 0) part_cnt[wt][l32][wn] = part[0];
+    }
+    __syncthreads();
+    int tot[TPW], rbase[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if constexpr (K == 256) {
+        const int c0 = part_cnt[wt][l32][0], c1 = part_cnt[wt][l32][1];
+        tot[j] = c0 + c1;
+        rbase[j] = wn ? c0 : 0;
+      } else {
+        tot[j] = part[j];
+        rbase[j] = 0;
+      }
+    }
+    // global tile index and in-workgroup tile slot of part j
+    int ktile[TPW], jslot[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if constexpr (K == 64) jslot[j] = 2 * wn + j;
+      else if constexpr (K == 128) jslot[j] = wn;
+      else jslot[j] = 0;
+      ktile[j] = n0 / K + jslot[j];
+    }
+    const bool owner = (K != 256) || (wn == 0);
+    int lrank[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const uint64_t om = __ballot(lane < 32 && tot[j] > W);
+      lrank[j] = popc64(om & ((1ull << l32) - 1ull));
+      const int n_ov = popc64(om);
+      if (owner && lane == 0) {
+        claim_base[jslot[j]][wt] = n_ov > 0 ? atomicAdd(ws.claim, n_ov) : 0;
+        if (tokblk < T) ws.ov_grp[(size_t)ktile[j] * d.ng + g] = n_ov;  // g < ng
+      }
+    }
+    __syncthreads();
+
+    // (4) scatter: main slots into the staging block, remainder into the staged backup
+    int slot[TPW];
+    bool stage[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      slot[j] = claim_base[jslot[j]][wt] + lrank[j];
+      stage[j] = tot[j] > W && slot[j] < d.cap;
+    }
+    int run[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) run[j] = 0;
+#pragma unroll
+    for (int gi = 0; gi < 16; ++gi) {
+      const int j = (TPW == 2) ? (gi >> 3) : 0;
+      // partner nonzeros in this tile part at lower columns than this group
+      const int shiftp = 4 * (gi + lh);
+      const uint64_t pbelow = (shiftp >= 64 ? ~0ull : ((1ull << shiftp) - 1ull)) & tmask[j];
+      const int pb = popc64(pm & pbelow);
+      uint16_t stbuf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = gi * 4 + i;
+        const int a = e >> 4, r = e & 15;
+        const float z = acc[a][bb][r] + bias[a][r];
+        const bool nz = (own >> e) & 1ull;
+        const int rank = rbase[j] + run[j] + pb;
+        run[j] += nz ? 1 : 0;
+        const int nl = a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        int col;
+        if constexpr (K == 64) col = nl - 64 * j;
+        else if constexpr (K == 128) col = nl;
+        else col = wn * 128 + nl;
+        const uint16_t zb = f32_to_bf16(z);
+        if (nz && rank < W) {
+          const int sidx = ((jslot[j] * 2 + wt) * 32 + l32) * W + rank;
+          st_vals[sidx] = zb;
+          st_cols[sidx] = (uint8_t)col;
+        }
+        stbuf[i] = (nz && rank >= W) ? zb : (uint16_t)0;
+      }
+      if (stage[j]) {
+        // 4 consecutive columns: col of i=0 .. i=3
+        const int nl0 = (gi >> 2) * 32 + 8 * (gi & 3) + 4 * lh;
+        int col0;
+        if constexpr (K == 64) col0 = nl0 - 64 * j;
+        else if constexpr (K == 128) col0 = nl0;
+        else col0 = wn * 128 + nl0;
+        uint2 pk;
+        pk.x = (uint32_t)stbuf[0] | ((uint32_t)stbuf[1] << 16);
+        pk.y = (uint32_t)stbuf[2] | ((uint32_t)stbuf[3] << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(ws.stage_vals) + (size_t)slot[j] * K + col0) = pk;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      if (valid && lh == 0 && owner) {
+        b.counts[(size_t)ktile[j] * T + tok] = (uint16_t)tot[j];
+        if (stage[j]) {
+          ws.stage_key[2 * slot[j]] = ktile[j];
+          ws.stage_key[2 * slot[j] + 1] = tok | (lrank[j] << 24);
+        }
+      }
+    }
+    __syncthreads();
+
+    // (5) copy the staging block out: for each (tile slot, wt) a contiguous run of
+    // nvalid*W values and columns.
+#pragma unroll
+    for (int js = 0; js < NTWG; ++js)
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const int tb0 = m0 + w2 * HM + bb * 32;
+        int nv = T - tb0;
+        nv = nv < 0 ? 0 : (nv > 32 ? 32 : nv);
+        if (nv == 0) continue;
+        const int kt_g = n0 / K + js;
+        const size_t gbase = ((size_t)kt_g * T + tb0) * (size_t)W;
+        const int sbase = (js * 2 + w2) * 32 * W;
+        const int n_el = nv * W;
+        uint16_t* gv = static_cast<uint16_t*>(b.vals) + gbase;
+        uint8_t* gc = b.cols + gbase;
+        if ((W & 7) == 0) {
+          for (int q = tid; q < n_el / 8; q += 256)
+            reinterpret_cast<uint4*>(gv)[q] = reinterpret_cast<const uint4*>(st_vals + sbase)[q];
+        } else {
+          for (int q = tid; q < n_el; q += 256) gv[q] = st_vals[sbase + q];
+        }
+        if ((W & 15) == 0) {
+          for (int q = tid; q < n_el / 16; q += 256)
+            reinterpret_cast<uint4*>(gc)[q] = reinterpret_cast<const uint4*>(st_cols + sbase)[q];
+        } else {
+          for (int q = tid; q < n_el; q += 256) gc[q] = st_cols[sbase + q];
+        }
+      }
+  }
+}
+
+template <int K, int NB>
+static hipError_t launch_up_t(const Dims& d, const uint16_t* x, const uint16_t* Wu,
+                              const uint16_t* bu, const twell_buffers_t& b, const Workspace& ws,
+                              float* zdump, hipStream_t s) {
+  constexpr int BM = 64 * NB;
+  const int nN = d.F / UP_BN;
+  const int nM = (d.T + BM - 1) / BM;
+  const int total = nN * nM;
+  const int per_xcd = (total + 7) / 8;
+  if (zdump)
+    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, true>), dim3(8 * per_xcd), dim3(256), 0, s, d,
+                       x, Wu, bu, b, ws, zdump);
+  else
+    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, false>), dim3(8 * per_xcd), dim3(256), 0, s,
+                       d, x, Wu, bu, b, ws, zdump);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
+                               const uint16_t* bu, const twell_buffers_t& b,
+                               const Workspace& ws, float* zdump, hipStream_t s) {
+  // 256-token workgroups when there are enough of them to fill the chip, else 128.
+  const bool big = (long long)(d.F / UP_BN) * ((d.T + 255) / 256) >= 512;
+  switch (d.K) {
+    case 64: return big ? launch_up_t<64, 4>(d, x, Wu, bu, b, ws, zdump, s)
+                        : launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 128: return big ? launch_up_t<128, 4>(d, x, Wu, bu, b, ws, zdump, s)
+                         : launch_up_t<128, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 256: return big ? launch_up_t<256, 4>(d, x, Wu, bu, b, ws, zdump, s)
+                         : launch_up_t<256, 2>(d, x, Wu, bu, b, ws, zdump, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sffn

@@ -1,0 +1,356 @@
+// Host side of the C ABI declared in include/sparse_ffn.h: argument validation (always
+// before any HIP call), buffer sizing, launch sequencing on the caller's stream, status
+// reporting and the optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "sffn_common.hpp"
+
+using namespace sffn;
+
+struct sparse_ffn {
+  sffn_config_t cfg;
+  const void* W_up;
+  const void* b_up;
+  const void* W_down;
+};
+
+namespace {
+
+#define SFFN_TRY_INNER(expr)                 \
+  do {                                       \
+    const sffn_status_t s__ = (expr);        \
+    if (s__ != SFFN_OK) return s__;          \
+  } while (0)
+
+thread_local std::string g_last_error;
+
+sffn_status_t fail(sffn_status_t s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+sffn_status_t dev_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return SFFN_ERR_DEVICE;
+}
+
+// ------------------------------------------------------------------ profiling
+struct ProfRec {
+  std::string name;
+  hipEvent_t e0, e1;
+};
+struct Prof {
+  bool enabled = false;
+  std::vector<ProfRec> recs;
+  ~Prof() { clear(); }
+  void clear() {
+    for (auto& r : recs) {
+      (void)hipEventDestroy(r.e0);
+      (void)hipEventDestroy(r.e1);
+    }
+    recs.clear();
+  }
+};
+thread_local Prof g_prof;
+
+// Launch `f` (returns hipError_t) under the kernel name `name`.
+template <typename Fn>
+sffn_status_t run(const char* name, hipStream_t s, Fn&& f) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (g_prof.enabled) {
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess ||
+        hipEventRecord(e0, s) != hipSuccess)
+      return dev_fail(hipGetLastError(), "profiling event");
+  }
+  const hipError_t err = f();
+  if (g_prof.enabled) {
+    (void)hipEventRecord(e1, s);
+    g_prof.recs.push_back({name, e0, e1});
+  }
+  if (err != hipSuccess) return dev_fail(err, name);
+  return SFFN_OK;
+}
+
+// ------------------------------------------------------------------ validation
+sffn_status_t check_cfg(const sffn_config_t* c) {
+  if (!c) return fail(SFFN_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->dtype != SFFN_F32 && c->dtype != SFFN_BF16)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "dtype must be SFFN_F32 or SFFN_BF16");
+  if (c->tile != 64 && c->tile != 128 && c->tile != 256)
+    return fail(SFFN_ERR_UNSUPPORTED, "tile must be 64, 128 or 256");
+  if (c->ell_width < 1 || c->ell_width > c->tile)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "ell_width must be in [1, tile]");
+  if (c->d_model <= 0 || c->d_ff <= 0)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "d_model and d_ff must be positive");
+  if (c->d_ff % c->tile != 0)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "d_ff must be a multiple of tile");
+  if (c->d_model % 64 != 0) return fail(SFFN_ERR_UNSUPPORTED, "d_model must be a multiple of 64");
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 24))
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "max_tokens must be in [1, 2^24]");
+  if (c->backup_capacity < 0) return fail(SFFN_ERR_INVALID_ARGUMENT, "backup_capacity < 0");
+  const long long nt = c->d_ff / c->tile;
+  if ((long long)c->backup_capacity > nt * (long long)c->max_tokens)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "backup_capacity exceeds the number of tile-rows");
+  const long long esz = c->dtype == SFFN_BF16 ? 2 : 4;
+  if (nt * (long long)c->max_tokens * c->ell_width * esz >= (1LL << 31) ||
+      (long long)c->backup_capacity * c->tile * esz >= (1LL << 31))
+    return fail(SFFN_ERR_UNSUPPORTED, "TwELL and backup arrays must each stay below 2 GiB");
+  return SFFN_OK;
+}
+
+// Extra shape constraints of the layer kernels (up-projection and down-projection).
+sffn_status_t check_layer_cfg(const sffn_config_t* c) {
+  SFFN_TRY_INNER(check_cfg(c));
+  if (c->dtype == SFFN_BF16 && c->d_model % 128 != 0)
+    return fail(SFFN_ERR_UNSUPPORTED, "bf16 layers need d_model to be a multiple of 128");
+  if (c->dtype == SFFN_BF16 && c->d_ff % 256 != 0)
+    return fail(SFFN_ERR_UNSUPPORTED, "bf16 layers need d_ff to be a multiple of 256");
+  return SFFN_OK;
+}
+
+sffn_status_t check_T(const sffn_config_t* c, int32_t T) {
+  if (T < 1 || T > c->max_tokens)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "T must be in [1, max_tokens]");
+  return SFFN_OK;
+}
+
+Dims make_dims(const sffn_config_t* c, int32_t T) {
+  Dims d;
+  d.D = c->d_model;
+  d.F = c->d_ff;
+  d.K = c->tile;
+  d.W = c->ell_width;
+  d.T = T;
+  d.nt = c->d_ff / c->tile;
+  d.ng = (T + GROUP - 1) / GROUP;
+  d.cap = c->backup_capacity;
+  d.bf16 = c->dtype == SFFN_BF16;
+  d.esz = d.bf16 ? 2 : 4;
+  return d;
+}
+
+sffn_status_t check_bufs(const twell_buffers_t* b, bool need_all) {
+  if (!b) return fail(SFFN_ERR_INVALID_ARGUMENT, "buffers struct is NULL");
+  if (!b->counts || !b->vals || !b->cols || !b->bk_tile_ptr || !b->bk_n || !b->status)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "a TwELL buffer pointer is NULL");
+  if (!b->bk_tile || !b->bk_tok || !b->bk_vals)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "a backup buffer pointer is NULL");
+  if (need_all && !b->workspace) return fail(SFFN_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  return SFFN_OK;
+}
+
+#define SFFN_TRY(expr)                       \
+  do {                                       \
+    const sffn_status_t s__ = (expr);        \
+    if (s__ != SFFN_OK) return s__;          \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* sffn_status_string(sffn_status_t s) {
+  switch (s) {
+    case SFFN_OK: return "SFFN_OK";
+    case SFFN_ERR_INVALID_ARGUMENT: return "SFFN_ERR_INVALID_ARGUMENT";
+    case SFFN_ERR_UNSUPPORTED: return "SFFN_ERR_UNSUPPORTED";
+    case SFFN_ERR_BACKUP_OVERFLOW: return "SFFN_ERR_BACKUP_OVERFLOW";
+    case SFFN_ERR_DEVICE: return "SFFN_ERR_DEVICE";
+  }
+  return "SFFN_UNKNOWN_STATUS";
+}
+
+const char* sffn_last_error(void) { return g_last_error.c_str(); }
+
+sffn_status_t twell_buffer_sizes(const sffn_config_t* cfg, int32_t T, twell_buffer_sizes_t* out) {
+  SFFN_TRY(check_cfg(cfg));
+  SFFN_TRY(check_T(cfg, T));
+  if (!out) return fail(SFFN_ERR_INVALID_ARGUMENT, "out is NULL");
+  const Dims d = make_dims(cfg, T);
+  const size_t slots = (size_t)d.nt * T * d.W;
+  const size_t cap = d.cap > 0 ? d.cap : 1;
+  out->counts = sizeof(uint16_t) * (size_t)d.nt * T;
+  out->vals = (size_t)d.esz * slots;
+  out->cols = slots;
+  out->bk_tile = sizeof(int32_t) * cap;
+  out->bk_tok = sizeof(int32_t) * cap;
+  out->bk_vals = (size_t)d.esz * cap * d.K;
+  out->bk_tile_ptr = sizeof(int32_t) * (size_t)(d.nt + 1);
+  out->bk_n = sizeof(int32_t);
+  out->status = sizeof(int32_t);
+  out->workspace = workspace_bytes(d);
+  return SFFN_OK;
+}
+
+sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* W_up, const void* b_up,
+                                const void* W_down, sparse_ffn_t* out) {
+  SFFN_TRY(check_layer_cfg(cfg));
+  if (!W_up || !b_up || !W_down || !out)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "NULL weight or output pointer");
+  sparse_ffn* h = new (std::nothrow) sparse_ffn;
+  if (!h) return fail(SFFN_ERR_DEVICE, "host allocation failed");
+  h->cfg = *cfg;
+  h->W_up = W_up;
+  h->b_up = b_up;
+  h->W_down = W_down;
+  *out = h;
+  return SFFN_OK;
+}
+
+sffn_status_t sparse_ffn_destroy(sparse_ffn_t h) {
+  delete h;
+  return SFFN_OK;
+}
+
+sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
+                         const twell_buffers_t* buf, void* stream) {
+  SFFN_TRY(check_cfg(cfg));
+  SFFN_TRY(check_T(cfg, T));
+  if (!h) return fail(SFFN_ERR_INVALID_ARGUMENT, "h is NULL");
+  SFFN_TRY(check_bufs(buf, true));
+  const Dims d = make_dims(cfg, T);
+  const Workspace ws = carve(buf->workspace, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SFFN_TRY(run("zero", s, [&] { return launch_zero_claim(ws, s); }));
+  SFFN_TRY(run("pack", s, [&] { return launch_pack(d, h, *buf, ws, s); }));
+  SFFN_TRY(run("order", s, [&] { return launch_order(d, *buf, ws, s); }));
+  return SFFN_OK;
+}
+
+static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, void* y,
+                                  const twell_buffers_t* act, float* z, void* stream) {
+  if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  SFFN_TRY(check_T(&hd->cfg, T));
+  if (!x || !y) return fail(SFFN_ERR_INVALID_ARGUMENT, "x or y is NULL");
+  SFFN_TRY(check_bufs(act, true));
+  const Dims d = make_dims(&hd->cfg, T);
+  const Workspace ws = carve(act->workspace, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SFFN_TRY(run("zero", s, [&] { return launch_zero_claim(ws, s); }));
+  if (d.bf16) {
+    SFFN_TRY(run("up_pack", s, [&] {
+      return launch_up_pack_bf16(d, static_cast<const uint16_t*>(x),
+                                 static_cast<const uint16_t*>(hd->W_up),
+                                 static_cast<const uint16_t*>(hd->b_up), *act, ws, z, s);
+    }));
+  } else {
+    SFFN_TRY(run("up_pack", s, [&] {
+      return launch_up_pack_f32(d, static_cast<const float*>(x),
+                                static_cast<const float*>(hd->W_up),
+                                static_cast<const float*>(hd->b_up), *act, ws, z, s);
+    }));
+  }
+  SFFN_TRY(run("order", s, [&] { return launch_order(d, *act, ws, s); }));
+  SFFN_TRY(run("down", s, [&] { return launch_down(d, *act, hd->W_down, y, s); }));
+  return SFFN_OK;
+}
+
+sffn_status_t sparse_ffn_forward(sparse_ffn_t hd, const void* x, int32_t T, void* y,
+                                 const twell_buffers_t* act, void* stream) {
+  return forward_impl(hd, x, T, y, act, nullptr, stream);
+}
+
+sffn_status_t sparse_ffn_forward_dump(sparse_ffn_t hd, const void* x, int32_t T, void* y,
+                                      const twell_buffers_t* act, float* z, void* stream) {
+  if (!z) return fail(SFFN_ERR_INVALID_ARGUMENT, "z is NULL");
+  return forward_impl(hd, x, T, y, act, z, stream);
+}
+
+sffn_status_t sparse_ffn_down(sparse_ffn_t hd, const twell_buffers_t* act, int32_t T, void* y,
+                              void* stream) {
+  if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  SFFN_TRY(check_T(&hd->cfg, T));
+  if (!y) return fail(SFFN_ERR_INVALID_ARGUMENT, "y is NULL");
+  SFFN_TRY(check_bufs(act, false));
+  const Dims d = make_dims(&hd->cfg, T);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SFFN_TRY(run("down", s, [&] { return launch_down(d, *act, hd->W_down, y, s); }));
+  return SFFN_OK;
+}
+
+sffn_status_t twell_stats(const sffn_config_t* cfg, const twell_buffers_t* buf, int32_t T,
+                          twell_stats_t* out, void* stream) {
+  SFFN_TRY(check_cfg(cfg));
+  SFFN_TRY(check_T(cfg, T));
+  SFFN_TRY(check_bufs(buf, true));
+  if (!out) return fail(SFFN_ERR_INVALID_ARGUMENT, "out is NULL");
+  const Dims d = make_dims(cfg, T);
+  const Workspace ws = carve(buf->workspace, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SFFN_TRY(run("stats", s, [&] { return launch_stats(d, *buf, ws, s); }));
+  long long host[8];
+  hipError_t e = hipMemcpyAsync(host, ws.stats, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return dev_fail(e, "stats copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return dev_fail(e, "stats sync");
+  std::memset(out, 0, sizeof(*out));
+  out->nnz = host[0];
+  out->slots_used = host[1];
+  out->overflow_tile_rows = host[2];
+  out->backup_nonzeros = host[3];
+  out->max_count = (int32_t)host[4];
+  out->backup_needed = host[5];
+  out->backup_overflowed = host[6] != 0 ? 1 : 0;
+  const double cells = (double)T * d.F;
+  out->density = cells > 0 ? (double)out->nnz / cells : 0.0;
+  const double slots = (double)d.nt * T * d.W;
+  out->ell_fill = slots > 0 ? (double)out->slots_used / slots : 0.0;
+  out->bytes_main = (int64_t)d.nt * T * (2 + (int64_t)d.W * (d.esz + 1));
+  const long long used = host[5] < d.cap ? host[5] : d.cap;
+  out->bytes_backup = used * ((int64_t)d.K * d.esz + 8);
+  out->bytes_dense_equiv = (int64_t)T * d.F * d.esz;
+  if (out->backup_overflowed)
+    return fail(SFFN_ERR_BACKUP_OVERFLOW, "backup capacity exceeded: outputs are undefined");
+  return SFFN_OK;
+}
+
+sffn_status_t sparse_ffn_check(const twell_buffers_t* buf, void* stream) {
+  if (!buf || !buf->status) return fail(SFFN_ERR_INVALID_ARGUMENT, "status buffer is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t st = 0;
+  hipError_t e = hipMemcpyAsync(&st, buf->status, sizeof(st), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return dev_fail(e, "status copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return dev_fail(e, "status sync");
+  if (st == SFFN_ERR_BACKUP_OVERFLOW)
+    return fail(SFFN_ERR_BACKUP_OVERFLOW, "backup capacity exceeded: outputs are undefined");
+  if (st != 0) return fail(SFFN_ERR_DEVICE, "unexpected device status word");
+  return SFFN_OK;
+}
+
+sffn_status_t sffn_profile_enable(int32_t enable) {
+  g_prof.enabled = enable != 0;
+  return SFFN_OK;
+}
+
+sffn_status_t sffn_profile_reset(void) {
+  g_prof.clear();
+  return SFFN_OK;
+}
+
+sffn_status_t sffn_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(SFFN_ERR_INVALID_ARGUMENT, "NULL argument");
+  double sum = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_prof.recs) {
+    if (r.name != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.e1);
+    if (e != hipSuccess) return dev_fail(e, "profile sync");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, r.e0, r.e1);
+    if (e != hipSuccess) return dev_fail(e, "profile elapsed");
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return SFFN_OK;
+}
+
+}  // extern "C"

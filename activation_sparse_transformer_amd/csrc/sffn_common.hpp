@@ -1,0 +1,111 @@
+// Internal definitions shared by the HIP kernels and the host launch code of the TwELL
+// sparse FFN library (gfx950).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sparse_ffn.h"
+
+namespace sffn {
+
+// Token group of the per-(tile, group) overflow counters.  Every kernel that writes a
+// TwELL also writes, for each tile k and each group of GROUP consecutive tokens, how many
+// of the group's tile-rows overflow (count > W), and tags each staged backup entry with
+// its rank inside the group.  An exclusive scan over (k, group) then gives every entry
+// its canonical position in ascending (tile, token) order, independent of the order in
+// which entries were staged.
+constexpr int GROUP = 32;
+
+struct Dims {
+  int32_t D, F, K, W, T;
+  int32_t nt;   // F / K tiles
+  int32_t ng;   // ceil(T / GROUP) token groups
+  int32_t cap;  // backup capacity (entries)
+  int32_t esz;  // bytes per TwELL value (2 bf16, 4 fp32)
+  bool bf16;
+};
+
+// Workspace carving.  Regions are 256-byte aligned.
+struct Workspace {
+  int32_t* claim;       // [1]      staging slots claimed so far
+  int32_t* ov_grp;      // [nt*ng]  overflowing tile-rows per (tile, group)
+  int32_t* stage_key;   // [2*cap]  (tile, token | rank_in_group << 24)
+  void* stage_vals;     // [cap*K]  dtype
+  long long* stats;     // [8]      stats reduction output
+};
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+inline size_t workspace_bytes(const Dims& d) {
+  size_t n = 0;
+  n += align256(sizeof(int32_t));
+  n += align256(sizeof(int32_t) * (size_t)d.nt * d.ng);
+  n += align256(sizeof(int32_t) * 2 * (size_t)(d.cap > 0 ? d.cap : 1));
+  n += align256((size_t)d.esz * (size_t)(d.cap > 0 ? d.cap : 1) * d.K);
+  n += align256(sizeof(long long) * 8);
+  return n;
+}
+
+inline Workspace carve(void* base, const Dims& d) {
+  char* p = static_cast<char*>(base);
+  Workspace w;
+  w.claim = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t));
+  w.ov_grp = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * (size_t)d.nt * d.ng);
+  w.stage_key = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * 2 * (size_t)(d.cap > 0 ? d.cap : 1));
+  w.stage_vals = p;
+  p += align256((size_t)d.esz * (size_t)(d.cap > 0 ? d.cap : 1) * d.K);
+  w.stats = reinterpret_cast<long long*>(p);
+  return w;
+}
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIPCC__)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round to nearest, ties to even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+// Number of set bits of `m` in lanes below this one.
+__device__ __forceinline__ int mbcnt64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+// Load through the constant address space: for a wave-uniform address of memory that no
+// kernel of the launch writes, this becomes a scalar (SMEM) load into SGPRs.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  typedef const __attribute__((address_space(4))) T* cptr;
+  return *(cptr)(uintptr_t)p;
+}
+#endif
+
+// ---------------------------------------------------------------- launchers
+// Each returns the launch's hipError_t (hipGetLastError after the launch).
+hipError_t launch_zero_claim(const Workspace& ws, hipStream_t s);
+hipError_t launch_pack(const Dims& d, const float* h, const twell_buffers_t& b,
+                       const Workspace& ws, hipStream_t s);
+hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                        hipStream_t s);
+hipError_t launch_stats(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                        hipStream_t s);
+hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, const float* bu,
+                              const twell_buffers_t& b, const Workspace& ws, float* zdump,
+                              hipStream_t s);
+hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
+                               const uint16_t* bu, const twell_buffers_t& b,
+                               const Workspace& ws, float* zdump, hipStream_t s);
+hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
+                       hipStream_t s);
+
+}  // namespace sffn

@@ -1,0 +1,234 @@
+"""Benchmark: FFN-layer tokens/s of the fused TwELL sparse FFN vs a dense bf16 FFN.
+
+One "step" is one pass of the whole forward hot path over one batch: the fused MFMA
+up-projection with its bias + ReLU + TwELL-pack epilogue, the canonical backup
+ordering, and the sparse down-projection (library call sparse_ffn_forward).
+
+Workload: the 1.5B-like ReLU FFN layer, bf16, T = 8192 tokens (16 x 512), d_model 2048,
+d_ff 8192, tile 128, ELL width 32, density 5%, 1% of tokens with inputs x3; seeded
+synthetic inputs (gen/layers.py), resident in device memory before timing starts.
+The other densities of the sweep (1/10/20%) and the dense bf16 FFN (torch -> hipBLASLt)
+are reported next to it.  Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FFN-layer tokens/s, fused TwELL vs dense bf16 FFN, at 1-20% density"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MAC (dot2) x 2.4 GHz
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "activation_sparse_transformer_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rho", type=float, default=0.05, help="density of the headline point")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the layer shards by tokens with no exchange, "
+              "so a multi-GPU figure is the one-GPU figure times N; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import torch.nn.functional as Fn
+    import activation_sparse_transformer_amd as sffn
+    from gen import CONFIGS, make_layer, bias_for_density
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    base = CONFIGS["C3"]
+    log("generating the 1.5B-like layer")
+    L0 = make_layer(base, seed=0, rho=args.rho)
+    c = L0["cfg"]
+    T, D, F = c.T, c.D, c.F
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = bf16_dev(L0["x"])
+    Wu = bf16_dev(L0["W_up"])
+    Wd = bf16_dev(L0["W_down"])
+    cap = c.n_tiles * T // 8
+    cfg = sffn.Config(d_model=D, d_ff=F, tile=c.tile, ell_width=c.ell_width, max_tokens=T,
+                      backup_capacity=cap, dtype="bf16")
+    act = sffn.TwellBuffers(cfg, T, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def time_steps(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def sparse_point(rho, steps, warmup, profile=False):
+        L = bias_for_density(L0, rho)
+        b = bf16_dev(L["b_up"])
+        layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+        fn = lambda: layer.forward(x, act=act, y=y)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        if profile:
+            sffn.profile_reset()
+            sffn.profile_enable(True)
+        ms, wall = time_steps(fn, steps, 0)
+        kt = {}
+        if profile:
+            sffn.profile_enable(False)
+            for k in ("zero", "up_pack", "order", "down"):
+                tot, n = sffn.profile_read(k)
+                kt[k] = tot / max(n, 1)
+            sffn.profile_reset()
+        st = sffn.twell_stats(cfg, act)
+        return ms, wall, kt, st, b
+
+    # ---- headline point (timed region, per-kernel HIP events on the launch stream)
+    log(f"sparse forward, rho={args.rho}, {args.warmup} warmup + {args.steps} timed steps")
+    ms, wall, kt, st, b0 = sparse_point(args.rho, args.steps, args.warmup, profile=True)
+    ms_plain, _, _, _, _ = sparse_point(args.rho, args.steps, 2, profile=False)
+    log(f"  {ms:.4f} ms/step (profiled), {ms_plain:.4f} ms/step (no events); kernels {kt}")
+
+    # ---- dense bf16 FFN baseline (hipBLASLt through torch), same inputs and stream
+    def dense():
+        h = Fn.relu(Fn.linear(x, Wu, b0))
+        return torch.matmul(h, Wd)
+    log("dense bf16 FFN baseline")
+    ms_dense, _ = time_steps(dense, args.steps, args.warmup)
+    log(f"  {ms_dense:.4f} ms/step")
+
+    # ---- density sweep
+    sweep = []
+    if not args.no_sweep:
+        for rho in (0.01, 0.05, 0.10, 0.20):
+            m, _, k2, s2, _ = sparse_point(rho, max(10, args.steps // 2), 3, profile=True)
+            sweep.append({"rho_target": rho, "density": round(s2["density"], 5),
+                          "overflow_tile_rows": int(s2["overflow_tile_rows"]),
+                          "ms_per_step": round(m, 4), "tokens_per_s": round(T / (m * 1e-3), 1),
+                          "dense_tokens_per_s": round(T / (ms_dense * 1e-3), 1),
+                          "speedup_vs_dense": round(ms_dense / m, 4),
+                          "kernel_ms": {k: round(v, 4) for k, v in k2.items()}})
+            log(f"  sweep rho={rho}: {m:.4f} ms, density {s2['density']:.4f}, {k2}")
+
+    # ---- roofline of the dominant kernel (the fused up-projection, MFMA-bound)
+    up_ms = kt["up_pack"]
+    up_flops = 2.0 * T * D * F
+    achieved = up_flops / (up_ms * 1e-3) / 1e12
+    traffic = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        tc = json.load(open(TRAFFIC_FILE))
+        ent = tc.get("up_pack")
+        if ent and ent.get("source_hash") == src_hash and ent.get("workload") == "C3-5%":
+            traffic = ent["bytes_per_launch"]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "up_pack_bf16_kernel (fused up-projection + ReLU + TwELL pack)",
+                "avg_launch_ms": round(up_ms, 5), "algorithmic_flops_per_launch": up_flops}
+    # second kernel: the sparse down-projection (VALU dot2 + LDS gather)
+    nnz = st["nnz"]
+    down_flops = 2.0 * nnz * D
+    down_ms = kt["down"]
+    down_bytes = (st["bytes_main"] + st["bytes_backup"]) + F * D * 2 + T * D * 2
+    kernels = {
+        "up_pack": {"ms": round(up_ms, 5), "tflops": round(achieved, 2),
+                    "frac_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "down": {"ms": round(down_ms, 5),
+                 "tflops": round(down_flops / (down_ms * 1e-3) / 1e12, 2),
+                 "frac_valu_peak": round(down_flops / (down_ms * 1e-3) / 1e12 / PEAK_VALU_TFLOPS, 4),
+                 "algorithmic_GBps": round(down_bytes / (down_ms * 1e-3) / 1e9, 1),
+                 "frac_hbm_peak": round(down_bytes / (down_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "order": {"ms": round(kt["order"], 5)}, "zero": {"ms": round(kt["zero"], 5)},
+    }
+
+    # ---- CPU fp64 oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        x64 = L0["x_f32"].astype(np.float64)
+        Wu64 = L0["W_up_f32"].astype(np.float64)
+        b64 = oracle.bf16_value(b0.view(torch.int16).cpu().numpy().view(np.uint16))
+        Wd64 = L0["W_down_f32"].astype(np.float64)
+        threads = oracle.num_threads()
+        n = max(threads, 16)
+        rows = np.arange(n, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.ffn_rows(x64, Wu64, b64, Wd64, rows, c.tile, c.ell_width, round_h=True)
+        t1 = time.perf_counter() - t0
+        n2 = int(min(T, max(n, n * args.cpu_seconds / max(t1, 1e-3))))
+        rows = np.linspace(0, T - 1, n2).astype(np.int64)
+        log(f"CPU oracle: {n2} tokens on {threads} threads")
+        t0 = time.perf_counter()
+        oracle.ffn_rows(x64, Wu64, b64, Wd64, rows, c.tile, c.ell_width, round_h=True)
+        t2 = time.perf_counter() - t0
+        cpu = {"value": round(n2 / t2, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n2} of {T} tokens of the same layer (per-token fp64 up-projection, "
+                         f"ReLU, TwELL-order sparse down-projection), {t2:.1f} s"}
+
+    tok_s = T / (ms * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; random N(0,1/fan_in) weights, bias-tuned density)",
+        "config": {"workload": "1.5B-like ReLU FFN layer forward: T=8192 (16x512), d_model=2048, "
+                               f"d_ff=8192, tile=128, ELL width=32, density {args.rho:.0%}, "
+                               "1% heavy tokens (inputs x3)",
+                   "global_batch": T, "seq_len": 512, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "dense_bf16": {"ms_per_step": round(ms_dense, 5), "tokens_per_s": round(T / (ms_dense * 1e-3), 1),
+                       "speedup_sparse_vs_dense": round(ms_dense / ms, 4)},
+        "ms_per_step_without_kernel_events": round(ms_plain, 5),
+        "measured": {"density": round(st["density"], 5), "nnz": int(nnz),
+                     "overflow_tile_rows": int(st["overflow_tile_rows"]),
+                     "ell_fill": round(st["ell_fill"], 4)},
+        "kernels": kernels,
+        "effective_tflops_dense_equiv": round(4.0 * T * D * F / (ms * 1e-3) / 1e12, 2),
+        "sweep": sweep,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

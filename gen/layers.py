@@ -165,6 +165,19 @@ def make_layer(cfg: LayerConfig, seed: int = 0, T: Optional[int] = None,
     return out
 
 
+def bias_for_density(L: dict, rho: float) -> dict:
+    """The same layer with the bias re-targeted to density rho (step 7 of the recipe);
+    x, weights and heavy rows are unchanged.  Returns a shallow copy of L."""
+    cfg = L["cfg"]
+    out = dict(L)
+    out["cfg"] = cfg.replace(rho=float(rho))
+    sigma = np.sqrt(np.sum(L["W_up_f32"].astype(np.float64) ** 2, axis=1))
+    b = (-sigma * density_threshold(rho)).astype(np.float32)
+    out["b_up"] = f32_to_bf16_bits(b) if cfg.dtype == "bf16" else b
+    out["b_up_f32"] = bf16_bits_to_f32(out["b_up"]) if cfg.dtype == "bf16" else out["b_up"]
+    return out
+
+
 def make_hidden(T: int, F: int, density: float, seed: int = 0, signed_zero: bool = False,
                 heavy_rows=(), heavy_density: float = 0.5) -> np.ndarray:
     """A float32 post-ReLU-like hidden tensor [T, F] for the standalone pack.

@@ -1,0 +1,170 @@
+/* sparse_ffn.h -- C ABI of the activation-sparse ReLU FFN layer in TwELL form (MI355X / gfx950).
+ *
+ * The layer (upppp.jp TwELL article of 2026-05-11, section "What is the waste in LLM FFN
+ * layers"): y = ReLU(x W_up^T + b) W_down, applied to each token on its own.  Most hidden
+ * activations are zero, so the library packs them into TwELL (same article, section "What
+ * TwELL and the custom CUDA kernels solve": hidden columns split into tiles, an ELL layout
+ * inside each tile, plus a few dense backups for what does not fit) and runs the
+ * down-projection over the stored nonzeros only.  The dense hidden tensor never reaches
+ * device memory on the forward path.
+ *
+ * Conventions
+ *   - Pointers are DEVICE pointers unless marked (host).  Row-major layouts.
+ *     x [T, d_model], W_up [d_ff, d_model], b_up [d_ff], W_down [d_ff, d_model],
+ *     y [T, d_model]; row j of W_down is neuron j's output weights.
+ *   - Element type of x, weights, bias, y and TwELL values: sffn_config_t.dtype.  All
+ *     accumulation is fp32; results are rounded to nearest-even into dtype.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous on it
+ *     unless marked (sync).  The caller keeps every buffer alive until the work finishes.
+ *   - Errors are status codes; no call aborts or throws.  Arguments are validated on the
+ *     host before anything is launched.  A HIP failure gives SFFN_ERR_DEVICE and the HIP
+ *     message in sffn_last_error().  Device-side overflow of the backup capacity is
+ *     reported through the buffers' status word: outputs of that call are then undefined,
+ *     and twell_stats / sparse_ffn_check return SFFN_ERR_BACKUP_OVERFLOW.
+ *   - The library allocates no device memory.  Every device buffer is the caller's.
+ *
+ * TwELL layout written by twell_pack and sparse_ffn_forward (n_t = d_ff / tile tiles,
+ * "tile-row (k, t)" = token t restricted to the tile's columns [k*tile, (k+1)*tile)):
+ *   counts [n_t, T]    uint16  true number of nonzeros of tile-row (k, t) (may exceed W)
+ *   vals   [n_t, T, W] dtype   first min(count, W) nonzeros in ascending column; then 0
+ *   cols   [n_t, T, W] uint8   their local column in 0..tile-1; then 0
+ *   backup, one entry per tile-row with count > W, in ascending (tile, token) order:
+ *   bk_tile[e], bk_tok[e] int32, bk_vals[e, tile] dtype = the nonzeros of rank >= W at
+ *   their local column, zero elsewhere (the "dense backup" of the hybrid form).
+ */
+#ifndef SPARSE_FFN_H_
+#define SPARSE_FFN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SFFN_OK = 0,
+  SFFN_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, T out of range, ... */
+  SFFN_ERR_UNSUPPORTED = 2,      /* valid but not implemented (shape constraint, dtype) */
+  SFFN_ERR_BACKUP_OVERFLOW = 3,  /* more overflowing tile-rows than backup_capacity */
+  SFFN_ERR_DEVICE = 4            /* a HIP call failed; see sffn_last_error() */
+} sffn_status_t;
+
+typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype_t;
+
+typedef struct {
+  int32_t d_model;         /* D: multiple of 64 (layers in bf16: of 128) */
+  int32_t d_ff;            /* F: multiple of tile (layers in bf16: also of 256) */
+  int32_t tile;            /* K: hidden columns per tile, one of 64, 128, 256 */
+  int32_t ell_width;       /* W: ELL slots per tile-row, 1 <= W <= tile */
+  int32_t max_tokens;      /* largest T any call may pass (1 <= T <= max_tokens <= 2^24) */
+  int32_t backup_capacity; /* backup entries the buffers hold (0 allowed) */
+  sffn_dtype_t dtype;      /* SFFN_BF16 (MFMA up-projection) or SFFN_F32 */
+} sffn_config_t;
+
+/* Caller-owned device buffers for one packed activation of T tokens.  Sizes come from
+ * twell_buffer_sizes().  The same struct holds the forward pass's packed activations
+ * (the saved activations of a training step). */
+typedef struct {
+  uint16_t *counts;      /* [n_t, T] */
+  void *vals;            /* [n_t, T, W] dtype */
+  uint8_t *cols;         /* [n_t, T, W] */
+  int32_t *bk_tile;      /* [backup_capacity] */
+  int32_t *bk_tok;       /* [backup_capacity] */
+  void *bk_vals;         /* [backup_capacity, tile] dtype */
+  int32_t *bk_tile_ptr;  /* [n_t + 1] entries of tile k are e in [ptr[k], ptr[k+1]) */
+  int32_t *bk_n;         /* [1] backup entries needed (may exceed the capacity) */
+  int32_t *status;       /* [1] device status word: 0, or SFFN_ERR_BACKUP_OVERFLOW */
+  void *workspace;       /* scratch: unordered backup staging and per-group counters */
+} twell_buffers_t;
+
+/* Byte sizes of each field of twell_buffers_t for T tokens.  Each buffer must be at
+ * least this large and 256-byte aligned (torch allocations are). */
+typedef struct {
+  size_t counts, vals, cols, bk_tile, bk_tok, bk_vals, bk_tile_ptr, bk_n, status, workspace;
+} twell_buffer_sizes_t;
+
+/* Counters of one packed activation, computed on the device from the counts. */
+typedef struct {
+  int64_t nnz;                /* stored nonzeros, main + backup */
+  int64_t slots_used;         /* sum over tile-rows of min(count, W) */
+  int64_t overflow_tile_rows; /* tile-rows with count > W (= backup entries needed) */
+  int64_t backup_nonzeros;    /* sum of max(count - W, 0) */
+  int64_t backup_needed;      /* entries the pass asked for (bk_n) */
+  int32_t max_count;          /* largest count of any tile-row */
+  int32_t backup_overflowed;  /* 1 if backup_needed > backup_capacity */
+  double density;             /* nnz / (T * d_ff) */
+  double ell_fill;            /* slots_used / (n_t * T * W) */
+  int64_t bytes_main;         /* counts + vals + cols bytes */
+  int64_t bytes_backup;       /* bytes of the backup entries in use */
+  int64_t bytes_dense_equiv;  /* T * d_ff * sizeof(dtype): the dense hidden tensor */
+} twell_stats_t;
+
+typedef struct sparse_ffn *sparse_ffn_t;
+
+/* Status name ("SFFN_OK", ...) for a code; never NULL. */
+const char *sffn_status_string(sffn_status_t s);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char *sffn_last_error(void);
+
+/* (host only) Sizes of the twell_buffers_t fields for T tokens.  Validates cfg and T. */
+sffn_status_t twell_buffer_sizes(const sffn_config_t *cfg, int32_t T, twell_buffer_sizes_t *out);
+
+/* (host only, no device work) Create a layer handle.  Beyond the checks every call
+ * makes, a bf16 layer needs d_model % 128 == 0 and d_ff % 256 == 0 (SFFN_ERR_UNSUPPORTED
+ * otherwise).  The weights are borrowed: they
+ * must stay valid while the handle is used and may be updated in place between calls.
+ * b_up may not be NULL (pass zeros for a bias-free layer). */
+sffn_status_t sparse_ffn_create(const sffn_config_t *cfg, const void *W_up, const void *b_up,
+                                const void *W_down, sparse_ffn_t *out);
+
+/* (host only) Release a handle; NULL is accepted. */
+sffn_status_t sparse_ffn_destroy(sparse_ffn_t h);
+
+/* Pack a dense fp32 hidden tensor h [T, d_ff] into TwELL (same article, section "What
+ * TwELL and the custom CUDA kernels solve").  A value is nonzero iff h != 0 (-0.0 is
+ * zero).  Values are stored in cfg->dtype (rounded to nearest-even for bf16).  Writes
+ * every field of `buf`, including the backup in canonical order and the status word. */
+sffn_status_t twell_pack(const sffn_config_t *cfg, const float *h, int32_t T,
+                         const twell_buffers_t *buf, void *stream);
+
+/* Forward pass y = ReLU(x W_up^T + b) W_down for T tokens.  The up-projection kernel
+ * applies bias and ReLU in fp32 (nonzero iff the fp32 pre-activation is > 0) and packs
+ * the result into `act` on the fly; the down-projection then reads only the stored
+ * entries (main slots and backup).  `act` doubles as the saved activations. */
+sffn_status_t sparse_ffn_forward(sparse_ffn_t h, const void *x, int32_t T, void *y,
+                                 const twell_buffers_t *act, void *stream);
+
+/* Down-projection only, y = unpack(act) W_down, from a TwELL that twell_pack or
+ * sparse_ffn_forward wrote for the same T.  Same arithmetic as the forward's second half. */
+sffn_status_t sparse_ffn_down(sparse_ffn_t h, const twell_buffers_t *act, int32_t T, void *y,
+                              void *stream);
+
+/* (sync) Counters of `buf` for T tokens; synchronises `stream`.  Returns
+ * SFFN_ERR_BACKUP_OVERFLOW (with *out filled) if the status word reports an overflow. */
+sffn_status_t twell_stats(const sffn_config_t *cfg, const twell_buffers_t *buf, int32_t T,
+                          twell_stats_t *out, void *stream);
+
+/* (sync) Synchronise `stream` and return the status word of `buf`. */
+sffn_status_t sparse_ffn_check(const twell_buffers_t *buf, void *stream);
+
+/* Test hook: sparse_ffn_forward that also writes the fp32 pre-activation
+ * z = x W_up^T + b [T, d_ff] (before ReLU) exactly as the up-projection kernel computed
+ * it, so its TwELL can be checked against a pack of the same z. */
+sffn_status_t sparse_ffn_forward_dump(sparse_ffn_t h, const void *x, int32_t T, void *y,
+                                      const twell_buffers_t *act, float *z, void *stream);
+
+/* Per-kernel timing: while enabled, every launch of this library on the calling thread
+ * is bracketed by HIP events on its stream.  sffn_profile_read synchronises the recorded
+ * events and returns, for a kernel name ("up_pack", "down", "pack", "order", ...), the
+ * summed duration in ms and the number of launches since the last reset. */
+sffn_status_t sffn_profile_enable(int32_t enable);
+sffn_status_t sffn_profile_reset(void);
+sffn_status_t sffn_profile_read(const char *kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_FFN_H_ */

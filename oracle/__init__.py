@@ -46,7 +46,7 @@ def _load():
     lib.oracle_down_sparse.restype = None
     lib.oracle_backward.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
     lib.oracle_backward.restype = None
-    lib.oracle_ffn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]
+    lib.oracle_ffn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int32, _P, _P, _P]
     lib.oracle_ffn_rows.restype = None
     lib.oracle_round_bf16.argtypes = [_P, _I, _P]
     lib.oracle_round_bf16.restype = None
@@ -172,10 +172,13 @@ def ffn_sparse(x, W_up, b, W_down, K: int, W: int):
     return down_sparse(tw, W_down), tw
 
 
-def ffn_rows(x, W_up, b, W_down, rows, K: int, W: int, return_z: bool = False):
+def ffn_rows(x, W_up, b, W_down, rows, K: int, W: int, return_z: bool = False,
+             round_h: bool = False):
     """O1..O3 + O6 for selected token rows only (the FFN is per token).
 
-    Returns (y_rows [R, D], counts_rows [R, n_t]) and optionally z_rows [R, F].
+    With ``round_h`` the activations are rounded to bf16 (O8) before the down-projection,
+    the values a bf16 TwELL stores.  Returns (y_rows [R, D], counts_rows [R, n_t]) and
+    optionally z_rows [R, F].
     """
     lib = _load()
     x = _c(x, np.float64); W_up = _c(W_up, np.float64); b = _c(b, np.float64)
@@ -188,7 +191,7 @@ def ffn_rows(x, W_up, b, W_down, rows, K: int, W: int, return_z: bool = False):
     counts = np.empty((R, F // K), np.uint16)
     z = np.empty((R, F), np.float64) if return_z else None
     lib.oracle_ffn_rows(_ptr(x), _ptr(W_up), _ptr(b), _ptr(W_down), _ptr(rows), R, D, F, K, W,
-                        _ptr(y), _ptr(counts), _ptr(z) if z is not None else None)
+                        1 if round_h else 0, _ptr(y), _ptr(counts), _ptr(z) if z is not None else None)
     return (y, counts, z) if return_z else (y, counts)
 
 

@@ -26,6 +26,17 @@
 #include <omp.h>
 #endif
 
+// fp64 -> fp32 (nearest) -> bf16 (nearest, ties to even), returned as its fp64 value.
+static double round_to_bf16_value(double v) {
+  float f = (float)v;
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  u &= 0xFFFF0000u;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
 extern "C" {
 
 // O1 + O2.  Up-projection, bias, ReLU (Page A, "What is the waste in LLM FFN layers":
@@ -227,12 +238,14 @@ void oracle_backward(const double* x, const double* h, const double* g,
 
 // O1..O3 + O6 for a chosen set of token rows (the FFN acts on each token on its own:
 // Page A, "What is the waste in LLM FFN layers"), without materialising [T, F].
-// Outputs per selected row r: y_rows[r, D], counts_rows[r, n_t] (true counts), and the
-// number of overflowing tile-rows.  Used for sampled checks at full layer sizes.
+// Outputs per selected row r: y_rows[r, D], counts_rows[r, n_t] (true counts) and, if
+// z_rows is not null, the pre-activations.  With round_h the stored activation values
+// follow the O8 rounding model (bf16, nearest-even) before the down-projection, as a
+// bf16 TwELL stores them.  Used for sampled checks at full layer sizes.
 void oracle_ffn_rows(const double* x, const double* W_up, const double* b,
                      const double* W_down, const int64_t* rows, int64_t n_rows, int64_t D,
-                     int64_t F, int64_t K, int64_t W, double* y_rows, uint16_t* counts_rows,
-                     double* z_rows) {
+                     int64_t F, int64_t K, int64_t W, int32_t round_h, double* y_rows,
+                     uint16_t* counts_rows, double* z_rows) {
   const int64_t nt = F / K;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
@@ -243,7 +256,9 @@ void oracle_ffn_rows(const double* x, const double* W_up, const double* b,
       for (int64_t i = 0; i < D; ++i) acc += xr[i] * W_up[j * D + i];
       acc += b[j];
       if (z_rows) z_rows[r * F + j] = acc;
-      h[(size_t)j] = acc > 0.0 ? acc : 0.0;
+      double hv = acc > 0.0 ? acc : 0.0;
+      if (round_h && hv != 0.0) hv = round_to_bf16_value(hv);
+      h[(size_t)j] = hv;
     }
     double* yr = y_rows + r * D;
     for (int64_t d = 0; d < D; ++d) yr[d] = 0.0;

@@ -1,0 +1,147 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the header
+declares, sizes buffers as documented, and rejects bad arguments before touching the GPU.
+Runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_ffn.h")
+
+
+@pytest.fixture(scope="module")
+def sffn():
+    import activation_sparse_transformer_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libsparse_ffn.so is not built (run __graft_entry__.build())")
+    m.lib()
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_header_symbols_exported(sffn):
+    names = _declared_functions()
+    assert "sparse_ffn_forward" in names and "twell_pack" in names and "twell_stats" in names
+    L = ctypes.CDLL(sffn.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # the binding wraps exactly the declared functions
+    from activation_sparse_transformer_amd import sparse_ffn as b
+    assert sorted(b.exported_names()) == names
+
+
+def test_status_strings(sffn):
+    from activation_sparse_transformer_amd.sparse_ffn import status_string
+    assert status_string(0) == "SFFN_OK"
+    assert status_string(3) == "SFFN_ERR_BACKUP_OVERFLOW"
+    assert status_string(99) == "SFFN_UNKNOWN_STATUS"
+
+
+def test_buffer_sizes_formula(sffn):
+    cfg = sffn.Config(d_model=2048, d_ff=8192, tile=128, ell_width=32, max_tokens=8192,
+                      backup_capacity=4096, dtype="bf16")
+    s = sffn.buffer_sizes(cfg, 8192)
+    nt = 64
+    assert s["counts"] == 2 * nt * 8192
+    assert s["vals"] == 2 * nt * 8192 * 32
+    assert s["cols"] == nt * 8192 * 32
+    assert s["bk_vals"] == 2 * 4096 * 128
+    assert s["bk_tile"] == s["bk_tok"] == 4 * 4096
+    assert s["bk_tile_ptr"] == 4 * (nt + 1)
+    assert s["workspace"] > 0
+    s32 = sffn.buffer_sizes(cfg.__class__(**{**cfg.__dict__, "dtype": "f32"}), 100)
+    assert s32["vals"] == 4 * nt * 100 * 32
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"tile": 100}, 2), ({"tile": 512}, 2), ({"ell_width": 0}, 1), ({"ell_width": 129}, 1),
+    ({"d_ff": 1000}, 1), ({"d_model": 100}, 2), ({"max_tokens": 0}, 1),
+    ({"backup_capacity": -1}, 1), ({"d_model": 0}, 1),
+])
+def test_config_validation(sffn, kw, code):
+    base = dict(d_model=256, d_ff=1024, tile=128, ell_width=32, max_tokens=64,
+                backup_capacity=16, dtype="bf16")
+    base.update(kw)
+    with pytest.raises(sffn.SffnError) as ei:
+        sffn.buffer_sizes(sffn.Config(**base), 8)
+    assert ei.value.status == code
+
+
+def test_T_range(sffn):
+    cfg = sffn.Config(256, 1024, 128, 32, 64, 16, "bf16")
+    for T in (0, 65, -1):
+        with pytest.raises(sffn.SffnError) as ei:
+            sffn.buffer_sizes(cfg, T)
+        assert ei.value.status == sffn.SFFN_ERR_INVALID_ARGUMENT
+    sffn.buffer_sizes(cfg, 64)
+
+
+def test_layer_shape_constraints(sffn):
+    from activation_sparse_transformer_amd.sparse_ffn import ConfigC, lib
+    L = lib()
+    dummy = ctypes.c_void_p(0x1000)
+    h = ctypes.c_void_p()
+    # bf16 layer with d_ff not a multiple of 256
+    c = ConfigC(256, 1152, 128, 32, 64, 16, 1)
+    assert L.sparse_ffn_create(ctypes.byref(c), dummy, dummy, dummy, ctypes.byref(h)) == 2
+    # bf16 layer with d_model not a multiple of 128
+    c = ConfigC(192, 1024, 128, 32, 64, 16, 1)
+    assert L.sparse_ffn_create(ctypes.byref(c), dummy, dummy, dummy, ctypes.byref(h)) == 2
+    # fp32 allows both
+    c = ConfigC(192, 1152, 128, 32, 64, 16, 0)
+    assert L.sparse_ffn_create(ctypes.byref(c), dummy, dummy, dummy, ctypes.byref(h)) == 0
+    assert L.sparse_ffn_destroy(h) == 0
+    # NULL weights
+    assert L.sparse_ffn_create(ctypes.byref(c), None, dummy, dummy, ctypes.byref(h)) == 1
+    assert L.sparse_ffn_destroy(None) == 0
+
+
+def test_null_arguments_rejected_before_launch(sffn):
+    """Every entry point validates pointers on the host; nothing reaches HIP."""
+    from activation_sparse_transformer_amd.sparse_ffn import BuffersC, ConfigC, StatsC, lib
+    L = lib()
+    c = ConfigC(256, 1024, 128, 32, 64, 16, 0)
+    empty = BuffersC()
+    dummy = ctypes.c_void_p(0x1000)
+    assert L.twell_pack(ctypes.byref(c), None, 8, ctypes.byref(empty), None) == 1
+    assert L.twell_pack(ctypes.byref(c), dummy, 8, ctypes.byref(empty), None) == 1
+    assert L.twell_pack(ctypes.byref(c), dummy, 8, None, None) == 1
+    assert L.twell_pack(None, dummy, 8, ctypes.byref(empty), None) == 1
+    assert L.sparse_ffn_forward(None, dummy, 8, dummy, ctypes.byref(empty), None) == 1
+    h = ctypes.c_void_p()
+    assert L.sparse_ffn_create(ctypes.byref(c), dummy, dummy, dummy, ctypes.byref(h)) == 0
+    assert L.sparse_ffn_forward(h, None, 8, dummy, ctypes.byref(empty), None) == 1
+    assert L.sparse_ffn_forward(h, dummy, 8, dummy, ctypes.byref(empty), None) == 1
+    assert L.sparse_ffn_forward(h, dummy, 65, dummy, ctypes.byref(empty), None) == 1
+    assert L.sparse_ffn_down(h, ctypes.byref(empty), 8, dummy, None) == 1
+    assert L.sparse_ffn_forward_dump(h, dummy, 8, dummy, ctypes.byref(empty), None, None) == 1
+    assert L.twell_stats(ctypes.byref(c), ctypes.byref(empty), 8, ctypes.byref(StatsC()), None) == 1
+    assert L.sparse_ffn_check(None, None) == 1
+    assert L.sffn_profile_read(None, None, None) == 1
+    assert L.sparse_ffn_destroy(h) == 0
+    assert b"NULL" in L.sffn_last_error()
+
+
+def test_profile_counters_host_only(sffn):
+    sffn.profile_enable(True)
+    sffn.profile_reset()
+    ms, n = sffn.profile_read("up_pack")
+    assert ms == 0.0 and n == 0
+    sffn.profile_enable(False)
+
+
+def test_product_path_does_not_import_oracle():
+    """The HIP binding must never reach the CPU oracle."""
+    pkg = os.path.join(ROOT, "activation_sparse_transformer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower().replace("oracle_", ""), f

@@ -1,0 +1,347 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+* twell_pack: bit-exact TwELL (counts, values, columns, padding, ordered backup) for the
+  same fp32 hidden tensor, fp32 and bf16 values, several tile/width settings, ragged T.
+* sparse_ffn_down: y from a TwELL within the layer tolerance of the oracle's y.
+* sparse_ffn_forward: y within tolerance; the fused TwELL pattern equals the oracle's
+  wherever the fp32 sign of z is certain, and equals the standalone pack of the kernel's
+  own fp32 z bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gen import CONFIGS, make_hidden, make_layer
+from tests.gpu_helpers import (assert_y_close, check_backup_structure, decode_dense,
+                               fp32_sum_band, layer_to_dev, need_gpu, to_dev_f32, vals_value,
+                               y_to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(sffn, T, D, F, K, W, dtype, cap=None):
+    nt = F // K
+    cap = nt * T if cap is None else cap
+    return sffn.Config(d_model=D, d_ff=F, tile=K, ell_width=W, max_tokens=T,
+                       backup_capacity=cap, dtype=dtype)
+
+
+def _compare_pack(cfg, host, tw, T, exact_values=True):
+    K, W = cfg.tile, cfg.ell_width
+    assert np.array_equal(host["counts"], tw.counts), "counts differ"
+    assert np.array_equal(host["cols"], tw.cols), "cols differ"
+    if cfg.dtype == "bf16":
+        want_vals = oracle.round_bf16(tw.vals)
+        want_bk = oracle.round_bf16(tw.bk_vals) if len(tw.bk_vals) else tw.bk_vals.astype(np.uint16)
+    else:
+        want_vals = tw.vals.astype(np.float32)
+        want_bk = tw.bk_vals.astype(np.float32)
+    assert np.array_equal(host["vals"].view(np.uint16 if cfg.dtype == "bf16" else np.uint32),
+                          want_vals.view(np.uint16 if cfg.dtype == "bf16" else np.uint32)), "vals differ"
+    assert host["bk_n"] == tw.n_backup
+    r = min(tw.n_backup, cfg.backup_capacity)
+    assert np.array_equal(host["bk_tile"][:r], tw.bk_tile[:r])
+    assert np.array_equal(host["bk_tok"][:r], tw.bk_tok[:r])
+    hb = host["bk_vals"][:r]
+    assert np.array_equal(hb.view(np.uint16 if cfg.dtype == "bf16" else np.uint32),
+                          want_bk[:r].view(np.uint16 if cfg.dtype == "bf16" else np.uint32)), "backup differs"
+
+
+PACK_CASES = [
+    # (T, F, K, W, dtype, density)
+    (1, 256, 128, 32, "bf16", 0.1),
+    (63, 512, 64, 8, "f32", 0.2),
+    (65, 512, 128, 16, "bf16", 0.2),
+    (300, 1024, 128, 32, "bf16", 0.05),
+    (300, 1024, 128, 32, "f32", 0.3),
+    (257, 1024, 256, 16, "bf16", 0.06),
+    (200, 768, 256, 256, "f32", 0.5),
+    (130, 512, 128, 1, "bf16", 0.02),
+    (100, 512, 128, 128, "bf16", 0.9),
+    (77, 384, 64, 63, "f32", 0.95),
+    (333, 1152, 64, 5, "bf16", 0.1),
+]
+
+
+@pytest.mark.parametrize("T,F,K,W,dtype,density", PACK_CASES)
+def test_pack_bitexact(T, F, K, W, dtype, density):
+    torch, sffn = need_gpu()
+    print(f"[pack] T={T} F={F} K={K} W={W} {dtype} rho={density}", flush=True)
+    h = make_hidden(T, F, density, seed=T + F + K + W, signed_zero=True,
+                    heavy_rows=(0, T - 1), heavy_density=0.7)
+    cfg = _cfg(sffn, T, 64, F, K, W, dtype)
+    buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+    host = buf.to_host()
+    assert host["status"] == 0
+    tw = oracle.pack(h.astype(np.float64), K, W)
+    _compare_pack(cfg, host, tw, T)
+    check_backup_structure(cfg, host, T)
+    st = sffn.twell_stats(cfg, buf)
+    ost = oracle.stats(tw)
+    for k in ("nnz", "slots_used", "overflow_tile_rows", "backup_nonzeros", "max_count"):
+        assert st[k] == ost[k], k
+
+
+def test_pack_edges():
+    torch, sffn = need_gpu()
+    T, F, K, W = 70, 512, 128, 16
+    cfg = _cfg(sffn, T, 64, F, K, W, "bf16")
+    for name, h in (("zeros", np.zeros((T, F), np.float32)),
+                    ("ones", np.full((T, F), 0.75, np.float32)),
+                    ("negzero", np.full((T, F), -0.0, np.float32))):
+        print(f"[pack-edge] {name}", flush=True)
+        buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+        host = buf.to_host()
+        tw = oracle.pack(h.astype(np.float64), K, W)
+        _compare_pack(cfg, host, tw, T)
+    # count == W and W + 1 in the same tile
+    h = np.zeros((T, F), np.float32)
+    h[3, :W] = 1.0
+    h[4, :W + 1] = 2.0
+    buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+    host = buf.to_host()
+    assert host["counts"][0, 3] == W and host["counts"][0, 4] == W + 1
+    assert host["bk_n"] == 1 and host["bk_tok"].tolist() == [4]
+
+
+def test_pack_capacity():
+    torch, sffn = need_gpu()
+    T, F, K, W = 96, 512, 128, 4
+    h = make_hidden(T, F, 0.1, seed=9)
+    need = oracle.pack(h.astype(np.float64), K, W).n_backup
+    assert need > 2
+    ok = _cfg(sffn, T, 64, F, K, W, "bf16", cap=need)
+    buf = sffn.twell_pack(ok, to_dev_f32(torch, h))
+    assert sffn.check(buf) == sffn.SFFN_OK
+    short = _cfg(sffn, T, 64, F, K, W, "bf16", cap=need - 1)
+    buf = sffn.twell_pack(short, to_dev_f32(torch, h))
+    assert sffn.check(buf) == sffn.SFFN_ERR_BACKUP_OVERFLOW
+    st = sffn.twell_stats(short, buf, raise_on_overflow=False)
+    assert st["status"] == sffn.SFFN_ERR_BACKUP_OVERFLOW and st["backup_needed"] == need
+    zero = _cfg(sffn, T, 64, F, K, W, "bf16", cap=0)
+    buf = sffn.twell_pack(zero, to_dev_f32(torch, h))
+    assert sffn.check(buf) == sffn.SFFN_ERR_BACKUP_OVERFLOW
+
+
+@pytest.mark.parametrize("T,D,F,K,W,dtype,density", [
+    (300, 256, 1024, 128, 32, "bf16", 0.05),
+    (97, 512, 1024, 128, 8, "bf16", 0.2),
+    (200, 256, 1024, 256, 16, "bf16", 0.08),
+    (130, 384, 512, 64, 6, "bf16", 0.15),
+    (150, 256, 1024, 128, 32, "f32", 0.1),
+    (64, 128, 512, 128, 7, "bf16", 0.1),
+])
+def test_down_from_pack(T, D, F, K, W, dtype, density):
+    torch, sffn = need_gpu()
+    print(f"[down] T={T} D={D} F={F} K={K} W={W} {dtype}", flush=True)
+    rng = np.random.default_rng(T + D)
+    h = make_hidden(T, F, density, seed=D + F, heavy_rows=(1, T // 2), heavy_density=0.6)
+    Wd = (rng.standard_normal((F, D)) / np.sqrt(F)).astype(np.float32)
+    cfg = _cfg(sffn, T, D, F, K, W, dtype)
+    if dtype == "bf16":
+        from gen import f32_to_bf16_bits, bf16_bits_to_f32
+        Wd_bits = f32_to_bf16_bits(Wd)
+        Wd64 = bf16_bits_to_f32(Wd_bits).astype(np.float64)
+        h_ref = oracle.bf16_value(oracle.round_bf16(h.astype(np.float64)))
+        Wd_dev = torch.from_numpy(Wd_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        Wu_dev = torch.zeros((F, D), dtype=torch.bfloat16, device="cuda")
+        b_dev = torch.zeros(F, dtype=torch.bfloat16, device="cuda")
+    else:
+        Wd64 = Wd.astype(np.float64)
+        h_ref = h.astype(np.float64)
+        Wd_dev = to_dev_f32(torch, Wd)
+        Wu_dev = torch.zeros((F, D), dtype=torch.float32, device="cuda")
+        b_dev = torch.zeros(F, dtype=torch.float32, device="cuda")
+    layer = sffn.SparseFFN(cfg, Wu_dev, b_dev, Wd_dev)
+    buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+    y = y_to_host(torch, layer.down(buf))
+    tw = oracle.pack(h_ref, K, W)
+    y_ref = oracle.down_sparse(tw, Wd64)
+    assert_y_close(y, y_ref, dtype, "down")
+    # bit-identical on a second run
+    y2 = y_to_host(torch, layer.down(buf))
+    assert np.array_equal(y, y2)
+
+
+def _forward_case(torch, sffn, L, cap=None, check_pattern=True):
+    cfg0 = L["cfg"]
+    T = cfg0.T
+    cfg = _cfg(sffn, T, cfg0.D, cfg0.F, cfg0.tile, cfg0.ell_width, cfg0.dtype, cap)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    y, act, z = layer.forward_dump(x)
+    assert sffn.check(act) == sffn.SFFN_OK
+    yh = y_to_host(torch, y)
+    x64, Wu64, b64, Wd64 = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+    h64, z64 = oracle.up_relu(x64, Wu64, b64, return_z=True)
+    # a bf16 TwELL stores the activations in bf16 (nearest-even): the oracle applies the
+    # same storage rounding (its O8 model) before the down-projection
+    h_st = oracle.bf16_value(oracle.round_bf16(h64)) if cfg.dtype == "bf16" else h64
+    tw = oracle.pack(h_st, cfg.tile, cfg.ell_width)
+    y_ref = oracle.down_sparse(tw, Wd64)
+    rel = assert_y_close(yh, y_ref, cfg.dtype, f"forward {cfg0.name}")
+    # against the unrounded activations the relative Frobenius bound still holds
+    y_exact = oracle.down_dense(h64, Wd64)
+    nrm = np.linalg.norm(y_exact)
+    if nrm == 0.0:
+        assert not np.any(yh), "an all-zero hidden layer must give y == 0"
+    else:
+        rel_exact = np.linalg.norm(yh - y_exact) / nrm
+        assert rel_exact <= (5e-3 if cfg.dtype == "bf16" else 1e-5), rel_exact
+    host = act.to_host()
+    check_backup_structure(cfg, host, T)
+    if check_pattern:
+        # fused pattern vs the oracle's, outside the fp32 rounding band of z
+        band = fp32_sum_band(x64, Wu64, b64)
+        gpu_h = decode_dense(cfg, host, T)
+        certain = np.abs(z64) > band
+        assert np.array_equal((gpu_h != 0)[certain], (z64 > 0)[certain]), "pattern differs"
+        # stored values: bf16/fp32 rounding of a z within the band of z64
+        nzc = certain & (z64 > 0)
+        if cfg.dtype == "bf16":
+            tol = np.abs(z64[nzc]) * 2.0 ** -8 + band[nzc]
+        else:
+            tol = np.abs(z64[nzc]) * 2.0 ** -23 + band[nzc]
+        assert np.all(np.abs(gpu_h[nzc] - z64[nzc]) <= tol * 1.0001), "stored values off"
+        # the fused epilogue equals the standalone pack of the kernel's own fp32 z
+        hz = torch.relu(z).contiguous()
+        ref_buf = sffn.twell_pack(cfg, hz)
+        rh = ref_buf.to_host()
+        for k in ("counts", "cols", "bk_tile", "bk_tok", "bk_tile_ptr"):
+            assert np.array_equal(host[k], rh[k]), f"fused vs pack: {k}"
+        assert np.array_equal(host["vals"].view(np.uint8), rh["vals"].view(np.uint8))
+        assert np.array_equal(host["bk_vals"].view(np.uint8), rh["bk_vals"].view(np.uint8))
+        assert host["bk_n"] == rh["bk_n"]
+    return rel
+
+
+@pytest.mark.parametrize("name,T,rho", [
+    ("C1", None, None), ("C1b", None, None),
+    ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
+    ("C4", 300, None),
+])
+def test_forward_parity(name, T, rho):
+    torch, sffn = need_gpu()
+    print(f"[forward] {name} T={T} rho={rho}", flush=True)
+    L = make_layer(CONFIGS[name], seed=0, T=T, rho=rho)
+    _forward_case(torch, sffn, L)
+
+
+def test_forward_heavy_rows_force_backup():
+    """2B-like layer at a reduced T with heavy rows: the backup is in use."""
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C4"], seed=0, T=400)
+    assert len(L["heavy"]) >= 2
+    _forward_case(torch, sffn, L)
+
+
+def test_forward_edge_all_zero_all_positive():
+    torch, sffn = need_gpu()
+    base = CONFIGS["C3"].replace(heavy_frac=0.0)
+    for label, bias in (("all-zero", -1e4), ("all-positive", 1e4)):
+        print(f"[forward-edge] {label}", flush=True)
+        L = make_layer(base, seed=0, T=100)
+        from gen import f32_to_bf16_bits, bf16_bits_to_f32
+        L["b_up"] = f32_to_bf16_bits(np.full(base.F, bias, np.float32))
+        L["b_up_f32"] = bf16_bits_to_f32(L["b_up"])
+        _forward_case(torch, sffn, L, check_pattern=(label == "all-zero"))
+
+
+def test_forward_capacity_overflow_reported():
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C1b"], seed=0)
+    c = L["cfg"]
+    cfg = _cfg(sffn, c.T, c.D, c.F, c.tile, c.ell_width, c.dtype, cap=1)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    y, act = layer.forward(x)
+    assert sffn.check(act) == sffn.SFFN_ERR_BACKUP_OVERFLOW
+
+
+def test_determinism_and_homogeneity():
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C3"], seed=0, T=257, rho=0.05)
+    c = L["cfg"]
+    cfg = _cfg(sffn, c.T, c.D, c.F, c.tile, c.ell_width, c.dtype)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    y1, a1 = layer.forward(x)
+    y2, a2 = layer.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    h1, h2 = a1.to_host(), a2.to_host()
+    for k in ("counts", "vals", "cols", "bk_tile", "bk_tok", "bk_vals"):
+        assert np.array_equal(h1[k], h2[k]), k
+    # y(2x, 2b) == 2 y(x, b) bit for bit (scaling by 2 is exact)
+    layer2 = sffn.SparseFFN(cfg, Wu, (b.float() * 2).to(torch.bfloat16), Wd)
+    y3, _ = layer2.forward((x.float() * 2).to(torch.bfloat16))
+    assert torch.equal((y1.float() * 2).to(torch.bfloat16).view(torch.int16), y3.view(torch.int16))
+    # token permutation: each token's output is computed the same way wherever it sits
+    perm = torch.randperm(c.T, generator=torch.Generator().manual_seed(0)).cuda()
+    yp, _ = layer.forward(x[perm].contiguous())
+    assert torch.equal(yp.view(torch.int16), y1[perm].view(torch.int16))
+
+
+def _decode_rows(cfg, host, rows):
+    """Dense [len(rows), F] of selected tokens of a device TwELL."""
+    K, W, nt = cfg.tile, cfg.ell_width, cfg.n_tiles
+    out = np.zeros((len(rows), cfg.d_ff), np.float64)
+    vals = vals_value(cfg, host["vals"][:, rows, :])
+    cols = host["cols"][:, rows, :].astype(np.int64)
+    counts = host["counts"][:, rows].astype(np.int64)
+    for i in range(len(rows)):
+        for k in range(nt):
+            m = min(counts[k, i], W)
+            out[i, k * K + cols[k, i, :m]] = vals[k, i, :m]
+    bt, bo = host["bk_tile"], host["bk_tok"]
+    bv = vals_value(cfg, host["bk_vals"])
+    pos = {int(t): i for i, t in enumerate(rows)}
+    for e in range(len(bt)):
+        i = pos.get(int(bo[e]))
+        if i is not None:
+            nz = np.nonzero(bv[e])[0]
+            out[i, int(bt[e]) * K + nz] = bv[e, nz]
+    return out
+
+
+@pytest.mark.parametrize("name,rho", [("C2", None), ("C3", 0.01), ("C3", 0.05), ("C3", 0.10),
+                                      ("C3", 0.20), ("C4", None)])
+def test_forward_full_size_sampled(name, rho):
+    """Full layer sizes, the launch configuration the benchmark times: sampled tokens
+    against the oracle, and size-independent invariants on the whole TwELL."""
+    torch, sffn = need_gpu()
+    print(f"[forward-full] {name} rho={rho}", flush=True)
+    L = make_layer(CONFIGS[name], seed=0, rho=rho)
+    c = L["cfg"]
+    T = c.T
+    cap = max(4096, c.n_tiles * T // 8)
+    cfg = _cfg(sffn, T, c.D, c.F, c.tile, c.ell_width, c.dtype, cap)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    y, act = layer.forward(x)
+    assert sffn.check(act) == sffn.SFFN_OK
+    st = sffn.twell_stats(cfg, act)
+    host = act.to_host()
+    check_backup_structure(cfg, host, T)
+    assert st["nnz"] == int(host["counts"].astype(np.int64).sum())
+    rng = np.random.default_rng(1)
+    heavy = L["heavy"][:8].tolist()
+    rows = sorted(set([0, 1, T - 1, T - 2] + heavy + rng.choice(T, 24, replace=False).tolist()))
+    rows = np.array(rows, np.int64)
+    x64, Wu64, b64, Wd64 = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+    y_r, c_r, z_r = oracle.ffn_rows(x64, Wu64, b64, Wd64, rows, c.tile, c.ell_width,
+                                    return_z=True, round_h=True)
+    yh = y_to_host(torch, y[torch.from_numpy(rows).cuda()])
+    assert_y_close(yh, y_r, c.dtype, f"full {name}")
+    # counts may differ only by pre-activations whose fp32 sign is uncertain
+    band = fp32_sum_band(x64, Wu64, b64, rows=rows)
+    unc = (np.abs(z_r) <= band).reshape(len(rows), c.n_tiles, c.tile).sum(axis=2)
+    gpu_c = host["counts"][:, rows].T.astype(np.int64)
+    assert np.all(np.abs(gpu_c - c_r.astype(np.int64)) <= unc)
+    # decoded activations of the sampled rows: same pattern where certain, values within
+    # bf16 rounding of the fp32 sum
+    hg = _decode_rows(cfg, host, rows)
+    certain = np.abs(z_r) > band
+    assert np.array_equal((hg != 0)[certain], (z_r > 0)[certain])
+    nzc = certain & (z_r > 0)
+    assert np.all(np.abs(hg[nzc] - z_r[nzc]) <= (np.abs(z_r[nzc]) * 2.0 ** -8 + band[nzc]) * 1.0001)

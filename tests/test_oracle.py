@@ -287,6 +287,21 @@ def test_sparse_equals_dense_bitwise():
     assert np.array_equal(c_r, tw.counts[:, rows].T)
 
 
+def test_rows_with_bf16_storage_model():
+    """ffn_rows(round_h) == dense FFN of the O8-rounded activations (bf16 TwELL values)."""
+    L = make_layer(CONFIGS["C3"], seed=0, T=24, rho=0.2)
+    x, Wu, b, Wd = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+    rows = np.array([0, 3, 23, 11])
+    y_r, c_r = oracle.ffn_rows(x, Wu, b, Wd, rows, 128, 32, round_h=True)
+    h = oracle.up_relu(x, Wu, b)
+    hr = oracle.bf16_value(oracle.round_bf16(h))
+    assert np.array_equal(y_r, oracle.down_dense(hr, Wd)[rows])
+    # rounding never turns a positive activation into zero here (no underflow)
+    assert np.array_equal(hr != 0, h != 0)
+    y_e, _ = oracle.ffn_rows(x, Wu, b, Wd, rows, 128, 32)
+    assert not np.array_equal(y_r, y_e)
+
+
 def test_positive_homogeneity_bitwise():
     L = make_layer(CONFIGS["C1"], seed=1, T=16)
     x, Wu, b, Wd = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
