@@ -9,103 +9,184 @@
 // section "What TwELL and the custom CUDA kernels solve") are folded in per tile.
 //
 // Design for MI355X
-//   * A workgroup owns a block of NW*TPW tokens x DC output columns; its fp32 accumulators
-//     stay in registers for the whole pass over the n_t tiles (TPW tokens per wave, DCL
-//     consecutive columns per lane).
-//   * For each tile k the workgroup stages W_down[kK : kK+K, d0 : d0+DC] in LDS (256 B per
-//     row, double-buffered; the next tile's global loads are in flight while the current
-//     one is consumed).  Each row is then reused by every token of the block that has
-//     that hidden column active.
-//   * A token's TwELL row is wave-uniform: values and columns arrive through scalar loads
-//     and every lane gathers its DCL columns of the selected W_down row from LDS
-//     (conflict-free: 64 lanes read one contiguous 256-byte row).
-//   * bf16: two slots are consumed at once: the two gathered rows are interleaved into
-//     bf16 pairs and fed to v_dot2_f32_bf16 together with the slot pair (fp32 accumulate).
-//   * Workgroups are mapped so that all token blocks of one column chunk run on the same
-//     XCD (blocks are dispatched to the 8 XCDs round-robin), keeping that chunk of W_down
-//     in the XCD's L2.
+//   * A workgroup (16 waves) owns NW*TPW tokens x 128 output columns (bf16; 64 for fp32):
+//     each lane accumulates 2 consecutive columns (1 for fp32) of TPW tokens in fp32
+//     registers for the whole pass over the n_t tiles.
+//   * Per tile k, W_down[kK : kK+K, d0 : d0+DC] (256 bytes per row) and each wave's TwELL
+//     block (its TPW tokens' W-slot rows of values and columns, contiguous in the
+//     tile-major layout) are copied global -> LDS with direct loads, double-buffered: tile
+//     k+1 is in flight while tile k is consumed.
+//   * A token's slots are wave-uniform: they are read from LDS by broadcast and used
+//     directly as VALU operands.  The LDS address of W_down row c for this lane is
+//     (c << 8) | (lane * 4), built by one v_perm from the byte holding c.  Slots are
+//     consumed in pairs: the two gathered rows are interleaved into bf16 pairs and fed to
+//     v_dot2_f32_bf16 together with the slot value pair (fp32 accumulate).
+//   * Workgroups are numbered token-block-major per XCD (blocks go to the 8 XCDs
+//     round-robin): the workgroups an XCD runs at once share their token blocks' TwELL
+//     through that XCD's L2 and together read W_down tiles across all memory channels.
+#include <type_traits>
+
 #include "sffn_common.hpp"
 
 namespace sffn {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-constexpr int DOWN_NW = 8;  // waves per workgroup
+constexpr int DOWN_NW = 16;   // waves per workgroup
+constexpr int DOWN_TPW = 16;  // tokens per wave
+constexpr int DOWN_BT = DOWN_NW * DOWN_TPW;
+constexpr int DOWN_GROUP = 4;  // tokens processed in lockstep by the bf16 fast path
+constexpr int DOWN_LDS = 160 * 1024;  // the whole LDS of a CU: one workgroup per CU
 
-template <int K, int TPW, bool BF16>
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Fold the backup slice of tile-row (k, t) into acc (rare: only overflowing tile-rows).
+template <int K, bool BF16>
+__device__ __forceinline__ void add_backup(const void* __restrict__ bk_vals, int e,
+                                           const uint32_t* wl, int lane, float& a0, float& a1) {
+  constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;
+  const uint32_t* sl = static_cast<const uint32_t*>(bk_vals) + (size_t)e * WORDS;
+#pragma unroll
+  for (int q0 = 0; q0 < WORDS; q0 += 64) {
+    const uint32_t dw = (q0 + lane < WORDS) ? sl[q0 + lane] : 0u;
+    if constexpr (BF16) {
+      uint64_t mm = __ballot((dw & 0xFFFFu) != 0u) | __ballot((dw >> 16) != 0u);
+      while (mm) {
+        const int l = __builtin_ctzll(mm);
+        mm &= mm - 1;
+        const uint32_t wsrc = __builtin_amdgcn_readlane(dw, l);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t bits = half ? (wsrc >> 16) : (wsrc & 0xFFFFu);
+          if (bits == 0u) continue;
+          const float v = __uint_as_float(bits << 16);
+          const uint32_t w = wl[(2 * (q0 + l) + half) * 64 + lane];
+          a0 = fmaf(v, __uint_as_float(w << 16), a0);
+          a1 = fmaf(v, __uint_as_float(w & 0xFFFF0000u), a1);
+        }
+      }
+    } else {
+      uint64_t mm = __ballot(dw != 0u);
+      while (mm) {
+        const int l = __builtin_ctzll(mm);
+        mm &= mm - 1;
+        const float v = __uint_as_float(__builtin_amdgcn_readlane(dw, l));
+        a0 = fmaf(v, __uint_as_float(wl[(q0 + l) * 64 + lane]), a0);
+      }
+    }
+  }
+}
+
+template <int K, bool BF16, bool FAST>
 __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
     Dims d, const uint16_t* __restrict__ counts, const void* __restrict__ vals_,
     const uint8_t* __restrict__ cols, const int32_t* __restrict__ bk_tile_ptr,
     const int32_t* __restrict__ bk_tok, const void* __restrict__ bk_vals,
-    const void* __restrict__ Wd_, void* __restrict__ y_) {
-  constexpr int DCL = BF16 ? 2 : 1;          // output columns per lane
-  constexpr int DC = 64 * DCL;               // output columns per workgroup
-  constexpr int ROWW = 64;                   // 32-bit words per staged row (256 bytes)
-  constexpr int NTHR = DOWN_NW * 64;
-  constexpr int LOADS = K * ROWW / 4 / NTHR;  // 16-byte loads per thread per tile
-  static_assert(LOADS >= 1, "tile too small for the workgroup");
-  __shared__ uint4 wl4[2][K * ROWW / 4];
+    const void* __restrict__ Wd_, void* __restrict__ y_, int tv_bytes, int tc_bytes) {
+  constexpr int DCL = BF16 ? 2 : 1;   // output columns per lane
+  constexpr int DC = 64 * DCL;        // output columns per workgroup
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int WROW = 256;           // bytes of one staged W_down row
+  constexpr int WTILE = K * WROW;     // bytes of one staged W_down tile
+  // LDS: [W tile 0][W tile 1][TwELL stage 0][TwELL stage 1]; a TwELL stage holds DOWN_NW
+  // blocks of (values tv_bytes, columns tc_bytes).  A static array, so that every LDS
+  // offset is a compile-time immediate (the launcher checks the layout fits).
+  __shared__ __attribute__((aligned(16))) unsigned char smem[DOWN_LDS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = d.T, W = d.W;
   const int nd = d.D / DC;
-  const int BT = DOWN_NW * TPW;
-  const int ntb = (T + BT - 1) / BT;
-  // XCD-aware mapping: consecutive (chunk, token-block) pairs share an XCD.
+  const int ntb = (T + DOWN_BT - 1) / DOWN_BT;
   const int total = nd * ntb;
   const int per_xcd = (total + 7) / 8;
   const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (P >= total) return;
-  const int dchunk = P / ntb;
-  const int tb = P - dchunk * ntb;
+  // token-block-major: the workgroups an XCD runs at once cover all column chunks of a few
+  // token blocks, so each TwELL block is fetched once into that XCD's L2 and the W_down
+  // tile loads spread over every memory channel
+  const int tb = P / nd;
+  const int dchunk = P - tb * nd;
   const int d0 = dchunk * DC;
-  const int tw0 = tb * BT + wv * TPW;  // first token of this wave
+  const int tw0 = tb * DOWN_BT + wv * DOWN_TPW;  // first token of this wave
+  const int ntok = max(0, min(DOWN_TPW, T - tw0));  // valid tokens of this wave
 
-  const uint4* __restrict__ Wd4 = static_cast<const uint4*>(Wd_);
-  const size_t row_u4 = (size_t)d.D * (BF16 ? 2 : 4) / 16;  // uint4 per W_down row
-  const size_t col_u4 = (size_t)d0 * (BF16 ? 2 : 4) / 16;
+  const int stage_bytes = DOWN_NW * (tv_bytes + tc_bytes);
+  auto wt_lds = [&](int buf) { return smem + buf * WTILE; };
+  auto tw_lds = [&](int buf) { return smem + 2 * WTILE + buf * stage_bytes; };
 
-  // Thread's share of a staged tile: LOADS 16-byte pieces (row = r, piece = tid % 16).
-  uint4 pre[LOADS];
-  auto load_tile = [&](int k) {
+  const unsigned char* Wd = static_cast<const unsigned char*>(Wd_);
+  const size_t wrow_g = (size_t)d.D * ESZ;  // bytes per W_down row in memory
+  const unsigned char* vals_b = static_cast<const unsigned char*>(vals_);
+
+  // ---- async staging of tile k into buffer `buf`
+  auto issue = [&](int k, int buf) {
+    // W_down tile: K rows x 256 B = K*16 pieces of 16 B, loaded by 64-lane instructions of
+    // 4 rows each, spread over the waves.
+    constexpr int INSTR = K * 16 / 64;
 #pragma unroll
-    for (int q = 0; q < LOADS; ++q) {
-      const int idx = q * NTHR + tid;
-      const int r = idx >> 4, pc = idx & 15;
-      pre[q] = Wd4[((size_t)k * K + r) * row_u4 + col_u4 + pc];
+    for (int j = 0; j < INSTR / DOWN_NW; ++j) {
+      const int ins = j * DOWN_NW + wv;
+      const int piece = ins * 64 + lane;
+      const int r = piece >> 4, pc = piece & 15;
+      __builtin_amdgcn_global_load_lds(
+          Wd + ((size_t)k * K + r) * wrow_g + (size_t)d0 * ESZ + pc * 16,
+          (lds_void_ptr)(wt_lds(buf) + ins * 1024), 16, 0, 0);
+    }
+    if constexpr (FAST) {
+      // this wave's TwELL block: ntok rows of W values and W columns
+      unsigned char* tv = tw_lds(buf) + wv * (tv_bytes + tc_bytes);
+      const size_t row0 = (size_t)k * T + tw0;
+      const int vb = ntok * W * ESZ, cb = ntok * W;
+      for (int off = 0; off < vb; off += 1024) {
+        if (off + lane * 16 < vb)
+          __builtin_amdgcn_global_load_lds(vals_b + row0 * W * ESZ + off + lane * 16,
+                                           (lds_void_ptr)(tv + off), 16, 0, 0);
+      }
+      for (int off = 0; off < cb; off += 1024) {
+        if (off + lane * 16 < cb)
+          __builtin_amdgcn_global_load_lds(cols + row0 * W + off + lane * 16,
+                                           (lds_void_ptr)(tv + tv_bytes + off), 16, 0, 0);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q) wl4[buf][q * NTHR + tid] = pre[q];
-  };
 
-  float acc[TPW][DCL];
+  float acc[DOWN_TPW][DCL];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i)
+  for (int i = 0; i < DOWN_TPW; ++i)
 #pragma unroll
     for (int j = 0; j < DCL; ++j) acc[i][j] = 0.0f;
 
-  const uint16_t* __restrict__ vals16 = static_cast<const uint16_t*>(vals_);
-  const float* __restrict__ vals32 = static_cast<const float*>(vals_);
+  auto load_counts = [&](int k) -> int {
+    return (lane < ntok) ? (int)counts[(size_t)k * T + tw0 + lane] : 0;
+  };
 
-  load_tile(0);
-  store_tile(0);
+  issue(0, 0);
+  int cnt_next = load_counts(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  for (int k = 0; k < d.nt; ++k) {
-    const int buf = k & 1;
-    if (k + 1 < d.nt) load_tile(k + 1);
-    const uint32_t* wl = reinterpret_cast<const uint32_t*>(wl4[buf]);
+  const uint32_t lane4 = (uint32_t)lane * 4u;
+  // One tile step; BUF is a compile-time buffer index so LDS offsets fold into immediates.
+  auto step = [&](int k, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int cnt_lane = cnt_next;
+    if (k + 1 < d.nt) {
+      issue(k + 1, buf ^ 1);
+      cnt_next = load_counts(k + 1);
+    }
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(wt_lds(buf));
+    const unsigned char* tv = tw_lds(buf) + wv * (tv_bytes + tc_bytes);
+    const unsigned char* tc = tv + tv_bytes;
 
-    // counts of this wave's tokens for tile k (lane i <-> token tw0 + i)
-    int cnt_lane = 0;
-    if (lane < TPW && tw0 + lane < T) cnt_lane = counts[(size_t)k * T + tw0 + lane];
     // backup entries of tile k: first entry with token >= tw0 (binary search)
-    int e_lo = 0, e_hi = 0;
+    int e_hi = 0, cursor = 0;
     if (__ballot(cnt_lane > W) != 0ull) {
-      e_lo = ld_uniform(bk_tile_ptr + k);
+      int e_lo = ld_uniform(bk_tile_ptr + k);
       e_hi = ld_uniform(bk_tile_ptr + k + 1);
       e_hi = e_hi < d.cap ? e_hi : d.cap;
       e_lo = e_lo < e_hi ? e_lo : e_hi;
@@ -114,132 +195,102 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
         const int mid = (lo + hi) >> 1;
         if (ld_uniform(bk_tok + mid) < tw0) lo = mid + 1; else hi = mid;
       }
-      e_lo = lo;
+      cursor = lo;
     }
-    int cursor = e_lo;
 
+    if constexpr (FAST && BF16) {
+      // Tokens in groups of G run in lockstep over slot pairs (up to the group's largest
+      // stored count): G independent LDS->perm->LDS->dot2 chains per step hide the LDS
+      // latency.  Slots past a token's count hold (0, 0) and add exact zeros.
+      constexpr int G = DOWN_GROUP;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = tw0 + i;
+      for (int g0 = 0; g0 < DOWN_TPW; g0 += G) {
+        int mg = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          const int c = __builtin_amdgcn_readlane(cnt_lane, g0 + j);
+          mg = max(mg, c < W ? c : W);
+        }
+        for (int s = 0; s < mg; s += 2) {
+          uint32_t vv[G], cc[G], w0[G], w1[G];
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            vv[j] = *reinterpret_cast<const uint32_t*>(tv + ((g0 + j) * W + s) * 2);
+            cc[j] = *reinterpret_cast<const uint16_t*>(tc + (g0 + j) * W + s);
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const uint32_t a0 = __builtin_amdgcn_perm(cc[j], lane4, 0x0C0C0400u);
+            const uint32_t a1 = __builtin_amdgcn_perm(cc[j], lane4, 0x0C0C0500u);
+            w0[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(wl) + a0);
+            w1[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(wl) + a1);
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            acc[g0 + j][0] =
+                dot2_bf16(__builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u), vv[j], acc[g0 + j][0]);
+            acc[g0 + j][1] =
+                dot2_bf16(__builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u), vv[j], acc[g0 + j][1]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DOWN_TPW; ++i) {
       const int cnt = __builtin_amdgcn_readlane(cnt_lane, i);
       if (cnt == 0) continue;
       const int m = cnt < W ? cnt : W;
-      // 32-bit index: the host keeps every TwELL array below 2 GiB
-      const uint32_t row = ((uint32_t)k * (uint32_t)T + (uint32_t)t) * (uint32_t)W;
-      if constexpr (BF16) {
-        if ((W & 3) == 0) {
-          // Slot quads: two bf16 value pairs and four 8-bit columns per step, read as
-          // whole dwords (scalar loads).  Slots past the count are padding (0, 0) and add
-          // exact zeros, so a quad may run past m up to W.
-          const uint32_t* __restrict__ vrow =
-              reinterpret_cast<const uint32_t*>(vals16 + row);
-          const uint32_t* __restrict__ crow = reinterpret_cast<const uint32_t*>(cols + row);
-          for (int s = 0; s < m; s += 4) {
-            const uint32_t vq0 = ld_uniform(vrow + (s >> 1)), vq1 = ld_uniform(vrow + (s >> 1) + 1);
-            const uint32_t cq = ld_uniform(crow + (s >> 2));
-            const uint32_t w0 = wl[(cq & 0xFFu) * ROWW + lane];
-            const uint32_t w1 = wl[((cq >> 8) & 0xFFu) * ROWW + lane];
-            const uint32_t w2 = wl[((cq >> 16) & 0xFFu) * ROWW + lane];
-            const uint32_t w3 = wl[(cq >> 24) * ROWW + lane];
-            // (row c0 col d, row c1 col d) and (row c0 col d+1, row c1 col d+1)
-            const uint32_t p0 = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-            const uint32_t p1 = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-            const uint32_t p2 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-            const uint32_t p3 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-            acc[i][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p0),
-                                                        __builtin_bit_cast(bf16x2_t, vq0),
-                                                        acc[i][0], false);
-            acc[i][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p1),
-                                                        __builtin_bit_cast(bf16x2_t, vq0),
-                                                        acc[i][1], false);
-            acc[i][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p2),
-                                                        __builtin_bit_cast(bf16x2_t, vq1),
-                                                        acc[i][0], false);
-            acc[i][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p3),
-                                                        __builtin_bit_cast(bf16x2_t, vq1),
-                                                        acc[i][1], false);
-          }
-        } else {
-          for (int s = 0; s < m; s += 2) {
-            const uint32_t v1 = ld_uniform(vals16 + row + s);
-            const bool two = s + 1 < m;
-            const uint32_t v2 = two ? (uint32_t)ld_uniform(vals16 + row + s + 1) : 0u;
-            const int c1 = ld_uniform(cols + row + s);
-            const int c2 = two ? (int)ld_uniform(cols + row + s + 1) : c1;
-            const uint32_t w1 = wl[c1 * ROWW + lane];
-            const uint32_t w2 = wl[c2 * ROWW + lane];
-            const uint32_t a_lo = __builtin_amdgcn_perm(w2, w1, 0x05040100u);
-            const uint32_t a_hi = __builtin_amdgcn_perm(w2, w1, 0x07060302u);
-            const uint32_t vv = v1 | (v2 << 16);
-            acc[i][0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a_lo),
-                                                        __builtin_bit_cast(bf16x2_t, vv),
-                                                        acc[i][0], false);
-            acc[i][1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a_hi),
-                                                        __builtin_bit_cast(bf16x2_t, vv),
-                                                        acc[i][1], false);
-          }
+      if constexpr (FAST && BF16) {
+        (void)m;  // main slots were consumed by the grouped loop above
+      } else if constexpr (FAST && !BF16) {
+        const float* vrow = reinterpret_cast<const float*>(tv + i * W * 4);
+        const uint8_t* crow = tc + i * W;
+        for (int s = 0; s < m; ++s) {
+          const float v = vrow[s];
+          const uint32_t c = crow[s];
+          acc[i][0] = fmaf(v, __uint_as_float(wl[c * 64 + lane]), acc[i][0]);
         }
       } else {
+        // generic slot layout (any W): scalar reads straight from the TwELL arrays
+        const uint32_t row = ((uint32_t)k * (uint32_t)T + (uint32_t)(tw0 + i)) * (uint32_t)W;
         for (int s = 0; s < m; ++s) {
-          const float v = ld_uniform(vals32 + row + s);
-          const int c = ld_uniform(cols + row + s);
-          acc[i][0] = fmaf(v, __uint_as_float(wl[c * ROWW + lane]), acc[i][0]);
+          const uint32_t c = ld_uniform(cols + row + s);
+          const uint32_t w = wl[c * 64 + lane];
+          if constexpr (BF16) {
+            const float v = __uint_as_float(
+                (uint32_t)static_cast<const uint16_t*>(vals_)[row + s] << 16);
+            acc[i][0] = fmaf(v, __uint_as_float(w << 16), acc[i][0]);
+            acc[i][DCL - 1] = fmaf(v, __uint_as_float(w & 0xFFFF0000u), acc[i][DCL - 1]);
+          } else {
+            const float v = static_cast<const float*>(vals_)[row + s];
+            acc[i][0] = fmaf(v, __uint_as_float(w), acc[i][0]);
+          }
         }
       }
       if (cnt > W) {
-        // this tile-row's dense remainder: the next entry of tile k in token order
-        const int e = cursor;
-        if (e < e_hi && ld_uniform(bk_tok + e) == t) {
+        const int t = tw0 + i;
+        if (cursor < e_hi && ld_uniform(bk_tok + cursor) == t) {
+          add_backup<K, BF16>(bk_vals, cursor, wl, lane, acc[i][0], acc[i][DCL - 1]);
           ++cursor;
-          constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;
-          const uint32_t* sl = static_cast<const uint32_t*>(bk_vals) + (size_t)e * WORDS;
-#pragma unroll
-          for (int q0 = 0; q0 < WORDS; q0 += 64) {
-            const uint32_t dw = (q0 + lane < WORDS) ? sl[q0 + lane] : 0u;
-            if constexpr (BF16) {
-              uint64_t mlo = __ballot((dw & 0xFFFFu) != 0u);
-              uint64_t mhi = __ballot((dw >> 16) != 0u);
-              uint64_t mm = mlo | mhi;
-              while (mm) {
-                const int l = __builtin_ctzll(mm);
-                mm &= mm - 1;
-                const uint32_t wsrc = __builtin_amdgcn_readlane(dw, l);
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                  const uint32_t bits = half ? (wsrc >> 16) : (wsrc & 0xFFFFu);
-                  if (bits == 0u) continue;
-                  const float v = __uint_as_float(bits << 16);
-                  const int c = 2 * (q0 + l) + half;
-                  const uint32_t w = wl[c * ROWW + lane];
-                  acc[i][0] = fmaf(v, __uint_as_float(w << 16), acc[i][0]);
-                  acc[i][1] = fmaf(v, __uint_as_float(w & 0xFFFF0000u), acc[i][1]);
-                }
-              }
-            } else {
-              uint64_t mm = __ballot(dw != 0u);
-              while (mm) {
-                const int l = __builtin_ctzll(mm);
-                mm &= mm - 1;
-                const float v = __uint_as_float(__builtin_amdgcn_readlane(dw, l));
-                const int c = q0 + l;
-                acc[i][0] = fmaf(v, __uint_as_float(wl[c * ROWW + lane]), acc[i][0]);
-              }
-            }
-          }
         }
       }
     }
-    if (k + 1 < d.nt) store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // tile k+1 landed in LDS
     __syncthreads();
+  };
+  for (int k = 0; k < d.nt; k += 2) {
+    step(k, std::integral_constant<int, 0>());
+    if (k + 1 < d.nt) step(k + 1, std::integral_constant<int, 1>());
   }
 
   // write y (rounded to the layer dtype)
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
+  for (int i = 0; i < DOWN_TPW; ++i) {
+    if (i >= ntok) break;
     const int t = tw0 + i;
-    if (t >= T) break;
     if constexpr (BF16) {
-      const uint32_t packed = (uint32_t)f32_to_bf16(acc[i][0]) | ((uint32_t)f32_to_bf16(acc[i][1]) << 16);
+      const uint32_t packed =
+          (uint32_t)f32_to_bf16(acc[i][0]) | ((uint32_t)f32_to_bf16(acc[i][1]) << 16);
       static_cast<uint32_t*>(y_)[((size_t)t * d.D + d0) / 2 + lane] = packed;
     } else {
       static_cast<float*>(y_)[(size_t)t * d.D + d0 + lane] = acc[i][0];
@@ -247,28 +298,34 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
   }
 }
 
-template <int K, int TPW, bool BF16>
+template <int K, bool BF16, bool FAST>
 static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
                                 hipStream_t s) {
   constexpr int DC = BF16 ? 128 : 64;
+  const int esz = BF16 ? 2 : 4;
   const int nd = d.D / DC;
-  const int ntb = (d.T + DOWN_NW * TPW - 1) / (DOWN_NW * TPW);
+  const int ntb = (d.T + DOWN_BT - 1) / DOWN_BT;
   const int total = nd * ntb;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((down_kernel<K, TPW, BF16>), dim3(8 * per_xcd), dim3(DOWN_NW * 64), 0, s,
-                     d, b.counts, b.vals, b.cols, b.bk_tile_ptr, b.bk_tok, b.bk_vals, Wd, y);
+  const int tv = FAST ? ((DOWN_TPW * d.W * esz + 15) & ~15) : 0;
+  const int tc = FAST ? ((DOWN_TPW * d.W + 15) & ~15) : 0;
+  const size_t lds = 2 * (size_t)K * 256 + 2 * (size_t)DOWN_NW * (tv + tc);
+  if (lds > DOWN_LDS) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((down_kernel<K, BF16, FAST>), dim3(8 * per_xcd), dim3(DOWN_NW * 64), 0, s, d,
+                     b.counts, b.vals, b.cols, b.bk_tile_ptr, b.bk_tok, b.bk_vals, Wd, y, tv, tc);
   return hipGetLastError();
 }
 
 template <int K, bool BF16>
 static hipError_t launch_down_k(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
                                 hipStream_t s) {
-  // Tokens per wave: as many as keep >= ~2 workgroups per CU on 256 CUs.
-  constexpr int DC = BF16 ? 128 : 64;
-  const long long units = (long long)(d.D / DC) * d.T;  // (chunk, token) pairs
-  if (units >= 512LL * DOWN_NW * 32) return launch_down_t<K, 32, BF16>(d, b, Wd, y, s);
-  if (units >= 512LL * DOWN_NW * 16) return launch_down_t<K, 16, BF16>(d, b, Wd, y, s);
-  return launch_down_t<K, 8, BF16>(d, b, Wd, y, s);
+  // The LDS fast path needs 16-byte aligned TwELL rows and room for two stages.
+  const int esz = BF16 ? 2 : 4;
+  const size_t lds_fast = 2 * (size_t)K * 256 +
+                          2 * (size_t)DOWN_NW * (((DOWN_TPW * d.W * esz + 15) & ~15) +
+                                                 ((DOWN_TPW * d.W + 15) & ~15));
+  if (d.W % 16 == 0 && lds_fast <= DOWN_LDS) return launch_down_t<K, BF16, true>(d, b, Wd, y, s);
+  return launch_down_t<K, BF16, false>(d, b, Wd, y, s);
 }
 
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,

@@ -263,8 +263,9 @@ __global__ __launch_bounds__(1024) void order_kernel(Dims d, twell_buffers_t b, 
 
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s) {
-  int blocks = (d.cap + 255) / 256;
-  blocks = blocks < 1 ? 1 : (blocks > 64 ? 64 : blocks);
+  // 16 waves per workgroup, about 4 staged entries per wave at full capacity
+  int blocks = (d.cap + 63) / 64;
+  blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
 #define SFFN_ORDER(KK, BB) \
   hipLaunchKernelGGL((order_kernel<KK, BB>), dim3(blocks), dim3(1024), 0, s, d, b, ws)
   if (d.bf16) {

@@ -52,15 +52,17 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
   constexpr int TPW = (K == 64) ? 2 : 1; // tile parts per wave
   constexpr int NTWG = UP_BN / K;        // tiles per workgroup (4, 2, 1)
 
-  // LDS: the main loop's double buffer, reused after the loop for the TwELL staging.
-  constexpr int MAIN_BYTES = 2 * (UP_BN + BM) * 128;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[MAIN_BYTES];
+  // LDS: two stages, each a separate object so that loads into one stage and reads of the
+  // other are known not to alias; after the loop the A stages hold the TwELL staging.
+  __shared__ __attribute__((aligned(16))) uint4 sA0[UP_BN * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sA1[UP_BN * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sB0[BM * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sB1[BM * 8];
   __shared__ int part_cnt[2][32][2];   // K=256: per (wt, token) count of each wave half
   __shared__ int claim_base[NTWG][2];  // staged-backup base per (tile, wt)
-  uint4* sA = reinterpret_cast<uint4*>(smem);                  // [2][UP_BN*8]
-  uint4* sB = reinterpret_cast<uint4*>(smem) + 2 * UP_BN * 8;  // [2][BM*8]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wt = wave >> 1;
   const int T = d.T, D = d.D, W = d.W;
 
@@ -80,34 +82,29 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
   const int n0 = nb * UP_BN, m0 = mb * BM;
 
   // ---- main loop
-  const size_t rowA = (size_t)D;  // elements per W_up / x row
-  const int pc = tid & 7;         // 16-byte piece within a 128-byte k-slice row
-  uint4 ra[ALD], rb[BLD];
-  auto gload = [&](int kt) {
-    const int k0 = kt * UP_BK + pc * 8;
+  // A k-slice stage is 256 rows x 128 bytes (8 chunks of 16 B); chunk c of row r sits at
+  // position c ^ (r & 7).  Direct global->LDS loads write 64 consecutive 16-byte slots per
+  // instruction (one 8-row block); lane i fills slot i, so it fetches the logical chunk
+  // (i & 7) ^ (i >> 3) of row (i >> 3) of the block.
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto issue = [&](int kt, uint4* sA, uint4* sB) {
+    const int k0 = kt * UP_BK + lchunk * 8;
 #pragma unroll
     for (int q = 0; q < ALD; ++q) {
-      const int r = (q * 256 + tid) >> 3;
-      ra[q] = *reinterpret_cast<const uint4*>(Wu + (size_t)(n0 + r) * rowA + k0);
+      const int blk = wave * ALD + q;
+      const int r = blk * 8 + lrow;
+      __builtin_amdgcn_global_load_lds(Wu + (size_t)(n0 + r) * D + k0, (lds_ptr)(sA + blk * 64),
+                                       16, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < BLD; ++q) {
-      const int r = (q * 256 + tid) >> 3;
-      int tok = m0 + r;
+      const int blk = wave * BLD + q;
+      int tok = m0 + blk * 8 + lrow;
       tok = tok < T ? tok : T - 1;
-      rb[q] = *reinterpret_cast<const uint4*>(x + (size_t)tok * rowA + k0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < ALD; ++q) {
-      const int r = (q * 256 + tid) >> 3;
-      sA[buf * UP_BN * 8 + r * 8 + (pc ^ (r & 7))] = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < BLD; ++q) {
-      const int r = (q * 256 + tid) >> 3;
-      sB[buf * BM * 8 + r * 8 + (pc ^ (r & 7))] = rb[q];
+      __builtin_amdgcn_global_load_lds(x + (size_t)tok * D + k0, (lds_ptr)(sB + blk * 64), 16, 0,
+                                       0);
     }
   };
 
@@ -119,37 +116,53 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][bb][r] = 0.0f;
 
-  const int nk = D / UP_BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int l32 = lane & 31, lh = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint4* A = sA + buf * UP_BN * 8;
-    const uint4* B = sB + buf * BM * 8;
+  // Fragments are double-buffered in registers: the LDS reads of k-step kk+1 are in
+  // flight while the MFMAs of step kk run (one wave per SIMD: nothing else hides them).
+  auto load_frags = [&](const uint4* A, const uint4* B, int kk, bf16x8_t (&fa)[4],
+                        bf16x8_t (&fb)[NB]) {
+    const int ch = kk * 2 + lh;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int r = wn * 128 + a * 32 + l32;
+      fa[a] = __builtin_bit_cast(bf16x8_t, A[r * 8 + (ch ^ (r & 7))]);
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int r = wt * HM + bb * 32 + l32;
+      fb[bb] = __builtin_bit_cast(bf16x8_t, B[r * 8 + (ch ^ (r & 7))]);
+    }
+  };
+  auto compute = [&](const uint4* A, const uint4* B) {
+    bf16x8_t fa[2][4], fb[2][NB];
+    load_frags(A, B, 0, fa[0], fb[0]);
 #pragma unroll
     for (int kk = 0; kk < UP_BK / 16; ++kk) {
-      const int ch = kk * 2 + lh;
-      bf16x8_t fa[4], fb[NB];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r = wn * 128 + a * 32 + l32;
-        fa[a] = __builtin_bit_cast(bf16x8_t, A[r * 8 + (ch ^ (r & 7))]);
-      }
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        const int r = wt * HM + bb * 32 + l32;
-        fb[bb] = __builtin_bit_cast(bf16x8_t, B[r * 8 + (ch ^ (r & 7))]);
-      }
+      const int cur = kk & 1;
+      if (kk + 1 < UP_BK / 16) load_frags(A, B, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
-          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[bb], acc[a][bb], 0, 0, 0);
+          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][bb],
+                                                               acc[a][bb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  const int nk = D / UP_BK;  // D % 128 == 0, so nk is even
+  issue(0, sA0, sB0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    issue(kt + 1, sA1, sB1);
+    compute(sA0, sB0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (kt + 2 < nk) issue(kt + 2, sA0, sB0);
+    compute(sA1, sB1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
@@ -170,9 +183,10 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
     }
 
   // staging: vals [NTWG][2 wt][32 tok][W] bf16, cols [NTWG][2][32][W] u8
-  uint16_t* st_vals = reinterpret_cast<uint16_t*>(smem);
-  uint8_t* st_cols = smem + (size_t)NTWG * 2 * 32 * W * 2;
-  const int st_words = NTWG * 2 * 32 * W * 3 / 4;  // W*3*64*NTWG bytes, multiple of 4
+  uint16_t* st_vals = reinterpret_cast<uint16_t*>(sA0);  // <= 32 KB
+  uint8_t* st_cols = reinterpret_cast<uint8_t*>(sA1);     // <= 16 KB
+  const int st_vwords = NTWG * 2 * 32 * W / 2;             // 32-bit words of st_vals
+  const int st_cwords = NTWG * 2 * 32 * W / 4;             // 32-bit words of st_cols
 
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
@@ -183,7 +197,8 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
 
     // (1) clear the staging block
     __syncthreads();
-    for (int q = tid; q < st_words; q += 256) reinterpret_cast<uint32_t*>(smem)[q] = 0u;
+    for (int q = tid; q < st_vwords; q += 256) reinterpret_cast<uint32_t*>(st_vals)[q] = 0u;
+    for (int q = tid; q < st_cwords; q += 256) reinterpret_cast<uint32_t*>(st_cols)[q] = 0u;
 
     // (2) positive mask of this lane's 64 elements
     uint64_t own = 0;
@@ -372,8 +387,8 @@ hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t*
   // 256-token workgroups when there are enough of them to fill the chip, else 128.
   const bool big = (long long)(d.F / UP_BN) * ((d.T + 255) / 256) >= 512;
   switch (d.K) {
-    case 64: return big ? launch_up_t<64, 4>(d, x, Wu, bu, b, ws, zdump, s)
-                        : launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 64:  // two tiles per wave: the 256-token variant would not fit its registers
+      return launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
     case 128: return big ? launch_up_t<128, 4>(d, x, Wu, bu, b, ws, zdump, s)
                          : launch_up_t<128, 2>(d, x, Wu, bu, b, ws, zdump, s);
     case 256: return big ? launch_up_t<256, 4>(d, x, Wu, bu, b, ws, zdump, s)
