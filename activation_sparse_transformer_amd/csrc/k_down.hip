@@ -36,7 +36,6 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 constexpr int DOWN_NW = 16;   // waves per workgroup
 constexpr int DOWN_TPW = 16;  // tokens per wave
 constexpr int DOWN_BT = DOWN_NW * DOWN_TPW;
-constexpr int DOWN_GROUP = 4;  // tokens processed in lockstep by the bf16 fast path
 constexpr int DOWN_LDS = 160 * 1024;  // the whole LDS of a CU: one workgroup per CU
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -86,7 +85,8 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
     Dims d, const uint16_t* __restrict__ counts, const void* __restrict__ vals_,
     const uint8_t* __restrict__ cols, const int32_t* __restrict__ bk_tile_ptr,
     const int32_t* __restrict__ bk_tok, const void* __restrict__ bk_vals,
-    const void* __restrict__ Wd_, void* __restrict__ y_, int tv_bytes, int tc_bytes) {
+    const void* __restrict__ Wd_, void* __restrict__ y_, int tv_bytes, int tc_bytes,
+    const int32_t* __restrict__ blk_nnz, int thr) {
   constexpr int DCL = BF16 ? 2 : 1;   // output columns per lane
   constexpr int DC = 64 * DCL;        // output columns per workgroup
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -110,6 +110,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
   // token blocks, so each TwELL block is fetched once into that XCD's L2 and the W_down
   // tile loads spread over every memory channel
   const int tb = P / nd;
+  if (blk_nnz != nullptr && ld_uniform(blk_nnz + tb) > thr) return;  // the MFMA kernel's block
   const int dchunk = P - tb * nd;
   const int d0 = dchunk * DC;
   const int tw0 = tb * DOWN_BT + wv * DOWN_TPW;  // first token of this wave
@@ -198,50 +199,38 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
       cursor = lo;
     }
 
-    if constexpr (FAST && BF16) {
-      // Tokens in groups of G run in lockstep over slot pairs (up to the group's largest
-      // stored count): G independent LDS->perm->LDS->dot2 chains per step hide the LDS
-      // latency.  Slots past a token's count hold (0, 0) and add exact zeros.
-      constexpr int G = DOWN_GROUP;
-#pragma unroll
-      for (int g0 = 0; g0 < DOWN_TPW; g0 += G) {
-        int mg = 0;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          const int c = __builtin_amdgcn_readlane(cnt_lane, g0 + j);
-          mg = max(mg, c < W ? c : W);
-        }
-        for (int s = 0; s < mg; s += 2) {
-          uint32_t vv[G], cc[G], w0[G], w1[G];
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            vv[j] = *reinterpret_cast<const uint32_t*>(tv + ((g0 + j) * W + s) * 2);
-            cc[j] = *reinterpret_cast<const uint16_t*>(tc + (g0 + j) * W + s);
-          }
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            const uint32_t a0 = __builtin_amdgcn_perm(cc[j], lane4, 0x0C0C0400u);
-            const uint32_t a1 = __builtin_amdgcn_perm(cc[j], lane4, 0x0C0C0500u);
-            w0[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(wl) + a0);
-            w1[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(wl) + a1);
-          }
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            acc[g0 + j][0] =
-                dot2_bf16(__builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u), vv[j], acc[g0 + j][0]);
-            acc[g0 + j][1] =
-                dot2_bf16(__builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u), vv[j], acc[g0 + j][1]);
-          }
-        }
-      }
-    }
 #pragma unroll
     for (int i = 0; i < DOWN_TPW; ++i) {
       const int cnt = __builtin_amdgcn_readlane(cnt_lane, i);
       if (cnt == 0) continue;
       const int m = cnt < W ? cnt : W;
       if constexpr (FAST && BF16) {
-        (void)m;  // main slots were consumed by the grouped loop above
+        // Slot quads (W % 16 == 0 here): slots past m are padding (0, 0) and add exact
+        // zeros; the second pair of a quad is skipped when m ends inside the first.
+        for (int s = 0; s < m; s += 4) {
+          const uint2 vq = *reinterpret_cast<const uint2*>(tv + (i * W + s) * 2);
+          const uint32_t cq = *reinterpret_cast<const uint32_t*>(tc + i * W + s);
+          {
+            const uint32_t a0 = __builtin_amdgcn_perm(cq, lane4, 0x0C0C0400u);  // (c0<<8)|4*lane
+            const uint32_t a1 = __builtin_amdgcn_perm(cq, lane4, 0x0C0C0500u);  // (c1<<8)|4*lane
+            const uint32_t w0 = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const unsigned char*>(wl) + a0);
+            const uint32_t w1 = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const unsigned char*>(wl) + a1);
+            acc[i][0] = dot2_bf16(__builtin_amdgcn_perm(w1, w0, 0x05040100u), vq.x, acc[i][0]);
+            acc[i][1] = dot2_bf16(__builtin_amdgcn_perm(w1, w0, 0x07060302u), vq.x, acc[i][1]);
+          }
+          if (s + 2 < m) {
+            const uint32_t a2 = __builtin_amdgcn_perm(cq, lane4, 0x0C0C0600u);
+            const uint32_t a3 = __builtin_amdgcn_perm(cq, lane4, 0x0C0C0700u);
+            const uint32_t w2 = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const unsigned char*>(wl) + a2);
+            const uint32_t w3 = *reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const unsigned char*>(wl) + a3);
+            acc[i][0] = dot2_bf16(__builtin_amdgcn_perm(w3, w2, 0x05040100u), vq.y, acc[i][0]);
+            acc[i][1] = dot2_bf16(__builtin_amdgcn_perm(w3, w2, 0x07060302u), vq.y, acc[i][1]);
+          }
+        }
       } else if constexpr (FAST && !BF16) {
         const float* vrow = reinterpret_cast<const float*>(tv + i * W * 4);
         const uint8_t* crow = tc + i * W;
@@ -300,7 +289,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
 
 template <int K, bool BF16, bool FAST>
 static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                                hipStream_t s) {
+                                const int32_t* blk_nnz, int thr, hipStream_t s) {
   constexpr int DC = BF16 ? 128 : 64;
   const int esz = BF16 ? 2 : 4;
   const int nd = d.D / DC;
@@ -312,32 +301,65 @@ static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const v
   const size_t lds = 2 * (size_t)K * 256 + 2 * (size_t)DOWN_NW * (tv + tc);
   if (lds > DOWN_LDS) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((down_kernel<K, BF16, FAST>), dim3(8 * per_xcd), dim3(DOWN_NW * 64), 0, s, d,
-                     b.counts, b.vals, b.cols, b.bk_tile_ptr, b.bk_tok, b.bk_vals, Wd, y, tv, tc);
+                     b.counts, b.vals, b.cols, b.bk_tile_ptr, b.bk_tok, b.bk_vals, Wd, y, tv, tc,
+                     blk_nnz, thr);
   return hipGetLastError();
 }
 
 template <int K, bool BF16>
 static hipError_t launch_down_k(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                                hipStream_t s) {
+                                const int32_t* blk_nnz, int thr, hipStream_t s) {
   // The LDS fast path needs 16-byte aligned TwELL rows and room for two stages.
   const int esz = BF16 ? 2 : 4;
   const size_t lds_fast = 2 * (size_t)K * 256 +
                           2 * (size_t)DOWN_NW * (((DOWN_TPW * d.W * esz + 15) & ~15) +
                                                  ((DOWN_TPW * d.W + 15) & ~15));
-  if (d.W % 16 == 0 && lds_fast <= DOWN_LDS) return launch_down_t<K, BF16, true>(d, b, Wd, y, s);
-  return launch_down_t<K, BF16, false>(d, b, Wd, y, s);
+  if (d.W % 16 == 0 && lds_fast <= DOWN_LDS) return launch_down_t<K, BF16, true>(d, b, Wd, y, blk_nnz, thr, s);
+  return launch_down_t<K, BF16, false>(d, b, Wd, y, blk_nnz, thr, s);
 }
 
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                       hipStream_t s) {
+                       const int32_t* blk_nnz, int thr, hipStream_t s) {
   if (d.bf16) {
-    if (d.K == 64) return launch_down_k<64, true>(d, b, Wd, y, s);
-    if (d.K == 128) return launch_down_k<128, true>(d, b, Wd, y, s);
-    return launch_down_k<256, true>(d, b, Wd, y, s);
+    if (d.K == 64) return launch_down_k<64, true>(d, b, Wd, y, blk_nnz, thr, s);
+    if (d.K == 128) return launch_down_k<128, true>(d, b, Wd, y, blk_nnz, thr, s);
+    return launch_down_k<256, true>(d, b, Wd, y, blk_nnz, thr, s);
   }
-  if (d.K == 64) return launch_down_k<64, false>(d, b, Wd, y, s);
-  if (d.K == 128) return launch_down_k<128, false>(d, b, Wd, y, s);
-  return launch_down_k<256, false>(d, b, Wd, y, s);
+  if (d.K == 64) return launch_down_k<64, false>(d, b, Wd, y, blk_nnz, thr, s);
+  if (d.K == 128) return launch_down_k<128, false>(d, b, Wd, y, blk_nnz, thr, s);
+  return launch_down_k<256, false>(d, b, Wd, y, blk_nnz, thr, s);
+}
+
+// Stored nonzeros (true tile-row counts) of every 256-token block: 1024 threads per block;
+// thread i sums tiles i/256, i/256 + 4, ... of token i%256 (coalesced 512-byte rows).
+__global__ __launch_bounds__(1024) void block_nnz_kernel(Dims d,
+                                                         const uint16_t* __restrict__ counts,
+                                                         int32_t* __restrict__ blk_nnz) {
+  __shared__ int part[16];
+  const int tb = blockIdx.x;
+  const int t = tb * 256 + (threadIdx.x & 255);
+  int sum = 0;
+  if (t < d.T) {
+#pragma unroll 8
+    for (int k = threadIdx.x >> 8; k < d.nt; k += 4) sum += counts[(size_t)k * d.T + t];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int v = threadIdx.x < 16 ? part[threadIdx.x] : 0;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (threadIdx.x == 0) blk_nnz[tb] = v;
+  }
+}
+
+hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* blk_nnz,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(block_nnz_kernel, dim3((d.T + 255) / 256), dim3(1024), 0, s, d, b.counts,
+                     blk_nnz);
+  return hipGetLastError();
 }
 
 }  // namespace sffn

@@ -1,0 +1,363 @@
+// Down-projection over a TwELL activation on the matrix cores (gfx950), for token blocks
+// dense enough that a dense contraction of the rebuilt tiles beats the vector gather (the
+// bf16 MFMA rate is ~16x the vector rate, so the crossover sits well below 1% density).
+//
+//   y[t, :] = sum_k  H_k[t, :] W_down[k*K : (k+1)*K, :]
+//
+// where H_k, tile k of the activations, is rebuilt in LDS from its TwELL rows: the main
+// slots (value, local column) plus, for overflowing tile-rows, the dense backup slice
+// (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom CUDA kernels
+// solve": tiles aligned with tiled matrix-multiply execution, sparse main part plus a few
+// dense backups).
+//
+// Workgroup = 256 tokens x 256 output columns, 4 waves in a 2 x 2 grid; each wave computes
+// 128 tokens x 128 columns with v_mfma_f32_32x32x16_bf16 (A = hidden rows, B = W_down;
+// 256 fp32 accumulators per lane).  The contraction runs in steps of 64 hidden columns:
+//   * B step = W_down[64 rows, 256 columns], copied global -> LDS with direct loads one
+//     step ahead (double buffer); B fragments come straight out of its row-major layout
+//     through ds_read_b64_tr_b16.
+//   * A step = 256 x 64 hidden values, double-buffered: while the MFMAs of step c read one
+//     buffer, each wave clears its 64 token rows of the other and writes step c+1's
+//     nonzeros there, from TwELL data prefetched into registers as 8-slot units (coalesced
+//     16 B value + 8 B column loads).  Padding slots hold value 0 and go to a dummy word,
+//     so these writes need no branch.  Backup slices of a wave's overflowing rows are
+//     loaded (up to 16 rows, 4 rows per load) before the MFMAs and written after them;
+//     their first entry comes from the per-(tile, 32-token group) offsets of the ordering
+//     pass.  The barrier at the top of each step publishes the A and B buffers.
+// Blocks whose stored-nonzero count is at most `thr` belong to the gather kernel and are
+// skipped here (blk_nnz == nullptr: every block runs here).
+#include "sffn_common.hpp"
+
+namespace sffn {
+
+typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
+typedef short short4_m __attribute__((ext_vector_type(4)));
+typedef short short8_m __attribute__((ext_vector_type(8)));
+typedef float floatx16_m __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(3))) short4_m* lds_s4ptr;
+typedef __attribute__((address_space(3))) uint16_t* lds_u16ptr;
+
+constexpr int DM_BM = 256;  // tokens per workgroup
+constexpr int DM_BN = 256;  // output columns per workgroup
+constexpr int DM_KC = 64;   // hidden columns per contraction step
+
+template <int K, int W>
+__global__ __launch_bounds__(256) void down_mfma_kernel(
+    Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
+    const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
+    const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, int thr) {
+  constexpr int KC = DM_KC;
+  constexpr int NCH = K / KC;          // steps per tile
+  constexpr int U = W / 8;             // 8-slot units per tile-row
+  constexpr int NKK = KC / 16;         // MFMA k-steps per step
+  constexpr int AROW = KC * 2;         // 128 B: one A row
+  constexpr int ABUF = DM_BM * AROW;   // 32 KB: one A buffer
+  constexpr int BROW = DM_BN * 2;      // 512 B: one B row
+  constexpr int BBUF = KC * BROW;      // 32 KB: one B buffer
+  __shared__ __attribute__((aligned(16))) unsigned char sA[2 * ABUF];
+  __shared__ __attribute__((aligned(16))) unsigned char sB0[BBUF];
+  __shared__ __attribute__((aligned(16))) unsigned char sB1[BBUF];
+  __shared__ __attribute__((aligned(16))) uint32_t sTrash[64];
+  __shared__ __attribute__((aligned(16))) uint8_t sPos[4][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 1, wc = wave & 1;  // MFMA tile: tokens 128wt.., columns 128wc..
+  const int T = d.T;
+  const int nd = (d.D + DM_BN - 1) / DM_BN;
+  const int ntb = (T + DM_BM - 1) / DM_BM;
+  const int total = nd * ntb;
+  const int per_xcd = (total + 7) / 8;
+  const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (P >= total) return;
+  // token-block-major: the workgroups an XCD runs together share token blocks (TwELL
+  // reads) and column chunks (W_down reads) in its L2
+  const int tb = P / nd;
+  if (blk_nnz != nullptr && ld_uniform(blk_nnz + tb) <= thr) return;
+  const int dchunk = P - tb * nd;
+  const int d0 = dchunk * DM_BN;
+  const bool active = d0 + 128 * wc < d.D;  // D % 256 == 128: the last chunk is half wide
+  const int t0 = tb * DM_BM;
+  const int tw = t0 + wave * 64;  // first token of the rows this wave writes into A
+  const uint32_t sA_lds = (uint32_t)(uintptr_t)(lds_vptr)sA;
+  const uint32_t trash = (uint32_t)(uintptr_t)(lds_vptr)(sTrash + lane);
+  uint8_t* const pos = sPos[wave];
+
+  // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (2*(r&3)), so the
+  // four rows touched by one transposed read land in distinct banks.
+  auto issue_B = [&](int ci, unsigned char* sB) __attribute__((always_inline)) {
+    const size_t row0 = (size_t)ci * KC;  // step ci = rows [ci*KC, +KC) of W_down
+#pragma unroll
+    for (int q = 0; q < BBUF / 1024 / 4; ++q) {
+      const int ins = q * 4 + wave;  // 1 KB (two rows) per 64-lane load
+      const int slot = ins * 64 + lane;
+      const int r = slot >> 5, pc = slot & 31;
+      const int lc = pc ^ (2 * (r & 3));
+      int col = d0 + lc * 8;
+      col = col < d.D ? col : d0;  // columns past D (half-wide chunk) are never read
+      __builtin_amdgcn_global_load_lds(Wd + (row0 + r) * (size_t)d.D + col,
+                                       (lds_vptr)(sB + ins * 1024), 16, 0, 0);
+    }
+  };
+
+  // ---- TwELL units of tile k for this wave's rows: unit u = lane + 64 j holds slots
+  // 8*(u % U) .. +7 of token tw + u / U.  cnt = count of token tw + lane.
+  uint4 uv[U];
+  uint2 uc[U];
+  uint32_t cnt = 0;
+  auto load_units = [&](int k) __attribute__((always_inline)) {
+    const size_t row_base = (size_t)k * T;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int u = lane + 64 * j;
+      const int tok = tw + u / U;
+      const int tk = tok < T ? tok : T - 1;
+      const size_t e0 = (row_base + tk) * W + 8 * (u % U);
+      const uint4 v = *reinterpret_cast<const uint4*>(vals + e0);
+      const uint2 c = *reinterpret_cast<const uint2*>(cols + e0);
+      uv[j] = tok < T ? v : make_uint4(0, 0, 0, 0);
+      uc[j] = c;
+    }
+    const int t = tw + lane;
+    cnt = t < T ? (uint32_t)counts[row_base + t] : 0u;
+  };
+
+  // A rows are 128 B; 16-byte piece p of block row R sits at p ^ ((R >> 1) & 7), so the
+  // 16 consecutive rows of one fragment read (alternating bank halves) hit distinct banks.
+  // Byte address of (this wave's row r, hidden column cc) in A buffer `buf`:
+  auto a_addr = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
+    return sA_lds + buf * ABUF + (wave * 64 + r) * AROW + ((cc ^ (((r >> 1) & 7) << 3)) << 1);
+  };
+
+  // ---- write step c (of the tile) of the units into A buffer `buf`
+  auto build_main = [&](int c, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const uint32_t r = (uint32_t)(lane + 64 * j) / U;
+      const uint32_t vv[4] = {uv[j].x, uv[j].y, uv[j].z, uv[j].w};
+      const uint32_t cw[2] = {uc[j].x, uc[j].y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+        const uint32_t word = vv[e >> 1];
+        const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
+        bool in = true;
+        if constexpr (NCH > 1) in = (col >> 6) == (uint32_t)c;
+        const uint32_t addr = (nz && in) ? a_addr(buf, r, col & (KC - 1)) : trash;
+        const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+        *(lds_u16ptr)(uintptr_t)addr = h;
+      }
+    }
+  };
+
+  // ---- backup slices of the wave's overflowing rows (bit b of ov = token tw + b); they are
+  // consecutive entries from the first entry of the wave's first 32-token group on.
+  // Batches of 16 rows: lane reads 4 columns (8 B) of row 4q + lane/16 of the batch.
+  uint2 bkv[4];
+  uint32_t bkr[4];
+  int bk_e0 = 0, bk_n = 0;
+  auto bk_load = [&](int k, int c, int first) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = first + 4 * q + (lane >> 4);
+      bkv[q] = make_uint2(0, 0);
+      bkr[q] = 0;
+      if (rr < bk_n && bk_e0 + rr < d.cap) {
+        bkr[q] = pos[rr];
+        bkv[q] = *reinterpret_cast<const uint2*>(bk_vals + (size_t)(bk_e0 + rr) * K + c * KC +
+                                                 4 * (lane & 15));
+      }
+    }
+  };
+  auto bk_write = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w2[2] = {bkv[q].x, bkv[q].y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t word = w2[e >> 1];
+        const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+        const uint32_t cc = 4 * (lane & 15) + e;
+        const uint32_t addr = h != 0 ? a_addr(buf, bkr[q], cc) : trash;
+        *(lds_u16ptr)(uintptr_t)addr = h;
+      }
+    }
+  };
+  // positions of the overflowing rows, entry of the first; loads the first batch
+  auto bk_begin = [&](uint64_t ov, int k, int c) __attribute__((always_inline)) {
+    bk_n = __builtin_popcountll(ov);
+    if (bk_n == 0) return;
+    if ((ov >> lane) & 1) pos[mbcnt64(ov)] = (uint8_t)lane;
+    bk_e0 = ld_uniform(grp_first + k * d.ng + tw / GROUP);
+    bk_load(k, c, 0);
+  };
+  // writes the first batch, then any further batches
+  auto bk_finish = [&](int k, int c, int buf) __attribute__((always_inline)) {
+    if (bk_n == 0) return;
+    bk_write(buf);
+    for (int first = 16; first < bk_n; first += 16) {
+      bk_load(k, c, first);
+      bk_write(buf);
+    }
+  };
+
+  // ---- clear this wave's 64 rows of A buffer `buf` (8 KB, 16 B per lane per store)
+  auto clear_a = [&](int buf) __attribute__((always_inline)) {
+    uint4* p = reinterpret_cast<uint4*>(sA + buf * ABUF + wave * 64 * AROW);
+#pragma unroll
+    for (int q = 0; q < 64 * AROW / 1024; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
+  };
+
+  // ---- fragments
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int g16 = lane >> 4, li = lane & 15;
+  auto a_frag = [&](int buf, int i, int kk) __attribute__((always_inline)) -> bf16x8_m {
+    const int R = 128 * wt + 32 * i + l32;  // block row; k = 16kk + 8lh ..
+    const int ch = kk * 2 + lh;
+    return __builtin_bit_cast(bf16x8_m, *reinterpret_cast<const uint4*>(
+                                            sA + buf * ABUF + R * AROW + ((ch ^ ((R >> 1) & 7)) << 4)));
+  };
+  auto b_frag = [&](const unsigned char* sB, int j, int kk) __attribute__((always_inline)) -> bf16x8_m {
+    // lane L of a 16-lane group reads row r0 + L/4, columns c0 + 4(L%4) .. +3; lane i then
+    // holds column c0 + i of rows r0 .. r0+3
+    const int c0 = 128 * wc + 32 * j + 16 * (g16 & 1);
+    const int col = c0 + 4 * (li & 3);
+    short4_m h[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = kk * 16 + 8 * (g16 >> 1) + 4 * q + (li >> 2);
+      const int off = r * BROW + ((((col >> 3) ^ (2 * (r & 3))) << 4) | ((col & 7) << 1));
+      h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(sB + off));
+    }
+    const short8_m v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8_m, v);
+  };
+
+  floatx16_m acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // ---- prologue: A(0) written, B(0) in flight, units of the step after it loaded
+  const int nch = d.nt * NCH;
+  issue_B(0, sB0);
+  load_units(0);
+  clear_a(0);
+  build_main(0, 0);
+  {
+    const uint64_t ov = ballot64(cnt > (uint32_t)W);
+    if (NCH == 1 && nch > 1) load_units(1);
+    bk_begin(ov, 0, 0);
+    bk_finish(0, 0, 0);
+  }
+
+  // step ci: MFMAs of step ci (A and B buffers ci&1) while the A rows of step ci+1 are
+  // written into the other A buffer
+  auto step = [&](int ci, int cb, unsigned char* sBc, unsigned char* sBn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): B(ci) and the units have landed
+    __syncthreads();                     // A(ci), B(ci) complete; step ci-1's buffers free
+    const int cn = ci + 1;
+    const bool more = cn < nch;
+    // fragments are double-buffered across the k-steps: the reads of k-step kk+1 are in
+    // flight while the MFMAs of kk run (the first ones during the A writes below)
+    bf16x8_m fa[2][4], fb[2][4];
+    auto load_frags = [&](int kk, bf16x8_m* a, bf16x8_m* b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = a_frag(cb, i, kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = b_frag(sBc, j, kk);
+    };
+    if (active) load_frags(0, fa[0], fb[0]);
+    if (more) {
+      issue_B(cn, sBn);
+      clear_a(cb ^ 1);
+      build_main(cn % NCH, cb ^ 1);
+      const uint64_t ov = ballot64(cnt > (uint32_t)W);
+      // units of step cn+1 when it starts a new tile; they land during the MFMAs
+      if ((cn + 1) % NCH == 0 && cn + 1 < nch) load_units((cn + 1) / NCH);
+      bk_begin(ov, cn / NCH, cn % NCH);
+    }
+    // the first fragments have long arrived; an explicit wait here lets the counter
+    // tracking start clean, so the reads of k-step 1 overlap the MFMAs of k-step 0
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (active) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) load_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (more) bk_finish(cn / NCH, cn % NCH, cb ^ 1);
+  };
+  for (int ci = 0; ci < nch; ci += 2) {
+    step(ci, 0, sB0, sB1);
+    if (ci + 1 < nch) step(ci + 1, 1, sB1, sB0);
+  }
+
+  // ---- y (bf16): C[m = token][n = column]; lane: column l32, rows 8(r/4) + 4lh + r%4
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 128 * wt + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (t < T) y[(size_t)t * d.D + d0 + 128 * wc + 32 * j + l32] = f32_to_bf16(acc[i][j][r]);
+      }
+}
+
+template <int K, int W>
+static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                              const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                              hipStream_t s) {
+  const int nd = (d.D + DM_BN - 1) / DM_BN;
+  const int ntb = (d.T + DM_BM - 1) / DM_BM;
+  const int total = nd * ntb;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((down_mfma_kernel<K, W>), dim3(8 * per_xcd), dim3(256), 0, s, d, b.counts,
+                     static_cast<const uint16_t*>(b.vals), b.cols,
+                     static_cast<const uint16_t*>(b.bk_vals), ws.grp_first,
+                     static_cast<const uint16_t*>(Wd), static_cast<uint16_t*>(y), blk_nnz, thr);
+  return hipGetLastError();
+}
+
+template <int K>
+static hipError_t launch_dm_k(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                              const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                              hipStream_t s) {
+  switch (d.W) {
+    case 16: return launch_dm_t<K, 16>(d, b, ws, Wd, y, blk_nnz, thr, s);
+    case 32: return launch_dm_t<K, 32>(d, b, ws, Wd, y, blk_nnz, thr, s);
+    case 48: return launch_dm_t<K, 48>(d, b, ws, Wd, y, blk_nnz, thr, s);
+    case 64: return launch_dm_t<K, 64>(d, b, ws, Wd, y, blk_nnz, thr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool down_mfma_supported(const Dims& d) {
+  return d.bf16 && (d.W == 16 || d.W == 32 || d.W == 48 || d.W == 64) && d.D % 128 == 0;
+}
+
+hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                            const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                            hipStream_t s) {
+  if (!down_mfma_supported(d)) return hipErrorInvalidValue;
+  if (d.K == 64) return launch_dm_k<64>(d, b, ws, Wd, y, blk_nnz, thr, s);
+  if (d.K == 128) return launch_dm_k<128>(d, b, ws, Wd, y, blk_nnz, thr, s);
+  return launch_dm_k<256>(d, b, ws, Wd, y, blk_nnz, thr, s);
+}
+
+}  // namespace sffn

@@ -235,6 +235,15 @@ __global__ __launch_bounds__(1024) void order_kernel(Dims d, twell_buffers_t b, 
 
   if (blockIdx.x == 0) {
     for (int kk = tid; kk <= d.nt; kk += 1024) b.bk_tile_ptr[kk] = prefix(kk * d.ng);
+    // first entry of every (tile, group): this thread's chunk, by a running sum
+    {
+      int r = part[tid];
+      for (int q = tid * chunk, e = min(N, (tid + 1) * chunk); q < e; ++q) {
+        ws.grp_first[q] = r;
+        r += ws.ov_grp[q];
+      }
+      if (tid == 0) ws.grp_first[N] = total;
+    }
     if (tid == 0) {
       *b.bk_n = total;
       *b.status = total > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;

@@ -18,6 +18,8 @@ struct sparse_ffn {
   const void* W_up;
   const void* b_up;
   const void* W_down;
+  int32_t down_policy = SFFN_DOWN_AUTO;
+  float down_mfma_density = SFFN_DOWN_MFMA_DENSITY_DEFAULT;
 };
 
 namespace {
@@ -223,6 +225,29 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
   return SFFN_OK;
 }
 
+// Down-projection of a packed activation: per 256-token block, the gather kernel or the MFMA
+// kernel by the block's stored density (bf16 layers); fp32 layers use the gather kernel.
+static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
+                               const Workspace& ws, void* y, hipStream_t s) {
+  const bool mfma_ok = down_mfma_supported(d);
+  int32_t policy = hd->down_policy;
+  if (!mfma_ok) policy = SFFN_DOWN_GATHER;
+  if (policy == SFFN_DOWN_GATHER)
+    return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, nullptr, 0, s); });
+  if (policy == SFFN_DOWN_MFMA)
+    return run("down_mfma", s,
+               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, nullptr, 0, s); });
+  // blocks whose stored nonzeros exceed thr go to the MFMA kernel
+  const double cells = 256.0 * (double)d.F;
+  const double thr_d = (double)hd->down_mfma_density * cells;
+  const int thr = thr_d >= 2147483647.0 ? 2147483647 : (int)thr_d;
+  SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
+  SFFN_TRY_INNER(
+      run("down", s, [&] { return launch_down(d, act, hd->W_down, y, ws.blk_nnz, thr, s); }));
+  return run("down_mfma", s,
+             [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, ws.blk_nnz, thr, s); });
+}
+
 static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, void* y,
                                   const twell_buffers_t* act, float* z, void* stream) {
   if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
@@ -247,8 +272,7 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
     }));
   }
   SFFN_TRY(run("order", s, [&] { return launch_order(d, *act, ws, s); }));
-  SFFN_TRY(run("down", s, [&] { return launch_down(d, *act, hd->W_down, y, s); }));
-  return SFFN_OK;
+  return down_impl(hd, d, *act, ws, y, s);
 }
 
 sffn_status_t sparse_ffn_forward(sparse_ffn_t hd, const void* x, int32_t T, void* y,
@@ -267,10 +291,21 @@ sffn_status_t sparse_ffn_down(sparse_ffn_t hd, const twell_buffers_t* act, int32
   if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
   SFFN_TRY(check_T(&hd->cfg, T));
   if (!y) return fail(SFFN_ERR_INVALID_ARGUMENT, "y is NULL");
-  SFFN_TRY(check_bufs(act, false));
+  SFFN_TRY(check_bufs(act, true));
   const Dims d = make_dims(&hd->cfg, T);
+  const Workspace ws = carve(act->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SFFN_TRY(run("down", s, [&] { return launch_down(d, *act, hd->W_down, y, s); }));
+  return down_impl(hd, d, *act, ws, y, s);
+}
+
+sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float mfma_density) {
+  if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  if (policy != SFFN_DOWN_AUTO && policy != SFFN_DOWN_GATHER && policy != SFFN_DOWN_MFMA)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "unknown down-projection policy");
+  if (!(mfma_density >= 0.0f && mfma_density <= 1.0f))
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "mfma_density must be in [0, 1]");
+  hd->down_policy = policy;
+  hd->down_mfma_density = mfma_density;
   return SFFN_OK;
 }
 

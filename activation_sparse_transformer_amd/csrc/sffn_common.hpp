@@ -33,6 +33,8 @@ struct Workspace {
   int32_t* stage_key;   // [2*cap]  (tile, token | rank_in_group << 24)
   void* stage_vals;     // [cap*K]  dtype
   long long* stats;     // [8]      stats reduction output
+  int32_t* blk_nnz;     // [nblk]   stored nonzeros per 256-token block (down-path choice)
+  int32_t* grp_first;   // [nt*ng+1] first backup entry of each (tile, group), canonical order
 };
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -44,6 +46,8 @@ inline size_t workspace_bytes(const Dims& d) {
   n += align256(sizeof(int32_t) * 2 * (size_t)(d.cap > 0 ? d.cap : 1));
   n += align256((size_t)d.esz * (size_t)(d.cap > 0 ? d.cap : 1) * d.K);
   n += align256(sizeof(long long) * 8);
+  n += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
+  n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
   return n;
 }
 
@@ -59,6 +63,10 @@ inline Workspace carve(void* base, const Dims& d) {
   w.stage_vals = p;
   p += align256((size_t)d.esz * (size_t)(d.cap > 0 ? d.cap : 1) * d.K);
   w.stats = reinterpret_cast<long long*>(p);
+  p += align256(sizeof(long long) * 8);
+  w.blk_nnz = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
+  w.grp_first = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -105,7 +113,17 @@ hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, co
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);
+// Down-projection.  Token blocks of 256 are split between two kernels by their stored
+// nonzero count (blk_nnz, from launch_block_nnz): the vector gather kernel takes blocks
+// with count <= thr, the MFMA kernel the others.  blk_nnz == nullptr hands every block to
+// the kernel launched.
+hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* blk_nnz,
+                            hipStream_t s);
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                       hipStream_t s);
+                       const int32_t* blk_nnz, int thr, hipStream_t s);
+bool down_mfma_supported(const Dims& d);
+hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                            const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                            hipStream_t s);
 
 }  // namespace sffn

@@ -60,6 +60,10 @@ class StatsC(ctypes.Structure):
                 ("bytes_backup", ctypes.c_int64), ("bytes_dense_equiv", ctypes.c_int64)]
 
 
+# Down-projection policies (mirror the header's SFFN_DOWN_* values).
+DOWN_AUTO, DOWN_GATHER, DOWN_MFMA = 0, 1, 2
+DOWN_MFMA_DENSITY_DEFAULT = 0.005
+
 # Exported entry points and their prototypes (restype is always the status enum unless set).
 _PROTOS = {
     "sffn_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -70,6 +74,7 @@ _PROTOS = {
     "twell_pack": ([ctypes.POINTER(ConfigC), _P, _I32, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_forward": ([_P, _P, _I32, _P, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_down": ([_P, ctypes.POINTER(BuffersC), _I32, _P, _P], ctypes.c_int),
+    "sparse_ffn_set_down_policy": ([_P, _I32, ctypes.c_float], ctypes.c_int),
     "twell_stats": ([ctypes.POINTER(ConfigC), ctypes.POINTER(BuffersC), _I32,
                      ctypes.POINTER(StatsC), _P], ctypes.c_int),
     "sparse_ffn_check": ([ctypes.POINTER(BuffersC), _P], ctypes.c_int),
@@ -282,6 +287,15 @@ class SparseFFN:
                                              ctypes.byref(act.c()), _ptr(z), _stream_ptr(stream)),
                "sparse_ffn_forward_dump")
         return y, act, z
+
+    def set_down_policy(self, policy: str = "auto", mfma_density: float = DOWN_MFMA_DENSITY_DEFAULT):
+        """Per-block choice of the down-projection kernel: "auto" (matrix cores above
+        `mfma_density` stored density, gather below), "gather" or "mfma" for every block."""
+        code = {"auto": DOWN_AUTO, "gather": DOWN_GATHER, "mfma": DOWN_MFMA}.get(policy)
+        if code is None:
+            raise ValueError(f"unknown down policy {policy!r}")
+        _check(lib().sparse_ffn_set_down_policy(self._h, code, float(mfma_density)),
+               "sparse_ffn_set_down_policy")
 
     def down(self, act: TwellBuffers, y=None, stream=None):
         """Down-projection only, from an existing TwELL."""

@@ -2,7 +2,9 @@
 
 One "step" is one pass of the whole forward hot path over one batch: the fused MFMA
 up-projection with its bias + ReLU + TwELL-pack epilogue, the canonical backup
-ordering, and the sparse down-projection (library call sparse_ffn_forward).
+ordering, and the down-projection over the packed activations (per 256-token block the
+vector gather kernel or the matrix-core kernel, by the block's stored density), i.e. the
+library call sparse_ffn_forward.
 
 Workload: the 1.5B-like ReLU FFN layer, bf16, T = 8192 tokens (16 x 512), d_model 2048,
 d_ff 8192, tile 128, ELL width 32, density 5%, 1% of tokens with inputs x3; seeded
@@ -27,6 +29,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MAC (dot2) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# launches of one forward, by the names the library's event timing uses
+KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_mfma")
 
 
 def log(msg):
@@ -115,7 +119,7 @@ def main():
         kt = {}
         if profile:
             sffn.profile_enable(False)
-            for k in ("zero", "up_pack", "order", "down"):
+            for k in KERNELS:
                 tot, n = sffn.profile_read(k)
                 kt[k] = tot / max(n, 1)
             sffn.profile_reset()
@@ -127,6 +131,20 @@ def main():
     ms, wall, kt, st, b0 = sparse_point(args.rho, args.steps, args.warmup, profile=True)
     ms_plain, _, _, _, _ = sparse_point(args.rho, args.steps, 2, profile=False)
     log(f"  {ms:.4f} ms/step (profiled), {ms_plain:.4f} ms/step (no events); kernels {kt}")
+
+    # ---- which 256-token blocks the matrix-core kernel took (the library's default rule:
+    # stored density above DOWN_MFMA_DENSITY_DEFAULT), from the headline point's counts
+    cnt = act.t["counts"][: c.n_tiles * T * 2].view(torch.int16).to(torch.int32) & 0xFFFF
+    per_tok = cnt.view(c.n_tiles, T).sum(dim=0)
+    nblk = (T + 255) // 256
+    blk = torch.zeros(nblk * 256, dtype=torch.int64, device=dev)
+    blk[:T] = per_tok
+    blk = blk.view(nblk, 256).sum(dim=1)
+    thr = int(sffn.DOWN_MFMA_DENSITY_DEFAULT * 256 * F)
+    mfma_blk = (blk > thr).cpu().numpy()
+    tok_mfma = int(sum(min(256, T - 256 * i) for i in range(nblk) if mfma_blk[i]))
+    nnz = st["nnz"]
+    nnz_gather = int(blk.cpu().numpy()[~mfma_blk].sum())
 
     # ---- dense bf16 FFN baseline (hipBLASLt through torch), same inputs and stream
     def dense():
@@ -149,36 +167,57 @@ def main():
                           "kernel_ms": {k: round(v, 4) for k, v in k2.items()}})
             log(f"  sweep rho={rho}: {m:.4f} ms, density {s2['density']:.4f}, {k2}")
 
-    # ---- roofline of the dominant kernel (the fused up-projection, MFMA-bound)
-    up_ms = kt["up_pack"]
-    up_flops = 2.0 * T * D * F
-    achieved = up_flops / (up_ms * 1e-3) / 1e12
-    traffic = None
+    # ---- per-kernel rates and the roofline of the dominant kernel
     src_hash = kernel_source_hash()
-    if os.path.exists(TRAFFIC_FILE):
-        tc = json.load(open(TRAFFIC_FILE))
-        ent = tc.get("up_pack")
-        if ent and ent.get("source_hash") == src_hash and ent.get("workload") == "C3-5%":
-            traffic = ent["bytes_per_launch"]
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "up_pack_bf16_kernel (fused up-projection + ReLU + TwELL pack)",
-                "avg_launch_ms": round(up_ms, 5), "algorithmic_flops_per_launch": up_flops}
-    # second kernel: the sparse down-projection (VALU dot2 + LDS gather)
-    nnz = st["nnz"]
-    down_flops = 2.0 * nnz * D
-    down_ms = kt["down"]
-    down_bytes = (st["bytes_main"] + st["bytes_backup"]) + F * D * 2 + T * D * 2
+    tc = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+
+    def traffic_of(name):
+        ent = tc.get(name)
+        if ent and ent.get("source_hash") == src_hash and ent.get("workload") == f"C3-{args.rho:.0%}":
+            return ent["bytes_per_launch"]
+        return None
+
+    up_ms, dg_ms, dm_ms = kt["up_pack"], kt["down"], kt["down_mfma"]
+    up_flops = 2.0 * T * D * F
+    dm_flops = 2.0 * tok_mfma * F * D          # dense-equivalent contraction of its blocks
+    dg_flops = 2.0 * nnz_gather * D            # one MAC per stored nonzero per output column
+    dg_bytes = (st["bytes_main"] + st["bytes_backup"]) + F * D * 2 + T * D * 2
+    rate = lambda fl, ms: fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
     kernels = {
-        "up_pack": {"ms": round(up_ms, 5), "tflops": round(achieved, 2),
-                    "frac_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4)},
-        "down": {"ms": round(down_ms, 5),
-                 "tflops": round(down_flops / (down_ms * 1e-3) / 1e12, 2),
-                 "frac_valu_peak": round(down_flops / (down_ms * 1e-3) / 1e12 / PEAK_VALU_TFLOPS, 4),
-                 "algorithmic_GBps": round(down_bytes / (down_ms * 1e-3) / 1e9, 1),
-                 "frac_hbm_peak": round(down_bytes / (down_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "up_pack": {"ms": round(up_ms, 5), "tflops": round(rate(up_flops, up_ms), 2),
+                    "frac_mfma_peak": round(rate(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4)},
+        "down_mfma": {"ms": round(dm_ms, 5), "tokens": tok_mfma,
+                      "dense_equiv_tflops": round(rate(dm_flops, dm_ms), 2),
+                      "frac_mfma_peak": round(rate(dm_flops, dm_ms) / PEAK_BF16_TFLOPS, 4)},
+        "down_gather": {"ms": round(dg_ms, 5), "tokens": T - tok_mfma, "nnz": nnz_gather,
+                        "tflops": round(rate(dg_flops, dg_ms), 2),
+                        "frac_valu_peak": round(rate(dg_flops, dg_ms) / PEAK_VALU_TFLOPS, 4)},
         "order": {"ms": round(kt["order"], 5)}, "zero": {"ms": round(kt["zero"], 5)},
+        "block_nnz": {"ms": round(kt["block_nnz"], 5)},
     }
+    dom = max((up_ms, "up_pack"), (dm_ms, "down_mfma"), (dg_ms, "down"))[1]
+    if dom == "up_pack":
+        roofline = {"bound": "mfma", "achieved": round(rate(up_flops, up_ms), 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(rate(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_of("up_pack"),
+                    "kernel": "up_pack_bf16_kernel (fused up-projection + bias + ReLU + TwELL pack)",
+                    "avg_launch_ms": round(up_ms, 5), "algorithmic_flops_per_launch": up_flops}
+    elif dom == "down_mfma":
+        roofline = {"bound": "mfma", "achieved": round(rate(dm_flops, dm_ms), 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(rate(dm_flops, dm_ms) / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_of("down_mfma"),
+                    "kernel": "down_mfma_kernel (TwELL tiles rebuilt in LDS, MFMA down-projection)",
+                    "avg_launch_ms": round(dm_ms, 5), "algorithmic_flops_per_launch": dm_flops}
+    else:
+        roofline = {"bound": "alu", "achieved": round(rate(dg_flops, dg_ms), 2),
+                    "peak": PEAK_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(rate(dg_flops, dg_ms) / PEAK_VALU_TFLOPS, 4),
+                    "traffic": traffic_of("down"),
+                    "kernel": "down_kernel (vector gather down-projection)",
+                    "avg_launch_ms": round(dg_ms, 5), "algorithmic_flops_per_launch": dg_flops,
+                    "algorithmic_bytes_per_launch": dg_bytes}
 
     # ---- CPU fp64 oracle on a bounded sample of the same workload
     cpu = None

@@ -75,7 +75,7 @@ typedef struct {
   int32_t *bk_tile_ptr;  /* [n_t + 1] entries of tile k are e in [ptr[k], ptr[k+1]) */
   int32_t *bk_n;         /* [1] backup entries needed (may exceed the capacity) */
   int32_t *status;       /* [1] device status word: 0, or SFFN_ERR_BACKUP_OVERFLOW */
-  void *workspace;       /* scratch: unordered backup staging and per-group counters */
+  void *workspace;       /* scratch: unordered backup staging, per-group and per-block counters */
 } twell_buffers_t;
 
 /* Byte sizes of each field of twell_buffers_t for T tokens.  Each buffer must be at
@@ -137,9 +137,30 @@ sffn_status_t sparse_ffn_forward(sparse_ffn_t h, const void *x, int32_t T, void 
                                  const twell_buffers_t *act, void *stream);
 
 /* Down-projection only, y = unpack(act) W_down, from a TwELL that twell_pack or
- * sparse_ffn_forward wrote for the same T.  Same arithmetic as the forward's second half. */
+ * sparse_ffn_forward wrote for the same T.  Same arithmetic as the forward's second half.
+ * act->workspace must be given (the per-block kernel choice is staged there). */
 sffn_status_t sparse_ffn_down(sparse_ffn_t h, const twell_buffers_t *act, int32_t T, void *y,
                               void *stream);
+
+/* How the down-projection (inside sparse_ffn_forward and sparse_ffn_down) runs each block
+ * of 256 tokens.  The TwELL tiles line up with tiled matrix-multiply execution (same
+ * article, section "What TwELL and the custom CUDA kernels solve"), so a block can either
+ * gather W_down rows for its stored nonzeros on the vector ALUs (work grows with the
+ * nonzeros) or rebuild its hidden tiles in on-chip memory and run them through the matrix
+ * cores (work independent of the density, at ~16x the vector rate).
+ *   SFFN_DOWN_AUTO:   matrix cores for blocks whose stored density (nonzeros / (256 d_ff))
+ *                     exceeds mfma_density, gather otherwise (the default, with
+ *                     SFFN_DOWN_MFMA_DENSITY_DEFAULT)
+ *   SFFN_DOWN_GATHER: every block on the gather kernel
+ *   SFFN_DOWN_MFMA:   every block on the matrix cores
+ * The matrix-core path needs a bf16 layer and ell_width in {16, 32, 48, 64}; other layers
+ * always gather.  Both paths accumulate in fp32; they differ only in summation order.  Host only; the setting belongs to the handle.  SFFN_ERR_INVALID_ARGUMENT for an
+ * unknown policy or mfma_density outside [0, 1]. */
+#define SFFN_DOWN_AUTO 0
+#define SFFN_DOWN_GATHER 1
+#define SFFN_DOWN_MFMA 2
+#define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
+sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float mfma_density);
 
 /* (sync) Counters of `buf` for T tokens; synchronises `stream`.  Returns
  * SFFN_ERR_BACKUP_OVERFLOW (with *out filled) if the status word reports an overflow. */

@@ -123,17 +123,27 @@ def test_pack_capacity():
     assert sffn.check(buf) == sffn.SFFN_ERR_BACKUP_OVERFLOW
 
 
-@pytest.mark.parametrize("T,D,F,K,W,dtype,density", [
+DOWN_CASES = [
     (300, 256, 1024, 128, 32, "bf16", 0.05),
     (97, 512, 1024, 128, 8, "bf16", 0.2),
     (200, 256, 1024, 256, 16, "bf16", 0.08),
     (130, 384, 512, 64, 6, "bf16", 0.15),
     (150, 256, 1024, 128, 32, "f32", 0.1),
     (64, 128, 512, 128, 7, "bf16", 0.1),
-])
-def test_down_from_pack(T, D, F, K, W, dtype, density):
+    # shapes the matrix-core down-projection takes (bf16, W in 16/32/48/64): every width,
+    # every tile size, ragged T, several token blocks
+    (300, 256, 1024, 128, 48, "bf16", 0.2),
+    (520, 384, 1024, 64, 64, "bf16", 0.3),
+    (257, 128, 2048, 256, 48, "bf16", 0.1),
+    (33, 256, 512, 64, 16, "bf16", 0.1),
+]
+
+
+@pytest.mark.parametrize("policy", ["gather", "mfma"])
+@pytest.mark.parametrize("T,D,F,K,W,dtype,density", DOWN_CASES)
+def test_down_from_pack(T, D, F, K, W, dtype, density, policy):
     torch, sffn = need_gpu()
-    print(f"[down] T={T} D={D} F={F} K={K} W={W} {dtype}", flush=True)
+    print(f"[down] T={T} D={D} F={F} K={K} W={W} {dtype} {policy}", flush=True)
     rng = np.random.default_rng(T + D)
     h = make_hidden(T, F, density, seed=D + F, heavy_rows=(1, T // 2), heavy_density=0.6)
     Wd = (rng.standard_normal((F, D)) / np.sqrt(F)).astype(np.float32)
@@ -153,22 +163,78 @@ def test_down_from_pack(T, D, F, K, W, dtype, density):
         Wu_dev = torch.zeros((F, D), dtype=torch.float32, device="cuda")
         b_dev = torch.zeros(F, dtype=torch.float32, device="cuda")
     layer = sffn.SparseFFN(cfg, Wu_dev, b_dev, Wd_dev)
+    layer.set_down_policy(policy)
     buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
     y = y_to_host(torch, layer.down(buf))
     tw = oracle.pack(h_ref, K, W)
     y_ref = oracle.down_sparse(tw, Wd64)
-    assert_y_close(y, y_ref, dtype, "down")
+    assert_y_close(y, y_ref, dtype, f"down {policy}")
     # bit-identical on a second run
     y2 = y_to_host(torch, layer.down(buf))
     assert np.array_equal(y, y2)
 
 
-def _forward_case(torch, sffn, L, cap=None, check_pattern=True):
+def test_down_mixed_block_densities():
+    """Token blocks of 256 on both sides of the density threshold: the gather and the
+    matrix-core kernels each take their blocks, every output row is written once, and the
+    result matches the oracle (and both single-kernel policies) within the tolerance."""
+    torch, sffn = need_gpu()
+    from gen import f32_to_bf16_bits, bf16_bits_to_f32
+    T, D, F, K, W = 1000, 256, 2048, 128, 32
+    # block densities 0.1%, 4%, 0.3%, 2% (the last block is ragged: 232 tokens)
+    parts = [make_hidden(256, F, 0.001, seed=11), make_hidden(256, F, 0.04, seed=12),
+             make_hidden(256, F, 0.003, seed=13), make_hidden(232, F, 0.02, seed=14)]
+    h = np.concatenate(parts, axis=0)
+    rng = np.random.default_rng(5)
+    Wd_bits = f32_to_bf16_bits((rng.standard_normal((F, D)) / np.sqrt(F)).astype(np.float32))
+    Wd64 = bf16_bits_to_f32(Wd_bits).astype(np.float64)
+    h_ref = oracle.bf16_value(oracle.round_bf16(h.astype(np.float64)))
+    y_ref = oracle.down_sparse(oracle.pack(h_ref, K, W), Wd64)
+    cfg = _cfg(sffn, T, D, F, K, W, "bf16")
+    Wd_dev = torch.from_numpy(Wd_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    layer = sffn.SparseFFN(cfg, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
+                           torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
+    buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+    ys = {}
+    for policy, dens in (("auto", 0.005), ("auto", 0.0), ("auto", 1.0), ("gather", 0.005),
+                         ("mfma", 0.005)):
+        layer.set_down_policy(policy, dens)
+        y = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        layer.down(buf, y=y)
+        yh = y_to_host(torch, y)
+        assert not np.isnan(yh).any(), f"{policy}/{dens}: rows not written"
+        assert_y_close(yh, y_ref, "bf16", f"mixed {policy}/{dens}")
+        ys[(policy, dens)] = yh
+    # thresholds 0 and 1 hand every block to one kernel: bit-equal to the forced policies
+    assert np.array_equal(ys[("auto", 0.0)], ys[("mfma", 0.005)])
+    assert np.array_equal(ys[("auto", 1.0)], ys[("gather", 0.005)])
+    # at 0.5%, blocks 0 and 2 are the gather kernel's, 1 and 3 the matrix cores'
+    a = ys[("auto", 0.005)]
+    g, m = ys[("gather", 0.005)], ys[("mfma", 0.005)]
+    for blk, src in ((0, g), (1, m), (2, g), (3, m)):
+        sl = slice(256 * blk, min(T, 256 * (blk + 1)))
+        assert np.array_equal(a[sl], src[sl]), f"block {blk}"
+
+
+def test_down_policy_arguments():
+    torch, sffn = need_gpu()
+    cfg = _cfg(sffn, 64, 128, 256, 128, 16, "bf16")
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    layer = sffn.SparseFFN(cfg, z(256, 128), z(256), z(256, 128))
+    for bad in (-0.1, 1.5, float("nan")):
+        with pytest.raises(sffn.SffnError):
+            layer.set_down_policy("auto", bad)
+    with pytest.raises(ValueError):
+        layer.set_down_policy("fastest")
+
+
+def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     cfg0 = L["cfg"]
     T = cfg0.T
     cfg = _cfg(sffn, T, cfg0.D, cfg0.F, cfg0.tile, cfg0.ell_width, cfg0.dtype, cap)
     x, Wu, b, Wd = layer_to_dev(torch, L)
     layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    layer.set_down_policy(policy)
     y, act, z = layer.forward_dump(x)
     assert sffn.check(act) == sffn.SFFN_OK
     yh = y_to_host(torch, y)
@@ -215,24 +281,26 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True):
     return rel
 
 
+@pytest.mark.parametrize("policy", ["gather", "mfma"])
 @pytest.mark.parametrize("name,T,rho", [
     ("C1", None, None), ("C1b", None, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
     ("C4", 300, None),
 ])
-def test_forward_parity(name, T, rho):
+def test_forward_parity(name, T, rho, policy):
     torch, sffn = need_gpu()
-    print(f"[forward] {name} T={T} rho={rho}", flush=True)
+    print(f"[forward] {name} T={T} rho={rho} {policy}", flush=True)
     L = make_layer(CONFIGS[name], seed=0, T=T, rho=rho)
-    _forward_case(torch, sffn, L)
+    _forward_case(torch, sffn, L, policy=policy)
 
 
-def test_forward_heavy_rows_force_backup():
+@pytest.mark.parametrize("policy", ["gather", "mfma"])
+def test_forward_heavy_rows_force_backup(policy):
     """2B-like layer at a reduced T with heavy rows: the backup is in use."""
     torch, sffn = need_gpu()
     L = make_layer(CONFIGS["C4"], seed=0, T=400)
     assert len(L["heavy"]) >= 2
-    _forward_case(torch, sffn, L)
+    _forward_case(torch, sffn, L, policy=policy)
 
 
 def test_forward_edge_all_zero_all_positive():
@@ -304,13 +372,14 @@ def _decode_rows(cfg, host, rows):
     return out
 
 
-@pytest.mark.parametrize("name,rho", [("C2", None), ("C3", 0.01), ("C3", 0.05), ("C3", 0.10),
-                                      ("C3", 0.20), ("C4", None)])
-def test_forward_full_size_sampled(name, rho):
+@pytest.mark.parametrize("name,rho,policy", [
+    ("C2", None, "auto"), ("C3", 0.01, "auto"), ("C3", 0.05, "auto"), ("C3", 0.05, "gather"),
+    ("C3", 0.10, "auto"), ("C3", 0.20, "auto"), ("C4", None, "auto"), ("C4", None, "gather")])
+def test_forward_full_size_sampled(name, rho, policy):
     """Full layer sizes, the launch configuration the benchmark times: sampled tokens
     against the oracle, and size-independent invariants on the whole TwELL."""
     torch, sffn = need_gpu()
-    print(f"[forward-full] {name} rho={rho}", flush=True)
+    print(f"[forward-full] {name} rho={rho} {policy}", flush=True)
     L = make_layer(CONFIGS[name], seed=0, rho=rho)
     c = L["cfg"]
     T = c.T
@@ -318,6 +387,7 @@ def test_forward_full_size_sampled(name, rho):
     cfg = _cfg(sffn, T, c.D, c.F, c.tile, c.ell_width, c.dtype, cap)
     x, Wu, b, Wd = layer_to_dev(torch, L)
     layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    layer.set_down_policy(policy)
     y, act = layer.forward(x)
     assert sffn.check(act) == sffn.SFFN_OK
     st = sffn.twell_stats(cfg, act)
