@@ -55,6 +55,9 @@ def main():
     ap.add_argument("--rho", type=float, default=0.05, help="density of the headline point")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (3 times): the reference "
+                         "kernel that scales hardware byte counters to bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -266,6 +269,14 @@ def main():
         "sweep": sweep,
         "kernel_source_hash": src_hash,
     }
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n
     print(json.dumps(out), flush=True)
 
 
