@@ -20,10 +20,13 @@
 //     buffer, each wave clears its 64 token rows of the other and writes step c+1's
 //     nonzeros there, from TwELL data prefetched into registers as 8-slot units (coalesced
 //     16 B value + 8 B column loads).  Padding slots hold value 0 and go to a dummy word,
-//     so these writes need no branch.  Backup slices of a wave's overflowing rows are
-//     loaded (up to 16 rows, 4 rows per load) before the MFMAs and written after them;
-//     their first entry comes from the per-(tile, 32-token group) offsets of the ordering
-//     pass.  The barrier at the top of each step publishes the A and B buffers.
+//     so these writes need no branch, and the step body between barriers is one basic
+//     block in which the A writes are interleaved with the MFMAs (one MFMA, then a few
+//     vector and LDS instructions in its shadow).  Backup slices of a wave's overflowing
+//     rows are loaded (up to 16 rows, 4 rows per load) at the start of the step and written
+//     at the start of the next, before its barrier; their first entry comes from the
+//     per-(tile, 32-token group) offsets of the ordering pass.  The barrier at the top of
+//     each step publishes the A and B buffers.
 // Blocks whose stored-nonzero count is at most `thr` belong to the gather kernel and are
 // skipped here (blk_nnz == nullptr: every block runs here).
 #include "sffn_common.hpp"
@@ -36,7 +39,6 @@ typedef short short8_m __attribute__((ext_vector_type(8)));
 typedef float floatx16_m __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_vptr;
 typedef __attribute__((address_space(3))) short4_m* lds_s4ptr;
-typedef __attribute__((address_space(3))) uint16_t* lds_u16ptr;
 
 constexpr int DM_BM = 256;  // tokens per workgroup
 constexpr int DM_BN = 256;  // output columns per workgroup
@@ -56,10 +58,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   constexpr int ABUF = DM_BM * AROW;   // 32 KB: one A buffer
   constexpr int BROW = DM_BN * 2;      // 512 B: one B row
   constexpr int BBUF = KC * BROW;      // 32 KB: one B buffer
-  __shared__ __attribute__((aligned(16))) unsigned char sA[2 * ABUF];
+  // A buffers, then 256 B of dummy words (one per lane) that padding writes go to; all A
+  // writes address this one array, so the compiler sees they never touch the B buffers
+  // filled by direct loads (and need not wait for those)
+  __shared__ __attribute__((aligned(16))) unsigned char sA[2 * ABUF + 256];
   __shared__ __attribute__((aligned(16))) unsigned char sB0[BBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sB1[BBUF];
-  __shared__ __attribute__((aligned(16))) uint32_t sTrash[64];
   __shared__ __attribute__((aligned(16))) uint8_t sPos[4][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -81,8 +85,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   const bool active = d0 + 128 * wc < d.D;  // D % 256 == 128: the last chunk is half wide
   const int t0 = tb * DM_BM;
   const int tw = t0 + wave * 64;  // first token of the rows this wave writes into A
-  const uint32_t sA_lds = (uint32_t)(uintptr_t)(lds_vptr)sA;
-  const uint32_t trash = (uint32_t)(uintptr_t)(lds_vptr)(sTrash + lane);
+  const uint32_t trash = 2 * ABUF + 4 * lane;  // byte offset in sA
   uint8_t* const pos = sPos[wave];
 
   // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (2*(r&3)), so the
@@ -108,33 +111,38 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   uint2 uc[U];
   uint32_t cnt = 0;
   auto load_units = [&](int k) __attribute__((always_inline)) {
+    // addresses are clamped into the buffers and rows past T masked to zero with an AND
+    // (a select on a loaded value would be turned into a branch around the load)
     const size_t row_base = (size_t)k * T;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int u = lane + 64 * j;
       const int tok = tw + u / U;
       const int tk = tok < T ? tok : T - 1;
+      const uint32_t m = tok < T ? 0xFFFFFFFFu : 0u;
       const size_t e0 = (row_base + tk) * W + 8 * (u % U);
       const uint4 v = *reinterpret_cast<const uint4*>(vals + e0);
-      const uint2 c = *reinterpret_cast<const uint2*>(cols + e0);
-      uv[j] = tok < T ? v : make_uint4(0, 0, 0, 0);
-      uc[j] = c;
+      uv[j] = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+      uc[j] = *reinterpret_cast<const uint2*>(cols + e0);
     }
     const int t = tw + lane;
-    cnt = t < T ? (uint32_t)counts[row_base + t] : 0u;
+    const uint32_t m = t < T ? 0xFFFFu : 0u;
+    cnt = (uint32_t)counts[row_base + (t < T ? t : T - 1)] & m;
   };
 
   // A rows are 128 B; 16-byte piece p of block row R sits at p ^ ((R >> 1) & 7), so the
   // 16 consecutive rows of one fragment read (alternating bank halves) hit distinct banks.
-  // Byte address of (this wave's row r, hidden column cc) in A buffer `buf`:
+  // Byte offset in sA of (this wave's row r, hidden column cc) in A buffer `buf`:
   auto a_addr = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
-    return sA_lds + buf * ABUF + (wave * 64 + r) * AROW + ((cc ^ (((r >> 1) & 7) << 3)) << 1);
+    return buf * ABUF + (wave * 64 + r) * AROW + ((cc ^ (((r >> 1) & 7) << 3)) << 1);
   };
 
-  // ---- write step c (of the tile) of the units into A buffer `buf`
-  auto build_main = [&](int c, int buf) __attribute__((always_inline)) {
+  // ---- write step c (of the tile) of the units into A buffer `buf`; the units are split
+  // into four parts (unit j in part 4j/U) so the writes spread over the four MFMA k-steps
+  auto build_part = [&](int part, int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
+      if ((4 * j) / U != part) continue;
       const uint32_t r = (uint32_t)(lane + 64 * j) / U;
       const uint32_t vv[4] = {uv[j].x, uv[j].y, uv[j].z, uv[j].w};
       const uint32_t cw[2] = {uc[j].x, uc[j].y};
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
         if constexpr (NCH > 1) in = (col >> 6) == (uint32_t)c;
         const uint32_t addr = (nz && in) ? a_addr(buf, r, col & (KC - 1)) : trash;
         const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
-        *(lds_u16ptr)(uintptr_t)addr = h;
+        *reinterpret_cast<uint16_t*>(sA + addr) = h;
       }
     }
   };
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
         const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
         const uint32_t cc = 4 * (lane & 15) + e;
         const uint32_t addr = h != 0 ? a_addr(buf, bkr[q], cc) : trash;
-        *(lds_u16ptr)(uintptr_t)addr = h;
+        *reinterpret_cast<uint16_t*>(sA + addr) = h;
       }
     }
   };
@@ -248,23 +256,30 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   issue_B(0, sB0);
   load_units(0);
   clear_a(0);
-  build_main(0, 0);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) build_part(part, 0, 0);
   {
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
-    if (NCH == 1 && nch > 1) load_units(1);
+    if (NCH == 1) load_units(d.nt > 1 ? 1 : 0);
     bk_begin(ov, 0, 0);
     bk_finish(0, 0, 0);
   }
 
   // step ci: MFMAs of step ci (A and B buffers ci&1) while the A rows of step ci+1 are
-  // written into the other A buffer
-  auto step = [&](int ci, int cb, unsigned char* sBc, unsigned char* sBn) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): B(ci) and the units have landed
+  // written into the other A buffer.  The last step rebuilds a chunk nobody reads instead
+  // of branching, so the whole body between the backup handling is one block: the A writes
+  // (VALU + LDS) interleave with the MFMAs (sched_group_barrier below).  load_next: the
+  // units of the tile after chunk ci+1 are fetched in this step (a compile-time pattern).
+  auto step = [&](int ci, int cb, unsigned char* sBc, unsigned char* sBn, bool load_next)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): B(ci), the units, backup rows landed
+    if (ci > 0) bk_finish(ci / NCH, ci % NCH, cb);  // backup rows of chunk ci (loaded last step)
     __syncthreads();                     // A(ci), B(ci) complete; step ci-1's buffers free
-    const int cn = ci + 1;
-    const bool more = cn < nch;
-    // fragments are double-buffered across the k-steps: the reads of k-step kk+1 are in
-    // flight while the MFMAs of kk run (the first ones during the A writes below)
+    const int cn = ci + 1 < nch ? ci + 1 : nch - 1;
+    const int c_next = cn % NCH;
+    const uint64_t ov = ballot64(cnt > (uint32_t)W);
+    bk_begin(ov, cn / NCH, c_next);  // overflowing rows of chunk cn: loads in flight until
+                                     // the top of the next step writes them
     bf16x8_m fa[2][4], fb[2][4];
     auto load_frags = [&](int kk, bf16x8_m* a, bf16x8_m* b) __attribute__((always_inline)) {
 #pragma unroll
@@ -272,38 +287,42 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = b_frag(sBc, j, kk);
     };
-    if (active) load_frags(0, fa[0], fb[0]);
-    if (more) {
-      issue_B(cn, sBn);
-      clear_a(cb ^ 1);
-      build_main(cn % NCH, cb ^ 1);
-      const uint64_t ov = ballot64(cnt > (uint32_t)W);
-      // units of step cn+1 when it starts a new tile; they land during the MFMAs
-      if ((cn + 1) % NCH == 0 && cn + 1 < nch) load_units((cn + 1) / NCH);
-      bk_begin(ov, cn / NCH, cn % NCH);
-    }
-    // the first fragments have long arrived; an explicit wait here lets the counter
-    // tracking start clean, so the reads of k-step 1 overlap the MFMAs of k-step 0
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    if (active) {
+    load_frags(0, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + 1 < NKK) load_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
-                                                                acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + 1 < NKK) load_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (kk == 0) {
+        issue_B(cn, sBn);
+        clear_a(cb ^ 1);
       }
+      build_part(kk, c_next, cb ^ 1);
+      if (kk == NKK - 1 && load_next) {
+        const int kt = (cn + 1) / NCH;
+        load_units(kt < d.nt ? kt : d.nt - 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+      // one MFMA, then a few vector and LDS instructions in its shadow
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x080, 2, 0);  // LDS
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) bk_finish(cn / NCH, cn % NCH, cb ^ 1);
   };
-  for (int ci = 0; ci < nch; ci += 2) {
-    step(ci, 0, sB0, sB1);
-    if (ci + 1 < nch) step(ci + 1, 1, sB1, sB0);
+  constexpr int UF = NCH < 2 ? 2 : NCH;  // steps per unrolled iteration (nch % UF == 0)
+  for (int base = 0; base < nch; base += UF) {
+#pragma unroll
+    for (int s2 = 0; s2 < UF; ++s2)
+      step(base + s2, s2 & 1, (s2 & 1) ? sB1 : sB0, (s2 & 1) ? sB0 : sB1, (s2 + 2) % NCH == 0);
   }
 
   // ---- y (bf16): C[m = token][n = column]; lane: column l32, rows 8(r/4) + 4lh + r%4
