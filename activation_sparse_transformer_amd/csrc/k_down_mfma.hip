@@ -194,12 +194,16 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     }
   };
   // positions of the overflowing rows, entry of the first; loads the first batch
-  auto bk_begin = [&](uint64_t ov, int k, int c) __attribute__((always_inline)) {
+  auto bk_begin = [&](uint64_t ov, int e0, int k, int c) __attribute__((always_inline)) {
     bk_n = __builtin_popcountll(ov);
     if (bk_n == 0) return;
     if ((ov >> lane) & 1) pos[mbcnt64(ov)] = (uint8_t)lane;
-    bk_e0 = ld_uniform(grp_first + k * d.ng + tw / GROUP);
+    bk_e0 = e0;
     bk_load(k, c, 0);
+  };
+  // first backup entry of this wave's rows in tile k (scalar load, issued a step ahead)
+  auto first_entry = [&](int k) __attribute__((always_inline)) -> int {
+    return ld_uniform(grp_first + (k < d.nt ? k : d.nt - 1) * d.ng + tw / GROUP);
   };
   // writes the first batch, then any further batches
   auto bk_finish = [&](int k, int c, int buf) __attribute__((always_inline)) {
@@ -261,9 +265,10 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   {
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
     if (NCH == 1) load_units(d.nt > 1 ? 1 : 0);
-    bk_begin(ov, 0, 0);
+    bk_begin(ov, first_entry(0), 0, 0);
     bk_finish(0, 0, 0);
   }
+  int e0_next = first_entry(1 / NCH);  // first backup entry for the chunk step 0 prepares
 
   // step ci: MFMAs of step ci (A and B buffers ci&1) while the A rows of step ci+1 are
   // written into the other A buffer.  The last step rebuilds a chunk nobody reads instead
@@ -278,7 +283,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     const int cn = ci + 1 < nch ? ci + 1 : nch - 1;
     const int c_next = cn % NCH;
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
-    bk_begin(ov, cn / NCH, c_next);  // overflowing rows of chunk cn: loads in flight until
+    const int e0 = e0_next;
+    e0_next = first_entry((ci + 2) / NCH);  // for the next step, ready by then
+    bk_begin(ov, e0, cn / NCH, c_next);  // overflowing rows of chunk cn: loads in flight until
                                      // the top of the next step writes them
     bf16x8_m fa[2][4], fb[2][4];
     auto load_frags = [&](int kk, bf16x8_m* a, bf16x8_m* b) __attribute__((always_inline)) {
