@@ -1,0 +1,491 @@
+// Backward pass of the activation-sparse ReLU FFN layer over its packed activations (gfx950).
+//
+// The layer is y = h W_down with h = ReLU(x W_up^T + b) (upppp.jp TwELL article of
+// 2026-05-11, section "What is the waste in LLM FFN layers").  Its training kernel works on
+// the same hybrid representation as the forward pass, without a dense hidden tensor (same
+// article, section "What TwELL and the custom CUDA kernels solve").  With g = dL/dy:
+//
+//   dh[t, j]      = sum_d g[t, d] W_down[j, d]   at the stored positions of h (ReLU mask)
+//   dW_down[j, :] = sum_t h[t, j]  g[t, :]        = H^T g
+//   dW_up[j, :]   = sum_t dh[t, j] x[t, :]        = dH^T x
+//   db[j]         = sum_t dh[t, j]
+//   dx[t, :]      = sum_j dh[t, j] W_up[j, :]     (the forward's matrix-core down kernel)
+//
+// dh is written in the TwELL structure of h (same counts, columns and backup entries; its own
+// values), rounded to bf16 like the forward's stored activations.
+//
+// sddmm_kernel: one workgroup per (256-token block, 128 hidden columns).  C = g_blk W_blk^T
+// on v_mfma_f32_32x32x16_bf16 (both operands contiguous along d, loaded global -> LDS with
+// direct loads, double-buffered, 64 columns of d per step); C goes through LDS as bf16 and
+// each token row picks the values of its stored slots (and its backup slice's nonzero
+// positions).
+//
+// tmm_kernel: one workgroup per (128 hidden columns, 256 columns of d): dW = H^T M summed
+// over 64-token steps.  Each step rebuilds the 64 x 128 block of H in LDS from TwELL rows
+// (as the forward's down kernel does) and loads M (g or x) rows with direct loads; both MFMA
+// operands come out of the token-major tiles through ds_read_b64_tr_b16.  With DB the same
+// kernel also sums the A fragments into db.
+#include "sffn_common.hpp"
+
+namespace sffn {
+
+typedef __bf16 bf16x8_b __attribute__((ext_vector_type(8)));
+typedef short short4_b __attribute__((ext_vector_type(4)));
+typedef short short8_b __attribute__((ext_vector_type(8)));
+typedef float floatx16_b __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_vptr_b;
+typedef __attribute__((address_space(3))) short4_b* lds_s4ptr_b;
+
+constexpr int BW_JB = 128;  // hidden columns per workgroup
+
+// ============================================================================ SDDMM
+template <int K, int W>
+__global__ __launch_bounds__(256) void sddmm_kernel(
+    Dims d, const uint16_t* __restrict__ g, const uint16_t* __restrict__ Wd,
+    const uint16_t* __restrict__ counts, const uint8_t* __restrict__ cols,
+    const uint16_t* __restrict__ h_bk, const int32_t* __restrict__ grp_first,
+    uint16_t* __restrict__ dh_vals, uint16_t* __restrict__ dh_bk) {
+  constexpr int HALVES = K / BW_JB;  // workgroups per tile along the hidden columns
+  constexpr int ROW = 128;           // bytes of one 64-column bf16 row of a step tile
+  // step tiles: g rows of 256 tokens (A) and W_down rows of 128 hidden columns (B), both
+  // 64 values of d; 16-byte piece p of row r at p ^ ((r >> 1) & 7)
+  __shared__ __attribute__((aligned(16))) unsigned char sA0[256 * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sA1[256 * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sB0[128 * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sB1[128 * ROW];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 1, wj = wave & 1;  // MFMA tile: tokens 128wt.., columns 64wj..
+  const int T = d.T, D = d.D;
+  const int nj = d.F / BW_JB;
+  const int ntb = (T + 255) / 256;
+  const int total = nj * ntb;
+  const int per_xcd = (total + 7) / 8;
+  const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (P >= total) return;
+  const int tb = P / nj;
+  const int jb = P - tb * nj;
+  const int t0 = tb * 256;
+  const int j0 = jb * BW_JB;
+  const int k = j0 / K, hf = (j0 % K) / BW_JB;
+
+  auto issue = [&](int s, unsigned char* sA, unsigned char* sB) __attribute__((always_inline)) {
+    const int dcol = s * 64;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // A: 32 loads of 1 KB (8 rows), 8 per wave
+      const int ins = q * 4 + wave;
+      const int r = ins * 8 + (lane >> 3), pc = lane & 7;
+      const int lc = pc ^ ((r >> 1) & 7);
+      int t = t0 + r;
+      t = t < T ? t : T - 1;  // rows past T: never written out
+      __builtin_amdgcn_global_load_lds(g + (size_t)t * D + dcol + lc * 8,
+                                       (lds_vptr_b)(sA + ins * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // B: 16 loads, 4 per wave
+      const int ins = q * 4 + wave;
+      const int r = ins * 8 + (lane >> 3), pc = lane & 7;
+      const int lc = pc ^ ((r >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(Wd + (size_t)(j0 + r) * D + dcol + lc * 8,
+                                       (lds_vptr_b)(sB + ins * 1024), 16, 0, 0);
+    }
+  };
+  const int l32 = lane & 31, lh = lane >> 5;
+  auto frag = [&](const unsigned char* s, int row, int kk) __attribute__((always_inline)) -> bf16x8_b {
+    const int ch = kk * 2 + lh;
+    return __builtin_bit_cast(
+        bf16x8_b, *reinterpret_cast<const uint4*>(s + row * ROW + ((ch ^ ((row >> 1) & 7)) << 4)));
+  };
+
+  floatx16_b acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nsteps = D / 64;
+  issue(0, sA0, sB0);
+  auto step = [&](int s, unsigned char* sA, unsigned char* sB, unsigned char* nA, unsigned char* nB)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (s + 1 < nsteps) issue(s + 1, nA, nB);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_b fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = frag(sA, 128 * wt + 32 * i + l32, kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = frag(sB, 64 * wj + 32 * j + l32, kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  for (int s = 0; s < nsteps; s += 2) {  // D % 256 == 0: nsteps is even
+    step(s, sA0, sB0, sA1, sB1);
+    step(s + 1, sA1, sB1, sA0, sB0);
+  }
+  __syncthreads();  // every wave is done with the step tiles
+
+  // ---- C (bf16) -> LDS: token row t (0..255) of 256 B at (t < 128 ? sA0 : sA1) + (t & 127) * 256
+  auto crow = [&](int t) __attribute__((always_inline)) -> unsigned char* {
+    return (t < 128 ? sA0 : sA1) + (t & 127) * 256;
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 128 * wt + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int c = 64 * wj + 32 * j + l32;
+        *reinterpret_cast<uint16_t*>(crow(t) + 2 * c) = f32_to_bf16(acc[i][j][r]);
+      }
+  __syncthreads();
+
+  // ---- main slots: thread tid <-> token t0 + tid
+  const int t = t0 + tid;
+  uint32_t cnt = 0;
+  if (t < T) {
+    cnt = counts[(size_t)k * T + t];
+    const unsigned char* cr = crow(tid);
+    const size_t e0 = ((size_t)k * T + t) * W;
+    const uint32_t m = cnt < (uint32_t)W ? cnt : (uint32_t)W;
+#pragma unroll
+    for (int q = 0; q < W / 8; ++q) {
+      const uint2 cw = *reinterpret_cast<const uint2*>(cols + e0 + 8 * q);
+      const uint32_t cc[2] = {cw.x, cw.y};
+      if constexpr (HALVES == 1) {
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t c0 = (cc[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+          const uint32_t c1 = (cc[(e + 1) >> 2] >> (8 * ((e + 1) & 3))) & 0xFFu;
+          const uint32_t v0 = (uint32_t)(8 * q + e) < m ? *reinterpret_cast<const uint16_t*>(cr + 2 * c0) : 0u;
+          const uint32_t v1 = (uint32_t)(8 * q + e + 1) < m ? *reinterpret_cast<const uint16_t*>(cr + 2 * c1) : 0u;
+          o[e >> 1] = v0 | (v1 << 16);
+        }
+        *reinterpret_cast<uint4*>(dh_vals + e0 + 8 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+        // two workgroups share the row: each writes the slots in its half; the first also
+        // writes the padding
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t s = 8 * q + e;
+          const uint32_t c = (cc[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+          if (s < m) {
+            if ((int)(c >> 7) == hf)
+              dh_vals[e0 + s] = *reinterpret_cast<const uint16_t*>(cr + 2 * (c & 127));
+          } else if (hf == 0) {
+            dh_vals[e0 + s] = 0;
+          }
+        }
+      }
+    }
+  }
+
+  // ---- backup slices: wave w covers tokens 64w..64w+63 of the block (two 32-token groups);
+  // the entries of a group's overflowing rows are consecutive, in token order
+  {
+    const int tw = t0 + 64 * wave;
+    const int tl = tw + lane;
+    uint32_t cl = 0;
+    if (tl < T) cl = counts[(size_t)k * T + tl];
+    const uint64_t ov_all = ballot64(cl > (uint32_t)W);
+    uint64_t ov = ov_all;
+    while (ov != 0) {
+      const int b = __builtin_ctzll(ov);
+      ov &= ov - 1;
+      const uint64_t below =
+          ov_all & ((1ull << b) - 1ull) & (b >= 32 ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
+      const int e = ld_uniform(grp_first + k * d.ng + tw / GROUP + (b >> 5)) + __builtin_popcountll(below);
+      if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
+      const unsigned char* cr = crow(64 * wave + b);
+      const size_t base = (size_t)e * K + hf * BW_JB + 2 * lane;
+      const uint32_t hv = *reinterpret_cast<const uint32_t*>(h_bk + base);
+      const uint32_t cv = *reinterpret_cast<const uint32_t*>(cr + 4 * lane);
+      const uint32_t lo = (hv & 0xFFFFu) ? (cv & 0xFFFFu) : 0u;
+      const uint32_t hi = (hv >> 16) ? (cv & 0xFFFF0000u) : 0u;
+      *reinterpret_cast<uint32_t*>(dh_bk + base) = lo | hi;
+    }
+  }
+}
+
+// ============================================================================ H^T M
+template <int K, int W, bool DB>
+__global__ __launch_bounds__(256) void tmm_kernel(
+    Dims d, const uint16_t* __restrict__ Hv, const uint16_t* __restrict__ Hbk,
+    const uint16_t* __restrict__ counts, const uint8_t* __restrict__ cols,
+    const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ M,
+    float* __restrict__ dW, float* __restrict__ db) {
+  constexpr int U = W / 8;                  // 8-slot units per tile-row
+  constexpr int NU = (16 * U + 63) / 64;    // units per lane (a wave writes 16 rows)
+  constexpr int HROW = 256;                 // H step tile: 64 tokens x 128 columns, bf16
+  constexpr int HBUF = 64 * HROW;
+  constexpr int MROW = 512;                 // M step tile: 64 tokens x 256 columns, bf16
+  constexpr int MBUF = 64 * MROW;
+  // H buffers (written by the waves) then 256 B of dummy words for padding writes; M
+  // buffers (filled by direct loads).  Piece p of row r sits at p ^ (2*(r&3)) in both, so
+  // the four rows of a transposed read hit distinct banks.
+  __shared__ __attribute__((aligned(16))) unsigned char sH[2 * HBUF + 256];
+  __shared__ __attribute__((aligned(16))) unsigned char sM0[MBUF];
+  __shared__ __attribute__((aligned(16))) unsigned char sM1[MBUF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wj = wave >> 1, wd = wave & 1;  // MFMA tile: columns j 64wj.., d 128wd..
+  const int T = d.T, D = d.D;
+  const int nj = d.F / BW_JB;
+  const int nd = D / 256;
+  const int total = nj * nd;
+  const int per_xcd = (total + 7) / 8;
+  const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (P >= total) return;
+  // column-chunk-major: the workgroups an XCD runs together read the same M columns
+  const int dchunk = P / nj;
+  const int jb = P - dchunk * nj;
+  const int d0 = dchunk * 256;
+  const int j0 = jb * BW_JB;
+  const int k = j0 / K, hf = (j0 % K) / BW_JB;
+  const uint32_t trash = 2 * HBUF + 4 * lane;
+  const size_t row_base = (size_t)k * T;
+
+  auto issue_M = [&](int ts, unsigned char* sM) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {  // 32 loads of 1 KB (two rows), 8 per wave
+      const int ins = q * 4 + wave;
+      const int slot = ins * 64 + lane;
+      const int r = slot >> 5, pc = slot & 31;
+      const int lc = pc ^ (2 * (r & 3));
+      int t = ts * 64 + r;
+      t = t < T ? t : T - 1;  // rows past T meet zero rows of H
+      __builtin_amdgcn_global_load_lds(M + (size_t)t * D + d0 + lc * 8,
+                                       (lds_vptr_b)(sM + ins * 1024), 16, 0, 0);
+    }
+  };
+
+  // ---- TwELL units of this wave's 16 rows of a 64-token step: unit u = lane + 64q
+  // (u < 16U) holds slots 8*(u%U) .. +7 of token 64ts + 16*wave + u/U
+  uint4 uv[NU];
+  uint2 uc[NU];
+  uint32_t cnt = 0;  // count of token 64ts + lane (for the backup rows of the whole step)
+  auto load_units = [&](int ts) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int u = lane + 64 * q;
+      const int uu = u < 16 * U ? u : 0;
+      int tok = ts * 64 + 16 * wave + uu / U;
+      tok = tok < T ? tok : T - 1;
+      const size_t e0 = (row_base + tok) * W + 8 * (uu % U);
+      uv[q] = *reinterpret_cast<const uint4*>(Hv + e0);
+      uc[q] = *reinterpret_cast<const uint2*>(cols + e0);
+    }
+    const int tl = ts * 64 + lane;
+    cnt = counts[row_base + (tl < T ? tl : T - 1)];
+  };
+  auto h_off = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
+    return buf * HBUF + r * HROW + ((((cc >> 3) ^ (2 * (r & 3))) << 4) | ((cc & 7) << 1));
+  };
+  auto build = [&](int ts, int buf) __attribute__((always_inline)) {
+    // clear this wave's 16 rows (4 KB)
+    uint4* p = reinterpret_cast<uint4*>(sH + buf * HBUF + 16 * wave * HROW);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int u = lane + 64 * q;
+      const uint32_t r = 16 * wave + (uint32_t)(u < 16 * U ? u : 0) / U;  // row of the step tile
+      const bool ok = u < 16 * U && ts * 64 + (int)r < T;
+      const uint32_t vv[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
+      const uint32_t cw[2] = {uc[q].x, uc[q].y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+        const uint32_t word = vv[e >> 1];
+        const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
+        bool in = true;
+        if constexpr (K > BW_JB) in = (int)(col >> 7) == hf;
+        const uint32_t a = (ok && nz && in) ? h_off(buf, r, col & (BW_JB - 1)) : trash;
+        *reinterpret_cast<uint16_t*>(sH + a) = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+      }
+    }
+    // backup slices of the overflowing rows among this wave's 16
+    const uint64_t ov_all = ballot64(cnt > (uint32_t)W && ts * 64 + lane < T);
+    uint64_t ov = ov_all & (0xFFFFull << (16 * wave));
+    while (ov != 0) {
+      const int b = __builtin_ctzll(ov);
+      ov &= ov - 1;
+      const uint64_t below = ov_all & ((1ull << b) - 1ull) & (b >= 32 ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
+      const int e = ld_uniform(grp_first + k * d.ng + ts * 2 + (b >> 5)) + __builtin_popcountll(below);
+      if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
+      const uint32_t hv = *reinterpret_cast<const uint32_t*>(Hbk + (size_t)e * K + hf * BW_JB + 2 * lane);
+      const uint32_t c0 = 2 * lane;
+      const uint32_t a0 = (hv & 0xFFFFu) ? h_off(buf, b, c0) : trash;
+      *reinterpret_cast<uint16_t*>(sH + a0) = (uint16_t)hv;
+      const uint32_t a1 = (hv >> 16) ? h_off(buf, b, c0 + 1) : trash;
+      *reinterpret_cast<uint16_t*>(sH + a1) = (uint16_t)(hv >> 16);
+    }
+  };
+
+  const int g16 = lane >> 4, li = lane & 15;
+  const int l32 = lane & 31, lh = lane >> 5;
+  // transposed read: lane L of a 16-lane group reads row r0 + L/4, columns c0 + 4(L%4)..;
+  // lane i then holds column c0 + i of rows r0..r0+3
+  auto tr_frag = [&](const unsigned char* base, int rowb, int c0, int kk) __attribute__((always_inline)) -> bf16x8_b {
+    const int col = c0 + 16 * (g16 & 1) + 4 * (li & 3);
+    short4_b h[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = kk * 16 + 8 * (g16 >> 1) + 4 * q + (li >> 2);
+      const int off = r * rowb + ((((col >> 3) ^ (2 * (r & 3))) << 4) | ((col & 7) << 1));
+      h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr_b)(base + off));
+    }
+    const short8_b v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8_b, v);
+  };
+
+  floatx16_b acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  float dbacc[2] = {0.0f, 0.0f};
+  const bool do_db = DB && dchunk == 0 && wd == 0;
+
+  const int nts = (T + 63) / 64;
+  issue_M(0, sM0);
+  load_units(0);
+  build(0, 0);
+  if (nts > 1) load_units(1);
+  auto step = [&](int ts, int cb, unsigned char* sMc, unsigned char* sMn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): M(ts) and the units have landed
+    __syncthreads();                     // H(ts), M(ts) complete; step ts-1's buffers free
+    const bool more = ts + 1 < nts;
+    if (more) {
+      issue_M(ts + 1, sMn);
+      build(ts + 1, cb ^ 1);
+      if (ts + 2 < nts) load_units(ts + 2);
+    }
+    const unsigned char* hb = sH + cb * HBUF;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_b fa[2], fb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = tr_frag(hb, HROW, 64 * wj + 32 * i, kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = tr_frag(sMc, MROW, 128 * wd + 32 * j, kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      if (do_db) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float s = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += (float)fa[i][e];
+          dbacc[i] += s;
+        }
+      }
+    }
+  };
+  for (int ts = 0; ts < nts; ts += 2) {
+    step(ts, 0, sM0, sM1);
+    if (ts + 1 < nts) step(ts + 1, 1, sM1, sM0);
+  }
+
+  // ---- dW (fp32): C[m = j][n = d]; lane: column l32, rows 8(r/4) + 4lh + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jr = j0 + 64 * wj + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        dW[(size_t)jr * D + d0 + 128 * wd + 32 * j + l32] = acc[i][j][r];
+      }
+  if (do_db) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float s = dbacc[i] + __shfl_xor(dbacc[i], 32);
+      if (lh == 0) db[j0 + 64 * wj + 32 * i + l32] = s;
+    }
+  }
+}
+
+// ============================================================================ launchers
+bool backward_supported(const Dims& d) {
+  return d.bf16 && (d.K == 128 || d.K == 256) && d.D % 256 == 0 &&
+         (d.W == 16 || d.W == 32 || d.W == 48 || d.W == 64);
+}
+
+template <int K, int W>
+static hipError_t launch_bwd_t(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
+                               const uint16_t* x, const uint16_t* g, const uint16_t* Wd,
+                               uint16_t* dh_vals, uint16_t* dh_bk, float* dW_up, float* dW_down,
+                               float* db, hipStream_t s) {
+  const int nj = d.F / BW_JB;
+  {
+    const int total = nj * ((d.T + 255) / 256);
+    hipLaunchKernelGGL((sddmm_kernel<K, W>), dim3(8 * ((total + 7) / 8)), dim3(256), 0, s, d, g,
+                       Wd, act.counts, act.cols, static_cast<const uint16_t*>(act.bk_vals),
+                       ws.grp_first, dh_vals, dh_bk);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int total = nj * (d.D / 256);
+  const dim3 grid(8 * ((total + 7) / 8));
+  hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(256), 0, s, d,
+                     static_cast<const uint16_t*>(act.vals),
+                     static_cast<const uint16_t*>(act.bk_vals), act.counts, act.cols,
+                     ws.grp_first, g, dW_down, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (db) {
+    hipLaunchKernelGGL((tmm_kernel<K, W, true>), grid, dim3(256), 0, s, d, dh_vals, dh_bk,
+                       act.counts, act.cols, ws.grp_first, x, dW_up, db);
+  } else {
+    hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(256), 0, s, d, dh_vals, dh_bk,
+                       act.counts, act.cols, ws.grp_first, x, dW_up, nullptr);
+  }
+  return hipGetLastError();
+}
+
+template <int K>
+static hipError_t launch_bwd_k(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
+                               const uint16_t* x, const uint16_t* g, const uint16_t* Wd,
+                               uint16_t* dh_vals, uint16_t* dh_bk, float* dW_up, float* dW_down,
+                               float* db, hipStream_t s) {
+  switch (d.W) {
+    case 16: return launch_bwd_t<K, 16>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 32: return launch_bwd_t<K, 32>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 48: return launch_bwd_t<K, 48>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 64: return launch_bwd_t<K, 64>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_weights(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
+                                   const void* x, const void* g, const void* Wd, void* dh_vals,
+                                   void* dh_bk, float* dW_up, float* dW_down, float* db,
+                                   hipStream_t s) {
+  if (!backward_supported(d)) return hipErrorInvalidValue;
+  auto* xx = static_cast<const uint16_t*>(x);
+  auto* gg = static_cast<const uint16_t*>(g);
+  auto* ww = static_cast<const uint16_t*>(Wd);
+  auto* hv = static_cast<uint16_t*>(dh_vals);
+  auto* hb = static_cast<uint16_t*>(dh_bk);
+  if (d.K == 128) return launch_bwd_k<128>(d, act, ws, xx, gg, ww, hv, hb, dW_up, dW_down, db, s);
+  return launch_bwd_k<256>(d, act, ws, xx, gg, ww, hv, hb, dW_up, dW_down, db, s);
+}
+
+}  // namespace sffn

@@ -298,6 +298,34 @@ sffn_status_t sparse_ffn_down(sparse_ffn_t hd, const twell_buffers_t* act, int32
   return down_impl(hd, d, *act, ws, y, s);
 }
 
+sffn_status_t sparse_ffn_backward(sparse_ffn_t hd, const void* x, const void* dy, int32_t T,
+                                  const twell_buffers_t* act, void* dh_vals, void* dh_bk_vals,
+                                  void* dx, float* dW_up, float* dW_down, float* db_up,
+                                  void* stream) {
+  if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  SFFN_TRY(check_T(&hd->cfg, T));
+  if (!x || !dy || !dx || !dW_up || !dW_down || !dh_vals || !dh_bk_vals)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "NULL input, output or dh buffer");
+  SFFN_TRY(check_bufs(act, true));
+  const Dims d = make_dims(&hd->cfg, T);
+  if (!backward_supported(d))
+    return fail(SFFN_ERR_UNSUPPORTED,
+                "backward needs a bf16 layer, tile 128 or 256, ell_width 16/32/48/64 and "
+                "d_model % 256 == 0");
+  const Workspace ws = carve(act->workspace, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SFFN_TRY(run("bwd_weights", s, [&] {
+    return launch_backward_weights(d, *act, ws, x, dy, hd->W_down, dh_vals, dh_bk_vals, dW_up,
+                                   dW_down, db_up, s);
+  }));
+  // dx = dh W_up: the down-projection kernel over dh's TwELL (the structure of act)
+  twell_buffers_t dact = *act;
+  dact.vals = dh_vals;
+  dact.bk_vals = dh_bk_vals;
+  return run("bwd_dx", s,
+             [&] { return launch_down_mfma(d, dact, ws, hd->W_up, dx, nullptr, 0, s); });
+}
+
 sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float mfma_density) {
   if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (policy != SFFN_DOWN_AUTO && policy != SFFN_DOWN_GATHER && policy != SFFN_DOWN_MFMA)

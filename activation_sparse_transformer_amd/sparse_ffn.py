@@ -75,6 +75,8 @@ _PROTOS = {
     "sparse_ffn_forward": ([_P, _P, _I32, _P, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_down": ([_P, ctypes.POINTER(BuffersC), _I32, _P, _P], ctypes.c_int),
     "sparse_ffn_set_down_policy": ([_P, _I32, ctypes.c_float], ctypes.c_int),
+    "sparse_ffn_backward": ([_P, _P, _P, _I32, ctypes.POINTER(BuffersC), _P, _P, _P, _P, _P, _P,
+                             _P], ctypes.c_int),
     "twell_stats": ([ctypes.POINTER(ConfigC), ctypes.POINTER(BuffersC), _I32,
                      ctypes.POINTER(StatsC), _P], ctypes.c_int),
     "sparse_ffn_check": ([ctypes.POINTER(BuffersC), _P], ctypes.c_int),
@@ -296,6 +298,31 @@ class SparseFFN:
             raise ValueError(f"unknown down policy {policy!r}")
         _check(lib().sparse_ffn_set_down_policy(self._h, code, float(mfma_density)),
                "sparse_ffn_set_down_policy")
+
+    def backward(self, x, dy, act: TwellBuffers, with_db: bool = True, stream=None):
+        """Gradients of sparse_ffn_forward(x) -> act for dL/dy = dy.  Returns
+        (dx, dW_up, dW_down, db_up or None, dh_vals, dh_bk_vals); dh is in act's TwELL
+        structure (dh_vals [n_t, T, W], dh_bk_vals [backup_capacity, tile], layer dtype)."""
+        import torch
+        self._check_x(x)
+        self._check_x(dy)
+        T = x.shape[0]
+        if dy.shape[0] != T or act.T != T:
+            raise ValueError("x, dy and act must have the same number of tokens")
+        cfg = self.cfg
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        dev = x.device
+        dh_vals = torch.empty((cfg.n_tiles, T, cfg.ell_width), dtype=dt, device=dev)
+        dh_bk = torch.empty((max(cfg.backup_capacity, 1), cfg.tile), dtype=dt, device=dev)
+        dx = torch.empty_like(x)
+        dW_up = torch.empty((cfg.d_ff, cfg.d_model), dtype=torch.float32, device=dev)
+        dW_down = torch.empty_like(dW_up)
+        db = torch.empty(cfg.d_ff, dtype=torch.float32, device=dev) if with_db else None
+        _check(lib().sparse_ffn_backward(self._h, _ptr(x), _ptr(dy), int(T), ctypes.byref(act.c()),
+                                         _ptr(dh_vals), _ptr(dh_bk), _ptr(dx), _ptr(dW_up),
+                                         _ptr(dW_down), _ptr(db) if db is not None else None,
+                                         _stream_ptr(stream)), "sparse_ffn_backward")
+        return dx, dW_up, dW_down, db, dh_vals, dh_bk
 
     def down(self, act: TwellBuffers, y=None, stream=None):
         """Down-projection only, from an existing TwELL."""

@@ -142,6 +142,28 @@ sffn_status_t sparse_ffn_forward(sparse_ffn_t h, const void *x, int32_t T, void 
 sffn_status_t sparse_ffn_down(sparse_ffn_t h, const twell_buffers_t *act, int32_t T, void *y,
                               void *stream);
 
+/* Backward pass of sparse_ffn_forward (same article, section "What TwELL and the custom
+ * CUDA kernels solve": training works on the same hybrid representation, with no dense
+ * hidden tensor).  Inputs: the forward's x [T, d_model] and act (its packed activations h,
+ * workspace included, unchanged since that forward), and dy = dL/dy [T, d_model], all in the
+ * layer dtype.  With g = dy and the ReLU mask taken as the stored positions of act:
+ *   dh[t, j]      = sum_d g[t, d] W_down[j, d]   at every stored position of h
+ *   dW_down[j, :] = sum_t h[t, j] g[t, :]
+ *   dW_up[j, :]   = sum_t dh[t, j] x[t, :]
+ *   db_up[j]      = sum_t dh[t, j]
+ *   dx[t, :]      = sum_j dh[t, j] W_up[j, :]
+ * Outputs (device, overwritten): dh_vals [n_t, T, W] and dh_bk_vals [backup_capacity, tile]
+ * (dtype; dh in the TwELL structure of act: act's counts, cols and backup entries index it;
+ * values rounded to nearest-even), dx [T, d_model] dtype, dW_up and dW_down [d_ff, d_model]
+ * fp32, db_up [d_ff] fp32 (may be NULL: then not computed).  Accumulation is fp32.
+ * Needs a bf16 layer with tile 128 or 256, ell_width in {16, 32, 48, 64} and d_model % 256
+ * == 0 (SFFN_ERR_UNSUPPORTED otherwise).  If act's status word reports a backup overflow the
+ * outputs are undefined. */
+sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy, int32_t T,
+                                  const twell_buffers_t *act, void *dh_vals, void *dh_bk_vals,
+                                  void *dx, float *dW_up, float *dW_down, float *db_up,
+                                  void *stream);
+
 /* How the down-projection (inside sparse_ffn_forward and sparse_ffn_down) runs each block
  * of 256 tokens.  The TwELL tiles line up with tiled matrix-multiply execution (same
  * article, section "What TwELL and the custom CUDA kernels solve"), so a block can either

@@ -44,8 +44,10 @@ def _load():
     lib.oracle_down_dense.restype = None
     lib.oracle_down_sparse.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
     lib.oracle_down_sparse.restype = None
-    lib.oracle_backward.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
+    lib.oracle_backward.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_int32, _P, _P, _P, _P, _P]
     lib.oracle_backward.restype = None
+    lib.oracle_backward_from_dh.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P]
+    lib.oracle_backward_from_dh.restype = None
     lib.oracle_ffn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int32, _P, _P, _P]
     lib.oracle_ffn_rows.restype = None
     lib.oracle_round_bf16.argtypes = [_P, _I, _P]
@@ -195,8 +197,9 @@ def ffn_rows(x, W_up, b, W_down, rows, K: int, W: int, return_z: bool = False,
     return (y, counts, z) if return_z else (y, counts)
 
 
-def backward(x, h, g, W_up, W_down):
-    """O9: (dx, dW_up, dW_down, db, dh) of loss = sum(y * g), ReLU mask = stored h != 0."""
+def backward(x, h, g, W_up, W_down, round_dh=False):
+    """O9: (dx, dW_up, dW_down, db, dh) of loss = sum(y * g), ReLU mask = stored h != 0.
+    With round_dh, dh is stored in bf16 (O8) before dW_up, db and dx use it."""
     lib = _load()
     x = _c(x, np.float64); h = _c(h, np.float64); g = _c(g, np.float64)
     W_up = _c(W_up, np.float64); W_down = _c(W_down, np.float64)
@@ -205,8 +208,21 @@ def backward(x, h, g, W_up, W_down):
     dx = np.empty((T, D)); dWu = np.empty((F, D)); dWd = np.empty((F, D))
     db = np.empty(F); dh = np.empty((T, F))
     lib.oracle_backward(_ptr(x), _ptr(h), _ptr(g), _ptr(W_up), _ptr(W_down), T, D, F,
+                        1 if round_dh else 0,
                         _ptr(dx), _ptr(dWu), _ptr(dWd), _ptr(db), _ptr(dh))
     return dx, dWu, dWd, db, dh
+
+
+def backward_from_dh(x, dh, W_up):
+    """(dx, dW_up, db) of O9 for a given dh [T, F] (e.g. the dh a layer stored)."""
+    lib = _load()
+    x = _c(x, np.float64); dh = _c(dh, np.float64); W_up = _c(W_up, np.float64)
+    T, D = x.shape
+    F = W_up.shape[0]
+    dx = np.empty((T, D)); dWu = np.empty((F, D)); db = np.empty(F)
+    lib.oracle_backward_from_dh(_ptr(x), _ptr(dh), _ptr(W_up), T, D, F, _ptr(dx), _ptr(dWu),
+                                _ptr(db))
+    return dx, dWu, db
 
 
 def round_bf16(a) -> np.ndarray:

@@ -194,11 +194,13 @@ void oracle_down_sparse(const uint16_t* counts, const double* vals, const uint8_
 //   db[j]        = sum_t dh[t,j]
 //   dW_up[j,:]   = sum_t dh[t,j] x[t,:]
 //   dx[t,:]      = sum_j dh[t,j] W_up[j,:]
-// Sums run in ascending index order.  dh may be null.
+// Sums run in ascending index order.  dh may be null.  With round_dh, dh is stored in bf16
+// (nearest-even, the O8 model) before it is used, as a bf16 TwELL of dh holds it; dh_out
+// then returns the rounded values.
 void oracle_backward(const double* x, const double* h, const double* g,
                      const double* W_up, const double* W_down, int64_t T, int64_t D,
-                     int64_t F, double* dx, double* dW_up, double* dW_down, double* db,
-                     double* dh_out) {
+                     int64_t F, int32_t round_dh, double* dx, double* dW_up, double* dW_down,
+                     double* db, double* dh_out) {
   std::vector<double> dh((size_t)(T * F), 0.0);
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t)
@@ -206,7 +208,7 @@ void oracle_backward(const double* x, const double* h, const double* g,
       if (h[t * F + j] == 0.0) continue;
       double acc = 0.0;
       for (int64_t d = 0; d < D; ++d) acc += g[t * D + d] * W_down[j * D + d];
-      dh[(size_t)(t * F + j)] = acc;
+      dh[(size_t)(t * F + j)] = round_dh ? round_to_bf16_value(acc) : acc;
     }
   if (dh_out) std::memcpy(dh_out, dh.data(), sizeof(double) * (size_t)(T * F));
 #pragma omp parallel for schedule(static)
@@ -230,6 +232,35 @@ void oracle_backward(const double* x, const double* h, const double* g,
     for (int64_t d = 0; d < D; ++d) r[d] = 0.0;
     for (int64_t j = 0; j < F; ++j) {
       double gv = dh[(size_t)(t * F + j)];
+      const double* w = W_up + j * D;
+      for (int64_t d = 0; d < D; ++d) r[d] += gv * w[d];
+    }
+  }
+}
+
+// The dh-consuming half of O9 for a given dh [T, F] (as a layer stores it): dW_up, db and
+// dx exactly as oracle_backward computes them from its own dh.
+//   dW_up[j,:] = sum_t dh[t,j] x[t,:];  db[j] = sum_t dh[t,j];  dx[t,:] = sum_j dh[t,j] W_up[j,:]
+void oracle_backward_from_dh(const double* x, const double* dh, const double* W_up, int64_t T,
+                             int64_t D, int64_t F, double* dx, double* dW_up, double* db) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < F; ++j) {
+    double* u = dW_up + j * D;
+    for (int64_t d = 0; d < D; ++d) u[d] = 0.0;
+    double bsum = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double gv = dh[t * F + j];
+      for (int64_t d = 0; d < D; ++d) u[d] += gv * x[t * D + d];
+      bsum += gv;
+    }
+    db[j] = bsum;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double* r = dx + t * D;
+    for (int64_t d = 0; d < D; ++d) r[d] = 0.0;
+    for (int64_t j = 0; j < F; ++j) {
+      const double gv = dh[t * F + j];
       const double* w = W_up + j * D;
       for (int64_t d = 0; d < D; ++d) r[d] += gv * w[d];
     }

@@ -408,6 +408,40 @@ def test_backward_euler_identities():
     assert abs(float((dWu * Wu).sum()) - rhs) <= 1e-9 * max(1.0, abs(rhs))
 
 
+def test_backward_bf16_storage_model():
+    """round_dh: dh is the O8 rounding of the exact dh, dW_down does not depend on it, dx and
+    dW_up stay consistent with each other for the rounded dh, and the change in dx is within
+    the bf16 rounding bound of dh."""
+    L = make_layer(CONFIGS["C1b"], seed=0, T=32)
+    x, Wu, b, Wd = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+    g = np.random.default_rng(6).standard_normal((32, x.shape[1]))
+    h = oracle.up_relu(x, Wu, b)
+    dx0, dWu0, dWd0, db0, dh0 = oracle.backward(x, h, g, Wu, Wd)
+    dx1, dWu1, dWd1, db1, dh1 = oracle.backward(x, h, g, Wu, Wd, round_dh=True)
+    assert np.array_equal(dh1, oracle.bf16_value(oracle.round_bf16(dh0)))
+    assert np.array_equal(dWd1, dWd0)
+    assert np.count_nonzero(dh1 != dh0) > 0
+    # <dx, x> = <dW_up, W_up> = sum dh * (z - b), for whichever dh the layer stores
+    z_b = x @ Wu.T
+    ref = float((dh1 * z_b).sum())
+    assert abs(float((dx1 * x).sum()) - ref) <= 1e-9 * max(1.0, abs(ref))
+    assert abs(float((dWu1 * Wu).sum()) - ref) <= 1e-9 * max(1.0, abs(ref))
+    assert abs(float(db1.sum()) - float(dh1.sum())) <= 1e-9 * max(1.0, float(np.abs(dh1).sum()))
+    # the dh-consuming half on its own reproduces the full backward for its dh
+    fx, fwu, fdb = oracle.backward_from_dh(x, dh1, Wu)
+    assert np.array_equal(fx, dx1) and np.array_equal(fwu, dWu1) and np.array_equal(fdb, db1)
+    # and the identity holds for an arbitrary dh
+    dh_any = np.random.default_rng(8).standard_normal(dh1.shape) * (dh1 != 0)
+    ax, awu, adb = oracle.backward_from_dh(x, dh_any, Wu)
+    r2 = float((dh_any * z_b).sum())
+    assert abs(float((ax * x).sum()) - r2) <= 1e-9 * max(1.0, abs(r2))
+    assert abs(float((awu * Wu).sum()) - r2) <= 1e-9 * max(1.0, abs(r2))
+    assert np.allclose(adb, dh_any.sum(axis=0), rtol=0, atol=1e-12)
+    # |dx1 - dx0| <= sum_j |dh1 - dh0| |W_up| <= 2^-8 sum_j |dh0| |W_up|
+    bound = 2.0 ** -8 * (np.abs(dh0) @ np.abs(Wu)) + 1e-12
+    assert np.all(np.abs(dx1 - dx0) <= bound)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
     """Plant plausible mistakes in the Python twin and check the pins reject them."""
