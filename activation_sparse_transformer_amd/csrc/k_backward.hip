@@ -428,29 +428,28 @@ bool backward_supported(const Dims& d) {
          (d.W == 16 || d.W == 32 || d.W == 48 || d.W == 64);
 }
 
+// which: 0 = dh (sddmm), 1 = dW_down (H^T g), 2 = dW_up (+ db if not null) (dH^T x)
 template <int K, int W>
-static hipError_t launch_bwd_t(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
-                               const uint16_t* x, const uint16_t* g, const uint16_t* Wd,
-                               uint16_t* dh_vals, uint16_t* dh_bk, float* dW_up, float* dW_down,
-                               float* db, hipStream_t s) {
+static hipError_t launch_bwd_t(int which, const Dims& d, const twell_buffers_t& act,
+                               const Workspace& ws, const uint16_t* x, const uint16_t* g,
+                               const uint16_t* Wd, uint16_t* dh_vals, uint16_t* dh_bk,
+                               float* dW_up, float* dW_down, float* db, hipStream_t s) {
   const int nj = d.F / BW_JB;
-  {
+  if (which == 0) {
     const int total = nj * ((d.T + 255) / 256);
     hipLaunchKernelGGL((sddmm_kernel<K, W>), dim3(8 * ((total + 7) / 8)), dim3(256), 0, s, d, g,
                        Wd, act.counts, act.cols, static_cast<const uint16_t*>(act.bk_vals),
                        ws.grp_first, dh_vals, dh_bk);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
   const int total = nj * (d.D / 256);
   const dim3 grid(8 * ((total + 7) / 8));
-  hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(256), 0, s, d,
-                     static_cast<const uint16_t*>(act.vals),
-                     static_cast<const uint16_t*>(act.bk_vals), act.counts, act.cols,
-                     ws.grp_first, g, dW_down, nullptr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (db) {
+  if (which == 1) {
+    hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(256), 0, s, d,
+                       static_cast<const uint16_t*>(act.vals),
+                       static_cast<const uint16_t*>(act.bk_vals), act.counts, act.cols,
+                       ws.grp_first, g, dW_down, nullptr);
+  } else if (db) {
     hipLaunchKernelGGL((tmm_kernel<K, W, true>), grid, dim3(256), 0, s, d, dh_vals, dh_bk,
                        act.counts, act.cols, ws.grp_first, x, dW_up, db);
   } else {
@@ -461,31 +460,32 @@ static hipError_t launch_bwd_t(const Dims& d, const twell_buffers_t& act, const 
 }
 
 template <int K>
-static hipError_t launch_bwd_k(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
-                               const uint16_t* x, const uint16_t* g, const uint16_t* Wd,
-                               uint16_t* dh_vals, uint16_t* dh_bk, float* dW_up, float* dW_down,
-                               float* db, hipStream_t s) {
+static hipError_t launch_bwd_k(int which, const Dims& d, const twell_buffers_t& act,
+                               const Workspace& ws, const uint16_t* x, const uint16_t* g,
+                               const uint16_t* Wd, uint16_t* dh_vals, uint16_t* dh_bk,
+                               float* dW_up, float* dW_down, float* db, hipStream_t s) {
   switch (d.W) {
-    case 16: return launch_bwd_t<K, 16>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
-    case 32: return launch_bwd_t<K, 32>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
-    case 48: return launch_bwd_t<K, 48>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
-    case 64: return launch_bwd_t<K, 64>(d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 16: return launch_bwd_t<K, 16>(which, d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 32: return launch_bwd_t<K, 32>(which, d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 48: return launch_bwd_t<K, 48>(which, d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
+    case 64: return launch_bwd_t<K, 64>(which, d, act, ws, x, g, Wd, dh_vals, dh_bk, dW_up, dW_down, db, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_backward_weights(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
-                                   const void* x, const void* g, const void* Wd, void* dh_vals,
-                                   void* dh_bk, float* dW_up, float* dW_down, float* db,
-                                   hipStream_t s) {
+hipError_t launch_backward_part(int which, const Dims& d, const twell_buffers_t& act,
+                                const Workspace& ws, const void* x, const void* g,
+                                const void* Wd, void* dh_vals, void* dh_bk, float* dW_up,
+                                float* dW_down, float* db, hipStream_t s) {
   if (!backward_supported(d)) return hipErrorInvalidValue;
   auto* xx = static_cast<const uint16_t*>(x);
   auto* gg = static_cast<const uint16_t*>(g);
   auto* ww = static_cast<const uint16_t*>(Wd);
   auto* hv = static_cast<uint16_t*>(dh_vals);
   auto* hb = static_cast<uint16_t*>(dh_bk);
-  if (d.K == 128) return launch_bwd_k<128>(d, act, ws, xx, gg, ww, hv, hb, dW_up, dW_down, db, s);
-  return launch_bwd_k<256>(d, act, ws, xx, gg, ww, hv, hb, dW_up, dW_down, db, s);
+  if (d.K == 128)
+    return launch_bwd_k<128>(which, d, act, ws, xx, gg, ww, hv, hb, dW_up, dW_down, db, s);
+  return launch_bwd_k<256>(which, d, act, ws, xx, gg, ww, hv, hb, dW_up, dW_down, db, s);
 }
 
 }  // namespace sffn

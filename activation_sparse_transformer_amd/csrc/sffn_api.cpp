@@ -314,10 +314,12 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t hd, const void* x, const void* dy
                 "d_model % 256 == 0");
   const Workspace ws = carve(act->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SFFN_TRY(run("bwd_weights", s, [&] {
-    return launch_backward_weights(d, *act, ws, x, dy, hd->W_down, dh_vals, dh_bk_vals, dW_up,
-                                   dW_down, db_up, s);
-  }));
+  static const char* const names[3] = {"bwd_dh", "bwd_dw_down", "bwd_dw_up"};
+  for (int which = 0; which < 3; ++which)
+    SFFN_TRY(run(names[which], s, [&] {
+      return launch_backward_part(which, d, *act, ws, x, dy, hd->W_down, dh_vals, dh_bk_vals,
+                                  dW_up, dW_down, db_up, s);
+    }));
   // dx = dh W_up: the down-projection kernel over dh's TwELL (the structure of act)
   twell_buffers_t dact = *act;
   dact.vals = dh_vals;

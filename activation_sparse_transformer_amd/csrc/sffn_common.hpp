@@ -123,12 +123,13 @@ hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, 
                        const int32_t* blk_nnz, int thr, hipStream_t s);
 bool down_mfma_supported(const Dims& d);
 bool backward_supported(const Dims& d);
-// dh at the stored positions of `act` (into dh_vals / dh_bk), dW_down = H^T g, dW_up = dH^T x
-// and, if db is not null, db = column sums of dH.
-hipError_t launch_backward_weights(const Dims& d, const twell_buffers_t& act, const Workspace& ws,
-                                   const void* x, const void* g, const void* Wd, void* dh_vals,
-                                   void* dh_bk, float* dW_up, float* dW_down, float* db,
-                                   hipStream_t s);
+// One part of the backward weights pass: which = 0: dh at the stored positions of `act`
+// (into dh_vals / dh_bk); 1: dW_down = H^T g; 2: dW_up = dH^T x and, if db is not null,
+// db = column sums of dH.
+hipError_t launch_backward_part(int which, const Dims& d, const twell_buffers_t& act,
+                                const Workspace& ws, const void* x, const void* g,
+                                const void* Wd, void* dh_vals, void* dh_bk, float* dW_up,
+                                float* dW_down, float* db, hipStream_t s);
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, int thr,
                             hipStream_t s);

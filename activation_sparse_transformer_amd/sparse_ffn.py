@@ -299,10 +299,11 @@ class SparseFFN:
         _check(lib().sparse_ffn_set_down_policy(self._h, code, float(mfma_density)),
                "sparse_ffn_set_down_policy")
 
-    def backward(self, x, dy, act: TwellBuffers, with_db: bool = True, stream=None):
+    def backward(self, x, dy, act: TwellBuffers, with_db: bool = True, out=None, stream=None):
         """Gradients of sparse_ffn_forward(x) -> act for dL/dy = dy.  Returns
         (dx, dW_up, dW_down, db_up or None, dh_vals, dh_bk_vals); dh is in act's TwELL
-        structure (dh_vals [n_t, T, W], dh_bk_vals [backup_capacity, tile], layer dtype)."""
+        structure (dh_vals [n_t, T, W], dh_bk_vals [backup_capacity, tile], layer dtype).
+        `out` may pass that tuple back in to be overwritten instead of allocated."""
         import torch
         self._check_x(x)
         self._check_x(dy)
@@ -310,14 +311,17 @@ class SparseFFN:
         if dy.shape[0] != T or act.T != T:
             raise ValueError("x, dy and act must have the same number of tokens")
         cfg = self.cfg
-        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-        dev = x.device
-        dh_vals = torch.empty((cfg.n_tiles, T, cfg.ell_width), dtype=dt, device=dev)
-        dh_bk = torch.empty((max(cfg.backup_capacity, 1), cfg.tile), dtype=dt, device=dev)
-        dx = torch.empty_like(x)
-        dW_up = torch.empty((cfg.d_ff, cfg.d_model), dtype=torch.float32, device=dev)
-        dW_down = torch.empty_like(dW_up)
-        db = torch.empty(cfg.d_ff, dtype=torch.float32, device=dev) if with_db else None
+        if out is not None:
+            dx, dW_up, dW_down, db, dh_vals, dh_bk = out
+        else:
+            dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+            dev = x.device
+            dh_vals = torch.empty((cfg.n_tiles, T, cfg.ell_width), dtype=dt, device=dev)
+            dh_bk = torch.empty((max(cfg.backup_capacity, 1), cfg.tile), dtype=dt, device=dev)
+            dx = torch.empty_like(x)
+            dW_up = torch.empty((cfg.d_ff, cfg.d_model), dtype=torch.float32, device=dev)
+            dW_down = torch.empty_like(dW_up)
+            db = torch.empty(cfg.d_ff, dtype=torch.float32, device=dev) if with_db else None
         _check(lib().sparse_ffn_backward(self._h, _ptr(x), _ptr(dy), int(T), ctypes.byref(act.c()),
                                          _ptr(dh_vals), _ptr(dh_bk), _ptr(dx), _ptr(dW_up),
                                          _ptr(dW_down), _ptr(db) if db is not None else None,

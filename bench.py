@@ -31,6 +31,7 @@ PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # launches of one forward, by the names the library's event timing uses
 KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_mfma")
+TRAIN_KERNELS = KERNELS + ("bwd_dh", "bwd_dw_down", "bwd_dw_up", "bwd_dx")
 
 
 def log(msg):
@@ -55,6 +56,7 @@ def main():
     ap.add_argument("--rho", type=float, default=0.05, help="density of the headline point")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the forward+backward timing")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times): the reference "
                          "kernel that scales hardware byte counters to bytes")
@@ -156,6 +158,61 @@ def main():
     log("dense bf16 FFN baseline")
     ms_dense, _ = time_steps(dense, args.steps, args.warmup)
     log(f"  {ms_dense:.4f} ms/step")
+
+    # ---- training step of the same layer (1.5B-like training layer): forward + backward over
+    # TwELL, against the dense bf16 FFN forward + its backward matmuls
+    train = None
+    if not args.no_train:
+        g = torch.from_numpy(np.random.default_rng(11).standard_normal((T, D)).astype(np.float32))
+        dy = g.to(dev).to(torch.bfloat16)
+        layer_t = sffn.SparseFFN(cfg, Wu, b0, Wd)
+        bout = layer_t.backward(x, dy, layer_t.forward(x, act=act, y=y)[1])
+
+        def sparse_train():
+            layer_t.forward(x, act=act, y=y)
+            layer_t.backward(x, dy, act, out=bout)
+
+        def sparse_bwd():
+            layer_t.backward(x, dy, act, out=bout)
+
+        def dense_train():
+            h = Fn.relu(Fn.linear(x, Wu, b0))
+            torch.matmul(h, Wd)
+            dWd_d = torch.matmul(h.t(), dy)
+            dh = torch.matmul(dy, Wd.t()) * (h > 0)
+            dWu_d = torch.matmul(dh.t(), x)
+            dh.sum(dim=0)
+            torch.matmul(dh, Wu)
+            return dWd_d, dWu_d
+
+        log("training step: sparse forward + backward, dense bf16 forward + backward")
+        for _ in range(3):
+            sparse_train()
+        torch.cuda.synchronize()
+        sffn.profile_reset()
+        sffn.profile_enable(True)
+        ms_tr, _ = time_steps(sparse_train, max(10, args.steps // 2), 0)
+        sffn.profile_enable(False)
+        ktr = {}
+        for k in TRAIN_KERNELS:
+            tot, n = sffn.profile_read(k)
+            ktr[k] = round(tot / max(n, 1), 5)
+        sffn.profile_reset()
+        ms_bwd, _ = time_steps(sparse_bwd, max(10, args.steps // 2), 3)
+        ms_dtr, _ = time_steps(dense_train, max(10, args.steps // 2), 3)
+        train = {"workload": "1.5B-like training layer (same shapes and density as the forward), "
+                             "dL/dy ~ N(0,1) in bf16; backward = dh at the stored positions, "
+                             "dW_down, dW_up, db (fp32) and dx",
+                 "ms_forward_backward": round(ms_tr, 5), "ms_backward": round(ms_bwd, 5),
+                 "tokens_per_s": round(T / (ms_tr * 1e-3), 1),
+                 "dense_ms_forward_backward": round(ms_dtr, 5),
+                 "dense_tokens_per_s": round(T / (ms_dtr * 1e-3), 1),
+                 "speedup_vs_dense": round(ms_dtr / ms_tr, 4),
+                 "kernel_ms": ktr,
+                 "saved_activation_bytes": int(st["bytes_main"] + st["bytes_backup"]),
+                 "dense_activation_bytes": int(st["bytes_dense_equiv"])}
+        log(f"  sparse {ms_tr:.4f} ms (backward {ms_bwd:.4f}), dense {ms_dtr:.4f} ms; {ktr}")
+        del bout
 
     # ---- density sweep
     sweep = []
@@ -266,6 +323,7 @@ def main():
                      "ell_fill": round(st["ell_fill"], 4)},
         "kernels": kernels,
         "effective_tflops_dense_equiv": round(4.0 * T * D * F / (ms * 1e-3) / 1e12, 2),
+        "train": train,
         "sweep": sweep,
         "kernel_source_hash": src_hash,
     }

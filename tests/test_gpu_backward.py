@@ -129,3 +129,85 @@ def test_backward_arguments():
     with pytest.raises(sffn.SffnError) as ei:
         layer2.backward(x2, x2, act2)
     assert "SFFN_ERR_UNSUPPORTED" in str(ei.value)
+
+
+def test_backward_full_size_sampled():
+    """The 1.5B-like training layer at its full size (T=8192), in the launch configuration
+    the benchmark times: dh and dx of sampled tokens against the oracle run on those tokens
+    (both are per-token quantities); dW_down and dW_up of sampled hidden columns against the
+    oracle run on that column over all tokens; db against the column sums of the stored dh."""
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C5"], seed=0)
+    c = L["cfg"]
+    T = c.T
+    cfg = _cfg(sffn, T, c, cap=c.n_tiles * T // 8)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    y, act = layer.forward(x)
+    assert sffn.check(act) == sffn.SFFN_OK
+    g_bits = f32_to_bf16_bits(np.random.default_rng(3).standard_normal((T, c.D)).astype(np.float32))
+    dy = to_dev_bf16(torch, g_bits)
+    dx, dWu, dWd, db, dh_vals, dh_bk = layer.backward(x, dy, act)
+    torch.cuda.synchronize()
+    host = act.to_host()
+    r = min(host["bk_n"], cfg.backup_capacity)
+    dhost = dict(host)
+    dhost["vals"] = dh_vals.view(torch.int16).cpu().numpy().view(np.uint16)
+    dhost["bk_vals"] = dh_bk.view(torch.int16).cpu().numpy().view(np.uint16)[:r]
+
+    rng = np.random.default_rng(4)
+    rows = np.array(sorted(set([0, T - 1] + L["heavy"][:6].tolist()
+                               + rng.choice(T, 16, replace=False).tolist())), np.int64)
+    from tests.test_gpu_parity import _decode_rows
+    h_rows = _decode_rows(cfg, host, rows)
+    dh_rows = _decode_rows(cfg, dhost, rows)
+    x64, Wu64, Wd64 = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "W_down_f32"))
+    g64 = oracle.bf16_value(g_bits)
+    dx_r, _, _, _, dh_r = oracle.backward(x64[rows], h_rows, g64[rows], Wu64, Wd64, round_dh=True)
+    mask = h_rows != 0
+    assert not np.any(dh_rows[~mask])
+    assert_y_close(dh_rows[mask], dh_r[mask], "bf16", "full dh")
+    fx, _, _ = oracle.backward_from_dh(x64[rows], dh_rows, Wu64)
+    dx_rows = y_to_host(torch, dx[torch.from_numpy(rows).cuda()])
+    assert_y_close(dx_rows, fx, "bf16", "full dx")
+    assert _rel(dx_rows, dx_r) <= 5e-3
+
+    # weight gradients of sampled hidden columns j, from the whole column of the stored h and
+    # dh (read straight from the TwELL arrays): dW_down[j] = sum_t h[t,j] g[t], dW_up[j] =
+    # sum_t dh[t,j] x[t] (the oracle on the one-column sub-problem)
+    def column(hst, j):
+        K, W = cfg.tile, cfg.ell_width
+        k, cl = divmod(j, K)
+        v = oracle.bf16_value(hst["vals"][k])
+        m = np.minimum(hst["counts"][k].astype(np.int64), W)[:, None] > np.arange(W)[None, :]
+        hit = m & (hst["cols"][k] == cl)
+        out = (v * hit).sum(axis=1)
+        bv = oracle.bf16_value(hst["bk_vals"])
+        for e in range(r):
+            if host["bk_tile"][e] == k:
+                out[host["bk_tok"][e]] += bv[e, cl]
+        return out
+    dWd_h = dWd.cpu().numpy().astype(np.float64)
+    dWu_h = dWu.cpu().numpy().astype(np.float64)
+    for j in rng.choice(c.F, 6, replace=False).tolist():
+        hc = column(host, j)[:, None]
+        dhc = column(dhost, j)[:, None]
+        _, _, dwd_j, _, _ = oracle.backward(x64, hc, g64, Wu64[[j]], Wd64[[j]])
+        _, dwu_j, _ = oracle.backward_from_dh(x64, dhc, Wu64[[j]])
+        assert_y_close(dWd_h[j], dwd_j[0], "bf16", f"full dW_down[{j}]")
+        assert_y_close(dWu_h[j], dwu_j[0], "bf16", f"full dW_up[{j}]")
+    # db is the column sum of dh
+    dbh = db.cpu().numpy().astype(np.float64)
+    col = np.zeros(c.F)
+    W = cfg.ell_width
+    K = cfg.tile
+    vals = oracle.bf16_value(dhost["vals"])
+    cols = host["cols"].astype(np.int64)
+    m = np.minimum(host["counts"].astype(np.int64), W)
+    for k in range(cfg.n_tiles):
+        sel = m[k][:, None] > np.arange(W)[None, :]
+        np.add.at(col, k * K + cols[k][sel], vals[k][sel])
+    bkv = oracle.bf16_value(dhost["bk_vals"])
+    for e in range(r):
+        col[host["bk_tile"][e] * K: (host["bk_tile"][e] + 1) * K] += bkv[e]
+    assert_y_close(dbh, col, "bf16", "full db")
