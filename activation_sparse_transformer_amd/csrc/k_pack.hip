@@ -191,9 +191,7 @@ hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, co
 // record, per (tile, group), how many overflowed and each entry's rank in its group.  The
 // final position of an entry of (k, t) is the exclusive prefix over (k, group) of those
 // counts, plus its rank: ascending (tile, token), the same for every run.
-//
-// Every workgroup scans the (small) counter array redundantly, then copies its share of
-// staged entries; workgroup 0 also writes bk_tile_ptr, bk_n and the status word.
+
 
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -205,60 +203,67 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-template <int K, bool BF16>
-__global__ __launch_bounds__(1024) void order_kernel(Dims d, twell_buffers_t b, Workspace ws) {
-  __shared__ int part[1024];
+// Two launches.  order_scan_kernel (one workgroup): exclusive scan of the per-(tile, group)
+// overflow counts into grp_first (the first canonical entry of every (tile, group)), plus
+// bk_tile_ptr, bk_n and the status word.  order_copy_kernel: every staged entry goes to
+// grp_first[tile, group] + its rank inside the group.
+constexpr int ORDER_PER_THREAD = 16;  // entries a scan thread holds in registers per pass
+
+__global__ __launch_bounds__(1024) void order_scan_kernel(Dims d, twell_buffers_t b, Workspace ws) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int N = d.nt * d.ng;
-  const int chunk = (N + 1023) / 1024;
-  int s = 0;
-  for (int q = tid * chunk, e = min(N, (tid + 1) * chunk); q < e; ++q) s += ws.ov_grp[q];
-  const int incl = wave_incl_scan(s);
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int woff = 0;
-  for (int w = 0; w < wv; ++w) woff += wsum[w];
-  part[tid] = woff + incl - s;  // exclusive prefix of this thread's chunk
-  __syncthreads();
-  int total = 0;
-  for (int w = 0; w < 16; ++w) total += wsum[w];
-
-  auto prefix = [&](int p) -> int {  // sum of ov_grp[0 .. p)
-    if (p >= N) return total;
-    const int c = p / chunk;
-    int r = part[c];
-    for (int q = c * chunk; q < p; ++q) r += ws.ov_grp[q];
-    return r;
-  };
-
-  if (blockIdx.x == 0) {
-    for (int kk = tid; kk <= d.nt; kk += 1024) b.bk_tile_ptr[kk] = prefix(kk * d.ng);
-    // first entry of every (tile, group): this thread's chunk, by a running sum
-    {
-      int r = part[tid];
-      for (int q = tid * chunk, e = min(N, (tid + 1) * chunk); q < e; ++q) {
-        ws.grp_first[q] = r;
-        r += ws.ov_grp[q];
-      }
-      if (tid == 0) ws.grp_first[N] = total;
+  int carry = 0;
+  for (int base = 0; base < N; base += 1024 * ORDER_PER_THREAD) {
+    int v[ORDER_PER_THREAD];
+#pragma unroll
+    for (int r = 0; r < ORDER_PER_THREAD; ++r) {  // coalesced: entry base + r*1024 + tid
+      const int q = base + r * 1024 + tid;
+      v[r] = q < N ? ws.ov_grp[q] : 0;
     }
-    if (tid == 0) {
-      *b.bk_n = total;
-      *b.status = total > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+#pragma unroll
+    for (int r = 0; r < ORDER_PER_THREAD; ++r) {
+      const int incl = wave_incl_scan(v[r]);
+      if (lane == 63) wsum[wv] = incl;
+      __syncthreads();
+      int woff = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int sw = wsum[w];
+        woff += w < wv ? sw : 0;
+        tot += sw;
+      }
+      const int q = base + r * 1024 + tid;
+      if (q < N) {
+        const int first = carry + woff + incl - v[r];
+        ws.grp_first[q] = first;
+        if (q % d.ng == 0) b.bk_tile_ptr[q / d.ng] = first;
+      }
+      carry += tot;
+      __syncthreads();  // wsum is rewritten by the next round
     }
   }
+  if (tid == 0) {
+    ws.grp_first[N] = carry;
+    b.bk_tile_ptr[d.nt] = carry;
+    *b.bk_n = carry;
+    *b.status = carry > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+  }
+}
 
+template <int K, bool BF16>
+__global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+  const int lane = threadIdx.x & 63;
   const int n_staged = min(*ws.claim, d.cap);
-  const int gw = blockIdx.x * 16 + wv;
-  const int nw = gridDim.x * 16;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
   constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;  // 32-bit words per slice
   for (int e = gw; e < n_staged; e += nw) {
     const int kk = ws.stage_key[2 * e];
     const int tw = ws.stage_key[2 * e + 1];
     const int t = tw & 0xFFFFFF, lr = tw >> 24;
-    const int fin = prefix(kk * d.ng + t / GROUP) + lr;
+    const int fin = ws.grp_first[kk * d.ng + t / GROUP] + lr;
     if (fin >= d.cap) continue;  // capacity exceeded: the status word reports it
     const uint32_t* src = static_cast<const uint32_t*>(ws.stage_vals) + (size_t)e * WORDS;
     uint32_t* dst = static_cast<uint32_t*>(b.bk_vals) + (size_t)fin * WORDS;
@@ -272,11 +277,14 @@ __global__ __launch_bounds__(1024) void order_kernel(Dims d, twell_buffers_t b, 
 
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s) {
-  // 16 waves per workgroup, about 4 staged entries per wave at full capacity
-  int blocks = (d.cap + 63) / 64;
-  blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
+  hipLaunchKernelGGL(order_scan_kernel, dim3(1), dim3(1024), 0, s, d, b, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 4 waves per workgroup, about one staged entry per wave at full capacity
+  int blocks = (d.cap + 3) / 4;
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
 #define SFFN_ORDER(KK, BB) \
-  hipLaunchKernelGGL((order_kernel<KK, BB>), dim3(blocks), dim3(1024), 0, s, d, b, ws)
+  hipLaunchKernelGGL((order_copy_kernel<KK, BB>), dim3(blocks), dim3(256), 0, s, d, b, ws)
   if (d.bf16) {
     if (d.K == 64) SFFN_ORDER(64, true);
     else if (d.K == 128) SFFN_ORDER(128, true);
