@@ -36,28 +36,33 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int UP_BN = 256;  // neurons per workgroup
-constexpr int UP_BK = 64;   // d_model slice per LDS stage
 constexpr int UP_GM = 8;    // token blocks per ordering group
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
-template <int K, int NB, bool DUMP>
-__global__ __launch_bounds__(256) void up_pack_bf16_kernel(
-    Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
-    const uint16_t* __restrict__ bu, twell_buffers_t b, Workspace ws, float* __restrict__ zdump) {
+// BK: d_model slice per LDS stage.  WPE: waves per SIMD the kernel is built for; with 2
+// (BK = 32, 128 tokens, 48 KB of LDS, at most 256 registers), two workgroups share a CU and
+// one's pack epilogue runs while the other's MFMA loop keeps the matrix cores busy.
+template <int K, int NB, bool DUMP, int BK, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
+up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
+                    const uint16_t* __restrict__ bu, twell_buffers_t b, Workspace ws,
+                    float* __restrict__ zdump) {
   constexpr int BM = 64 * NB;            // tokens per workgroup
   constexpr int HM = BM / 2;             // tokens per wave
-  constexpr int ALD = UP_BN * 8 / 256;   // 16-byte A pieces per thread per stage (8)
-  constexpr int BLD = BM * 8 / 256;      // 16-byte B pieces per thread per stage
+  constexpr int CH = BK / 8;             // 16-byte pieces per LDS row (8 or 4)
+  constexpr int RPI = 64 / CH;           // rows filled by one 64-lane direct load
+  constexpr int ALD = UP_BN / RPI / 4;   // direct loads of A per wave per stage
+  constexpr int BLD = BM / RPI / 4;      // direct loads of B per wave per stage
   constexpr int TPW = (K == 64) ? 2 : 1; // tile parts per wave
   constexpr int NTWG = UP_BN / K;        // tiles per workgroup (4, 2, 1)
 
   // LDS: two stages, each a separate object so that loads into one stage and reads of the
   // other are known not to alias; after the loop the A stages hold the TwELL staging.
-  __shared__ __attribute__((aligned(16))) uint4 sA0[UP_BN * 8];
-  __shared__ __attribute__((aligned(16))) uint4 sA1[UP_BN * 8];
-  __shared__ __attribute__((aligned(16))) uint4 sB0[BM * 8];
-  __shared__ __attribute__((aligned(16))) uint4 sB1[BM * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sA0[UP_BN * CH];
+  __shared__ __attribute__((aligned(16))) uint4 sA1[UP_BN * CH];
+  __shared__ __attribute__((aligned(16))) uint4 sB0[BM * CH];
+  __shared__ __attribute__((aligned(16))) uint4 sB1[BM * CH];
   __shared__ int part_cnt[2][32][2];   // K=256: per (wt, token) count of each wave half
   __shared__ int claim_base[NTWG][2];  // staged-backup base per (tile, wt)
 
@@ -82,26 +87,28 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
   const int n0 = nb * UP_BN, m0 = mb * BM;
 
   // ---- main loop
-  // A k-slice stage is 256 rows x 128 bytes (8 chunks of 16 B); chunk c of row r sits at
-  // position c ^ (r & 7).  Direct global->LDS loads write 64 consecutive 16-byte slots per
-  // instruction (one 8-row block); lane i fills slot i, so it fetches the logical chunk
-  // (i & 7) ^ (i >> 3) of row (i >> 3) of the block.
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
+  // A k-slice stage is 256 rows x 2*BK bytes (CH chunks of 16 B); chunk c of row r sits at
+  // position c ^ swz(r), swz(r) = r & 7 for CH = 8 and (r >> 2) & 3 for CH = 4, so the 16
+  // consecutive rows one fragment read touches land in distinct banks.  Direct
+  // global->LDS loads write 64 consecutive 16-byte slots per instruction (RPI rows); lane
+  // i fills slot i, so it fetches the logical chunk (i % CH) ^ swz of row i / CH.
+  auto swz = [](int r) { return CH == 8 ? (r & 7) : ((r >> 2) & 3); };
+  const int lrow = lane / CH;
+  const int lchunk = (lane % CH) ^ swz(lrow);
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto issue = [&](int kt, uint4* sA, uint4* sB) {
-    const int k0 = kt * UP_BK + lchunk * 8;
+    const int k0 = kt * BK + lchunk * 8;
 #pragma unroll
     for (int q = 0; q < ALD; ++q) {
       const int blk = wave * ALD + q;
-      const int r = blk * 8 + lrow;
+      const int r = blk * RPI + lrow;
       __builtin_amdgcn_global_load_lds(Wu + (size_t)(n0 + r) * D + k0, (lds_ptr)(sA + blk * 64),
                                        16, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < BLD; ++q) {
       const int blk = wave * BLD + q;
-      int tok = m0 + blk * 8 + lrow;
+      int tok = m0 + blk * RPI + lrow;
       tok = tok < T ? tok : T - 1;
       __builtin_amdgcn_global_load_lds(x + (size_t)tok * D + k0, (lds_ptr)(sB + blk * 64), 16, 0,
                                        0);
@@ -125,21 +132,21 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int r = wn * 128 + a * 32 + l32;
-      fa[a] = __builtin_bit_cast(bf16x8_t, A[r * 8 + (ch ^ (r & 7))]);
+      fa[a] = __builtin_bit_cast(bf16x8_t, A[r * CH + (ch ^ swz(r))]);
     }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       const int r = wt * HM + bb * 32 + l32;
-      fb[bb] = __builtin_bit_cast(bf16x8_t, B[r * 8 + (ch ^ (r & 7))]);
+      fb[bb] = __builtin_bit_cast(bf16x8_t, B[r * CH + (ch ^ swz(r))]);
     }
   };
   auto compute = [&](const uint4* A, const uint4* B) {
     bf16x8_t fa[2][4], fb[2][NB];
     load_frags(A, B, 0, fa[0], fb[0]);
 #pragma unroll
-    for (int kk = 0; kk < UP_BK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       const int cur = kk & 1;
-      if (kk + 1 < UP_BK / 16) load_frags(A, B, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      if (kk + 1 < BK / 16) load_frags(A, B, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
       __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
     }
   };
 
-  const int nk = D / UP_BK;  // D % 128 == 0, so nk is even
+  const int nk = D / BK;  // D % 128 == 0, so nk is even
   issue(0, sA0, sB0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
@@ -168,18 +175,20 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
 
   // ---- epilogue
   // Own element e = a*16 + r holds wave-local neuron nl = a*32 + 8*(r>>2) + 4*lh + (r&3);
-  // e ascending <=> nl ascending among this lane's elements.
-  float bias[4][16];
+  // e ascending <=> nl ascending among this lane's elements.  The bias is added into the
+  // accumulators once (z = acc + b in fp32).
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nl = a * 32 + 8 * q + 4 * lh;
       const uint2 bw = *reinterpret_cast<const uint2*>(bu + n0 + wn * 128 + nl);
-      bias[a][4 * q + 0] = __uint_as_float(bw.x << 16);
-      bias[a][4 * q + 1] = __uint_as_float(bw.x & 0xFFFF0000u);
-      bias[a][4 * q + 2] = __uint_as_float(bw.y << 16);
-      bias[a][4 * q + 3] = __uint_as_float(bw.y & 0xFFFF0000u);
+      const float bv[4] = {__uint_as_float(bw.x << 16), __uint_as_float(bw.x & 0xFFFF0000u),
+                           __uint_as_float(bw.y << 16), __uint_as_float(bw.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[a][bb][4 * q + i] += bv[i];
     }
 
   // staging: vals [NTWG][2 wt][32 tok][W] bf16, cols [NTWG][2][32][W] u8
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float z = acc[a][bb][r] + bias[a][r];
+        const float z = acc[a][bb][r];
         if (DUMP && valid)
           zdump[(size_t)tok * d.F + n0 + wn * 128 + a * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = z;
         own |= (uint64_t)(valid && z > 0.0f) << (a * 16 + r);
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
       for (int i = 0; i < 4; ++i) {
         const int e = gi * 4 + i;
         const int a = e >> 4, r = e & 15;
-        const float z = acc[a][bb][r] + bias[a][r];
+        const float z = acc[a][bb][r];
         const bool nz = (own >> e) & 1ull;
         const int rank = rbase[j] + run[j] + pb;
         run[j] += nz ? 1 : 0;
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(256) void up_pack_bf16_kernel(
   }
 }
 
-template <int K, int NB>
+template <int K, int NB, int BK = 64, int WPE = 1>
 static hipError_t launch_up_t(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                               const uint16_t* bu, const twell_buffers_t& b, const Workspace& ws,
                               float* zdump, hipStream_t s) {
@@ -373,10 +382,10 @@ static hipError_t launch_up_t(const Dims& d, const uint16_t* x, const uint16_t* 
   const int total = nN * nM;
   const int per_xcd = (total + 7) / 8;
   if (zdump)
-    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, true>), dim3(8 * per_xcd), dim3(256), 0, s, d,
+    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, true, BK, WPE>), dim3(8 * per_xcd), dim3(256), 0, s, d,
                        x, Wu, bu, b, ws, zdump);
   else
-    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, false>), dim3(8 * per_xcd), dim3(256), 0, s,
+    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, false, BK, WPE>), dim3(8 * per_xcd), dim3(256), 0, s,
                        d, x, Wu, bu, b, ws, zdump);
   return hipGetLastError();
 }
@@ -384,15 +393,12 @@ static hipError_t launch_up_t(const Dims& d, const uint16_t* x, const uint16_t* 
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s) {
-  // 256-token workgroups when there are enough of them to fill the chip, else 128.
-  const bool big = (long long)(d.F / UP_BN) * ((d.T + 255) / 256) >= 512;
+  // 128-token workgroups, two per CU (BK = 32); K = 64 keeps one per CU (its staging of
+  // four tiles needs the larger LDS stages)
   switch (d.K) {
-    case 64:  // two tiles per wave: the 256-token variant would not fit its registers
-      return launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
-    case 128: return big ? launch_up_t<128, 4>(d, x, Wu, bu, b, ws, zdump, s)
-                         : launch_up_t<128, 2>(d, x, Wu, bu, b, ws, zdump, s);
-    case 256: return big ? launch_up_t<256, 4>(d, x, Wu, bu, b, ws, zdump, s)
-                         : launch_up_t<256, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 64: return launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 128: return launch_up_t<128, 2, 32, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 256: return launch_up_t<256, 2, 32, 2>(d, x, Wu, bu, b, ws, zdump, s);
   }
   return hipErrorInvalidValue;
 }
