@@ -86,7 +86,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
     const uint8_t* __restrict__ cols, const int32_t* __restrict__ bk_tile_ptr,
     const int32_t* __restrict__ bk_tok, const void* __restrict__ bk_vals,
     const void* __restrict__ Wd_, void* __restrict__ y_, int tv_bytes, int tc_bytes,
-    const int32_t* __restrict__ blk_nnz, int thr) {
+    const int32_t* __restrict__ blk_nnz, long long thr) {
   constexpr int DCL = BF16 ? 2 : 1;   // output columns per lane
   constexpr int DC = 64 * DCL;        // output columns per workgroup
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
   // token blocks, so each TwELL block is fetched once into that XCD's L2 and the W_down
   // tile loads spread over every memory channel
   const int tb = P / nd;
-  if (blk_nnz != nullptr && ld_uniform(blk_nnz + tb) > thr) return;  // the MFMA kernel's block
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) > thr) return;  // the matrix cores' layer
   const int dchunk = P - tb * nd;
   const int d0 = dchunk * DC;
   const int tw0 = tb * DOWN_BT + wv * DOWN_TPW;  // first token of this wave
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
 
 template <int K, bool BF16, bool FAST>
 static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                                const int32_t* blk_nnz, int thr, hipStream_t s) {
+                                const int32_t* blk_nnz, long long thr, hipStream_t s) {
   constexpr int DC = BF16 ? 128 : 64;
   const int esz = BF16 ? 2 : 4;
   const int nd = d.D / DC;
@@ -308,7 +308,7 @@ static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const v
 
 template <int K, bool BF16>
 static hipError_t launch_down_k(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                                const int32_t* blk_nnz, int thr, hipStream_t s) {
+                                const int32_t* blk_nnz, long long thr, hipStream_t s) {
   // The LDS fast path needs 16-byte aligned TwELL rows and room for two stages.
   const int esz = BF16 ? 2 : 4;
   const size_t lds_fast = 2 * (size_t)K * 256 +
@@ -319,7 +319,7 @@ static hipError_t launch_down_k(const Dims& d, const twell_buffers_t& b, const v
 }
 
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                       const int32_t* blk_nnz, int thr, hipStream_t s) {
+                       const int32_t* blk_nnz, long long thr, hipStream_t s) {
   if (d.bf16) {
     if (d.K == 64) return launch_down_k<64, true>(d, b, Wd, y, blk_nnz, thr, s);
     if (d.K == 128) return launch_down_k<128, true>(d, b, Wd, y, blk_nnz, thr, s);

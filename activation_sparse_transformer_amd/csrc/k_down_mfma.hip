@@ -27,8 +27,9 @@
 //     at the start of the next, before its barrier; their first entry comes from the
 //     per-(tile, 32-token group) offsets of the ordering pass.  The barrier at the top of
 //     each step publishes the A and B buffers.
-// Blocks whose stored-nonzero count is at most `thr` belong to the gather kernel and are
-// skipped here (blk_nnz == nullptr: every block runs here).
+// When the layer's stored-nonzero count (the sum of the per-block counts) is at most `thr`
+// the gather kernel takes the layer and every workgroup here returns at once
+// (blk_nnz == nullptr: this kernel runs).
 #include "sffn_common.hpp"
 
 namespace sffn {
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, int thr) {
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr) {
   constexpr int KC = DM_KC;
   constexpr int NCH = K / KC;          // steps per tile
   constexpr int U = W / 8;             // 8-slot units per tile-row
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   // token-block-major: the workgroups an XCD runs together share token blocks (TwELL
   // reads) and column chunks (W_down reads) in its L2
   const int tb = P / nd;
-  if (blk_nnz != nullptr && ld_uniform(blk_nnz + tb) <= thr) return;
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
   const int dchunk = P - tb * nd;
   const int d0 = dchunk * DM_BN;
   const bool active = d0 + 128 * wc < d.D;  // D % 256 == 128: the last chunk is half wide
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
 
 template <int K, int W>
 static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                              const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                               hipStream_t s) {
   const int nd = (d.D + DM_BN - 1) / DM_BN;
   const int ntb = (d.T + DM_BM - 1) / DM_BM;
@@ -362,7 +363,7 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
 
 template <int K>
 static hipError_t launch_dm_k(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                              const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                               hipStream_t s) {
   switch (d.W) {
     case 16: return launch_dm_t<K, 16>(d, b, ws, Wd, y, blk_nnz, thr, s);
@@ -378,7 +379,7 @@ bool down_mfma_supported(const Dims& d) {
 }
 
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                            const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                             hipStream_t s) {
   if (!down_mfma_supported(d)) return hipErrorInvalidValue;
   if (d.K == 64) return launch_dm_k<64>(d, b, ws, Wd, y, blk_nnz, thr, s);

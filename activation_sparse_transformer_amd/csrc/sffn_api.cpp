@@ -225,8 +225,8 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
   return SFFN_OK;
 }
 
-// Down-projection of a packed activation: per 256-token block, the gather kernel or the MFMA
-// kernel by the block's stored density (bf16 layers); fp32 layers use the gather kernel.
+// Down-projection of a packed activation: the gather kernel or the MFMA kernel by the layer's
+// stored density, decided on the device (bf16 layers); fp32 layers use the gather kernel.
 static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
                                const Workspace& ws, void* y, hipStream_t s) {
   const bool mfma_ok = down_mfma_supported(d);
@@ -237,10 +237,9 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
   if (policy == SFFN_DOWN_MFMA)
     return run("down_mfma", s,
                [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, nullptr, 0, s); });
-  // blocks whose stored nonzeros exceed thr go to the MFMA kernel
-  const double cells = 256.0 * (double)d.F;
-  const double thr_d = (double)hd->down_mfma_density * cells;
-  const int thr = thr_d >= 2147483647.0 ? 2147483647 : (int)thr_d;
+  // the layer goes to the matrix cores when its stored nonzeros exceed thr
+  const double thr_d = (double)hd->down_mfma_density * (double)d.T * (double)d.F;
+  const long long thr = (long long)thr_d;
   SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
   SFFN_TRY_INNER(
       run("down", s, [&] { return launch_down(d, act, hd->W_down, y, ws.blk_nnz, thr, s); }));

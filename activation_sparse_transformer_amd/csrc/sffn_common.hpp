@@ -96,6 +96,14 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
   typedef const __attribute__((address_space(4))) T* cptr;
   return *(cptr)(uintptr_t)p;
 }
+// Sum of the n per-block counts (the layer's stored nonzeros), the same in every lane.
+__device__ __forceinline__ long long layer_nnz(const int32_t* blk_nnz, int n) {
+  long long s = 0;
+  for (int q = (int)(threadIdx.x & 63); q < n; q += 64) s += blk_nnz[q];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
 #endif
 
 // ---------------------------------------------------------------- launchers
@@ -113,14 +121,15 @@ hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, co
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);
-// Down-projection.  Token blocks of 256 are split between two kernels by their stored
-// nonzero count (blk_nnz, from launch_block_nnz): the vector gather kernel takes blocks
-// with count <= thr, the MFMA kernel the others.  blk_nnz == nullptr hands every block to
+// Down-projection.  Two kernels: the vector gather kernel and the matrix-core kernel.  With
+// blk_nnz (per-256-token-block stored-nonzero counts from launch_block_nnz) both are
+// launched and each reads the layer's total: the gather kernel runs when it is <= thr and
+// the matrix-core kernel otherwise; the other returns at once.  blk_nnz == nullptr runs
 // the kernel launched.
 hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* blk_nnz,
                             hipStream_t s);
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                       const int32_t* blk_nnz, int thr, hipStream_t s);
+                       const int32_t* blk_nnz, long long thr, hipStream_t s);
 bool down_mfma_supported(const Dims& d);
 bool backward_supported(const Dims& d);
 // One part of the backward weights pass: which = 0: dh at the stored positions of `act`
@@ -131,7 +140,7 @@ hipError_t launch_backward_part(int which, const Dims& d, const twell_buffers_t&
                                 const void* Wd, void* dh_vals, void* dh_bk, float* dW_up,
                                 float* dW_down, float* db, hipStream_t s);
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                            const void* Wd, void* y, const int32_t* blk_nnz, int thr,
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                             hipStream_t s);
 
 }  // namespace sffn

@@ -62,7 +62,7 @@ class StatsC(ctypes.Structure):
 
 # Down-projection policies (mirror the header's SFFN_DOWN_* values).
 DOWN_AUTO, DOWN_GATHER, DOWN_MFMA = 0, 1, 2
-DOWN_MFMA_DENSITY_DEFAULT = 0.005
+DOWN_MFMA_DENSITY_DEFAULT = 0.001
 
 # Exported entry points and their prototypes (restype is always the status enum unless set).
 _PROTOS = {
@@ -291,8 +291,9 @@ class SparseFFN:
         return y, act, z
 
     def set_down_policy(self, policy: str = "auto", mfma_density: float = DOWN_MFMA_DENSITY_DEFAULT):
-        """Per-block choice of the down-projection kernel: "auto" (matrix cores above
-        `mfma_density` stored density, gather below), "gather" or "mfma" for every block."""
+        """Choice of the down-projection kernel: "auto" (matrix cores when the layer's stored
+        density exceeds `mfma_density`, gather otherwise; decided on the device), "gather" or
+        "mfma"."""
         code = {"auto": DOWN_AUTO, "gather": DOWN_GATHER, "mfma": DOWN_MFMA}.get(policy)
         if code is None:
             raise ValueError(f"unknown down policy {policy!r}")

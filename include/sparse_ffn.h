@@ -164,24 +164,26 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
                                   void *dx, float *dW_up, float *dW_down, float *db_up,
                                   void *stream);
 
-/* How the down-projection (inside sparse_ffn_forward and sparse_ffn_down) runs each block
- * of 256 tokens.  The TwELL tiles line up with tiled matrix-multiply execution (same
- * article, section "What TwELL and the custom CUDA kernels solve"), so a block can either
- * gather W_down rows for its stored nonzeros on the vector ALUs (work grows with the
- * nonzeros) or rebuild its hidden tiles in on-chip memory and run them through the matrix
- * cores (work independent of the density, at ~16x the vector rate).
- *   SFFN_DOWN_AUTO:   matrix cores for blocks whose stored density (nonzeros / (256 d_ff))
- *                     exceeds mfma_density, gather otherwise (the default, with
- *                     SFFN_DOWN_MFMA_DENSITY_DEFAULT)
- *   SFFN_DOWN_GATHER: every block on the gather kernel
- *   SFFN_DOWN_MFMA:   every block on the matrix cores
+/* Which kernel runs the down-projection (inside sparse_ffn_forward and sparse_ffn_down).
+ * The TwELL tiles line up with tiled matrix-multiply execution (same article, section "What
+ * TwELL and the custom CUDA kernels solve"), so the layer can either gather W_down rows for
+ * its stored nonzeros on the vector ALUs (work grows with the nonzeros) or rebuild its hidden
+ * tiles in on-chip memory and run them through the matrix cores (work independent of the
+ * density, at ~16x the vector rate).
+ *   SFFN_DOWN_AUTO:   matrix cores when the layer's stored density (stored nonzeros /
+ *                     (T d_ff)) exceeds mfma_density, gather otherwise; the count is taken on
+ *                     the device, so the choice costs no host synchronisation (the default,
+ *                     with SFFN_DOWN_MFMA_DENSITY_DEFAULT)
+ *   SFFN_DOWN_GATHER: always the gather kernel
+ *   SFFN_DOWN_MFMA:   always the matrix cores
  * The matrix-core path needs a bf16 layer and ell_width in {16, 32, 48, 64}; other layers
- * always gather.  Both paths accumulate in fp32; they differ only in summation order.  Host only; the setting belongs to the handle.  SFFN_ERR_INVALID_ARGUMENT for an
- * unknown policy or mfma_density outside [0, 1]. */
+ * always gather.  Both paths accumulate in fp32; they differ only in summation order.  Host
+ * only; the setting belongs to the handle.  SFFN_ERR_INVALID_ARGUMENT for an unknown policy
+ * or mfma_density outside [0, 1]. */
 #define SFFN_DOWN_AUTO 0
 #define SFFN_DOWN_GATHER 1
 #define SFFN_DOWN_MFMA 2
-#define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
+#define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.001f
 sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float mfma_density);
 
 /* (sync) Counters of `buf` for T tokens; synchronises `stream`.  Returns
