@@ -1,0 +1,212 @@
+// Down-projection of very sparse bf16 layers: each token reads only the W_down rows that its
+// stored nonzeros select (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the
+// custom CUDA kernels solve": the down-projection runs over the stored nonzeros only, and
+// W_down rows are the natural coalesced gather unit).
+//
+//   y[t, :] = sum over the stored (tile k, column c, value v) of token t of  v W_down[kK + c, :]
+//
+// The work and the W_down bytes read grow with the nonzeros (4 KB of W_down per nonzero for
+// d_model 2048), so this kernel wins when few rows are used; the matrix-core kernel (whose
+// work does not depend on the density) takes dense layers.
+//
+// One workgroup per token at a time, 4 waves; wave w takes a contiguous quarter of the tiles, lane l of
+// it tile k = k0 + l: its count, then its slots 8 at a time (16 B values + 8 B columns).  The
+// (row, value) pairs of the lanes are broadcast with readlane in batches of up to 8 (4 for
+// d_model > 2048) whose
+// W_down row loads are all issued before any is used, so a token with many nonzeros (heavy
+// tokens run at 10-20x the mean density) is not a chain of single-row latencies.  Lane L owns
+// output columns 512q + 8L (q < NQ): every row is read as NQ coalesced 1 KB wave loads.  The
+// waves' partial rows are summed in LDS and y is written as 16-byte stores.
+#include "sffn_common.hpp"
+
+namespace sffn {
+
+constexpr int ROWS_WAVES = 4;
+
+template <int NQ>
+__global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
+    Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
+    const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
+    const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr) {
+  constexpr int ROWS_BATCH = NQ <= 4 ? 8 : 4;  // rows in flight per wave (registers: 4*NQ each)
+  __shared__ __attribute__((aligned(16))) float part[ROWS_WAVES - 1][NQ * 512];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int T = d.T, D = d.D, K = d.K, W = d.W;
+  // the layer goes to this kernel only when its stored-nonzero count is at most thr
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, (T + 255) / 256) > thr) return;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {  // workgroup-uniform token loop
+  float acc[NQ][8];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
+
+  // a batch of up to ROWS_BATCH (row, value) pairs: loads first, then the FMAs
+  int bj[ROWS_BATCH];
+  float bv[ROWS_BATCH];
+  int nb = 0;
+  auto flush = [&]() __attribute__((always_inline)) {
+    uint4 w[ROWS_BATCH][NQ];
+#pragma unroll
+    for (int i = 0; i < ROWS_BATCH; ++i) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) w[i][q] = make_uint4(0, 0, 0, 0);
+      if (i < nb) {  // wave-uniform
+        const uint16_t* wr = Wd + (size_t)bj[i] * D;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int c0 = 512 * q + 8 * lane;
+          if (q < NQ - 1 || c0 < D) w[i][q] = *reinterpret_cast<const uint4*>(wr + c0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ROWS_BATCH; ++i) {
+      const float v = i < nb ? bv[i] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const uint32_t ww[4] = {w[i][q].x, w[i][q].y, w[i][q].z, w[i][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[q][2 * e] = fmaf(v, __uint_as_float(ww[e] << 16), acc[q][2 * e]);
+          acc[q][2 * e + 1] = fmaf(v, __uint_as_float(ww[e] & 0xFFFF0000u), acc[q][2 * e + 1]);
+        }
+      }
+    }
+    nb = 0;
+  };
+  // add the pairs (jl, vl) of the lanes in `act` (lane-varying values, broadcast one by one)
+  auto add_lanes = [&](uint64_t act, int jl, uint32_t vl) __attribute__((always_inline)) {
+    while (act != 0) {
+      const int b = __builtin_ctzll(act);
+      act &= act - 1;
+      // nb is wave-uniform, so the batch slots stay in registers after unrolling
+#pragma unroll
+      for (int i = 0; i < ROWS_BATCH; ++i)
+        if (i == nb) {
+          bj[i] = __builtin_amdgcn_readlane(jl, b);
+          bv[i] = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)vl, b) << 16);
+        }
+      if (++nb == ROWS_BATCH) flush();
+    }
+  };
+
+  const int per = (d.nt + ROWS_WAVES - 1) / ROWS_WAVES;  // tiles per wave (<= 64 checked)
+  const int k0 = wave * per;
+  const int k = k0 + lane;
+  const bool own = lane < per && k < d.nt;
+  const uint32_t cnt = own ? counts[(size_t)k * T + t] : 0u;
+  const uint32_t m = cnt < (uint32_t)W ? cnt : (uint32_t)W;
+  int mx = (int)m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+  const int mmax = __builtin_amdgcn_readfirstlane(mx);
+  const size_t row = ((size_t)(own ? k : 0) * T + t) * W;
+  for (int s0 = 0; s0 < mmax; s0 += 8) {
+    // slots s0 .. s0+7 of this lane's tile-row (rows are W bytes / 2W bytes, W % 8 == 0)
+    uint4 v4 = make_uint4(0, 0, 0, 0);
+    uint2 c2 = make_uint2(0, 0);
+    if ((uint32_t)s0 < m) {
+      v4 = *reinterpret_cast<const uint4*>(vals + row + s0);
+      c2 = *reinterpret_cast<const uint2*>(cols + row + s0);
+    }
+    const uint32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+    const uint32_t cc[2] = {c2.x, c2.y};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t col = (cc[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+      const uint32_t val = (e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xFFFFu);
+      add_lanes(ballot64((uint32_t)(s0 + e) < m), k * K + (int)col, val);
+    }
+  }
+  // backup slices of this wave's overflowing tiles: the entry of (k, t) is the first of its
+  // 32-token group plus the number of the group's earlier tokens that overflow in tile k
+  uint64_t ovt = ballot64(cnt > (uint32_t)W);
+  while (ovt != 0) {
+    const int b = __builtin_ctzll(ovt);
+    ovt &= ovt - 1;
+    const int kb = k0 + b;
+    const int g = t / GROUP;
+    const int tl = g * GROUP + (lane & 31);
+    const uint32_t cg = (lane < 32 && tl < T) ? counts[(size_t)kb * T + tl] : 0u;
+    const uint64_t ov = ballot64(cg > (uint32_t)W);
+    const int rank = __builtin_popcountll(ov & ((1ull << (t - g * GROUP)) - 1ull));
+    const int e = ld_uniform(grp_first + kb * d.ng + g) + rank;
+    if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
+    const uint16_t* sl = bk_vals + (size_t)e * K;
+    for (int c0 = 0; c0 < K; c0 += 64) {
+      const uint32_t v = sl[c0 + lane];
+      add_lanes(ballot64(v != 0u), kb * K + c0 + lane, v);
+    }
+  }
+  if (nb > 0) flush();
+
+  // ---- sum the waves' partial rows in LDS; wave 0 writes y
+  if (wave > 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float4* p = reinterpret_cast<float4*>(&part[wave - 1][512 * q + 8 * lane]);
+      p[0] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+      p[1] = make_float4(acc[q][4], acc[q][5], acc[q][6], acc[q][7]);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int c0 = 512 * q + 8 * lane;
+      if (q < NQ - 1 || c0 < D) {
+#pragma unroll
+        for (int w2 = 0; w2 < ROWS_WAVES - 1; ++w2) {
+          const float4* p = reinterpret_cast<const float4*>(&part[w2][512 * q + 8 * lane]);
+          const float4 a = p[0], c = p[1];
+          acc[q][0] += a.x; acc[q][1] += a.y; acc[q][2] += a.z; acc[q][3] += a.w;
+          acc[q][4] += c.x; acc[q][5] += c.y; acc[q][6] += c.z; acc[q][7] += c.w;
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (uint32_t)f32_to_bf16(acc[q][2 * e]) |
+                 ((uint32_t)f32_to_bf16(acc[q][2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>(y + (size_t)t * D + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+  __syncthreads();  // part[] is rewritten for the next token
+  }
+}
+
+bool down_rows_supported(const Dims& d) {
+  return d.bf16 && d.D <= 4096 && d.D % 8 == 0 && d.W % 8 == 0 &&
+         (d.nt + ROWS_WAVES - 1) / ROWS_WAVES <= 64;
+}
+
+hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                            hipStream_t s) {
+  if (!down_rows_supported(d)) return hipErrorInvalidValue;
+  // at most 2048 workgroups, each looping over tokens: a skipped launch (the layer went to the
+  // matrix cores) then costs little
+  const dim3 grid(d.T < 2048 ? d.T : 2048), block(64 * ROWS_WAVES);
+  auto* c = b.counts;
+  auto* v = static_cast<const uint16_t*>(b.vals);
+  auto* bk = static_cast<const uint16_t*>(b.bk_vals);
+  auto* w = static_cast<const uint16_t*>(Wd);
+  auto* yy = static_cast<uint16_t*>(y);
+  switch ((d.D + 511) / 512) {
+#define SFFN_ROWS(NQ)                                                                      \
+  case NQ:                                                                                 \
+    hipLaunchKernelGGL(down_rows_kernel<NQ>, grid, block, 0, s, d, c, v, b.cols, bk,        \
+                       ws.grp_first, w, yy, blk_nnz, thr);                                 \
+    break;
+    SFFN_ROWS(1) SFFN_ROWS(2) SFFN_ROWS(3) SFFN_ROWS(4)
+    SFFN_ROWS(5) SFFN_ROWS(6) SFFN_ROWS(7) SFFN_ROWS(8)
+#undef SFFN_ROWS
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sffn

@@ -225,15 +225,21 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
   return SFFN_OK;
 }
 
-// Down-projection of a packed activation: the gather kernel or the MFMA kernel by the layer's
-// stored density, decided on the device (bf16 layers); fp32 layers use the gather kernel.
+// Down-projection of a packed activation.  The gather side is the per-token row gather for
+// bf16 layers (the staged-tile gather for fp32 layers and d_model > 4096); the matrix-core
+// kernel takes bf16 layers whose stored density exceeds the threshold, decided on the device.
 static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
                                const Workspace& ws, void* y, hipStream_t s) {
   const bool mfma_ok = down_mfma_supported(d);
+  const bool rows_ok = down_rows_supported(d);
+  auto gather = [&](const int32_t* blk, long long thr) {
+    if (rows_ok)
+      return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, blk, thr, s); });
+    return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, blk, thr, s); });
+  };
   int32_t policy = hd->down_policy;
   if (!mfma_ok) policy = SFFN_DOWN_GATHER;
-  if (policy == SFFN_DOWN_GATHER)
-    return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, nullptr, 0, s); });
+  if (policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
   if (policy == SFFN_DOWN_MFMA)
     return run("down_mfma", s,
                [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, nullptr, 0, s); });
@@ -241,8 +247,7 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
   const double thr_d = (double)hd->down_mfma_density * (double)d.T * (double)d.F;
   const long long thr = (long long)thr_d;
   SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
-  SFFN_TRY_INNER(
-      run("down", s, [&] { return launch_down(d, act, hd->W_down, y, ws.blk_nnz, thr, s); }));
+  SFFN_TRY_INNER(gather(ws.blk_nnz, thr));
   return run("down_mfma", s,
              [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, ws.blk_nnz, thr, s); });
 }

@@ -131,6 +131,11 @@ hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* bl
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
                        const int32_t* blk_nnz, long long thr, hipStream_t s);
 bool down_mfma_supported(const Dims& d);
+// One wave per token over the W_down rows its nonzeros select (bf16, d_model <= 4096).
+bool down_rows_supported(const Dims& d);
+hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                            hipStream_t s);
 bool backward_supported(const Dims& d);
 // One part of the backward weights pass: which = 0: dh at the stored positions of `act`
 // (into dh_vals / dh_bk); 1: dW_down = H^T g; 2: dW_up = dH^T x and, if db is not null,

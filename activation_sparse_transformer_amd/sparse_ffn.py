@@ -62,7 +62,7 @@ class StatsC(ctypes.Structure):
 
 # Down-projection policies (mirror the header's SFFN_DOWN_* values).
 DOWN_AUTO, DOWN_GATHER, DOWN_MFMA = 0, 1, 2
-DOWN_MFMA_DENSITY_DEFAULT = 0.001
+DOWN_MFMA_DENSITY_DEFAULT = 0.005
 
 # Exported entry points and their prototypes (restype is always the status enum unless set).
 _PROTOS = {

@@ -183,7 +183,7 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
 #define SFFN_DOWN_AUTO 0
 #define SFFN_DOWN_GATHER 1
 #define SFFN_DOWN_MFMA 2
-#define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.001f
+#define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
 sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float mfma_density);
 
 /* (sync) Counters of `buf` for T tokens; synchronises `stream`.  Returns
