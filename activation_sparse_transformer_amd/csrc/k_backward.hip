@@ -21,7 +21,7 @@
 // positions).
 //
 // tmm_kernel: one workgroup per (128 hidden columns, 256 columns of d): dW = H^T M summed
-// over 64-token steps.  Each step rebuilds the 64 x 128 block of H in LDS from TwELL rows
+// over 32-token steps.  Each step rebuilds the 32 x 128 block of H in LDS from TwELL rows
 // (as the forward's down kernel does) and loads M (g or x) rows with direct loads; both MFMA
 // operands come out of the token-major tiles through ds_read_b64_tr_b16.  With DB the same
 // kernel also sums the A fragments into db.
@@ -218,18 +218,25 @@ __global__ __launch_bounds__(256) void sddmm_kernel(
 }
 
 // ============================================================================ H^T M
+// 32-token steps, 48 KB of LDS and at most 256 registers: two workgroups share a CU, so one's
+// H rebuild and barrier waits overlap the other's MFMAs.
+constexpr int TMM_TS = 32;  // tokens per step
+
 template <int K, int W, bool DB>
-__global__ __launch_bounds__(256) void tmm_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tmm_kernel(
     Dims d, const uint16_t* __restrict__ Hv, const uint16_t* __restrict__ Hbk,
     const uint16_t* __restrict__ counts, const uint8_t* __restrict__ cols,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ M,
     float* __restrict__ dW, float* __restrict__ db) {
+  constexpr int TS = TMM_TS;
   constexpr int U = W / 8;                  // 8-slot units per tile-row
-  constexpr int NU = (16 * U + 63) / 64;    // units per lane (a wave writes 16 rows)
-  constexpr int HROW = 256;                 // H step tile: 64 tokens x 128 columns, bf16
-  constexpr int HBUF = 64 * HROW;
-  constexpr int MROW = 512;                 // M step tile: 64 tokens x 256 columns, bf16
-  constexpr int MBUF = 64 * MROW;
+  constexpr int RPW = TS / 4;               // H rows each wave writes per step (8)
+  constexpr int NU = (RPW * U + 63) / 64;   // units per lane
+  constexpr int HROW = 256;                 // H step tile: TS tokens x 128 columns, bf16
+  constexpr int HBUF = TS * HROW;
+  constexpr int MROW = 512;                 // M step tile: TS tokens x 256 columns, bf16
+  constexpr int MBUF = TS * MROW;
+  constexpr int NKK = TS / 16;              // MFMA k-steps per step
   // H buffers (written by the waves) then 256 B of dummy words for padding writes; M
   // buffers (filled by direct loads).  Piece p of row r sits at p ^ (2*(r&3)) in both, so
   // the four rows of a transposed read hit distinct banks.
@@ -258,50 +265,50 @@ __global__ __launch_bounds__(256) void tmm_kernel(
 
   auto issue_M = [&](int ts, unsigned char* sM) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {  // 32 loads of 1 KB (two rows), 8 per wave
+    for (int q = 0; q < MBUF / 1024 / 4; ++q) {  // loads of 1 KB (two rows), 4 per wave
       const int ins = q * 4 + wave;
       const int slot = ins * 64 + lane;
       const int r = slot >> 5, pc = slot & 31;
       const int lc = pc ^ (2 * (r & 3));
-      int t = ts * 64 + r;
+      int t = ts * TS + r;
       t = t < T ? t : T - 1;  // rows past T meet zero rows of H
       __builtin_amdgcn_global_load_lds(M + (size_t)t * D + d0 + lc * 8,
                                        (lds_vptr_b)(sM + ins * 1024), 16, 0, 0);
     }
   };
 
-  // ---- TwELL units of this wave's 16 rows of a 64-token step: unit u = lane + 64q
-  // (u < 16U) holds slots 8*(u%U) .. +7 of token 64ts + 16*wave + u/U
+  // ---- TwELL units of this wave's RPW rows of a step: unit u = lane + 64q (u < RPW*U) holds
+  // slots 8*(u%U) .. +7 of token TS*ts + RPW*wave + u/U
   uint4 uv[NU];
   uint2 uc[NU];
-  uint32_t cnt = 0;  // count of token 64ts + lane (for the backup rows of the whole step)
+  uint32_t cnt = 0;  // count of token TS*ts + lane (lanes < TS; the backup rows of the step)
   auto load_units = [&](int ts) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       const int u = lane + 64 * q;
-      const int uu = u < 16 * U ? u : 0;
-      int tok = ts * 64 + 16 * wave + uu / U;
+      const int uu = u < RPW * U ? u : 0;
+      int tok = ts * TS + RPW * wave + uu / U;
       tok = tok < T ? tok : T - 1;
       const size_t e0 = (row_base + tok) * W + 8 * (uu % U);
       uv[q] = *reinterpret_cast<const uint4*>(Hv + e0);
       uc[q] = *reinterpret_cast<const uint2*>(cols + e0);
     }
-    const int tl = ts * 64 + lane;
+    const int tl = ts * TS + (lane & (TS - 1));
     cnt = counts[row_base + (tl < T ? tl : T - 1)];
   };
   auto h_off = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
     return buf * HBUF + r * HROW + ((((cc >> 3) ^ (2 * (r & 3))) << 4) | ((cc & 7) << 1));
   };
   auto build = [&](int ts, int buf) __attribute__((always_inline)) {
-    // clear this wave's 16 rows (4 KB)
-    uint4* p = reinterpret_cast<uint4*>(sH + buf * HBUF + 16 * wave * HROW);
+    // clear this wave's RPW rows (2 KB)
+    uint4* p = reinterpret_cast<uint4*>(sH + buf * HBUF + RPW * wave * HROW);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < RPW * HROW / 1024; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       const int u = lane + 64 * q;
-      const uint32_t r = 16 * wave + (uint32_t)(u < 16 * U ? u : 0) / U;  // row of the step tile
-      const bool ok = u < 16 * U && ts * 64 + (int)r < T;
+      const uint32_t r = RPW * wave + (uint32_t)(u < RPW * U ? u : 0) / U;  // row of the step tile
+      const bool ok = u < RPW * U && ts * TS + (int)r < T;
       const uint32_t vv[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
       const uint32_t cw[2] = {uc[q].x, uc[q].y};
 #pragma unroll
@@ -315,14 +322,16 @@ __global__ __launch_bounds__(256) void tmm_kernel(
         *reinterpret_cast<uint16_t*>(sH + a) = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
       }
     }
-    // backup slices of the overflowing rows among this wave's 16
-    const uint64_t ov_all = ballot64(cnt > (uint32_t)W && ts * 64 + lane < T);
-    uint64_t ov = ov_all & (0xFFFFull << (16 * wave));
+    // backup slices of the overflowing rows among this wave's RPW (the step is one 32-token
+    // group: its overflowing rows are consecutive entries from the group's first)
+    const uint64_t ov_all =
+        ballot64(lane < TS && cnt > (uint32_t)W && ts * TS + lane < T);
+    uint64_t ov = ov_all & (((1ull << RPW) - 1ull) << (RPW * wave));
     while (ov != 0) {
       const int b = __builtin_ctzll(ov);
       ov &= ov - 1;
-      const uint64_t below = ov_all & ((1ull << b) - 1ull) & (b >= 32 ? 0xFFFFFFFF00000000ull : 0xFFFFFFFFull);
-      const int e = ld_uniform(grp_first + k * d.ng + ts * 2 + (b >> 5)) + __builtin_popcountll(below);
+      const int e = ld_uniform(grp_first + k * d.ng + ts) +
+                    __builtin_popcountll(ov_all & ((1ull << b) - 1ull));
       if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
       const uint32_t hv = *reinterpret_cast<const uint32_t*>(Hbk + (size_t)e * K + hf * BW_JB + 2 * lane);
       const uint32_t c0 = 2 * lane;
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(256) void tmm_kernel(
   float dbacc[2] = {0.0f, 0.0f};
   const bool do_db = DB && dchunk == 0 && wd == 0;
 
-  const int nts = (T + 63) / 64;
+  const int nts = (T + TS - 1) / TS;
   issue_M(0, sM0);
   load_units(0);
   build(0, 0);
@@ -368,31 +377,33 @@ __global__ __launch_bounds__(256) void tmm_kernel(
   auto step = [&](int ts, int cb, unsigned char* sMc, unsigned char* sMn) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): M(ts) and the units have landed
     __syncthreads();                     // H(ts), M(ts) complete; step ts-1's buffers free
-    const bool more = ts + 1 < nts;
-    if (more) {
+    const unsigned char* hb = sH + cb * HBUF;
+    bf16x8_b fa[NKK][2], fb[NKK][4];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {  // all fragments of the step first (16 KB per wave)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[kk][i] = tr_frag(hb, HROW, 64 * wj + 32 * i, kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[kk][j] = tr_frag(sMc, MROW, 128 * wd + 32 * j, kk);
+    }
+    if (ts + 1 < nts) {  // next step's tiles while these MFMAs run
       issue_M(ts + 1, sMn);
       build(ts + 1, cb ^ 1);
       if (ts + 2 < nts) load_units(ts + 2);
     }
-    const unsigned char* hb = sH + cb * HBUF;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_b fa[2], fb[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = tr_frag(hb, HROW, 64 * wj + 32 * i, kk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = tr_frag(sMc, MROW, 128 * wd + 32 * j, kk);
+    for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
       if (do_db) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           float s = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += (float)fa[i][e];
+          for (int e = 0; e < 8; ++e) s += (float)fa[kk][i][e];
           dbacc[i] += s;
         }
       }

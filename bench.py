@@ -217,7 +217,7 @@ def main():
     # ---- density sweep
     sweep = []
     if not args.no_sweep:
-        for rho in (0.01, 0.05, 0.10, 0.20):
+        for rho in (0.002, 0.01, 0.05, 0.10, 0.20):
             m, _, k2, s2, _ = sparse_point(rho, max(10, args.steps // 2), 3, profile=True)
             sweep.append({"rho_target": rho, "density": round(s2["density"], 5),
                           "overflow_tile_rows": int(s2["overflow_tile_rows"]),
