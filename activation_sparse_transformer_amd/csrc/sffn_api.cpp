@@ -19,6 +19,7 @@ struct sparse_ffn {
   const void* b_up;
   const void* W_down;
   int32_t down_policy = SFFN_DOWN_AUTO;
+  float down_gather_density = SFFN_DOWN_GATHER_DENSITY_DEFAULT;
   float down_mfma_density = SFFN_DOWN_MFMA_DENSITY_DEFAULT;
 };
 
@@ -175,9 +176,11 @@ sffn_status_t twell_buffer_sizes(const sffn_config_t* cfg, int32_t T, twell_buff
   SFFN_TRY(check_T(cfg, T));
   if (!out) return fail(SFFN_ERR_INVALID_ARGUMENT, "out is NULL");
   const Dims d = make_dims(cfg, T);
-  const size_t slots = (size_t)d.nt * T * d.W;
+  // GROUP rows of padding after the last tile-row: kernels load the slot pairs of a whole
+  // 32-token group at a time and may read (never use) rows past the last token
+  const size_t slots = ((size_t)d.nt * T + GROUP) * d.W;
   const size_t cap = d.cap > 0 ? d.cap : 1;
-  out->counts = sizeof(uint16_t) * (size_t)d.nt * T;
+  out->counts = sizeof(uint16_t) * ((size_t)d.nt * T + GROUP);  // + padding, as vals/cols
   out->vals = (size_t)d.esz * slots;
   out->cols = slots;
   out->bk_tile = sizeof(int32_t) * cap;
@@ -225,31 +228,47 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
   return SFFN_OK;
 }
 
-// Down-projection of a packed activation.  The gather side is the per-token row gather for
-// bf16 layers (the staged-tile gather for fp32 layers and d_model > 4096); the matrix-core
-// kernel takes bf16 layers whose stored density exceeds the threshold, decided on the device.
+// Down-projection of a packed activation.  The gather kernel is the per-token row gather
+// for bf16 layers (the staged-tile gather for fp32 layers and d_model > 4096); under the auto
+// policy the kernel is chosen by the layer's stored nonzeros, counted and compared on the
+// device: every candidate is launched with its range and all but one return at once.
 static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
                                const Workspace& ws, void* y, hipStream_t s) {
   const bool mfma_ok = down_mfma_supported(d);
+  const bool tiles_ok = down_lds_supported(d);
   const bool rows_ok = down_rows_supported(d);
   auto gather = [&](const int32_t* blk, long long thr) {
     if (rows_ok)
       return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, blk, thr, s); });
     return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, blk, thr, s); });
   };
-  int32_t policy = hd->down_policy;
-  if (!mfma_ok) policy = SFFN_DOWN_GATHER;
-  if (policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
-  if (policy == SFFN_DOWN_MFMA)
+  auto tiles = [&](const int32_t* blk, long long lo, long long hi) {
+    return run("down_tiles", s,
+               [&] { return launch_down_lds(d, act, ws, hd->W_down, y, blk, lo, hi, s); });
+  };
+  auto mfma = [&](const int32_t* blk, long long thr) {
     return run("down_mfma", s,
-               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, nullptr, 0, s); });
-  // the layer goes to the matrix cores when its stored nonzeros exceed thr
-  const double thr_d = (double)hd->down_mfma_density * (double)d.T * (double)d.F;
-  const long long thr = (long long)thr_d;
+               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, blk, thr, s); });
+  };
+  int32_t policy = hd->down_policy;
+  if (policy == SFFN_DOWN_MFMA && !mfma_ok) policy = SFFN_DOWN_TILES;
+  if (policy == SFFN_DOWN_TILES && !tiles_ok) policy = SFFN_DOWN_GATHER;
+  if (policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
+  if (policy == SFFN_DOWN_TILES) return tiles(nullptr, 0, 0);
+  if (policy == SFFN_DOWN_MFMA) return mfma(nullptr, 0);
+  // auto: stored nonzeros n of the layer; gather for n <= thr_g, tiles for thr_g < n <= thr_m,
+  // mfma for n > thr_m.  An unsupported kernel's range goes to the next one down.
+  const double cells = (double)d.T * (double)d.F;
+  long long thr_g = (long long)((double)hd->down_gather_density * cells);
+  long long thr_m = (long long)((double)hd->down_mfma_density * cells);
+  const long long all = (long long)cells + 1;  // above any count
+  if (!mfma_ok) thr_m = all;
+  if (!tiles_ok || d.T < SFFN_DOWN_TILES_MIN_T) thr_g = thr_m;
   SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
-  SFFN_TRY_INNER(gather(ws.blk_nnz, thr));
-  return run("down_mfma", s,
-             [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, ws.blk_nnz, thr, s); });
+  SFFN_TRY_INNER(gather(ws.blk_nnz, thr_g));
+  if (thr_m > thr_g) SFFN_TRY_INNER(tiles(ws.blk_nnz, thr_g, thr_m));
+  if (thr_m < all) SFFN_TRY_INNER(mfma(ws.blk_nnz, thr_m));
+  return SFFN_OK;
 }
 
 static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, void* y,
@@ -332,13 +351,17 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t hd, const void* x, const void* dy
              [&] { return launch_down_mfma(d, dact, ws, hd->W_up, dx, nullptr, 0, s); });
 }
 
-sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float mfma_density) {
+sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float gather_density,
+                                         float mfma_density) {
   if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
-  if (policy != SFFN_DOWN_AUTO && policy != SFFN_DOWN_GATHER && policy != SFFN_DOWN_MFMA)
+  if (policy != SFFN_DOWN_AUTO && policy != SFFN_DOWN_GATHER && policy != SFFN_DOWN_MFMA &&
+      policy != SFFN_DOWN_TILES)
     return fail(SFFN_ERR_INVALID_ARGUMENT, "unknown down-projection policy");
-  if (!(mfma_density >= 0.0f && mfma_density <= 1.0f))
-    return fail(SFFN_ERR_INVALID_ARGUMENT, "mfma_density must be in [0, 1]");
+  if (!(gather_density >= 0.0f && gather_density <= mfma_density && mfma_density <= 1.0f))
+    return fail(SFFN_ERR_INVALID_ARGUMENT,
+                "down-projection thresholds must satisfy 0 <= gather_density <= mfma_density <= 1");
   hd->down_policy = policy;
+  hd->down_gather_density = gather_density;
   hd->down_mfma_density = mfma_density;
   return SFFN_OK;
 }

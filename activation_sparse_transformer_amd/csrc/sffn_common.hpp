@@ -121,11 +121,11 @@ hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, co
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);
-// Down-projection.  Two kernels: the vector gather kernel and the matrix-core kernel.  With
-// blk_nnz (per-256-token-block stored-nonzero counts from launch_block_nnz) both are
-// launched and each reads the layer's total: the gather kernel runs when it is <= thr and
-// the matrix-core kernel otherwise; the other returns at once.  blk_nnz == nullptr runs
-// the kernel launched.
+// Down-projection.  Three kernels: the per-token gather, the LDS-tile vector kernel and the
+// matrix-core kernel.  With blk_nnz (per-256-token-block stored-nonzero counts from
+// launch_block_nnz) each is launched with its range of the layer's total and reads the
+// total at entry: the one whose range holds it runs, the others return at once.
+// blk_nnz == nullptr runs the kernel launched.
 hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* blk_nnz,
                             hipStream_t s);
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
@@ -136,6 +136,12 @@ bool down_rows_supported(const Dims& d);
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                             hipStream_t s);
+// 256 tokens per workgroup over W_down tiles staged in LDS, bf16 dot products (bf16, even
+// W <= 128).  With blk_nnz it runs only when the layer's stored nonzeros are in (lo, hi].
+bool down_lds_supported(const Dims& d);
+hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                           const void* Wd, void* y, const int32_t* blk_nnz, long long lo,
+                           long long hi, hipStream_t s);
 bool backward_supported(const Dims& d);
 // One part of the backward weights pass: which = 0: dh at the stored positions of `act`
 // (into dh_vals / dh_bk); 1: dW_down = H^T g; 2: dW_up = dH^T x and, if db is not null,

@@ -61,8 +61,10 @@ class StatsC(ctypes.Structure):
 
 
 # Down-projection policies (mirror the header's SFFN_DOWN_* values).
-DOWN_AUTO, DOWN_GATHER, DOWN_MFMA = 0, 1, 2
+DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES = 0, 1, 2, 3
+DOWN_GATHER_DENSITY_DEFAULT = 0.0005
 DOWN_MFMA_DENSITY_DEFAULT = 0.005
+DOWN_TILES_MIN_T = 4096
 
 # Exported entry points and their prototypes (restype is always the status enum unless set).
 _PROTOS = {
@@ -74,7 +76,7 @@ _PROTOS = {
     "twell_pack": ([ctypes.POINTER(ConfigC), _P, _I32, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_forward": ([_P, _P, _I32, _P, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_down": ([_P, ctypes.POINTER(BuffersC), _I32, _P, _P], ctypes.c_int),
-    "sparse_ffn_set_down_policy": ([_P, _I32, ctypes.c_float], ctypes.c_int),
+    "sparse_ffn_set_down_policy": ([_P, _I32, ctypes.c_float, ctypes.c_float], ctypes.c_int),
     "sparse_ffn_backward": ([_P, _P, _P, _I32, ctypes.POINTER(BuffersC), _P, _P, _P, _P, _P, _P,
                              _P], ctypes.c_int),
     "twell_stats": ([ctypes.POINTER(ConfigC), ctypes.POINTER(BuffersC), _I32,
@@ -185,10 +187,10 @@ class TwellBuffers:
     def to_host(self) -> dict:
         cfg, T = self.cfg, self.T
         nt, W, K = cfg.n_tiles, cfg.ell_width, cfg.tile
-        counts = self._np("counts", np.uint16).reshape(nt, T)
+        counts = self._np("counts", np.uint16)[: nt * T].reshape(nt, T)
         vdt = np.uint16 if cfg.dtype == "bf16" else np.float32
-        vals = self._np("vals", vdt).reshape(nt, T, W)
-        cols = self._np("cols", np.uint8).reshape(nt, T, W)
+        vals = self._np("vals", vdt)[: nt * T * W].reshape(nt, T, W)
+        cols = self._np("cols", np.uint8)[: nt * T * W].reshape(nt, T, W)
         bk_n = int(self._np("bk_n", np.int32)[0])
         status = int(self._np("status", np.int32)[0])
         r = min(bk_n, cfg.backup_capacity)
@@ -290,14 +292,19 @@ class SparseFFN:
                "sparse_ffn_forward_dump")
         return y, act, z
 
-    def set_down_policy(self, policy: str = "auto", mfma_density: float = DOWN_MFMA_DENSITY_DEFAULT):
-        """Choice of the down-projection kernel: "auto" (matrix cores when the layer's stored
-        density exceeds `mfma_density`, gather otherwise; decided on the device), "gather" or
-        "mfma"."""
-        code = {"auto": DOWN_AUTO, "gather": DOWN_GATHER, "mfma": DOWN_MFMA}.get(policy)
+    def set_down_policy(self, policy: str = "auto",
+                        gather_density: float = DOWN_GATHER_DENSITY_DEFAULT,
+                        mfma_density: float = DOWN_MFMA_DENSITY_DEFAULT):
+        """Choice of the down-projection kernel: "auto" (by the layer's stored density,
+        decided on the device: the per-token gather up to `gather_density`, the LDS-tile
+        vector kernel up to `mfma_density`, the matrix cores above), or always "gather",
+        "tiles" or "mfma"."""
+        code = {"auto": DOWN_AUTO, "gather": DOWN_GATHER, "mfma": DOWN_MFMA,
+                "tiles": DOWN_TILES}.get(policy)
         if code is None:
             raise ValueError(f"unknown down policy {policy!r}")
-        _check(lib().sparse_ffn_set_down_policy(self._h, code, float(mfma_density)),
+        _check(lib().sparse_ffn_set_down_policy(self._h, code, float(gather_density),
+                                                float(mfma_density)),
                "sparse_ffn_set_down_policy")
 
     def backward(self, x, dy, act: TwellBuffers, with_db: bool = True, out=None, stream=None):

@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MAC (dot2) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # launches of one forward, by the names the library's event timing uses
-KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_mfma")
+KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_tiles", "down_mfma")
 TRAIN_KERNELS = KERNELS + ("bwd_dh", "bwd_dw_down", "bwd_dw_up", "bwd_dx")
 
 
@@ -137,19 +137,11 @@ def main():
     ms_plain, _, _, _, _ = sparse_point(args.rho, args.steps, 2, profile=False)
     log(f"  {ms:.4f} ms/step (profiled), {ms_plain:.4f} ms/step (no events); kernels {kt}")
 
-    # ---- which 256-token blocks the matrix-core kernel took (the library's default rule:
-    # stored density above DOWN_MFMA_DENSITY_DEFAULT), from the headline point's counts
-    cnt = act.t["counts"][: c.n_tiles * T * 2].view(torch.int16).to(torch.int32) & 0xFFFF
-    per_tok = cnt.view(c.n_tiles, T).sum(dim=0)
-    nblk = (T + 255) // 256
-    blk = torch.zeros(nblk * 256, dtype=torch.int64, device=dev)
-    blk[:T] = per_tok
-    blk = blk.view(nblk, 256).sum(dim=1)
-    thr = int(sffn.DOWN_MFMA_DENSITY_DEFAULT * 256 * F)
-    mfma_blk = (blk > thr).cpu().numpy()
-    tok_mfma = int(sum(min(256, T - 256 * i) for i in range(nblk) if mfma_blk[i]))
+    # ---- which down-projection kernel took the layer: under the auto policy all candidates
+    # are launched and all but one return at once (a few microseconds)
+    down_names = ("down", "down_tiles", "down_mfma")
+    down_ran = max(down_names, key=lambda k: kt.get(k, 0.0))
     nnz = st["nnz"]
-    nnz_gather = int(blk.cpu().numpy()[~mfma_blk].sum())
 
     # ---- dense bf16 FFN baseline (hipBLASLt through torch), same inputs and stream
     def dense():
@@ -217,7 +209,7 @@ def main():
     # ---- density sweep
     sweep = []
     if not args.no_sweep:
-        for rho in (0.002, 0.01, 0.05, 0.10, 0.20):
+        for rho in (0.002, 0.005, 0.01, 0.05, 0.10, 0.20):
             m, _, k2, s2, _ = sparse_point(rho, max(10, args.steps // 2), 3, profile=True)
             sweep.append({"rho_target": rho, "density": round(s2["density"], 5),
                           "overflow_tile_rows": int(s2["overflow_tile_rows"]),
@@ -237,47 +229,48 @@ def main():
             return ent["bytes_per_launch"]
         return None
 
-    up_ms, dg_ms, dm_ms = kt["up_pack"], kt["down"], kt["down_mfma"]
+    up_ms, dn_ms = kt["up_pack"], kt[down_ran]
     up_flops = 2.0 * T * D * F
-    dm_flops = 2.0 * tok_mfma * F * D          # dense-equivalent contraction of its blocks
-    dg_flops = 2.0 * nnz_gather * D            # one MAC per stored nonzero per output column
-    dg_bytes = (st["bytes_main"] + st["bytes_backup"]) + F * D * 2 + T * D * 2
+    dense_flops = 2.0 * T * F * D              # the matrix-core kernel's dense-equivalent work
+    sparse_flops = 2.0 * nnz * D               # one MAC per stored nonzero per output column
     rate = lambda fl, ms: fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
     kernels = {
         "up_pack": {"ms": round(up_ms, 5), "tflops": round(rate(up_flops, up_ms), 2),
                     "frac_mfma_peak": round(rate(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4)},
-        "down_mfma": {"ms": round(dm_ms, 5), "tokens": tok_mfma,
-                      "dense_equiv_tflops": round(rate(dm_flops, dm_ms), 2),
-                      "frac_mfma_peak": round(rate(dm_flops, dm_ms) / PEAK_BF16_TFLOPS, 4)},
-        "down_gather": {"ms": round(dg_ms, 5), "tokens": T - tok_mfma, "nnz": nnz_gather,
-                        "tflops": round(rate(dg_flops, dg_ms), 2),
-                        "frac_valu_peak": round(rate(dg_flops, dg_ms) / PEAK_VALU_TFLOPS, 4)},
         "order": {"ms": round(kt["order"], 5)}, "zero": {"ms": round(kt["zero"], 5)},
         "block_nnz": {"ms": round(kt["block_nnz"], 5)},
+        "down_launches_ms": {k: round(kt[k], 5) for k in down_names},
     }
-    dom = max((up_ms, "up_pack"), (dm_ms, "down_mfma"), (dg_ms, "down"))[1]
-    if dom == "up_pack":
+    if down_ran == "down_mfma":
+        kernels["down"] = {"kernel": "down_mfma", "ms": round(dn_ms, 5),
+                           "dense_equiv_tflops": round(rate(dense_flops, dn_ms), 2),
+                           "frac_mfma_peak": round(rate(dense_flops, dn_ms) / PEAK_BF16_TFLOPS, 4)}
+    else:
+        kernels["down"] = {"kernel": down_ran, "ms": round(dn_ms, 5), "nnz": int(nnz),
+                           "tflops": round(rate(sparse_flops, dn_ms), 2),
+                           "frac_valu_peak": round(rate(sparse_flops, dn_ms) / PEAK_VALU_TFLOPS, 4)}
+    if up_ms >= dn_ms:
         roofline = {"bound": "mfma", "achieved": round(rate(up_flops, up_ms), 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(rate(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_of("up_pack"),
                     "kernel": "up_pack_bf16_kernel (fused up-projection + bias + ReLU + TwELL pack)",
                     "avg_launch_ms": round(up_ms, 5), "algorithmic_flops_per_launch": up_flops}
-    elif dom == "down_mfma":
-        roofline = {"bound": "mfma", "achieved": round(rate(dm_flops, dm_ms), 2),
+    elif down_ran == "down_mfma":
+        roofline = {"bound": "mfma", "achieved": round(rate(dense_flops, dn_ms), 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(rate(dm_flops, dm_ms) / PEAK_BF16_TFLOPS, 4),
+                    "frac": round(rate(dense_flops, dn_ms) / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_of("down_mfma"),
                     "kernel": "down_mfma_kernel (TwELL tiles rebuilt in LDS, MFMA down-projection)",
-                    "avg_launch_ms": round(dm_ms, 5), "algorithmic_flops_per_launch": dm_flops}
+                    "avg_launch_ms": round(dn_ms, 5), "algorithmic_flops_per_launch": dense_flops}
     else:
-        roofline = {"bound": "alu", "achieved": round(rate(dg_flops, dg_ms), 2),
+        kname = {"down": "down_rows_kernel (per-token W_down row gather)",
+                 "down_tiles": "down_lds_kernel (W_down tiles in LDS, bf16 dot products)"}[down_ran]
+        roofline = {"bound": "alu", "achieved": round(rate(sparse_flops, dn_ms), 2),
                     "peak": PEAK_VALU_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(rate(dg_flops, dg_ms) / PEAK_VALU_TFLOPS, 4),
-                    "traffic": traffic_of("down"),
-                    "kernel": "down_kernel (vector gather down-projection)",
-                    "avg_launch_ms": round(dg_ms, 5), "algorithmic_flops_per_launch": dg_flops,
-                    "algorithmic_bytes_per_launch": dg_bytes}
+                    "frac": round(rate(sparse_flops, dn_ms) / PEAK_VALU_TFLOPS, 4),
+                    "traffic": traffic_of(down_ran), "kernel": kname,
+                    "avg_launch_ms": round(dn_ms, 5), "algorithmic_flops_per_launch": sparse_flops}
 
     # ---- CPU fp64 oracle on a bounded sample of the same workload
     cpu = None

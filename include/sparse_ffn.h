@@ -79,7 +79,9 @@ typedef struct {
 } twell_buffers_t;
 
 /* Byte sizes of each field of twell_buffers_t for T tokens.  Each buffer must be at
- * least this large and 256-byte aligned (torch allocations are). */
+ * least this large and 256-byte aligned (torch allocations are).  counts, vals and cols
+ * hold 32 tile-rows of padding after [n_t, T(, W)] (read by whole-group and whole-word
+ * loads, never used). */
 typedef struct {
   size_t counts, vals, cols, bk_tile, bk_tok, bk_vals, bk_tile_ptr, bk_n, status, workspace;
 } twell_buffer_sizes_t;
@@ -166,25 +168,38 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
 
 /* Which kernel runs the down-projection (inside sparse_ffn_forward and sparse_ffn_down).
  * The TwELL tiles line up with tiled matrix-multiply execution (same article, section "What
- * TwELL and the custom CUDA kernels solve"), so the layer can either gather W_down rows for
- * its stored nonzeros on the vector ALUs (work grows with the nonzeros) or rebuild its hidden
- * tiles in on-chip memory and run them through the matrix cores (work independent of the
- * density, at ~16x the vector rate).
- *   SFFN_DOWN_AUTO:   matrix cores when the layer's stored density (stored nonzeros /
- *                     (T d_ff)) exceeds mfma_density, gather otherwise; the count is taken on
- *                     the device, so the choice costs no host synchronisation (the default,
- *                     with SFFN_DOWN_MFMA_DENSITY_DEFAULT)
- *   SFFN_DOWN_GATHER: always the gather kernel
- *   SFFN_DOWN_MFMA:   always the matrix cores
- * The matrix-core path needs a bf16 layer and ell_width in {16, 32, 48, 64}; other layers
- * always gather.  Both paths accumulate in fp32; they differ only in summation order.  Host
- * only; the setting belongs to the handle.  SFFN_ERR_INVALID_ARGUMENT for an unknown policy
- * or mfma_density outside [0, 1]. */
+ * TwELL and the custom CUDA kernels solve"), so the layer can gather the W_down rows its
+ * stored nonzeros select on the vector ALUs (work grows with the nonzeros) or rebuild its
+ * hidden tiles in on-chip memory and run them through the matrix cores (work independent of
+ * the density, at ~16x the vector rate).  Three kernels:
+ *   gather: one token at a time, W_down rows read straight from memory (cheapest when very
+ *           few rows are used);
+ *   tiles:  256 tokens share each W_down tile staged in LDS, two nonzeros per bf16
+ *           dot-product instruction (bf16 layers with an even ell_width <= 128);
+ *   mfma:   hidden tiles rebuilt in LDS, matrix-core contraction (bf16 layers with
+ *           ell_width in {16, 32, 48, 64}).
+ * Policies:
+ *   SFFN_DOWN_AUTO:   by the layer's stored density (stored nonzeros / (T d_ff)): gather up to
+ *                     gather_density, tiles up to mfma_density, mfma above; the count is taken
+ *                     on the device, so the choice costs no host synchronisation (the default,
+ *                     with the *_DEFAULT thresholds).  A kernel the layer does not support
+ *                     hands its range to the next one down (mfma -> tiles -> gather), and so
+ *                     does tiles below SFFN_DOWN_TILES_MIN_T tokens (its 256-token workgroups
+ *                     walk every tile in turn and need many tokens to fill the GPU).
+ *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA: always that kernel (tiles and mfma
+ *                     fall back as above when the layer does not support them).
+ * All accumulate in fp32; they differ only in summation order.  Host only; the setting
+ * belongs to the handle.  SFFN_ERR_INVALID_ARGUMENT for an unknown policy or thresholds
+ * outside 0 <= gather_density <= mfma_density <= 1. */
 #define SFFN_DOWN_AUTO 0
 #define SFFN_DOWN_GATHER 1
 #define SFFN_DOWN_MFMA 2
+#define SFFN_DOWN_TILES 3
+#define SFFN_DOWN_GATHER_DENSITY_DEFAULT 0.0005f
 #define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
-sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float mfma_density);
+#define SFFN_DOWN_TILES_MIN_T 4096
+sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float gather_density,
+                                         float mfma_density);
 
 /* (sync) Counters of `buf` for T tokens; synchronises `stream`.  Returns
  * SFFN_ERR_BACKUP_OVERFLOW (with *out filled) if the status word reports an overflow. */

@@ -49,15 +49,16 @@ def test_buffer_sizes_formula(sffn):
                       backup_capacity=4096, dtype="bf16")
     s = sffn.buffer_sizes(cfg, 8192)
     nt = 64
-    assert s["counts"] == 2 * nt * 8192
-    assert s["vals"] == 2 * nt * 8192 * 32
-    assert s["cols"] == nt * 8192 * 32
+    assert s["counts"] == 2 * (nt * 8192 + 32)
+    # [n_t, T, W] plus 32 tile-rows of padding read by whole-group loads
+    assert s["vals"] == 2 * (nt * 8192 + 32) * 32
+    assert s["cols"] == (nt * 8192 + 32) * 32
     assert s["bk_vals"] == 2 * 4096 * 128
     assert s["bk_tile"] == s["bk_tok"] == 4 * 4096
     assert s["bk_tile_ptr"] == 4 * (nt + 1)
     assert s["workspace"] > 0
     s32 = sffn.buffer_sizes(cfg.__class__(**{**cfg.__dict__, "dtype": "f32"}), 100)
-    assert s32["vals"] == 4 * nt * 100 * 32
+    assert s32["vals"] == 4 * (nt * 100 + 32) * 32
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -139,7 +139,7 @@ DOWN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("policy", ["gather", "mfma"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma"])
 @pytest.mark.parametrize("T,D,F,K,W,dtype,density", DOWN_CASES)
 def test_down_from_pack(T, D, F, K, W, dtype, density, policy):
     torch, sffn = need_gpu()
@@ -175,15 +175,17 @@ def test_down_from_pack(T, D, F, K, W, dtype, density, policy):
 
 
 def test_down_auto_policy_choice():
-    """Token blocks of 256 with very different densities (0.1%, 4%, 0.3%, 2%; the last block
-    ragged): the auto policy hands the whole layer to one kernel by its total stored density
-    (about 1.6% here), decided on the device.  Every row is written, the result matches the
-    oracle, and it equals bit for bit the single-kernel result the threshold selects."""
+    """Token blocks with very different densities (0.1%, 4%, 0.3%, 2%; the last one ragged):
+    the auto policy hands the whole layer to one kernel by its total stored density (about
+    1.6% here), decided on the device.  Every row is written, the result matches the oracle,
+    and it equals bit for bit the single-kernel result the thresholds select.  Below
+    DOWN_TILES_MIN_T tokens the tiles range goes to the gather kernel."""
     torch, sffn = need_gpu()
     from gen import f32_to_bf16_bits, bf16_bits_to_f32
-    T, D, F, K, W = 1000, 256, 2048, 128, 32
-    parts = [make_hidden(256, F, 0.001, seed=11), make_hidden(256, F, 0.04, seed=12),
-             make_hidden(256, F, 0.003, seed=13), make_hidden(232, F, 0.02, seed=14)]
+    T, D, F, K, W = 4200, 256, 2048, 128, 32
+    assert T >= sffn.DOWN_TILES_MIN_T
+    parts = [make_hidden(1024, F, 0.001, seed=11), make_hidden(1024, F, 0.04, seed=12),
+             make_hidden(1024, F, 0.003, seed=13), make_hidden(1128, F, 0.02, seed=14)]
     h = np.concatenate(parts, axis=0)
     dens = np.count_nonzero(h) / h.size
     assert 0.01 < dens < 0.02
@@ -197,21 +199,49 @@ def test_down_auto_policy_choice():
     layer = sffn.SparseFFN(cfg, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
                            torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
     buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+    # (policy, gather_density, mfma_density) -> the kernel that must run
+    cases = [("gather", 0.0, 0.0, "gather"), ("tiles", 0.0, 0.0, "tiles"),
+             ("mfma", 0.0, 0.0, "mfma"), ("auto", 0.0, 0.0, "mfma"),
+             ("auto", 1.0, 1.0, "gather"), ("auto", 0.0, 1.0, "tiles"),
+             ("auto", 0.005, 0.03, "tiles"), ("auto", 0.02, 0.03, "gather"),
+             ("auto", 0.002, 0.01, "mfma")]
     ys = {}
-    for policy, thr in (("gather", 0.0), ("mfma", 0.0), ("auto", 0.0), ("auto", 1.0),
-                        ("auto", 0.005), ("auto", 0.03)):
-        layer.set_down_policy(policy, thr)
+    for policy, tg, tm, expect in cases:
+        layer.set_down_policy(policy, tg, tm)
         y = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        sffn.profile_reset()
+        sffn.profile_enable(True)
         layer.down(buf, y=y)
+        sffn.profile_enable(False)
         yh = y_to_host(torch, y)
-        assert not np.isnan(yh).any(), f"{policy}/{thr}: rows not written"
-        assert_y_close(yh, y_ref, "bf16", f"{policy}/{thr}")
-        ys[(policy, thr)] = yh
-    g, m = ys[("gather", 0.0)], ys[("mfma", 0.0)]
-    assert np.array_equal(ys[("auto", 0.0)], m)     # any stored nonzero exceeds 0
-    assert np.array_equal(ys[("auto", 1.0)], g)
-    assert np.array_equal(ys[("auto", 0.005)], m)   # 1.6% > 0.5%
-    assert np.array_equal(ys[("auto", 0.03)], g)    # 1.6% <= 3%
+        assert not np.isnan(yh).any(), f"{policy}/{tg}/{tm}: rows not written"
+        assert_y_close(yh, y_ref, "bf16", f"{policy}/{tg}/{tm}")
+        if policy != "auto":
+            ys[expect] = yh
+        else:
+            assert np.array_equal(yh, ys[expect]), f"auto {tg}/{tm} should run {expect}"
+        launched = {k: sffn.profile_read(n)[1] for k, n in
+                    (("gather", "down"), ("tiles", "down_tiles"), ("mfma", "down_mfma"))}
+        if policy == "auto":
+            assert all(v == 1 for v in launched.values() if v) and launched[expect] == 1
+        else:
+            assert launched == {k: int(k == expect) for k in launched}, launched
+    sffn.profile_reset()
+    # a short activation (the first 1000 tokens): the tiles range goes to the gather kernel
+    Ts = 1000
+    cfg_s = _cfg(sffn, Ts, D, F, K, W, "bf16")
+    layer_s = sffn.SparseFFN(cfg_s, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
+                             torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
+    buf_s = sffn.twell_pack(cfg_s, to_dev_f32(torch, h[:Ts]))
+    y_refs = oracle.down_sparse(oracle.pack(h_ref[:Ts], K, W), Wd64)
+    outs = {}
+    for policy, tg, tm in (("gather", 0.0, 0.0), ("auto", 0.0, 1.0)):
+        layer_s.set_down_policy(policy, tg, tm)
+        y = torch.full((Ts, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        layer_s.down(buf_s, y=y)
+        outs[policy] = y_to_host(torch, y)
+        assert_y_close(outs[policy], y_refs, "bf16", f"short {policy}")
+    assert np.array_equal(outs["auto"], outs["gather"])
 
 
 def test_down_policy_arguments():
@@ -219,11 +249,12 @@ def test_down_policy_arguments():
     cfg = _cfg(sffn, 64, 128, 256, 128, 16, "bf16")
     z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
     layer = sffn.SparseFFN(cfg, z(256, 128), z(256), z(256, 128))
-    for bad in (-0.1, 1.5, float("nan")):
+    for g, m in ((-0.1, 0.5), (0.0, 1.5), (0.3, 0.2), (float("nan"), 0.5), (0.0, float("nan"))):
         with pytest.raises(sffn.SffnError):
-            layer.set_down_policy("auto", bad)
+            layer.set_down_policy("auto", g, m)
     with pytest.raises(ValueError):
         layer.set_down_policy("fastest")
+    layer.set_down_policy("auto", 0.3, 0.3)  # equal thresholds: no tiles range
 
 
 def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
@@ -279,7 +310,7 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     return rel
 
 
-@pytest.mark.parametrize("policy", ["gather", "mfma"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma"])
 @pytest.mark.parametrize("name,T,rho", [
     ("C1", None, None), ("C1b", None, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
@@ -292,7 +323,7 @@ def test_forward_parity(name, T, rho, policy):
     _forward_case(torch, sffn, L, policy=policy)
 
 
-@pytest.mark.parametrize("policy", ["gather", "mfma"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma"])
 def test_forward_heavy_rows_force_backup(policy):
     """2B-like layer at a reduced T with heavy rows: the backup is in use."""
     torch, sffn = need_gpu()
@@ -372,7 +403,8 @@ def _decode_rows(cfg, host, rows):
 
 @pytest.mark.parametrize("name,rho,policy", [
     ("C2", None, "auto"), ("C3", 0.01, "auto"), ("C3", 0.05, "auto"), ("C3", 0.05, "gather"),
-    ("C3", 0.10, "auto"), ("C3", 0.20, "auto"), ("C4", None, "auto"), ("C4", None, "gather")])
+    ("C3", 0.05, "tiles"), ("C3", 0.05, "mfma"), ("C3", 0.10, "auto"), ("C3", 0.20, "auto"),
+    ("C4", None, "auto"), ("C4", None, "gather"), ("C4", None, "tiles")])
 def test_forward_full_size_sampled(name, rho, policy):
     """Full layer sizes, the launch configuration the benchmark times: sampled tokens
     against the oracle, and size-independent invariants on the whole TwELL."""
