@@ -43,7 +43,8 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // BK: d_model slice per LDS stage.  WPE: waves per SIMD the kernel is built for; with 2
 // (BK = 32, 128 tokens, 48 KB of LDS, at most 256 registers), two workgroups share a CU and
 // one's pack epilogue runs while the other's MFMA loop keeps the matrix cores busy.
-template <int K, int NB, bool DUMP, int BK, int WPE>
+// NS: LDS stages in the ring (the loads of a stage are issued NS - 1 stages ahead).
+template <int K, int NB, bool DUMP, int BK, int WPE, int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
                     const uint16_t* __restrict__ bu, twell_buffers_t b, Workspace ws,
@@ -57,12 +58,14 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
   constexpr int TPW = (K == 64) ? 2 : 1; // tile parts per wave
   constexpr int NTWG = UP_BN / K;        // tiles per workgroup (4, 2, 1)
 
-  // LDS: two stages, each a separate object so that loads into one stage and reads of the
-  // other are known not to alias; after the loop the A stages hold the TwELL staging.
+  // LDS: NS stages, each a separate object so that loads into one stage and reads of the
+  // others are known not to alias; after the loop the A stages hold the TwELL staging.
   __shared__ __attribute__((aligned(16))) uint4 sA0[UP_BN * CH];
   __shared__ __attribute__((aligned(16))) uint4 sA1[UP_BN * CH];
+  __shared__ __attribute__((aligned(16))) uint4 sA2[NS > 2 ? UP_BN * CH : 1];
   __shared__ __attribute__((aligned(16))) uint4 sB0[BM * CH];
   __shared__ __attribute__((aligned(16))) uint4 sB1[BM * CH];
+  __shared__ __attribute__((aligned(16))) uint4 sB2[NS > 2 ? BM * CH : 1];
   __shared__ int part_cnt[2][32][2];   // K=256: per (wt, token) count of each wave half
   __shared__ int claim_base[NTWG][2];  // staged-backup base per (tile, wt)
 
@@ -140,38 +143,72 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
       fb[bb] = __builtin_bit_cast(bf16x8_t, B[r * CH + (ch ^ swz(r))]);
     }
   };
-  auto compute = [&](const uint4* A, const uint4* B) {
-    bf16x8_t fa[2][4], fb[2][NB];
-    load_frags(A, B, 0, fa[0], fb[0]);
+  // The k-loop is a ring of NS LDS stages of BK columns, each stage KS = BK/16 MFMA k-steps;
+  // the fragments of the next k-step are read while the current one's MFMAs run.  At the
+  // last k-step of a stage the next stage is waited for (its loads, and every wave's reads
+  // of this stage done: one barrier), the freed buffer is refilled with the stage NS ahead,
+  // and the next stage's first fragments are read, all before that k-step's MFMAs.
+  constexpr int KS = BK / 16;
+  constexpr int LPS = ALD + BLD;  // direct loads per wave per stage
+  static_assert(LPS * (NS - 1) <= 15, "vmcnt immediate");
+  const int nk = D / BK;          // D % 128 == 0
+  bf16x8_t fa[2][4], fb[2][NB];
+  auto mfmas = [&](int c) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) load_frags(A, B, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the next step's reads ahead of these MFMAs
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int bb = 0; bb < NB; ++bb)
+        acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][a], fb[c][bb], acc[a][bb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Every stage runs the same instructions: the last one also waits, reloads (the last
+  // stage again, into a buffer nothing reads) and reads fragments it does not use.  With
+  // one path through each stage, and a loop over whole rings of NS stages, the compiler
+  // knows at every fragment read which buffers the loads in flight fill, and adds no waits.
+  auto stage = [&](int st, uint4* A, uint4* B, const uint4* An, const uint4* Bn)
+      __attribute__((always_inline)) {
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb)
-          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][bb],
-                                                               acc[a][bb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kk = 0; kk < KS; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < KS) {
+        load_frags(A, B, kk + 1, fa[c ^ 1], fb[c ^ 1]);
+      } else {
+        // the next stage is in once only the NS - 2 stages after it may still be loading
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 2)));
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage's reads are done
+        // a plain barrier: the workgroup fence of __syncthreads would also wait for the
+        // loads still in flight (they write LDS); the clobber keeps memory accesses in place
+        __asm__ volatile("s_barrier" ::: "memory");
+        issue(st + NS < nk ? st + NS : nk - 1, A, B);
+        load_frags(An, Bn, 0, fa[c ^ 1], fb[c ^ 1]);
+      }
+      mfmas(c);
     }
   };
 
-  const int nk = D / BK;  // D % 128 == 0, so nk is even
   issue(0, sA0, sB0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    issue(kt + 1, sA1, sB1);
-    compute(sA0, sB0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (kt + 2 < nk) issue(kt + 2, sA0, sB0);
-    compute(sA1, sB1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+  issue(1 < nk ? 1 : 0, sA1, sB1);
+  if constexpr (NS > 2) issue(2 < nk ? 2 : nk - 1, sA2, sB2);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 1)));  // stage 0 is in
+  __asm__ volatile("s_barrier" ::: "memory");
+  load_frags(sA0, sB0, 0, fa[0], fb[0]);
+  const int nring = nk / NS * NS;
+  for (int st = 0; st < nring; st += NS) {
+    stage(st, sA0, sB0, sA1, sB1);
+    if constexpr (NS == 2) {
+      stage(st + 1, sA1, sB1, sA0, sB0);
+    } else {
+      stage(st + 1, sA1, sB1, sA2, sB2);
+      stage(st + 2, sA2, sB2, sA0, sB0);
+    }
   }
+  // the last nk % NS stages (the ring position is back at buffer 0)
+  if (nring < nk) stage(nring, sA0, sB0, sA1, sB1);
+  if constexpr (NS > 2) {
+    if (nring + 1 < nk) stage(nring + 1, sA1, sB1, sA2, sB2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated loads land before the staging reuses LDS
 
   // ---- epilogue
   // Own element e = a*16 + r holds wave-local neuron nl = a*32 + 8*(r>>2) + 4*lh + (r&3);
@@ -372,7 +409,7 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
   }
 }
 
-template <int K, int NB, int BK = 64, int WPE = 1>
+template <int K, int NB, int BK = 64, int WPE = 1, int NS = 2>
 static hipError_t launch_up_t(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                               const uint16_t* bu, const twell_buffers_t& b, const Workspace& ws,
                               float* zdump, hipStream_t s) {
@@ -382,10 +419,10 @@ static hipError_t launch_up_t(const Dims& d, const uint16_t* x, const uint16_t* 
   const int total = nN * nM;
   const int per_xcd = (total + 7) / 8;
   if (zdump)
-    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, true, BK, WPE>), dim3(8 * per_xcd), dim3(256), 0, s, d,
+    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, true, BK, WPE, NS>), dim3(8 * per_xcd), dim3(256), 0, s, d,
                        x, Wu, bu, b, ws, zdump);
   else
-    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, false, BK, WPE>), dim3(8 * per_xcd), dim3(256), 0, s,
+    hipLaunchKernelGGL((up_pack_bf16_kernel<K, NB, false, BK, WPE, NS>), dim3(8 * per_xcd), dim3(256), 0, s,
                        d, x, Wu, bu, b, ws, zdump);
   return hipGetLastError();
 }
@@ -397,8 +434,8 @@ hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t*
   // four tiles needs the larger LDS stages)
   switch (d.K) {
     case 64: return launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
-    case 128: return launch_up_t<128, 2, 32, 2>(d, x, Wu, bu, b, ws, zdump, s);
-    case 256: return launch_up_t<256, 2, 32, 2>(d, x, Wu, bu, b, ws, zdump, s);
+    case 128: return launch_up_t<128, 2, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s);
+    case 256: return launch_up_t<256, 2, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s);
   }
   return hipErrorInvalidValue;
 }
