@@ -154,13 +154,34 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
   const int nk = D / BK;          // D % 128 == 0
   bf16x8_t fa[2][4], fb[2][NB];
   auto mfmas = [&](int c) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb)
         acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][a], fb[c][bb], acc[a][bb], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Instruction order of a k-step: its 4*NB MFMAs with the next fragments' LDS reads (and,
+  // at a stage's end, the direct loads of the freed buffer and their address arithmetic)
+  // placed between them, so the matrix pipe is fed while those issue.
+  constexpr int NFR = 4 + NB;  // fragment reads per k-step
+  auto order_step = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NFR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - NFR, 0);
+  };
+  auto order_boundary = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (load addresses)
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (direct load)
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);  // the next stage's first reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - LPS - 1, 0);
   };
   // Every stage runs the same instructions: the last one also waits, reloads (the last
   // stage again, into a buffer nothing reads) and reads fragments it does not use.  With
@@ -172,7 +193,11 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
     for (int kk = 0; kk < KS; ++kk) {
       const int c = kk & 1;
       if (kk + 1 < KS) {
+        __builtin_amdgcn_sched_barrier(0);
         load_frags(A, B, kk + 1, fa[c ^ 1], fb[c ^ 1]);
+        mfmas(c);
+        order_step();
+        __builtin_amdgcn_sched_barrier(0);
       } else {
         // the next stage is in once only the NS - 2 stages after it may still be loading
         __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 2)));
@@ -180,10 +205,13 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
         // a plain barrier: the workgroup fence of __syncthreads would also wait for the
         // loads still in flight (they write LDS); the clobber keeps memory accesses in place
         __asm__ volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         issue(st + NS < nk ? st + NS : nk - 1, A, B);
         load_frags(An, Bn, 0, fa[c ^ 1], fb[c ^ 1]);
+        mfmas(c);
+        order_boundary();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      mfmas(c);
     }
   };
 
