@@ -9,21 +9,22 @@
 // d_model 2048), so this kernel wins when few rows are used; the matrix-core kernel (whose
 // work does not depend on the density) takes dense layers.
 //
-// One workgroup per token at a time, 4 waves; wave w takes a contiguous quarter of the tiles, lane l of
-// it tile k = k0 + l: its count, then its slots 8 at a time (16 B values + 8 B columns).  The
+// One workgroup per token at a time (NW waves; for few tokens NW = 16 and the workgroups of a
+// token also split its columns into 512-wide chunks, so a short batch still spreads over
+// many CUs); wave w takes a contiguous 1/NW of the tiles, lane l of it tile k = k0 + l: its
+// count, then its slots 8 at a time (16 B values + 8 B columns).  The
 // (row, value) pairs of the lanes are broadcast with readlane in batches of up to 8 (4 for
 // d_model > 2048) whose
 // W_down row loads are all issued before any is used, so a token with many nonzeros (heavy
 // tokens run at 10-20x the mean density) is not a chain of single-row latencies.  Lane L owns
-// output columns 512q + 8L (q < NQ): every row is read as NQ coalesced 1 KB wave loads.  The
-// waves' partial rows are summed in LDS and y is written as 16-byte stores.
+// output columns c0 + 512q + 8L (q < NQ; c0 = the workgroup's column chunk): every row is
+// read as NQ coalesced 1 KB wave loads.  The waves' partial rows are summed in LDS and y is
+// written as 16-byte stores.
 #include "sffn_common.hpp"
 
 namespace sffn {
 
-constexpr int ROWS_WAVES = 4;
-
-template <int NQ>
+template <int NQ, int ROWS_WAVES>
 __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int T = d.T, D = d.D, K = d.K, W = d.W;
+  const int cb = blockIdx.y * NQ * 512;  // first output column of this workgroup
   // the layer goes to this kernel only when its stored-nonzero count is at most thr
   if (blk_nnz != nullptr && layer_nnz(blk_nnz, (T + 255) / 256) > thr) return;
   for (int t = blockIdx.x; t < T; t += gridDim.x) {  // workgroup-uniform token loop
@@ -57,8 +59,8 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
         const uint16_t* wr = Wd + (size_t)bj[i] * D;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          const int c0 = 512 * q + 8 * lane;
-          if (q < NQ - 1 || c0 < D) w[i][q] = *reinterpret_cast<const uint4*>(wr + c0);
+          const int c0 = cb + 512 * q + 8 * lane;
+          if (c0 < D) w[i][q] = *reinterpret_cast<const uint4*>(wr + c0);
         }
       }
     }
@@ -156,8 +158,8 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   if (wave == 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int c0 = 512 * q + 8 * lane;
-      if (q < NQ - 1 || c0 < D) {
+      const int c0 = cb + 512 * q + 8 * lane;
+      if (c0 < D) {
 #pragma unroll
         for (int w2 = 0; w2 < ROWS_WAVES - 1; ++w2) {
           const float4* p = reinterpret_cast<const float4*>(&part[w2][512 * q + 8 * lane]);
@@ -178,27 +180,35 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   }
 }
 
+// Few tokens: 16 waves per workgroup and one 512-column chunk per workgroup.
+constexpr int ROWS_FEW_T = 1024;
+
 bool down_rows_supported(const Dims& d) {
-  return d.bf16 && d.D <= 4096 && d.D % 8 == 0 && d.W % 8 == 0 &&
-         (d.nt + ROWS_WAVES - 1) / ROWS_WAVES <= 64;
+  return d.bf16 && d.D <= 4096 && d.D % 8 == 0 && d.W % 8 == 0 && (d.nt + 3) / 4 <= 64;
 }
 
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                             hipStream_t s) {
   if (!down_rows_supported(d)) return hipErrorInvalidValue;
-  // at most 2048 workgroups, each looping over tokens: a skipped launch (the layer went to the
-  // matrix cores) then costs little
-  const dim3 grid(d.T < 2048 ? d.T : 2048), block(64 * ROWS_WAVES);
+  // at most 2048 workgroups (x), each looping over tokens: a skipped launch (the layer went to
+  // the matrix cores) then costs little
   auto* c = b.counts;
   auto* v = static_cast<const uint16_t*>(b.vals);
   auto* bk = static_cast<const uint16_t*>(b.bk_vals);
   auto* w = static_cast<const uint16_t*>(Wd);
   auto* yy = static_cast<uint16_t*>(y);
+  if (d.T < ROWS_FEW_T) {
+    const dim3 grid(d.T, (d.D + 511) / 512), block(64 * 16);
+    hipLaunchKernelGGL((down_rows_kernel<1, 16>), grid, block, 0, s, d, c, v, b.cols, bk,
+                       ws.grp_first, w, yy, blk_nnz, thr);
+    return hipGetLastError();
+  }
+  const dim3 grid(d.T < 2048 ? d.T : 2048), block(64 * 4);
   switch ((d.D + 511) / 512) {
 #define SFFN_ROWS(NQ)                                                                      \
   case NQ:                                                                                 \
-    hipLaunchKernelGGL(down_rows_kernel<NQ>, grid, block, 0, s, d, c, v, b.cols, bk,        \
+    hipLaunchKernelGGL((down_rows_kernel<NQ, 4>), grid, block, 0, s, d, c, v, b.cols, bk,   \
                        ws.grp_first, w, yy, blk_nnz, thr);                                 \
     break;
     SFFN_ROWS(1) SFFN_ROWS(2) SFFN_ROWS(3) SFFN_ROWS(4)

@@ -262,8 +262,9 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
   long long thr_g = (long long)((double)hd->down_gather_density * cells);
   long long thr_m = (long long)((double)hd->down_mfma_density * cells);
   const long long all = (long long)cells + 1;  // above any count
-  if (!mfma_ok) thr_m = all;
+  if (!mfma_ok || d.T < SFFN_DOWN_MFMA_MIN_T) thr_m = all;
   if (!tiles_ok || d.T < SFFN_DOWN_TILES_MIN_T) thr_g = thr_m;
+  if (thr_g >= all) return gather(nullptr, 0);  // one candidate: no count needed
   SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
   SFFN_TRY_INNER(gather(ws.blk_nnz, thr_g));
   if (thr_m > thr_g) SFFN_TRY_INNER(tiles(ws.blk_nnz, thr_g, thr_m));
@@ -281,7 +282,15 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
   const Workspace ws = carve(act->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   SFFN_TRY(run("zero", s, [&] { return launch_zero_claim(ws, s); }));
-  if (d.bf16) {
+  if (up_small_supported(d)) {
+    // decode-shaped batch: up-projection over many small workgroups, then the pack kernel
+    SFFN_TRY(run("up_small", s, [&] {
+      return launch_up_small(d, static_cast<const uint16_t*>(x),
+                             static_cast<const uint16_t*>(hd->W_up),
+                             static_cast<const uint16_t*>(hd->b_up), ws.hsmall, z, s);
+    }));
+    SFFN_TRY(run("pack", s, [&] { return launch_pack(d, ws.hsmall, *act, ws, s); }));
+  } else if (d.bf16) {
     SFFN_TRY(run("up_pack", s, [&] {
       return launch_up_pack_bf16(d, static_cast<const uint16_t*>(x),
                                  static_cast<const uint16_t*>(hd->W_up),

@@ -35,7 +35,12 @@ struct Workspace {
   long long* stats;     // [8]      stats reduction output
   int32_t* blk_nnz;     // [nblk]   stored nonzeros per 256-token block (down-path choice)
   int32_t* grp_first;   // [nt*ng+1] first backup entry of each (tile, group), canonical order
+  float* hsmall;        // [min(T, UP_SMALL_T), F] ReLU output of the decode-shaped up path
 };
+
+// Batches of at most this many tokens take the decode-shaped up-projection (one workgroup
+// per 32 neurons, then the TwELL pack kernel) instead of the fused up + pack kernel.
+constexpr int UP_SMALL_T = 32;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -48,6 +53,7 @@ inline size_t workspace_bytes(const Dims& d) {
   n += align256(sizeof(long long) * 8);
   n += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
+  n += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
   return n;
 }
 
@@ -67,6 +73,8 @@ inline Workspace carve(void* base, const Dims& d) {
   w.blk_nnz = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   w.grp_first = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
+  w.hsmall = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -118,6 +126,11 @@ hipError_t launch_stats(const Dims& d, const twell_buffers_t& b, const Workspace
 hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, const float* bu,
                               const twell_buffers_t& b, const Workspace& ws, float* zdump,
                               hipStream_t s);
+// Decode-shaped up-projection: h = max(x W_up^T + b, 0) as fp32 [T, F] (T <= UP_SMALL_T),
+// and z = x W_up^T + b into zdump if it is not null.
+bool up_small_supported(const Dims& d);
+hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
+                           const uint16_t* bu, float* h, float* zdump, hipStream_t s);
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);

@@ -17,6 +17,8 @@ import hashlib
 import json
 import os
 import sys
+import glob
+import threading
 import time
 
 import numpy as np
@@ -48,6 +50,48 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def power_sensor():
+    """Path of the GPU's board power reading (hwmon power1_input, microwatts), or None."""
+    for p in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")):
+        try:
+            dev_dir = p.split("/hwmon/")[0]
+            with open(os.path.join(dev_dir, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+            with open(p) as f:
+                int(f.read())
+            return p
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+def average_power(path, run, seconds):
+    """Mean board power (W) while `run()` is called repeatedly for about `seconds` (the first
+    fifth of the samples, the ramp, is dropped); returns (watts, calls, elapsed_s)."""
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            with open(path) as f:
+                samples.append(int(f.read()) * 1e-6)
+            time.sleep(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    calls, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            run()
+        calls += 20
+        run.sync()
+    elapsed = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    keep = samples[len(samples) // 5:] or samples
+    return (sum(keep) / len(keep) if keep else float("nan")), calls, elapsed
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,6 +105,9 @@ def main():
                     help="also run a plain device copy of this many MiB (3 times): the reference "
                          "kernel that scales hardware byte counters to bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--energy-seconds", type=float, default=2.0,
+                    help="seconds of repeated forwards per energy measurement (0: skip)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped points")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the layer shards by tokens with no exchange, "
@@ -272,6 +319,83 @@ def main():
                     "traffic": traffic_of(down_ran), "kernel": kname,
                     "avg_launch_ms": round(dn_ms, 5), "algorithmic_flops_per_launch": sparse_flops}
 
+    # ---- energy per token of the headline forward, sparse and dense (board power sampled
+    # every 10 ms while the forward runs back to back)
+    energy = None
+    sensor = power_sensor() if args.energy_seconds > 0 else None
+    if sensor:
+        class Runner:
+            def __init__(self, f):
+                self.f = f
+
+            def __call__(self):
+                self.f()
+
+            def sync(self):
+                torch.cuda.synchronize()
+        layer_e = sffn.SparseFFN(cfg, Wu, b0, Wd)
+        run_s = Runner(lambda: layer_e.forward(x, act=act, y=y))
+        run_d = Runner(dense)
+        time.sleep(0.5)
+        with open(sensor) as f:
+            idle_w = int(f.read()) * 1e-6
+        res = {}
+        for name, run in (("sparse", run_s), ("dense_bf16", run_d)):
+            for _ in range(10):
+                run()
+            run.sync()
+            w, calls, el = average_power(sensor, run, args.energy_seconds)
+            tps = calls * T / el
+            res[name] = {"avg_power_w": round(w, 1), "tokens_per_s": round(tps, 1),
+                         "joules_per_token": w / tps, "microjoules_per_token": round(w / tps * 1e6, 4)}
+            log(f"  energy {name}: {w:.1f} W, {tps:.3e} tokens/s, {w / tps * 1e6:.4f} uJ/token")
+        energy = {"sensor": sensor, "idle_power_w": round(idle_w, 1),
+                  "seconds_per_point": args.energy_seconds, **res,
+                  "sparse_vs_dense_energy_per_token": round(
+                      res["sparse"]["joules_per_token"] / res["dense_bf16"]["joules_per_token"], 4)}
+        del layer_e
+
+    # ---- decode-shaped points: few tokens, the layer reads all of W_up but only the W_down
+    # rows the stored nonzeros select; sparse (auto policy and each down kernel) vs dense
+    decode = []
+    if not args.no_decode:
+        for Td in (1, 8, 32, 128, 256):
+            cfg_d = sffn.Config(d_model=D, d_ff=F, tile=c.tile, ell_width=c.ell_width,
+                                max_tokens=Td, backup_capacity=max(64, c.n_tiles * Td // 8),
+                                dtype="bf16")
+            act_d = sffn.TwellBuffers(cfg_d, Td, device=dev)
+            xd = x[:Td].contiguous()
+            yd = torch.empty_like(xd)
+            layer_d = sffn.SparseFFN(cfg_d, Wu, b0, Wd)
+            pt = {"T": Td}
+            for pol in ("auto", "gather", "mfma"):
+                layer_d.set_down_policy(pol)
+                ms_d, _ = time_steps(lambda: layer_d.forward(xd, act=act_d, y=yd), 50, 10)
+                pt[f"ms_{pol}"] = round(ms_d, 5)
+            layer_d.set_down_policy("auto")
+            ms_dd, _ = time_steps(lambda: torch.matmul(Fn.relu(Fn.linear(xd, Wu, b0)), Wd), 50, 10)
+            hs = act_d.to_host()
+            used = np.zeros(F, bool)
+            K = c.tile
+            for k in range(c.n_tiles):
+                m = np.minimum(hs["counts"][k].astype(np.int64), c.ell_width)
+                for t in range(Td):
+                    used[k * K + hs["cols"][k, t, :m[t]].astype(np.int64)] = True
+            for e in range(len(hs["bk_tile"])):
+                used[int(hs["bk_tile"][e]) * K + np.nonzero(hs["bk_vals"][e])[0]] = True
+            rows = int(used.sum())
+            sp_bytes = F * D * 2 + F * 2 + rows * D * 2 + 2 * Td * D * 2
+            dn_bytes = 2 * F * D * 2 + F * 2 + 2 * Td * D * 2
+            pt.update({"ms_dense": round(ms_dd, 5), "speedup_vs_dense": round(ms_dd / pt["ms_auto"], 4),
+                       "tokens_per_s": round(Td / (pt["ms_auto"] * 1e-3), 1),
+                       "w_down_rows_used": rows, "w_down_rows": F,
+                       "weight_bytes_sparse": sp_bytes, "weight_bytes_dense": dn_bytes,
+                       "hbm_gbs_sparse": round(sp_bytes / (pt["ms_auto"] * 1e-3) / 1e9, 1),
+                       "hbm_gbs_dense": round(dn_bytes / (ms_dd * 1e-3) / 1e9, 1)})
+            decode.append(pt)
+            log(f"  decode T={Td}: {pt}")
+            del layer_d, act_d
+
     # ---- CPU fp64 oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu:
@@ -317,6 +441,8 @@ def main():
         "kernels": kernels,
         "effective_tflops_dense_equiv": round(4.0 * T * D * F / (ms * 1e-3) / 1e12, 2),
         "train": train,
+        "energy": energy,
+        "decode": decode,
         "sweep": sweep,
         "kernel_source_hash": src_hash,
     }

@@ -227,21 +227,24 @@ def test_down_auto_policy_choice():
         else:
             assert launched == {k: int(k == expect) for k in launched}, launched
     sffn.profile_reset()
-    # a short activation (the first 1000 tokens): the tiles range goes to the gather kernel
+    # a short activation (the first 1000 tokens): the tiles range goes to the gather kernel,
+    # and below DOWN_MFMA_MIN_T the matrix-core range too
     Ts = 1000
+    assert Ts < sffn.DOWN_MFMA_MIN_T
     cfg_s = _cfg(sffn, Ts, D, F, K, W, "bf16")
     layer_s = sffn.SparseFFN(cfg_s, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
                              torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
     buf_s = sffn.twell_pack(cfg_s, to_dev_f32(torch, h[:Ts]))
     y_refs = oracle.down_sparse(oracle.pack(h_ref[:Ts], K, W), Wd64)
     outs = {}
-    for policy, tg, tm in (("gather", 0.0, 0.0), ("auto", 0.0, 1.0)):
+    for policy, tg, tm in (("gather", 0.0, 0.0), ("auto", 0.0, 1.0), ("auto", 0.0, 0.0)):
         layer_s.set_down_policy(policy, tg, tm)
         y = torch.full((Ts, D), float("nan"), dtype=torch.bfloat16, device="cuda")
         layer_s.down(buf_s, y=y)
-        outs[policy] = y_to_host(torch, y)
-        assert_y_close(outs[policy], y_refs, "bf16", f"short {policy}")
-    assert np.array_equal(outs["auto"], outs["gather"])
+        outs[(policy, tm)] = y_to_host(torch, y)
+        assert_y_close(outs[(policy, tm)], y_refs, "bf16", f"short {policy} {tm}")
+    assert np.array_equal(outs[("auto", 1.0)], outs[("gather", 0.0)])
+    assert np.array_equal(outs[("auto", 0.0)], outs[("gather", 0.0)])
 
 
 def test_down_policy_arguments():
@@ -315,6 +318,8 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     ("C1", None, None), ("C1b", None, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
     ("C4", 300, None),
+    # decode-shaped batches (at most 32 tokens: the small-batch up-projection + pack path)
+    ("C3", 1, 0.05), ("C3", 7, 0.01), ("C3", 32, 0.05), ("C2", 3, None), ("C4", 5, None),
 ])
 def test_forward_parity(name, T, rho, policy):
     torch, sffn = need_gpu()
