@@ -37,6 +37,23 @@ def test_header_symbols_exported(sffn):
     assert sorted(b.exported_names()) == names
 
 
+def test_header_constants_match_binding(sffn):
+    """The binding's down-policy codes, thresholds and token-count rules equal the header's
+    #defines (the library reads the header's)."""
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(SFFN_DOWN_[A-Z_]+)\s+([0-9.]+)f?", text))
+    want = {"SFFN_DOWN_AUTO": sffn.DOWN_AUTO, "SFFN_DOWN_GATHER": sffn.DOWN_GATHER,
+            "SFFN_DOWN_MFMA": sffn.DOWN_MFMA, "SFFN_DOWN_TILES": sffn.DOWN_TILES,
+            "SFFN_DOWN_GATHER_DENSITY_DEFAULT": sffn.DOWN_GATHER_DENSITY_DEFAULT,
+            "SFFN_DOWN_MFMA_DENSITY_DEFAULT": sffn.DOWN_MFMA_DENSITY_DEFAULT,
+            "SFFN_DOWN_TILES_MIN_T": sffn.DOWN_TILES_MIN_T,
+            "SFFN_DOWN_MFMA_MIN_T": sffn.DOWN_MFMA_MIN_T}
+    assert set(defs) == set(want), sorted(defs)
+    for k, v in want.items():
+        assert float(defs[k]) == pytest.approx(v, rel=1e-6), k
+    assert sffn.DOWN_GATHER_DENSITY_DEFAULT <= sffn.DOWN_MFMA_DENSITY_DEFAULT
+
+
 def test_status_strings(sffn):
     from activation_sparse_transformer_amd.sparse_ffn import status_string
     assert status_string(0) == "SFFN_OK"
