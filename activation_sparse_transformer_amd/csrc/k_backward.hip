@@ -49,10 +49,13 @@ __global__ __launch_bounds__(256) void sddmm_kernel(
   constexpr int ROW = 128;           // bytes of one 64-column bf16 row of a step tile
   // step tiles: g rows of 256 tokens (A) and W_down rows of 128 hidden columns (B), both
   // 64 values of d; 16-byte piece p of row r at p ^ ((r >> 1) & 7)
+  // three stages (separate objects: loads into one and reads of the others never alias)
   __shared__ __attribute__((aligned(16))) unsigned char sA0[256 * ROW];
   __shared__ __attribute__((aligned(16))) unsigned char sA1[256 * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sA2[256 * ROW];
   __shared__ __attribute__((aligned(16))) unsigned char sB0[128 * ROW];
   __shared__ __attribute__((aligned(16))) unsigned char sB1[128 * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char sB2[128 * ROW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -106,31 +109,89 @@ __global__ __launch_bounds__(256) void sddmm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // The d-loop is a ring of three LDS stages of 64 columns (4 MFMA k-steps each); a stage's
+  // loads are issued two stages ahead, the next k-step's fragments are read while the current
+  // one's MFMAs run, and at a stage's last k-step the next stage is waited for (its loads and
+  // every wave's reads of this stage: one barrier), the freed buffer refilled and the next
+  // stage's first fragments read before that k-step's MFMAs.  Every stage runs the same
+  // instructions (past the end the last stage is loaded again into a buffer nothing reads)
+  // and the loop runs over whole rings, so the compiler adds no load waits of its own.
+  constexpr int NS = 3;
+  constexpr int LPS = 12;  // direct loads per wave per stage (8 of g, 4 of W_down)
+  constexpr int VM_NEXT = LPS * (NS - 2), VM_FIRST = LPS * (NS - 1);
+  static_assert(VM_FIRST <= 63, "vmcnt immediate");
   const int nsteps = D / 64;
-  issue(0, sA0, sB0);
-  auto step = [&](int s, unsigned char* sA, unsigned char* sB, unsigned char* nA, unsigned char* nB)
-      __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (s + 1 < nsteps) issue(s + 1, nA, nB);
+  bf16x8_b fa[2][4], fb[2][2];
+  auto load_frags = [&](const unsigned char* sA, const unsigned char* sB, int kk, bf16x8_b (&a)[4],
+                        bf16x8_b (&b)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = frag(sA, 128 * wt + 32 * i + l32, kk);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = frag(sB, 64 * wj + 32 * j + l32, kk);
+  };
+  auto mfmas = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j], 0, 0, 0);
+  };
+  auto stage = [&](int st, unsigned char* A, unsigned char* B, const unsigned char* An,
+                   const unsigned char* Bn) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_b fa[4], fb[2];
+      const int c = kk & 1;
+      if (kk < 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(A, B, kk + 1, fa[c ^ 1], fb[c ^ 1]);
+        mfmas(c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag(sA, 128 * wt + 32 * i + l32, kk);
+        for (int i = 0; i < 6; ++i) {  // one fragment read after each of the first MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // the next stage is in once only the stage after it may still be loading
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_NEXT & 15) | ((VM_NEXT >> 4) << 14));
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage's reads are done
+        // a plain barrier: the fence of __syncthreads would also wait for the loads in
+        // flight (they write LDS); the clobber keeps memory accesses in place
+        __asm__ volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issue(st + NS < nsteps ? st + NS : nsteps - 1, A, B);
+        load_frags(An, Bn, 0, fa[c ^ 1], fb[c ^ 1]);
+        mfmas(c);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = frag(sB, 64 * wj + 32 * j + l32, kk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 6; ++i) {  // the refill loads between the MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
-  for (int s = 0; s < nsteps; s += 2) {  // D % 256 == 0: nsteps is even
-    step(s, sA0, sB0, sA1, sB1);
-    step(s + 1, sA1, sB1, sA0, sB0);
+  issue(0, sA0, sB0);
+  issue(1 < nsteps ? 1 : 0, sA1, sB1);
+  issue(2 < nsteps ? 2 : nsteps - 1, sA2, sB2);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (VM_FIRST & 15) | ((VM_FIRST >> 4) << 14));  // stage 0
+  __asm__ volatile("s_barrier" ::: "memory");
+  load_frags(sA0, sB0, 0, fa[0], fb[0]);
+  const int nring = nsteps / NS * NS;
+  for (int st = 0; st < nring; st += NS) {
+    stage(st, sA0, sB0, sA1, sB1);
+    stage(st + 1, sA1, sB1, sA2, sB2);
+    stage(st + 2, sA2, sB2, sA0, sB0);
   }
+  // the last nsteps % 3 stages (the ring position is back at buffer 0)
+  if (nring < nsteps) stage(nring, sA0, sB0, sA1, sB1);
+  if (nring + 1 < nsteps) stage(nring + 1, sA1, sB1, sA2, sB2);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the repeated loads land before LDS is reused
   __syncthreads();  // every wave is done with the step tiles
 
   // ---- C (bf16) -> LDS: token row t (0..255) of 256 B at (t < 128 ? sA0 : sA1) + (t & 127) * 256
