@@ -275,8 +275,78 @@ __global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t
   }
 }
 
+// Few (tile, group) pairs (decode-shaped batches): one workgroup scans the counts (one per
+// thread) and then moves the staged entries itself, one launch instead of two.  The scan
+// result the copy needs is kept in LDS.
+constexpr int ORDER_SMALL_N = 1024;
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+  __shared__ int wsum[16];
+  __shared__ int first_s[ORDER_SMALL_N];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int N = d.nt * d.ng;
+  const int v = tid < N ? ws.ov_grp[tid] : 0;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int woff = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int sw = wsum[w];
+    woff += w < wv ? sw : 0;
+    tot += sw;
+  }
+  const int first = woff + incl - v;
+  if (tid < N) {
+    ws.grp_first[tid] = first;
+    first_s[tid] = first;
+    if (tid % d.ng == 0) b.bk_tile_ptr[tid / d.ng] = first;
+  }
+  if (tid == 0) {
+    ws.grp_first[N] = tot;
+    b.bk_tile_ptr[d.nt] = tot;
+    *b.bk_n = tot;
+    *b.status = tot > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+  }
+  __syncthreads();
+  // the copy: entry e of the staging goes to first(tile, group) + its rank in the group
+  const int n_staged = min(*ws.claim, d.cap);
+  constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;  // 32-bit words per slice
+  for (int e = wv; e < n_staged; e += 16) {
+    const int kk = ws.stage_key[2 * e];
+    const int tw = ws.stage_key[2 * e + 1];
+    const int t = tw & 0xFFFFFF, lr = tw >> 24;
+    const int fin = first_s[kk * d.ng + t / GROUP] + lr;
+    if (fin >= d.cap) continue;  // capacity exceeded: the status word reports it
+    const uint32_t* src = static_cast<const uint32_t*>(ws.stage_vals) + (size_t)e * WORDS;
+    uint32_t* dst = static_cast<uint32_t*>(b.bk_vals) + (size_t)fin * WORDS;
+    for (int q = lane; q < WORDS; q += 64) dst[q] = src[q];
+    if (lane == 0) {
+      b.bk_tile[fin] = kk;
+      b.bk_tok[fin] = t;
+    }
+  }
+}
+
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s) {
+  if (d.nt * d.ng <= ORDER_SMALL_N) {
+#define SFFN_ORDER_SMALL(KK, BB) \
+  hipLaunchKernelGGL((order_small_kernel<KK, BB>), dim3(1), dim3(1024), 0, s, d, b, ws)
+    if (d.bf16) {
+      if (d.K == 64) SFFN_ORDER_SMALL(64, true);
+      else if (d.K == 128) SFFN_ORDER_SMALL(128, true);
+      else SFFN_ORDER_SMALL(256, true);
+    } else {
+      if (d.K == 64) SFFN_ORDER_SMALL(64, false);
+      else if (d.K == 128) SFFN_ORDER_SMALL(128, false);
+      else SFFN_ORDER_SMALL(256, false);
+    }
+#undef SFFN_ORDER_SMALL
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(order_scan_kernel, dim3(1), dim3(1024), 0, s, d, b, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -24,12 +24,15 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
                                                        const uint16_t* __restrict__ Wu,
                                                        const uint16_t* __restrict__ bu,
                                                        float* __restrict__ h,
-                                                       float* __restrict__ zdump) {
+                                                       float* __restrict__ zdump,
+                                                       int32_t* __restrict__ claim) {
   __shared__ __attribute__((aligned(16))) float red[4][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int D = d.D, T = d.T, F = d.F;
   const int n0 = blockIdx.x * US_NB;
+  // the backup staging counter the pack kernel (the next launch) claims from
+  if (blockIdx.x == 0 && threadIdx.x == 0) *claim = 0;
   const int r = lane & 31, hh = lane >> 5;
   const int nks = D / 16;                          // 16-column steps (D % 16 == 0)
   const int ks0 = wave * nks / 4, ks1 = (wave + 1) * nks / 4;
@@ -95,10 +98,11 @@ bool up_small_supported(const Dims& d) {
 }
 
 hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
-                           const uint16_t* bu, float* h, float* zdump, hipStream_t s) {
+                           const uint16_t* bu, float* h, float* zdump, int32_t* claim,
+                           hipStream_t s) {
   if (!up_small_supported(d)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(up_small_kernel, dim3(d.F / US_NB), dim3(256), 0, s, d, x, Wu, bu, h,
-                     zdump);
+                     zdump, claim);
   return hipGetLastError();
 }
 

@@ -127,10 +127,11 @@ hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, co
                               const twell_buffers_t& b, const Workspace& ws, float* zdump,
                               hipStream_t s);
 // Decode-shaped up-projection: h = max(x W_up^T + b, 0) as fp32 [T, F] (T <= UP_SMALL_T),
-// and z = x W_up^T + b into zdump if it is not null.
+// and z = x W_up^T + b into zdump if it is not null; also sets the staging claim to 0.
 bool up_small_supported(const Dims& d);
 hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
-                           const uint16_t* bu, float* h, float* zdump, hipStream_t s);
+                           const uint16_t* bu, float* h, float* zdump, int32_t* claim,
+                           hipStream_t s);
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);
