@@ -175,8 +175,120 @@ static hipError_t launch_pack_dispatch(const Dims& d, const float* h, const floa
   return hipErrorInvalidValue;
 }
 
+// Few (tile, group) pairs (decode-shaped batches): pack_kernel would leave most CUs idle and
+// walk 32 tokens one after another.  Here a workgroup of 8 waves owns one (tile, group),
+// each wave 4 of its tokens; the 32 counts meet in LDS, so every wave knows which rows of
+// the group overflow and its rows' ranks among them, and one staging claim serves the
+// group.  The output is the one pack_kernel writes.
+constexpr int PS_WAVES = 8;
+constexpr int PS_TPW = GROUP / PS_WAVES;  // tokens per wave
+constexpr int PS_MAX_PAIRS = 2048;         // (tile, group) pairs below which it is used
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(512) void pack_small_kernel(Dims d, const float* __restrict__ h,
+                                                         twell_buffers_t b, Workspace ws) {
+  constexpr int C = K / 64;
+  __shared__ int cnt_s[GROUP];
+  __shared__ int base_s;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int k = blockIdx.x / d.ng;
+  const int g = blockIdx.x - k * d.ng;
+  const int i0 = wv * PS_TPW;  // first row of the group this wave owns
+  const int t0 = g * GROUP + i0;
+  const int T = d.T, W = d.W;
+
+  float v[PS_TPW][C];
+#pragma unroll
+  for (int i = 0; i < PS_TPW; ++i) {
+    const int t = t0 + i;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      v[i][c] = t < T ? h[(int64_t)t * d.F + (int64_t)k * K + c * 64 + lane] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < PS_TPW; ++i) {
+    int cnt = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) cnt += __popcll(ballot64(v[i][c] != 0.0f));
+    if (lane == 0) cnt_s[i0 + i] = cnt;  // rows past T hold zeros: count 0
+  }
+  __syncthreads();
+  const int cnt_lane = lane < GROUP ? cnt_s[lane] : 0;
+  const uint64_t om = ballot64(lane < GROUP && cnt_lane > W);
+  const int n_ov = __popcll(om);
+  if (threadIdx.x == 0) {
+    base_s = n_ov > 0 ? atomicAdd(ws.claim, n_ov) : 0;
+    ws.ov_grp[(int64_t)k * d.ng + g] = n_ov;
+  }
+  __syncthreads();
+  const int base = base_s;
+
+#pragma unroll
+  for (int i = 0; i < PS_TPW; ++i) {
+    const int t = t0 + i;
+    if (t >= T) break;
+    const int cnt = __builtin_amdgcn_readlane(cnt_lane, i0 + i);
+    const bool over = cnt > W;
+    const int lr = __popcll(om & ((1ull << (i0 + i)) - 1));  // rank among the group's overflows
+    const int slot = base + lr;
+    const bool stage = over && slot < d.cap;
+    const size_t row = ((size_t)k * T + t) * (size_t)W;
+    int prefix = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bool nz = v[i][c] != 0.0f;
+      const uint64_t m = ballot64(nz);
+      const int r = prefix + mbcnt64(m);
+      prefix += __popcll(m);
+      const int col = c * 64 + lane;
+      if (nz && r < W) {
+        store_val<BF16>(b.vals, row + r, v[i][c]);
+        b.cols[row + r] = (uint8_t)col;
+      }
+      if (stage) store_val<BF16>(ws.stage_vals, (size_t)slot * K + col, (nz && r >= W) ? v[i][c] : 0.0f);
+    }
+    const int used = cnt < W ? cnt : W;
+    for (int s = used + lane; s < W; s += 64) {
+      store_val<BF16>(b.vals, row + s, 0.0f);
+      b.cols[row + s] = 0;
+    }
+    if (lane == 0) {
+      b.counts[(size_t)k * T + t] = (uint16_t)cnt;
+      if (stage) {
+        ws.stage_key[2 * slot] = k;
+        ws.stage_key[2 * slot + 1] = t | (lr << 24);
+      }
+    }
+  }
+}
+
+template <int K, bool BF16>
+static hipError_t launch_pack_small_t(const Dims& d, const float* h, const twell_buffers_t& b,
+                                      const Workspace& ws, hipStream_t s) {
+  hipLaunchKernelGGL((pack_small_kernel<K, BF16>), dim3(d.nt * d.ng), dim3(64 * PS_WAVES), 0, s,
+                     d, h, b, ws);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const Dims& d, const float* h, const twell_buffers_t& b,
                        const Workspace& ws, hipStream_t s) {
+  if (d.nt * d.ng < PS_MAX_PAIRS) {
+    if (d.bf16) {
+      switch (d.K) {
+        case 64: return launch_pack_small_t<64, true>(d, h, b, ws, s);
+        case 128: return launch_pack_small_t<128, true>(d, h, b, ws, s);
+        case 256: return launch_pack_small_t<256, true>(d, h, b, ws, s);
+      }
+    } else {
+      switch (d.K) {
+        case 64: return launch_pack_small_t<64, false>(d, h, b, ws, s);
+        case 128: return launch_pack_small_t<128, false>(d, h, b, ws, s);
+        case 256: return launch_pack_small_t<256, false>(d, h, b, ws, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   return launch_pack_dispatch<MODE_H>(d, h, nullptr, nullptr, nullptr, b, ws, nullptr, s);
 }
 

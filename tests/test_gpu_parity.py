@@ -60,6 +60,9 @@ PACK_CASES = [
     (100, 512, 128, 128, "bf16", 0.9),
     (77, 384, 64, 63, "f32", 0.95),
     (333, 1152, 64, 5, "bf16", 0.1),
+    # at least 2048 (tile, 32-token group) pairs: the one-wave-per-group pack kernel
+    (4100, 4096, 64, 16, "bf16", 0.05),
+    (2049, 4096, 128, 8, "f32", 0.1),
 ]
 
 
