@@ -423,21 +423,29 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
     *b.status = tot > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
   }
   __syncthreads();
-  // the copy: entry e of the staging goes to first(tile, group) + its rank in the group
+  // the copy: entry e of the staging goes to first(tile, group) + its rank in the group.
+  // A slice is LPE 16-byte pieces (slices start 16-byte aligned), so a wave moves EPW
+  // entries at once and the workgroup 16 EPW.
   const int n_staged = min(*ws.claim, d.cap);
-  constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;  // 32-bit words per slice
-  for (int e = wv; e < n_staged; e += 16) {
-    const int kk = ws.stage_key[2 * e];
-    const int tw = ws.stage_key[2 * e + 1];
-    const int t = tw & 0xFFFFFF, lr = tw >> 24;
-    const int fin = first_s[kk * d.ng + t / GROUP] + lr;
-    if (fin >= d.cap) continue;  // capacity exceeded: the status word reports it
-    const uint32_t* src = static_cast<const uint32_t*>(ws.stage_vals) + (size_t)e * WORDS;
-    uint32_t* dst = static_cast<uint32_t*>(b.bk_vals) + (size_t)fin * WORDS;
-    for (int q = lane; q < WORDS; q += 64) dst[q] = src[q];
-    if (lane == 0) {
-      b.bk_tile[fin] = kk;
-      b.bk_tok[fin] = t;
+  constexpr int LPE = K * (BF16 ? 2 : 4) / 16;  // lanes per entry: 8 .. 64
+  constexpr int EPW = 64 / LPE;
+  const int sub = lane / LPE, q = lane - sub * LPE;
+  for (int e0 = wv * EPW; e0 < n_staged; e0 += 16 * EPW) {
+    const int e = e0 + sub;
+    if (e < n_staged) {
+      const int kk = ws.stage_key[2 * e];
+      const int tw = ws.stage_key[2 * e + 1];
+      const int t = tw & 0xFFFFFF, lr = tw >> 24;
+      const int fin = first_s[kk * d.ng + t / GROUP] + lr;
+      if (fin < d.cap) {  // capacity exceeded: the status word reports it
+        const uint4* src = static_cast<const uint4*>(ws.stage_vals) + (size_t)e * LPE;
+        uint4* dst = static_cast<uint4*>(b.bk_vals) + (size_t)fin * LPE;
+        dst[q] = src[q];
+        if (q == 0) {
+          b.bk_tile[fin] = kk;
+          b.bk_tok[fin] = t;
+        }
+      }
     }
   }
 }
