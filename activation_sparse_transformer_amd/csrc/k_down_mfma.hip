@@ -90,19 +90,20 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   uint8_t* const pos = sPos[wave];
 
   // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (2*(r&3)), so the
-  // four rows touched by one transposed read land in distinct banks.
+  // four rows touched by one transposed read land in distinct banks.  Load q of a wave is
+  // 1 KB (two rows: 2 ins + lane/32, ins = 4q + wave), so r & 3 = 2 (wave & 1) + lane/32 for
+  // every load and the lane's part of the offset is the same each time.
+  const int b_hl = lane >> 5;
+  int b_col = d0 + ((lane & 31) ^ (2 * (2 * (wave & 1) + b_hl))) * 8;
+  b_col = b_col < d.D ? b_col : d0;  // columns past D (half-wide chunk) are never read
+  const uint32_t b_off = (uint32_t)(b_hl * d.D + b_col);
   auto issue_B = [&](int ci, unsigned char* sB) __attribute__((always_inline)) {
-    const size_t row0 = (size_t)ci * KC;  // step ci = rows [ci*KC, +KC) of W_down
+    const int row0 = ci * KC;  // step ci = rows [ci*KC, +KC) of W_down
 #pragma unroll
     for (int q = 0; q < BBUF / 1024 / 4; ++q) {
-      const int ins = q * 4 + wave;  // 1 KB (two rows) per 64-lane load
-      const int slot = ins * 64 + lane;
-      const int r = slot >> 5, pc = slot & 31;
-      const int lc = pc ^ (2 * (r & 3));
-      int col = d0 + lc * 8;
-      col = col < d.D ? col : d0;  // columns past D (half-wide chunk) are never read
-      __builtin_amdgcn_global_load_lds(Wd + (row0 + r) * (size_t)d.D + col,
-                                       (lds_vptr)(sB + ins * 1024), 16, 0, 0);
+      const int ins = q * 4 + wave;
+      const uint16_t* src = Wd + (size_t)(row0 + 2 * ins) * d.D;
+      __builtin_amdgcn_global_load_lds(src + b_off, (lds_vptr)(sB + ins * 1024), 16, 0, 0);
     }
   };
 
@@ -139,7 +140,13 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   };
 
   // ---- write step c (of the tile) of the units into A buffer `buf`; the units are split
-  // into four parts (unit j in part 4j/U) so the writes spread over the four MFMA k-steps
+  // into four parts (unit j in part 4j/U) so the writes spread over the four MFMA k-steps.
+  // 128-column tiles with at most 32 slots (PRE): chunk c of a tile always goes to buffer c.
+  // The chunk-0 pass also works out every slot's chunk-1 address (offset from buffer 1: its
+  // place there, or the lane's trash word just past it) and keeps it, two 16-bit offsets
+  // per register, so the chunk-1 pass only unpacks it.
+  constexpr bool PRE = NCH == 2 && W <= 32;
+  uint32_t pa[PRE ? 4 * U : 1];
   auto build_part = [&](int part, int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -149,14 +156,31 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
       const uint32_t cw[2] = {uc[j].x, uc[j].y};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
         const uint32_t word = vv[e >> 1];
-        const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
-        bool in = true;
-        if constexpr (NCH > 1) in = (col >> 6) == (uint32_t)c;
-        const uint32_t addr = (nz && in) ? a_addr(buf, r, col & (KC - 1)) : trash;
         const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
-        *reinterpret_cast<uint16_t*>(sA + addr) = h;
+        if constexpr (PRE) {
+          uint32_t& pk = pa[4 * j + (e >> 1)];
+          if (c == 1) {  // buffer 1
+            const uint32_t s1 = (e & 1) ? (pk >> 16) : (pk & 0xFFFFu);
+            *reinterpret_cast<uint16_t*>(sA + ABUF + s1) = h;
+            continue;
+          }
+          const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+          const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
+          const uint32_t rel = a_addr(0, r, col & (KC - 1));
+          const bool hi = col >= (uint32_t)KC;
+          const uint32_t a0 = (nz && !hi) ? rel : trash;
+          const uint32_t s1 = (nz && hi) ? rel : (uint32_t)(ABUF + 4 * lane);
+          pk = (e & 1) ? (pk | (s1 << 16)) : s1;
+          *reinterpret_cast<uint16_t*>(sA + a0) = h;
+        } else {
+          const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+          const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
+          bool in = true;
+          if constexpr (NCH > 1) in = (col >> 6) == (uint32_t)c;
+          const uint32_t addr = (nz && in) ? a_addr(buf, r, col & (KC - 1)) : trash;
+          *reinterpret_cast<uint16_t*>(sA + addr) = h;
+        }
       }
     }
   };
@@ -283,6 +307,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     __syncthreads();                     // A(ci), B(ci) complete; step ci-1's buffers free
     const int cn = ci + 1 < nch ? ci + 1 : nch - 1;
     const int c_next = cn % NCH;
+    // PRE: chunk cb ^ 1 into buffer cb ^ 1; in the last step (cb = 1) that is a chunk-0
+    // pass into buffer 0, which nothing reads any more
+    const int c_build = PRE ? (cb ^ 1) : c_next;
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
     const int e0 = e0_next;
     e0_next = first_entry((ci + 2) / NCH);  // for the next step, ready by then
@@ -304,7 +331,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
         issue_B(cn, sBn);
         clear_a(cb ^ 1);
       }
-      build_part(kk, c_next, cb ^ 1);
+      build_part(kk, c_build, cb ^ 1);
       if (kk == NKK - 1 && load_next) {
         const int kt = (cn + 1) / NCH;
         load_units(kt < d.nt ? kt : d.nt - 1);
