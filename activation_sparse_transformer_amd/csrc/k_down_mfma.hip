@@ -331,10 +331,23 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
         issue_B(cn, sBn);
         clear_a(cb ^ 1);
       }
-      build_part(kk, c_build, cb ^ 1);
-      if (kk == NKK - 1 && load_next) {
-        const int kt = (cn + 1) / NCH;
-        load_units(kt < d.nt ? kt : d.nt - 1);
+      if (PRE && cb == 0) {
+        // chunk-1 pass (only unpacks): all of it first, so the units of the next tile,
+        // which overwrite the registers it reads, go out a whole step before their use
+        if (kk == 0) {
+#pragma unroll
+          for (int part = 0; part < 4; ++part) build_part(part, c_build, cb ^ 1);
+          if (load_next) {
+            const int kt = (cn + 1) / NCH;
+            load_units(kt < d.nt ? kt : d.nt - 1);
+          }
+        }
+      } else {
+        build_part(kk, c_build, cb ^ 1);
+        if (kk == NKK - 1 && load_next) {
+          const int kt = (cn + 1) / NCH;
+          load_units(kt < d.nt ? kt : d.nt - 1);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
