@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int MROW = 512;                 // M step tile: TS tokens x 256 columns, bf16
   constexpr int MBUF = TS * MROW;
   constexpr int NKK = TS / 16;              // MFMA k-steps per step
-  // H buffers (written by the waves) then 256 B of dummy words for padding writes; M
+  // H buffers (written by the waves) then 256 B holding the dummy word of padding writes; M
   // buffers (filled by direct loads).  Piece p of row r sits at p ^ (2*(r&3)) in both, so
   // the four rows of a transposed read hit distinct banks.
   __shared__ __attribute__((aligned(16))) unsigned char sH[2 * HBUF + 256];
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int d0 = dchunk * 256;
   const int j0 = jb * BW_JB;
   const int k = j0 / K, hf = (j0 % K) / BW_JB;
-  const uint32_t trash = 2 * HBUF + 4 * lane;
+  const uint32_t trash = 2 * HBUF;  // one dummy word for every discarded write
   const size_t row_base = (size_t)k * T;
 
   auto issue_M = [&](int ts, unsigned char* sM) __attribute__((always_inline)) {

@@ -59,9 +59,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   constexpr int ABUF = DM_BM * AROW;   // 32 KB: one A buffer
   constexpr int BROW = DM_BN * 2;      // 512 B: one B row
   constexpr int BBUF = KC * BROW;      // 32 KB: one B buffer
-  // A buffers, then 256 B of dummy words (one per lane) that padding writes go to; all A
-  // writes address this one array, so the compiler sees they never touch the B buffers
-  // filled by direct loads (and need not wait for those)
+  // A buffers, then 256 B holding the dummy word that padding writes go to; all A writes
+  // address this one array, so the compiler sees they never touch the B buffers filled by
+  // direct loads (and need not wait for those)
   __shared__ __attribute__((aligned(16))) unsigned char sA[2 * ABUF + 256];
   __shared__ __attribute__((aligned(16))) unsigned char sB0[BBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sB1[BBUF];
@@ -86,7 +86,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   const bool active = d0 + 128 * wc < d.D;  // D % 256 == 128: the last chunk is half wide
   const int t0 = tb * DM_BM;
   const int tw = t0 + wave * 64;  // first token of the rows this wave writes into A
-  const uint32_t trash = 2 * ABUF + 4 * lane;  // byte offset in sA
+  // byte offset in sA of the dummy word every discarded write goes to (one word for all
+  // lanes: writes to one address do not add bank conflicts to the real writes beside them)
+  const uint32_t trash = 2 * ABUF;
   uint8_t* const pos = sPos[wave];
 
   // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (2*(r&3)), so the
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   // into four parts (unit j in part 4j/U) so the writes spread over the four MFMA k-steps.
   // 128-column tiles with at most 32 slots (PRE): chunk c of a tile always goes to buffer c.
   // The chunk-0 pass also works out every slot's chunk-1 address (offset from buffer 1: its
-  // place there, or the lane's trash word just past it) and keeps it, two 16-bit offsets
+  // place there, or the trash word just past it) and keeps it, two 16-bit offsets
   // per register, so the chunk-1 pass only unpacks it.
   constexpr bool PRE = NCH == 2 && W <= 32;
   uint32_t pa[PRE ? 4 * U : 1];
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
           const uint32_t rel = a_addr(0, r, col & (KC - 1));
           const bool hi = col >= (uint32_t)KC;
           const uint32_t a0 = (nz && !hi) ? rel : trash;
-          const uint32_t s1 = (nz && hi) ? rel : (uint32_t)(ABUF + 4 * lane);
+          const uint32_t s1 = (nz && hi) ? rel : (uint32_t)ABUF;
           pk = (e & 1) ? (pk | (s1 << 16)) : s1;
           *reinterpret_cast<uint16_t*>(sA + a0) = h;
         } else {
