@@ -13,6 +13,8 @@
 // columns of every token of the group in registers; a token's tile-row is compacted with
 // ballot + mbcnt: the rank of a nonzero is the number of nonzeros at lower columns, so
 // slots come out in ascending column order with no shared-memory traffic.
+#include <algorithm>
+
 #include "sffn_common.hpp"
 
 namespace sffn {
@@ -387,10 +389,11 @@ __global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t
   }
 }
 
-// Few (tile, group) pairs (decode-shaped batches): one workgroup scans the counts (one per
-// thread) and then moves the staged entries itself, one launch instead of two.  The scan
-// result the copy needs is kept in LDS.
+// Few (tile, group) pairs (decode-shaped batches): one launch instead of two.  Every
+// workgroup scans the counts (one per thread, at most 1024) into LDS, the first one also
+// writes the scan's outputs, and the workgroups then share the moves of the staged entries.
 constexpr int ORDER_SMALL_N = 1024;
+constexpr int ORDER_SMALL_MAX_WG = 128;
 
 template <int K, bool BF16>
 __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers_t b, Workspace ws) {
@@ -411,26 +414,28 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
     tot += sw;
   }
   const int first = woff + incl - v;
-  if (tid < N) {
-    ws.grp_first[tid] = first;
-    first_s[tid] = first;
-    if (tid % d.ng == 0) b.bk_tile_ptr[tid / d.ng] = first;
-  }
-  if (tid == 0) {
-    ws.grp_first[N] = tot;
-    b.bk_tile_ptr[d.nt] = tot;
-    *b.bk_n = tot;
-    *b.status = tot > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+  if (tid < N) first_s[tid] = first;
+  if (blockIdx.x == 0) {
+    if (tid < N) {
+      ws.grp_first[tid] = first;
+      if (tid % d.ng == 0) b.bk_tile_ptr[tid / d.ng] = first;
+    }
+    if (tid == 0) {
+      ws.grp_first[N] = tot;
+      b.bk_tile_ptr[d.nt] = tot;
+      *b.bk_n = tot;
+      *b.status = tot > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+    }
   }
   __syncthreads();
   // the copy: entry e of the staging goes to first(tile, group) + its rank in the group.
   // A slice is LPE 16-byte pieces (slices start 16-byte aligned), so a wave moves EPW
-  // entries at once and the workgroup 16 EPW.
+  // entries at once and the grid 16 EPW per workgroup.
   const int n_staged = min(*ws.claim, d.cap);
   constexpr int LPE = K * (BF16 ? 2 : 4) / 16;  // lanes per entry: 8 .. 64
   constexpr int EPW = 64 / LPE;
   const int sub = lane / LPE, q = lane - sub * LPE;
-  for (int e0 = wv * EPW; e0 < n_staged; e0 += 16 * EPW) {
+  for (int e0 = (blockIdx.x * 16 + wv) * EPW; e0 < n_staged; e0 += gridDim.x * 16 * EPW) {
     const int e = e0 + sub;
     if (e < n_staged) {
       const int kk = ws.stage_key[2 * e];
@@ -453,8 +458,11 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s) {
   if (d.nt * d.ng <= ORDER_SMALL_N) {
+    // workgroups for the copy: 64 staged entries each, of at most min(cap, n_t T)
+    const long long most = std::min<long long>((long long)d.cap, (long long)d.nt * d.T);
+    const int nwg = (int)std::min<long long>(ORDER_SMALL_MAX_WG, std::max<long long>(1, (most + 63) / 64));
 #define SFFN_ORDER_SMALL(KK, BB) \
-  hipLaunchKernelGGL((order_small_kernel<KK, BB>), dim3(1), dim3(1024), 0, s, d, b, ws)
+  hipLaunchKernelGGL((order_small_kernel<KK, BB>), dim3(nwg), dim3(1024), 0, s, d, b, ws)
     if (d.bf16) {
       if (d.K == 64) SFFN_ORDER_SMALL(64, true);
       else if (d.K == 128) SFFN_ORDER_SMALL(128, true);

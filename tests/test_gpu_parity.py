@@ -63,6 +63,9 @@ PACK_CASES = [
     # at least 2048 (tile, 32-token group) pairs: the one-wave-per-group pack kernel
     (4100, 4096, 64, 16, "bf16", 0.05),
     (2049, 4096, 128, 8, "f32", 0.1),
+    # exactly 1024 pairs (the last size the one-launch backup order takes), and 2064 pairs
+    (4096, 1024, 128, 16, "bf16", 0.1),
+    (4097, 2048, 128, 16, "f32", 0.1),
 ]
 
 
@@ -139,6 +142,8 @@ DOWN_CASES = [
     (520, 384, 1024, 64, 64, "bf16", 0.3),
     (257, 128, 2048, 256, 48, "bf16", 0.1),
     (33, 256, 512, 64, 16, "bf16", 0.1),
+    # 128-column tiles with 16 slots: two 8-slot units per row in the decode-once rebuild
+    (200, 256, 1024, 128, 16, "bf16", 0.1),
 ]
 
 
