@@ -299,8 +299,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int MBUF = TS * MROW;
   constexpr int NKK = TS / 16;              // MFMA k-steps per step
   // H buffers (written by the waves) then 256 B holding the dummy word of padding writes; M
-  // buffers (filled by direct loads).  Piece p of row r sits at p ^ (2*(r&3)) in both, so
-  // the four rows of a transposed read hit distinct banks.
+  // buffers (filled by direct loads).  Piece p of row r sits at p ^ (4*(r&3)) in both, so
+  // the four rows (4 pieces each) that one half-wave of a transposed read touches cover all
+  // 64 banks.
   __shared__ __attribute__((aligned(16))) unsigned char sH[2 * HBUF + 256];
   __shared__ __attribute__((aligned(16))) unsigned char sM0[MBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sM1[MBUF];
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int ins = q * 4 + wave;
       const int slot = ins * 64 + lane;
       const int r = slot >> 5, pc = slot & 31;
-      const int lc = pc ^ (2 * (r & 3));
+      const int lc = pc ^ (4 * (r & 3));
       int t = ts * TS + r;
       t = t < T ? t : T - 1;  // rows past T meet zero rows of H
       __builtin_amdgcn_global_load_lds(M + (size_t)t * D + d0 + lc * 8,
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     cnt = counts[row_base + (tl < T ? tl : T - 1)];
   };
   auto h_off = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
-    return buf * HBUF + r * HROW + ((((cc >> 3) ^ (2 * (r & 3))) << 4) | ((cc & 7) << 1));
+    return buf * HBUF + r * HROW + ((((cc >> 3) ^ (4 * (r & 3))) << 4) | ((cc & 7) << 1));
   };
   auto build = [&](int ts, int buf) __attribute__((always_inline)) {
     // clear this wave's RPW rows (2 KB)
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = kk * 16 + 8 * (g16 >> 1) + 4 * q + (li >> 2);
-      const int off = r * rowb + ((((col >> 3) ^ (2 * (r & 3))) << 4) | ((col & 7) << 1));
+      const int off = r * rowb + ((((col >> 3) ^ (4 * (r & 3))) << 4) | ((col & 7) << 1));
       h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr_b)(base + off));
     }
     const short8_b v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};

@@ -91,12 +91,13 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   const uint32_t trash = 2 * ABUF;
   uint8_t* const pos = sPos[wave];
 
-  // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (2*(r&3)), so the
-  // four rows touched by one transposed read land in distinct banks.  Load q of a wave is
+  // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (4*(r&3)), so the four
+  // rows (4 pieces each) that one half-wave of a transposed read touches land on 16
+  // different 4-bank groups, i.e. all 64 banks.  Load q of a wave is
   // 1 KB (two rows: 2 ins + lane/32, ins = 4q + wave), so r & 3 = 2 (wave & 1) + lane/32 for
   // every load and the lane's part of the offset is the same each time.
   const int b_hl = lane >> 5;
-  int b_col = d0 + ((lane & 31) ^ (2 * (2 * (wave & 1) + b_hl))) * 8;
+  int b_col = d0 + ((lane & 31) ^ (4 * (2 * (wave & 1) + b_hl))) * 8;
   b_col = b_col < d.D ? b_col : d0;  // columns past D (half-wide chunk) are never read
   const uint32_t b_off = (uint32_t)(b_hl * d.D + b_col);
   auto issue_B = [&](int ci, unsigned char* sB) __attribute__((always_inline)) {
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = kk * 16 + 8 * (g16 >> 1) + 4 * q + (li >> 2);
-      const int off = r * BROW + ((((col >> 3) ^ (2 * (r & 3))) << 4) | ((col & 7) << 1));
+      const int off = r * BROW + ((((col >> 3) ^ (4 * (r & 3))) << 4) | ((col & 7) << 1));
       h[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(sB + off));
     }
     const short8_m v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
