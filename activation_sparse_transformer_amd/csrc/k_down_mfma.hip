@@ -10,14 +10,16 @@
 // solve": tiles aligned with tiled matrix-multiply execution, sparse main part plus a few
 // dense backups).
 //
-// Workgroup = 256 tokens x 256 output columns, 4 waves in a 2 x 2 grid; each wave computes
-// 128 tokens x 128 columns with v_mfma_f32_32x32x16_bf16 (A = hidden rows, B = W_down;
-// 256 fp32 accumulators per lane).  The contraction runs in steps of 64 hidden columns:
+// Workgroup = 256 tokens x 256 output columns, 8 waves in a 2 x 4 grid (two per SIMD, so
+// one wave's A writes run while the other's MFMAs keep the matrix core busy); each wave
+// computes 128 tokens x 64 columns with v_mfma_f32_32x32x16_bf16 (A = hidden rows,
+// B = W_down; 128 fp32 accumulators per lane).  The contraction runs in steps of 64 hidden
+// columns:
 //   * B step = W_down[64 rows, 256 columns], copied global -> LDS with direct loads one
 //     step ahead (double buffer); B fragments come straight out of its row-major layout
 //     through ds_read_b64_tr_b16.
 //   * A step = 256 x 64 hidden values, double-buffered: while the MFMAs of step c read one
-//     buffer, each wave clears its 64 token rows of the other and writes step c+1's
+//     buffer, each wave clears its 32 token rows of the other and writes step c+1's
 //     nonzeros there, from TwELL data prefetched into registers as 8-slot units (coalesced
 //     16 B value + 8 B column loads).  Padding slots hold value 0 and go to a dummy word,
 //     so these writes need no branch, and the step body between barriers is one basic
@@ -44,9 +46,10 @@ typedef __attribute__((address_space(3))) short4_m* lds_s4ptr;
 constexpr int DM_BM = 256;  // tokens per workgroup
 constexpr int DM_BN = 256;  // output columns per workgroup
 constexpr int DM_KC = 64;   // hidden columns per contraction step
+constexpr int DM_NW = 8;    // waves per workgroup: 2 along the tokens x DM_NW / 2 along the columns
 
 template <int K, int W>
-__global__ __launch_bounds__(256) void down_mfma_kernel(
+__global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_NW / 4, DM_NW / 4))) void down_mfma_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
@@ -59,17 +62,24 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   constexpr int ABUF = DM_BM * AROW;   // 32 KB: one A buffer
   constexpr int BROW = DM_BN * 2;      // 512 B: one B row
   constexpr int BBUF = KC * BROW;      // 32 KB: one B buffer
+  constexpr int NW = DM_NW;
+  constexpr int RW = DM_BM / NW;       // A rows each wave writes
+  constexpr int NWC = NW / 2;          // waves along the columns
+  constexpr int WN = DM_BN / NWC;      // output columns per wave
+  constexpr int NJ = WN / 32;          // 32-column MFMA blocks per wave
+  constexpr int UL = RW * U / 64;      // 8-slot units per lane
+  static_assert(RW * U % 64 == 0 && RW <= 64, "units must fill whole waves");
   // A buffers, then 256 B holding the dummy word that padding writes go to; all A writes
   // address this one array, so the compiler sees they never touch the B buffers filled by
   // direct loads (and need not wait for those)
   __shared__ __attribute__((aligned(16))) unsigned char sA[2 * ABUF + 256];
   __shared__ __attribute__((aligned(16))) unsigned char sB0[BBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sB1[BBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t sPos[4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t sPos[NW][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wave >> 1, wc = wave & 1;  // MFMA tile: tokens 128wt.., columns 128wc..
+  const int wt = wave / NWC, wc = wave % NWC;  // MFMA tile: tokens 128wt.., columns WN wc..
   const int T = d.T;
   const int nd = (d.D + DM_BN - 1) / DM_BN;
   const int ntb = (T + DM_BM - 1) / DM_BM;
@@ -83,9 +93,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
   const int dchunk = P - tb * nd;
   const int d0 = dchunk * DM_BN;
-  const bool active = d0 + 128 * wc < d.D;  // D % 256 == 128: the last chunk is half wide
+  const bool active = d0 + WN * wc < d.D;  // D % 256 == 128: the last chunk is half wide
   const int t0 = tb * DM_BM;
-  const int tw = t0 + wave * 64;  // first token of the rows this wave writes into A
+  const int tw = t0 + wave * RW;  // first token of the rows this wave writes into A
   // byte offset in sA of the dummy word every discarded write goes to (one word for all
   // lanes: writes to one address do not add bank conflicts to the real writes beside them)
   const uint32_t trash = 2 * ABUF;
@@ -94,8 +104,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   // ---- B step -> LDS.  Row r (512 B) keeps 16-byte piece c at c ^ (4*(r&3)), so the four
   // rows (4 pieces each) that one half-wave of a transposed read touches land on 16
   // different 4-bank groups, i.e. all 64 banks.  Load q of a wave is
-  // 1 KB (two rows: 2 ins + lane/32, ins = 4q + wave), so r & 3 = 2 (wave & 1) + lane/32 for
-  // every load and the lane's part of the offset is the same each time.
+  // 1 KB (two rows: 2 ins + lane/32, ins = NW q + wave), so r & 3 = 2 (wave & 1) + lane/32
+  // for every load and the lane's part of the offset is the same each time.
   const int b_hl = lane >> 5;
   int b_col = d0 + ((lane & 31) ^ (4 * (2 * (wave & 1) + b_hl))) * 8;
   b_col = b_col < d.D ? b_col : d0;  // columns past D (half-wide chunk) are never read
@@ -103,24 +113,24 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   auto issue_B = [&](int ci, unsigned char* sB) __attribute__((always_inline)) {
     const int row0 = ci * KC;  // step ci = rows [ci*KC, +KC) of W_down
 #pragma unroll
-    for (int q = 0; q < BBUF / 1024 / 4; ++q) {
-      const int ins = q * 4 + wave;
+    for (int q = 0; q < BBUF / 1024 / NW; ++q) {
+      const int ins = q * NW + wave;
       const uint16_t* src = Wd + (size_t)(row0 + 2 * ins) * d.D;
       __builtin_amdgcn_global_load_lds(src + b_off, (lds_vptr)(sB + ins * 1024), 16, 0, 0);
     }
   };
 
   // ---- TwELL units of tile k for this wave's rows: unit u = lane + 64 j holds slots
-  // 8*(u % U) .. +7 of token tw + u / U.  cnt = count of token tw + lane.
-  uint4 uv[U];
-  uint2 uc[U];
+  // 8*(u % U) .. +7 of token tw + u / U.  cnt = count of token tw + lane (lanes < RW).
+  uint4 uv[UL];
+  uint2 uc[UL];
   uint32_t cnt = 0;
   auto load_units = [&](int k) __attribute__((always_inline)) {
     // addresses are clamped into the buffers and rows past T masked to zero with an AND
     // (a select on a loaded value would be turned into a branch around the load)
     const size_t row_base = (size_t)k * T;
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
+    for (int j = 0; j < UL; ++j) {
       const int u = lane + 64 * j;
       const int tok = tw + u / U;
       const int tk = tok < T ? tok : T - 1;
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
       uc[j] = *reinterpret_cast<const uint2*>(cols + e0);
     }
     const int t = tw + lane;
-    const uint32_t m = t < T ? 0xFFFFu : 0u;
+    const uint32_t m = (t < T && lane < RW) ? 0xFFFFu : 0u;
     cnt = (uint32_t)counts[row_base + (t < T ? t : T - 1)] & m;
   };
 
@@ -139,51 +149,28 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   // 16 consecutive rows of one fragment read (alternating bank halves) hit distinct banks.
   // Byte offset in sA of (this wave's row r, hidden column cc) in A buffer `buf`:
   auto a_addr = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
-    return buf * ABUF + (wave * 64 + r) * AROW + ((cc ^ (((r >> 1) & 7) << 3)) << 1);
+    return buf * ABUF + (wave * RW + r) * AROW + ((cc ^ (((r >> 1) & 7) << 3)) << 1);
   };
 
   // ---- write step c (of the tile) of the units into A buffer `buf`; the units are split
-  // into four parts (unit j in part 4j/U) so the writes spread over the four MFMA k-steps.
-  // 128-column tiles with at most 32 slots (PRE): chunk c of a tile always goes to buffer c.
-  // The chunk-0 pass also works out every slot's chunk-1 address (offset from buffer 1: its
-  // place there, or the trash word just past it) and keeps it, two 16-bit offsets
-  // per register, so the chunk-1 pass only unpacks it.
-  constexpr bool PRE = NCH == 2 && W <= 32;
-  uint32_t pa[PRE ? 4 * U : 1];
+  // into four parts (unit j in part 4j/UL) so the writes spread over the four MFMA k-steps
   auto build_part = [&](int part, int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      if ((4 * j) / U != part) continue;
+    for (int j = 0; j < UL; ++j) {
+      if ((4 * j) / UL != part) continue;
       const uint32_t r = (uint32_t)(lane + 64 * j) / U;
       const uint32_t vv[4] = {uv[j].x, uv[j].y, uv[j].z, uv[j].w};
       const uint32_t cw[2] = {uc[j].x, uc[j].y};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
         const uint32_t word = vv[e >> 1];
+        const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
+        bool in = true;
+        if constexpr (NCH > 1) in = (col >> 6) == (uint32_t)c;
+        const uint32_t addr = (nz && in) ? a_addr(buf, r, col & (KC - 1)) : trash;
         const uint16_t h = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
-        if constexpr (PRE) {
-          uint32_t& pk = pa[4 * j + (e >> 1)];
-          if (c == 1) {  // buffer 1
-            const uint32_t s1 = (e & 1) ? (pk >> 16) : (pk & 0xFFFFu);
-            *reinterpret_cast<uint16_t*>(sA + ABUF + s1) = h;
-            continue;
-          }
-          const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-          const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
-          const uint32_t rel = a_addr(0, r, col & (KC - 1));
-          const bool hi = col >= (uint32_t)KC;
-          const uint32_t a0 = (nz && !hi) ? rel : trash;
-          const uint32_t s1 = (nz && hi) ? rel : (uint32_t)ABUF;
-          pk = (e & 1) ? (pk | (s1 << 16)) : s1;
-          *reinterpret_cast<uint16_t*>(sA + a0) = h;
-        } else {
-          const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-          const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
-          bool in = true;
-          if constexpr (NCH > 1) in = (col >> 6) == (uint32_t)c;
-          const uint32_t addr = (nz && in) ? a_addr(buf, r, col & (KC - 1)) : trash;
-          *reinterpret_cast<uint16_t*>(sA + addr) = h;
-        }
+        *reinterpret_cast<uint16_t*>(sA + addr) = h;
       }
     }
   };
@@ -243,11 +230,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     }
   };
 
-  // ---- clear this wave's 64 rows of A buffer `buf` (8 KB, 16 B per lane per store)
+  // ---- clear this wave's RW rows of A buffer `buf` (16 B per lane per store)
   auto clear_a = [&](int buf) __attribute__((always_inline)) {
-    uint4* p = reinterpret_cast<uint4*>(sA + buf * ABUF + wave * 64 * AROW);
+    uint4* p = reinterpret_cast<uint4*>(sA + buf * ABUF + wave * RW * AROW);
 #pragma unroll
-    for (int q = 0; q < 64 * AROW / 1024; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < RW * AROW / 1024; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
   };
 
   // ---- fragments
@@ -262,7 +249,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
   auto b_frag = [&](const unsigned char* sB, int j, int kk) __attribute__((always_inline)) -> bf16x8_m {
     // lane L of a 16-lane group reads row r0 + L/4, columns c0 + 4(L%4) .. +3; lane i then
     // holds column c0 + i of rows r0 .. r0+3
-    const int c0 = 128 * wc + 32 * j + 16 * (g16 & 1);
+    const int c0 = WN * wc + 32 * j + 16 * (g16 & 1);
     const int col = c0 + 4 * (li & 3);
     short4_m h[2];
 #pragma unroll
@@ -275,11 +262,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     return __builtin_bit_cast(bf16x8_m, v);
   };
 
-  floatx16_m acc[4][4];
+  floatx16_m acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -310,20 +297,17 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
     __syncthreads();                     // A(ci), B(ci) complete; step ci-1's buffers free
     const int cn = ci + 1 < nch ? ci + 1 : nch - 1;
     const int c_next = cn % NCH;
-    // PRE: chunk cb ^ 1 into buffer cb ^ 1; in the last step (cb = 1) that is a chunk-0
-    // pass into buffer 0, which nothing reads any more
-    const int c_build = PRE ? (cb ^ 1) : c_next;
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
     const int e0 = e0_next;
     e0_next = first_entry((ci + 2) / NCH);  // for the next step, ready by then
     bk_begin(ov, e0, cn / NCH, c_next);  // overflowing rows of chunk cn: loads in flight until
                                      // the top of the next step writes them
-    bf16x8_m fa[2][4], fb[2][4];
+    bf16x8_m fa[2][4], fb[2][NJ];
     auto load_frags = [&](int kk, bf16x8_m* a, bf16x8_m* b) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = a_frag(cb, i, kk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = b_frag(sBc, j, kk);
+      for (int j = 0; j < NJ; ++j) b[j] = b_frag(sBc, j, kk);
     };
     load_frags(0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -334,33 +318,20 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
         issue_B(cn, sBn);
         clear_a(cb ^ 1);
       }
-      if (PRE && cb == 0) {
-        // chunk-1 pass (only unpacks): all of it first, so the units of the next tile,
-        // which overwrite the registers it reads, go out a whole step before their use
-        if (kk == 0) {
-#pragma unroll
-          for (int part = 0; part < 4; ++part) build_part(part, c_build, cb ^ 1);
-          if (load_next) {
-            const int kt = (cn + 1) / NCH;
-            load_units(kt < d.nt ? kt : d.nt - 1);
-          }
-        }
-      } else {
-        build_part(kk, c_build, cb ^ 1);
-        if (kk == NKK - 1 && load_next) {
-          const int kt = (cn + 1) / NCH;
-          load_units(kt < d.nt ? kt : d.nt - 1);
-        }
+      build_part(kk, c_next, cb ^ 1);
+      if (kk == NKK - 1 && load_next) {
+        const int kt = (cn + 1) / NCH;
+        load_units(kt < d.nt ? kt : d.nt - 1);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                               acc[i][j], 0, 0, 0);
       // one MFMA, then a few vector and LDS instructions in its shadow
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
+      for (int m = 0; m < 4 * NJ; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x080, 2, 0);  // LDS
@@ -381,11 +352,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + 128 * wt + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (t < T) y[(size_t)t * d.D + d0 + 128 * wc + 32 * j + l32] = f32_to_bf16(acc[i][j][r]);
+        if (t < T) y[(size_t)t * d.D + d0 + WN * wc + 32 * j + l32] = f32_to_bf16(acc[i][j][r]);
       }
 }
 
@@ -397,7 +368,7 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
   const int ntb = (d.T + DM_BM - 1) / DM_BM;
   const int total = nd * ntb;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((down_mfma_kernel<K, W>), dim3(8 * per_xcd), dim3(256), 0, s, d, b.counts,
+  hipLaunchKernelGGL((down_mfma_kernel<K, W>), dim3(8 * per_xcd), dim3(64 * DM_NW), 0, s, d, b.counts,
                      static_cast<const uint16_t*>(b.vals), b.cols,
                      static_cast<const uint16_t*>(b.bk_vals), ws.grp_first,
                      static_cast<const uint16_t*>(Wd), static_cast<uint16_t*>(y), blk_nnz, thr);
