@@ -20,8 +20,8 @@
 // each token row picks the values of its stored slots (and its backup slice's nonzero
 // positions).
 //
-// tmm_kernel: one workgroup per (128 hidden columns, 256 columns of d): dW = H^T M summed
-// over 32-token steps.  Each step rebuilds the 32 x 128 block of H in LDS from TwELL rows
+// tmm_kernel: one workgroup per (256 hidden columns, 256 columns of d): dW = H^T M summed
+// over 64-token steps.  Each step rebuilds the 64 x 256 block of H in LDS from TwELL rows
 // (as the forward's down kernel does) and loads M (g or x) rows with direct loads; both MFMA
 // operands come out of the token-major tiles through ds_read_b64_tr_b16.  With DB the same
 // kernel also sums the A fragments into db.
@@ -36,7 +36,7 @@ typedef float floatx16_b __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_vptr_b;
 typedef __attribute__((address_space(3))) short4_b* lds_s4ptr_b;
 
-constexpr int BW_JB = 128;  // hidden columns per workgroup
+constexpr int BW_JB = 128;  // hidden columns per sddmm workgroup
 
 // ============================================================================ SDDMM
 template <int K, int W>
@@ -281,36 +281,42 @@ __global__ __launch_bounds__(256) void sddmm_kernel(
 // ============================================================================ H^T M
 // 32-token steps, 48 KB of LDS and at most 256 registers: two workgroups share a CU, so one's
 // H rebuild and barrier waits overlap the other's MFMAs.
-constexpr int TMM_TS = 32;  // tokens per step
+// tmm_kernel: dW = H^T M with 8 waves (two per SIMD) per workgroup of (256 hidden columns,
+// 256 columns of d), 64-token steps; wave (wj, wd) computes hidden 64 wj.. x d 128 wd...  The H step tile is 64 tokens x 256 hidden columns.  Each wave owns whole row
+// segments of it (one token x one tile: 16 segments of 128 columns or 8 of 256): it clears
+// them, writes their slots and their backup slices, so no other wave touches them within the
+// step.  Fragments of the next k-step are read while the current one's MFMAs run.
+constexpr int TMM_JB = 256;  // hidden columns per workgroup
+constexpr int TMM_TS = 64;   // tokens per step
 
 template <int K, int W, bool DB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tmm_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void tmm_kernel(
     Dims d, const uint16_t* __restrict__ Hv, const uint16_t* __restrict__ Hbk,
     const uint16_t* __restrict__ counts, const uint8_t* __restrict__ cols,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ M,
     float* __restrict__ dW, float* __restrict__ db) {
   constexpr int TS = TMM_TS;
+  constexpr int NTL = TMM_JB / K;           // tiles per workgroup (2 or 1)
   constexpr int U = W / 8;                  // 8-slot units per tile-row
-  constexpr int RPW = TS / 4;               // H rows each wave writes per step (8)
-  constexpr int NU = (RPW * U + 63) / 64;   // units per lane
-  constexpr int HROW = 256;                 // H step tile: TS tokens x 128 columns, bf16
-  constexpr int HBUF = TS * HROW;
-  constexpr int MROW = 512;                 // M step tile: TS tokens x 256 columns, bf16
-  constexpr int MBUF = TS * MROW;
+  constexpr int SPW = TS * NTL / 8;         // row segments per wave (16 or 8)
+  constexpr int NU = (SPW * U + 63) / 64;   // units per lane
+  constexpr int SEGB = K * 2;               // bytes of one segment
+  constexpr int HROW = TMM_JB * 2;          // 512 B: one token row of the H step tile
+  constexpr int HBUF = TS * HROW;           // 32 KB
+  constexpr int MROW = 512;                 // M step tile: TS tokens x 256 columns
+  constexpr int MBUF = TS * MROW;           // 32 KB
   constexpr int NKK = TS / 16;              // MFMA k-steps per step
-  // H buffers (written by the waves) then 256 B holding the dummy word of padding writes; M
-  // buffers (filled by direct loads).  Piece p of row r sits at p ^ (4*(r&3)) in both, so
-  // the four rows (4 pieces each) that one half-wave of a transposed read touches cover all
-  // 64 banks.
+  constexpr int VPL = K / 64;               // backup values per lane (2 or 4)
+  static_assert(SPW * SEGB == 4096, "a wave clears 4 KB per step");
   __shared__ __attribute__((aligned(16))) unsigned char sH[2 * HBUF + 256];
   __shared__ __attribute__((aligned(16))) unsigned char sM0[MBUF];
   __shared__ __attribute__((aligned(16))) unsigned char sM1[MBUF];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wj = wave >> 1, wd = wave & 1;  // MFMA tile: columns j 64wj.., d 128wd..
+  const int wj = wave >> 1, wd = wave & 1;  // MFMA tile: hidden 64 wj.., d 128 wd..
   const int T = d.T, D = d.D;
-  const int nj = d.F / BW_JB;
+  const int nj = d.F / TMM_JB;
   const int nd = D / 256;
   const int total = nj * nd;
   const int per_xcd = (total + 7) / 8;
@@ -320,15 +326,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int dchunk = P / nj;
   const int jb = P - dchunk * nj;
   const int d0 = dchunk * 256;
-  const int j0 = jb * BW_JB;
-  const int k = j0 / K, hf = (j0 % K) / BW_JB;
+  const int j0 = jb * TMM_JB;
+  const int k0 = j0 / K;  // first tile of the workgroup
   const uint32_t trash = 2 * HBUF;  // one dummy word for every discarded write
-  const size_t row_base = (size_t)k * T;
+  // this wave's segments: s = wave * SPW + i, tile s / TS, token s % TS of the step
+  const int seg_tl = (wave * SPW) / TS;
+  const int seg_t0 = (wave * SPW) % TS;
 
   auto issue_M = [&](int ts, unsigned char* sM) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < MBUF / 1024 / 4; ++q) {  // loads of 1 KB (two rows), 4 per wave
-      const int ins = q * 4 + wave;
+    for (int q = 0; q < MBUF / 1024 / 8; ++q) {  // loads of 1 KB (two rows), 4 per wave
+      const int ins = q * 8 + wave;
       const int slot = ins * 64 + lane;
       const int r = slot >> 5, pc = slot & 31;
       const int lc = pc ^ (4 * (r & 3));
@@ -339,38 +347,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // ---- TwELL units of this wave's RPW rows of a step: unit u = lane + 64q (u < RPW*U) holds
-  // slots 8*(u%U) .. +7 of token TS*ts + RPW*wave + u/U
+  // ---- TwELL units of this wave's segments: unit v = lane + 64 q (v < SPW U) holds slots
+  // 8 (v % U) .. +7 of segment v / U (token seg_t0 + v / U of tile k0 + seg_tl)
   uint4 uv[NU];
   uint2 uc[NU];
-  uint32_t cnt = 0;  // count of token TS*ts + lane (lanes < TS; the backup rows of the step)
+  uint32_t cnt = 0;  // count of token TS ts + lane in tile k0 + seg_tl (the backup rows)
   auto load_units = [&](int ts) __attribute__((always_inline)) {
+    const size_t row_base = (size_t)(k0 + seg_tl) * T;
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
-      const int u = lane + 64 * q;
-      const int uu = u < RPW * U ? u : 0;
-      int tok = ts * TS + RPW * wave + uu / U;
+      const int v = lane + 64 * q;
+      const int vv = v < SPW * U ? v : 0;
+      int tok = ts * TS + seg_t0 + vv / U;
       tok = tok < T ? tok : T - 1;
-      const size_t e0 = (row_base + tok) * W + 8 * (uu % U);
+      const size_t e0 = (row_base + tok) * W + 8 * (vv % U);
       uv[q] = *reinterpret_cast<const uint4*>(Hv + e0);
       uc[q] = *reinterpret_cast<const uint2*>(cols + e0);
     }
-    const int tl = ts * TS + (lane & (TS - 1));
-    cnt = counts[row_base + (tl < T ? tl : T - 1)];
+    const int tl = ts * TS + lane;
+    const uint32_t m = tl < T ? 0xFFFFu : 0u;
+    cnt = (uint32_t)counts[row_base + (tl < T ? tl : T - 1)] & m;
   };
-  auto h_off = [&](int buf, uint32_t r, uint32_t cc) __attribute__((always_inline)) -> uint32_t {
-    return buf * HBUF + r * HROW + ((((cc >> 3) ^ (4 * (r & 3))) << 4) | ((cc & 7) << 1));
+  // byte offset of (token row r, hidden column hc of the workgroup) in H buffer `buf`; piece
+  // p of a row sits at p ^ (4 (r & 3)), which keeps a segment's pieces inside the segment
+  auto h_off = [&](int buf, uint32_t r, uint32_t hc) __attribute__((always_inline)) -> uint32_t {
+    return buf * HBUF + r * HROW + ((((hc >> 3) ^ (4 * (r & 3))) << 4) | ((hc & 7) << 1));
   };
   auto build = [&](int ts, int buf) __attribute__((always_inline)) {
-    // clear this wave's RPW rows (2 KB)
-    uint4* p = reinterpret_cast<uint4*>(sH + buf * HBUF + RPW * wave * HROW);
+    // clear this wave's segments (4 KB): piece i of the wave is piece i % (SEGB/16) of
+    // segment i / (SEGB/16)
 #pragma unroll
-    for (int q = 0; q < RPW * HROW / 1024; ++q) p[q * 64 + lane] = make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const int pi = lane + 64 * q;
+      const int sg = pi / (SEGB / 16), pc = pi % (SEGB / 16);
+      uint4* p = reinterpret_cast<uint4*>(sH + buf * HBUF + (seg_t0 + sg) * HROW + seg_tl * SEGB +
+                                          pc * 16);
+      *p = make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
-      const int u = lane + 64 * q;
-      const uint32_t r = RPW * wave + (uint32_t)(u < RPW * U ? u : 0) / U;  // row of the step tile
-      const bool ok = u < RPW * U && ts * TS + (int)r < T;
+      const int v = lane + 64 * q;
+      const uint32_t r = (uint32_t)(seg_t0 + (v < SPW * U ? v : 0) / U);  // token row of the step
+      const bool ok = v < SPW * U && ts * TS + (int)r < T;
       const uint32_t vv[4] = {uv[q].x, uv[q].y, uv[q].z, uv[q].w};
       const uint32_t cw[2] = {uc[q].x, uc[q].y};
 #pragma unroll
@@ -378,29 +396,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
         const uint32_t word = vv[e >> 1];
         const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
-        bool in = true;
-        if constexpr (K > BW_JB) in = (int)(col >> 7) == hf;
-        const uint32_t a = (ok && nz && in) ? h_off(buf, r, col & (BW_JB - 1)) : trash;
+        const uint32_t a = (ok && nz) ? h_off(buf, r, seg_tl * K + col) : trash;
         *reinterpret_cast<uint16_t*>(sH + a) = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
       }
     }
-    // backup slices of the overflowing rows among this wave's RPW (the step is one 32-token
-    // group: its overflowing rows are consecutive entries from the group's first)
-    const uint64_t ov_all =
-        ballot64(lane < TS && cnt > (uint32_t)W && ts * TS + lane < T);
-    uint64_t ov = ov_all & (((1ull << RPW) - 1ull) << (RPW * wave));
+    // backup slices of the overflowing rows among this wave's segments; entry = first entry
+    // of the row's (tile, 32-token group) + its rank among the group's overflowing rows
+    const uint64_t ov_all = ballot64(cnt > (uint32_t)W);  // token TS ts + lane
+    uint64_t ov = (ov_all >> seg_t0) & ((1ull << SPW) - 1ull);
     while (ov != 0) {
-      const int b = __builtin_ctzll(ov);
+      const int i = __builtin_ctzll(ov);
       ov &= ov - 1;
-      const int e = ld_uniform(grp_first + k * d.ng + ts) +
-                    __builtin_popcountll(ov_all & ((1ull << b) - 1ull));
+      const int tt = seg_t0 + i;  // token row of the step
+      const int gb = tt & ~(GROUP - 1);
+      const uint64_t below = ov_all & ((1ull << tt) - 1ull) & ~((1ull << gb) - 1ull);
+      const int e = ld_uniform(grp_first + (k0 + seg_tl) * d.ng + (ts * TS + gb) / GROUP) +
+                    __builtin_popcountll(below);
       if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
-      const uint32_t hv = *reinterpret_cast<const uint32_t*>(Hbk + (size_t)e * K + hf * BW_JB + 2 * lane);
-      const uint32_t c0 = 2 * lane;
-      const uint32_t a0 = (hv & 0xFFFFu) ? h_off(buf, b, c0) : trash;
-      *reinterpret_cast<uint16_t*>(sH + a0) = (uint16_t)hv;
-      const uint32_t a1 = (hv >> 16) ? h_off(buf, b, c0 + 1) : trash;
-      *reinterpret_cast<uint16_t*>(sH + a1) = (uint16_t)(hv >> 16);
+      const uint16_t* src = Hbk + (size_t)e * K + VPL * lane;
+      uint16_t hv[VPL];
+      if constexpr (VPL == 2) {
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(src);
+        hv[0] = (uint16_t)w2;
+        hv[1] = (uint16_t)(w2 >> 16);
+      } else {
+        const uint2 w4 = *reinterpret_cast<const uint2*>(src);
+        hv[0] = (uint16_t)w4.x;
+        hv[1] = (uint16_t)(w4.x >> 16);
+        hv[2] = (uint16_t)w4.y;
+        hv[3] = (uint16_t)(w4.y >> 16);
+      }
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const uint32_t a = hv[v] ? h_off(buf, tt, seg_tl * K + VPL * lane + v) : trash;
+        *reinterpret_cast<uint16_t*>(sH + a) = hv[v];
+      }
     }
   };
 
@@ -440,14 +470,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): M(ts) and the units have landed
     __syncthreads();                     // H(ts), M(ts) complete; step ts-1's buffers free
     const unsigned char* hb = sH + cb * HBUF;
-    bf16x8_b fa[NKK][2], fb[NKK][4];
+    bf16x8_b fa[2][2], fb[2][4];
+    auto load_frags = [&](int kk, bf16x8_b (&a)[2], bf16x8_b (&b)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {  // all fragments of the step first (16 KB per wave)
+      for (int i = 0; i < 2; ++i) a[i] = tr_frag(hb, HROW, 64 * wj + 32 * i, kk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[kk][i] = tr_frag(hb, HROW, 64 * wj + 32 * i, kk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[kk][j] = tr_frag(sMc, MROW, 128 * wd + 32 * j, kk);
-    }
+      for (int j = 0; j < 4; ++j) b[j] = tr_frag(sMc, MROW, 128 * wd + 32 * j, kk);
+    };
+    load_frags(0, fa[0], fb[0]);
     if (ts + 1 < nts) {  // next step's tiles while these MFMAs run
       issue_M(ts + 1, sMn);
       build(ts + 1, cb ^ 1);
@@ -455,17 +485,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + 1 < NKK) load_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                              acc[i][j], 0, 0, 0);
       if (do_db) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           float s = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += (float)fa[kk][i][e];
+          for (int e = 0; e < 8; ++e) s += (float)fa[kk & 1][i][e];
           dbacc[i] += s;
         }
       }
@@ -515,18 +547,18 @@ static hipError_t launch_bwd_t(int which, const Dims& d, const twell_buffers_t& 
                        ws.grp_first, dh_vals, dh_bk);
     return hipGetLastError();
   }
-  const int total = nj * (d.D / 256);
+  const int total = (d.F / TMM_JB) * (d.D / 256);
   const dim3 grid(8 * ((total + 7) / 8));
   if (which == 1) {
-    hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(256), 0, s, d,
+    hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(512), 0, s, d,
                        static_cast<const uint16_t*>(act.vals),
                        static_cast<const uint16_t*>(act.bk_vals), act.counts, act.cols,
                        ws.grp_first, g, dW_down, nullptr);
   } else if (db) {
-    hipLaunchKernelGGL((tmm_kernel<K, W, true>), grid, dim3(256), 0, s, d, dh_vals, dh_bk,
+    hipLaunchKernelGGL((tmm_kernel<K, W, true>), grid, dim3(512), 0, s, d, dh_vals, dh_bk,
                        act.counts, act.cols, ws.grp_first, x, dW_up, db);
   } else {
-    hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(256), 0, s, d, dh_vals, dh_bk,
+    hipLaunchKernelGGL((tmm_kernel<K, W, false>), grid, dim3(512), 0, s, d, dh_vals, dh_bk,
                        act.counts, act.cols, ws.grp_first, x, dW_up, nullptr);
   }
   return hipGetLastError();

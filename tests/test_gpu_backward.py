@@ -90,13 +90,17 @@ def _backward_case(torch, sffn, L, seed=7):
     ("C2", 200, None),      # 0.5B-like: W 48, 20% density
     ("C4", 260, None),      # 2B-like: tile 256 (two column halves per tile), W 16
     ("C5", 130, 0.20),      # dense enough that many rows overflow into the backup
+    ("C5/w16", 200, None),  # tile 128 with 16 slots: half of the unit lanes idle
+    ("C5/w64", 140, 0.50),  # tile 128 with 64 slots (two units per lane); rows overflow
 ])
 def test_backward_parity(name, T, rho):
     torch, sffn = need_gpu()
     print(f"[backward] {name} T={T} rho={rho}", flush=True)
-    L = make_layer(CONFIGS[name], seed=0, T=T, rho=rho)
+    base, _, w = name.partition("/w")
+    cfg = CONFIGS[base] if not w else CONFIGS[base].replace(ell_width=int(w))
+    L = make_layer(cfg, seed=0, T=T, rho=rho)
     host = _backward_case(torch, sffn, L)
-    if rho == 0.20:
+    if rho is not None and rho >= 0.20:
         assert host["bk_n"] > 0, "the case should exercise backup rows"
 
 
