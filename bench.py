@@ -40,10 +40,21 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# the sources each kernel with stored traffic counters is built from (its own file and the
+# shared header): its counters stay valid while these files are unchanged
+KERNEL_SOURCES = {
+    "up_pack": ("k_up_pack.hip", "sffn_common.hpp"),
+    "down_mfma": ("k_down_mfma.hip", "sffn_common.hpp"),
+    "down_tiles": ("k_down_lds.hip", "sffn_common.hpp"),
+    "down": ("k_down_rows.hip", "sffn_common.hpp"),
+}
+
+
+def kernel_source_hash(files=None) -> str:
+    """sha256 prefix of the named csrc files (all of them when files is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "activation_sparse_transformer_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -272,7 +283,9 @@ def main():
 
     def traffic_of(name):
         ent = tc.get(name)
-        if ent and ent.get("source_hash") == src_hash and ent.get("workload") == f"C3-{args.rho:.0%}":
+        if ent and name in KERNEL_SOURCES and \
+                ent.get("source_hash") == kernel_source_hash(KERNEL_SOURCES[name]) and \
+                ent.get("workload") == f"C3-{args.rho:.0%}":
             return ent["bytes_per_launch"]
         return None
 

@@ -41,3 +41,14 @@ def test_power_sensor_absent_or_readable():
     if p is not None:
         with open(p) as f:
             int(f.read())
+
+
+def test_traffic_counters_name_their_sources():
+    """Stored HBM traffic figures carry the hash of exactly the sources of their kernel."""
+    import json
+    tc = json.load(open(os.path.join(ROOT, "profiles", "traffic_counters.json")))
+    for name, ent in tc.items():
+        assert name in bench.KERNEL_SOURCES, name
+        assert tuple(ent["sources"]) == bench.KERNEL_SOURCES[name]
+        assert len(ent["source_hash"]) == 16
+        assert abs(ent["bytes_per_launch"] - ent["fetch_bytes"] - ent["write_bytes"]) <= 1
