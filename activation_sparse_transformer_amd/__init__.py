@@ -9,4 +9,5 @@ from .sparse_ffn import (  # noqa: F401
     SFFN_OK, SFFN_ERR_INVALID_ARGUMENT, SFFN_ERR_UNSUPPORTED, SFFN_ERR_BACKUP_OVERFLOW,
     SFFN_ERR_DEVICE, DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES,
     DOWN_GATHER_DENSITY_DEFAULT, DOWN_MFMA_DENSITY_DEFAULT, DOWN_TILES_MIN_T, DOWN_MFMA_MIN_T,
+    MAX_TILES,
 )

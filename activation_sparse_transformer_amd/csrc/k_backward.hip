@@ -279,8 +279,6 @@ __global__ __launch_bounds__(256) void sddmm_kernel(
 }
 
 // ============================================================================ H^T M
-// 32-token steps, 48 KB of LDS and at most 256 registers: two workgroups share a CU, so one's
-// H rebuild and barrier waits overlap the other's MFMAs.
 // tmm_kernel: dW = H^T M with 8 waves (two per SIMD) per workgroup of (256 hidden columns,
 // 256 columns of d), 64-token steps; wave (wj, wd) computes hidden 64 wj.. x d 128 wd...  The H step tile is 64 tokens x 256 hidden columns.  Each wave owns whole row
 // segments of it (one token x one tile: 16 segments of 128 columns or 8 of 256): it clears

@@ -317,67 +317,88 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Two launches.  order_scan_kernel (one workgroup): exclusive scan of the per-(tile, group)
-// overflow counts into grp_first (the first canonical entry of every (tile, group)), plus
-// bk_tile_ptr, bk_n and the status word.  order_copy_kernel: every staged entry goes to
+// Two launches.  order_tile_kernel (one workgroup per tile): exclusive scan of the tile's
+// per-group overflow counts, in place in ov_grp, and the tile's total.  order_copy_kernel:
+// every workgroup scans the tile totals into tile offsets in LDS; together they write
+// grp_first (tile offset + group offset: the first canonical entry of every (tile, group)),
+// the first one bk_tile_ptr, bk_n and the status word, and every staged entry goes to
 // grp_first[tile, group] + its rank inside the group.
-constexpr int ORDER_PER_THREAD = 16;  // entries a scan thread holds in registers per pass
+constexpr int ORDER_COPY_MAX_NT = SFFN_MAX_TILES;  // tile offsets the copy kernel's LDS holds
 
-__global__ __launch_bounds__(1024) void order_scan_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+__global__ __launch_bounds__(1024) void order_tile_kernel(Dims d, Workspace ws) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int N = d.nt * d.ng;
+  int32_t* grp = ws.ov_grp + (size_t)blockIdx.x * d.ng;
   int carry = 0;
-  for (int base = 0; base < N; base += 1024 * ORDER_PER_THREAD) {
-    int v[ORDER_PER_THREAD];
+  for (int base = 0; base < d.ng; base += 1024) {
+    const int i = base + tid;
+    const int v = i < d.ng ? grp[i] : 0;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int woff = 0, tot = 0;
 #pragma unroll
-    for (int r = 0; r < ORDER_PER_THREAD; ++r) {  // coalesced: entry base + r*1024 + tid
-      const int q = base + r * 1024 + tid;
-      v[r] = q < N ? ws.ov_grp[q] : 0;
+    for (int w = 0; w < 16; ++w) {
+      const int sw = wsum[w];
+      woff += w < wv ? sw : 0;
+      tot += sw;
     }
-#pragma unroll
-    for (int r = 0; r < ORDER_PER_THREAD; ++r) {
-      const int incl = wave_incl_scan(v[r]);
-      if (lane == 63) wsum[wv] = incl;
-      __syncthreads();
-      int woff = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const int sw = wsum[w];
-        woff += w < wv ? sw : 0;
-        tot += sw;
-      }
-      const int q = base + r * 1024 + tid;
-      if (q < N) {
-        const int first = carry + woff + incl - v[r];
-        ws.grp_first[q] = first;
-        if (q % d.ng == 0) b.bk_tile_ptr[q / d.ng] = first;
-      }
-      carry += tot;
-      __syncthreads();  // wsum is rewritten by the next round
-    }
+    if (i < d.ng) grp[i] = carry + woff + incl - v;
+    carry += tot;
+    __syncthreads();  // wsum is rewritten by the next round
   }
-  if (tid == 0) {
-    ws.grp_first[N] = carry;
-    b.bk_tile_ptr[d.nt] = carry;
-    *b.bk_n = carry;
-    *b.status = carry > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
-  }
+  if (tid == 0) ws.tile_tot[blockIdx.x] = carry;
 }
 
 template <int K, bool BF16>
 __global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t b, Workspace ws) {
-  const int lane = threadIdx.x & 63;
+  __shared__ int toff[ORDER_COPY_MAX_NT + 1];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // tile offsets: exclusive scan of the tile totals, 256 at a time
+  int carry = 0;
+  for (int base = 0; base < d.nt; base += 256) {
+    const int k = base + tid;
+    const int v = k < d.nt ? ws.tile_tot[k] : 0;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int woff = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int sw = wsum[w];
+      woff += w < wv ? sw : 0;
+      tot += sw;
+    }
+    if (k < d.nt) toff[k] = carry + woff + incl - v;
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) toff[d.nt] = carry;
+  __syncthreads();
+  const int total = carry;
+  const int N = d.nt * d.ng;
+  if (blockIdx.x == 0) {
+    for (int k = tid; k <= d.nt; k += 256) b.bk_tile_ptr[k] = toff[k];
+    if (tid == 0) {
+      ws.grp_first[N] = total;
+      *b.bk_n = total;
+      *b.status = total > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
+    }
+  }
+  for (int q = blockIdx.x * 256 + tid; q < N; q += gridDim.x * 256)
+    ws.grp_first[q] = toff[q / d.ng] + ws.ov_grp[q];
+  // the copy
   const int n_staged = min(*ws.claim, d.cap);
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wv;
   const int nw = gridDim.x * 4;
   constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;  // 32-bit words per slice
   for (int e = gw; e < n_staged; e += nw) {
     const int kk = ws.stage_key[2 * e];
     const int tw = ws.stage_key[2 * e + 1];
     const int t = tw & 0xFFFFFF, lr = tw >> 24;
-    const int fin = ws.grp_first[kk * d.ng + t / GROUP] + lr;
+    const int fin = toff[kk] + ws.ov_grp[kk * d.ng + t / GROUP] + lr;
     if (fin >= d.cap) continue;  // capacity exceeded: the status word reports it
     const uint32_t* src = static_cast<const uint32_t*>(ws.stage_vals) + (size_t)e * WORDS;
     uint32_t* dst = static_cast<uint32_t*>(b.bk_vals) + (size_t)fin * WORDS;
@@ -475,7 +496,8 @@ hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace
 #undef SFFN_ORDER_SMALL
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(order_scan_kernel, dim3(1), dim3(1024), 0, s, d, b, ws);
+  if (d.nt > ORDER_COPY_MAX_NT) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(order_tile_kernel, dim3(d.nt), dim3(1024), 0, s, d, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 4 waves per workgroup, about one staged entry per wave at full capacity

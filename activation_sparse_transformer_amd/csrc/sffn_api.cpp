@@ -98,6 +98,8 @@ sffn_status_t check_cfg(const sffn_config_t* c) {
     return fail(SFFN_ERR_INVALID_ARGUMENT, "max_tokens must be in [1, 2^24]");
   if (c->backup_capacity < 0) return fail(SFFN_ERR_INVALID_ARGUMENT, "backup_capacity < 0");
   const long long nt = c->d_ff / c->tile;
+  if (nt > SFFN_MAX_TILES)
+    return fail(SFFN_ERR_UNSUPPORTED, "d_ff / tile must be at most SFFN_MAX_TILES (4096)");
   if ((long long)c->backup_capacity > nt * (long long)c->max_tokens)
     return fail(SFFN_ERR_INVALID_ARGUMENT, "backup_capacity exceeds the number of tile-rows");
   const long long esz = c->dtype == SFFN_BF16 ? 2 : 4;

@@ -35,6 +35,7 @@ struct Workspace {
   long long* stats;     // [8]      stats reduction output
   int32_t* blk_nnz;     // [nblk]   stored nonzeros per 256-token block (down-path choice)
   int32_t* grp_first;   // [nt*ng+1] first backup entry of each (tile, group), canonical order
+  int32_t* tile_tot;    // [nt]     overflowing tile-rows per tile (ordering pass)
   float* hsmall;        // [min(T, UP_SMALL_T), F] ReLU output of the decode-shaped up path
 };
 
@@ -53,6 +54,7 @@ inline size_t workspace_bytes(const Dims& d) {
   n += align256(sizeof(long long) * 8);
   n += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
+  n += align256(sizeof(int32_t) * (size_t)d.nt);
   n += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
   return n;
 }
@@ -74,6 +76,8 @@ inline Workspace carve(void* base, const Dims& d) {
   p += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   w.grp_first = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
+  w.tile_tot = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * (size_t)d.nt);
   w.hsmall = reinterpret_cast<float*>(p);
   return w;
 }

@@ -66,6 +66,8 @@ DOWN_GATHER_DENSITY_DEFAULT = 0.0005
 DOWN_MFMA_DENSITY_DEFAULT = 0.005
 DOWN_TILES_MIN_T = 4096
 DOWN_MFMA_MIN_T = 1024
+# Largest d_ff / tile a configuration may have (the header's SFFN_MAX_TILES).
+MAX_TILES = 4096
 
 # Exported entry points and their prototypes (restype is always the status enum unless set).
 _PROTOS = {

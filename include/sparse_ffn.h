@@ -52,9 +52,13 @@ typedef enum {
 
 typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype_t;
 
+/* Largest number of tiles (d_ff / tile) a configuration may have (SFFN_ERR_UNSUPPORTED
+ * beyond it): the ordering pass keeps one offset per tile in workgroup-local memory. */
+#define SFFN_MAX_TILES 4096
+
 typedef struct {
   int32_t d_model;         /* D: multiple of 64 (layers in bf16: of 128) */
-  int32_t d_ff;            /* F: multiple of tile (layers in bf16: also of 256) */
+  int32_t d_ff;            /* F: multiple of tile (layers in bf16: also of 256), F / tile <= SFFN_MAX_TILES */
   int32_t tile;            /* K: hidden columns per tile, one of 64, 128, 256 */
   int32_t ell_width;       /* W: ELL slots per tile-row, 1 <= W <= tile */
   int32_t max_tokens;      /* largest T any call may pass (1 <= T <= max_tokens <= 2^24) */

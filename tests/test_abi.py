@@ -52,6 +52,8 @@ def test_header_constants_match_binding(sffn):
     for k, v in want.items():
         assert float(defs[k]) == pytest.approx(v, rel=1e-6), k
     assert sffn.DOWN_GATHER_DENSITY_DEFAULT <= sffn.DOWN_MFMA_DENSITY_DEFAULT
+    mt = re.search(r"#define\s+SFFN_MAX_TILES\s+([0-9]+)", text)
+    assert mt and int(mt.group(1)) == sffn.MAX_TILES
 
 
 def test_status_strings(sffn):
@@ -82,6 +84,7 @@ def test_buffer_sizes_formula(sffn):
     ({"tile": 100}, 2), ({"tile": 512}, 2), ({"ell_width": 0}, 1), ({"ell_width": 129}, 1),
     ({"d_ff": 1000}, 1), ({"d_model": 100}, 2), ({"max_tokens": 0}, 1),
     ({"backup_capacity": -1}, 1), ({"d_model": 0}, 1),
+    ({"d_ff": 4097 * 64, "tile": 64, "backup_capacity": 0}, 2),  # more than SFFN_MAX_TILES tiles
 ])
 def test_config_validation(sffn, kw, code):
     base = dict(d_model=256, d_ff=1024, tile=128, ell_width=32, max_tokens=64,
