@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--energy-seconds", type=float, default=2.0,
                     help="seconds of repeated forwards per energy measurement (0: skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped points")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the 0.5B-like (20%%) and 2B-like (3%%) layer points")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the layer shards by tokens with no exchange, "
@@ -368,6 +370,37 @@ def main():
                       res["sparse"]["joules_per_token"] / res["dense_bf16"]["joules_per_token"], 4)}
         del layer_e
 
+    # ---- the other layer shapes at their own densities: 0.5B-like (T=4096, d_model 1536,
+    # d_ff 6144, tile 128, W 48, 20%) and 2B-like (T=16384, d_model 2304, d_ff 9216, tile 256,
+    # W 16, 3% with 0.5% heavy tokens); the auto down policy, against the dense bf16 FFN
+    layers = []
+    if not args.no_layers:
+        for name in ("C2", "C4"):
+            Lc = make_layer(CONFIGS[name], seed=0)
+            cc = Lc["cfg"]
+            cfg_c = sffn.Config(d_model=cc.D, d_ff=cc.F, tile=cc.tile, ell_width=cc.ell_width,
+                                max_tokens=cc.T, backup_capacity=cc.n_tiles * cc.T // 8,
+                                dtype="bf16")
+            xc, Wuc, bc, Wdc = (bf16_dev(Lc[k]) for k in ("x", "W_up", "b_up", "W_down"))
+            layer_c = sffn.SparseFFN(cfg_c, Wuc, bc, Wdc)
+            act_c = sffn.TwellBuffers(cfg_c, cc.T)
+            yc = torch.empty_like(xc)
+            ms_c, _ = time_steps(lambda: layer_c.forward(xc, act=act_c, y=yc), max(10, args.steps // 2), 3)
+            ms_cd, _ = time_steps(lambda: torch.matmul(Fn.relu(Fn.linear(xc, Wuc, bc)), Wdc),
+                                  max(10, args.steps // 2), 3)
+            stc = sffn.twell_stats(cfg_c, act_c)
+            layers.append({"layer": cc.name, "T": cc.T, "d_model": cc.D, "d_ff": cc.F,
+                           "tile": cc.tile, "ell_width": cc.ell_width,
+                           "density": round(stc["density"], 5),
+                           "overflow_tile_rows": int(stc["overflow_tile_rows"]),
+                           "ms_sparse": round(ms_c, 5), "ms_dense": round(ms_cd, 5),
+                           "tokens_per_s": round(cc.T / (ms_c * 1e-3), 1),
+                           "speedup_vs_dense": round(ms_cd / ms_c, 4)})
+            log(f"  layer {cc.name}: sparse {ms_c:.4f} ms, dense {ms_cd:.4f} ms, "
+                f"density {stc['density']:.4f}")
+            del layer_c, act_c, xc, Wuc, bc, Wdc, yc
+            torch.cuda.empty_cache()
+
     # ---- decode-shaped points: few tokens, the layer reads all of W_up but only the W_down
     # rows the stored nonzeros select; sparse (auto policy and each down kernel) vs dense
     decode = []
@@ -456,6 +489,9 @@ def main():
         "train": train,
         "energy": energy,
         "decode": decode,
+        "layers": layers,
+        "device": {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+                   "torch": torch.__version__},
         "sweep": sweep,
         "kernel_source_hash": src_hash,
     }
