@@ -32,6 +32,8 @@
 // When the layer's stored-nonzero count (the sum of the per-block counts) is at most `thr`
 // the gather kernel takes the layer and every workgroup here returns at once
 // (blk_nnz == nullptr: this kernel runs).
+#include <algorithm>
+
 #include "sffn_common.hpp"
 
 namespace sffn {
@@ -53,7 +55,8 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr) {
+    uint16_t* __restrict__ y, float* __restrict__ dpart, int S, const int32_t* __restrict__ blk_nnz,
+    long long thr) {
   constexpr int KC = DM_KC;
   constexpr int NCH = K / KC;          // steps per tile
   constexpr int U = W / 8;             // 8-slot units per tile-row
@@ -83,15 +86,23 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   const int T = d.T;
   const int nd = (d.D + DM_BN - 1) / DM_BN;
   const int ntb = (T + DM_BM - 1) / DM_BM;
-  const int total = nd * ntb;
+  const int total = nd * ntb * S;
   const int per_xcd = (total + 7) / 8;
   const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (P >= total) return;
-  // token-block-major: the workgroups an XCD runs together share token blocks (TwELL
-  // reads) and column chunks (W_down reads) in its L2
-  const int tb = P / nd;
+  // split-major, then token-block-major: the workgroups an XCD runs together share a tile
+  // range, token blocks (TwELL reads) and column chunks (W_down reads) in its L2
+  const int split = P / (nd * ntb);
+  const int Pl = P - split * nd * ntb;
+  const int tb = Pl / nd;
   if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
-  const int dchunk = P - tb * nd;
+  const int dchunk = Pl - tb * nd;
+  // tiles [k_lo, k_hi) of this part (in pairs for 64-column tiles, whose one-step tiles run
+  // two per unrolled iteration)
+  constexpr int TQ = NCH == 1 ? 2 : 1;
+  const int nunits = d.nt / TQ;
+  const int k_lo = split * nunits / S * TQ;
+  const int k_hi = split + 1 == S ? d.nt : (split + 1) * nunits / S * TQ;
   const int d0 = dchunk * DM_BN;
   const bool active = d0 + WN * wc < d.D;  // D % 256 == 128: the last chunk is half wide
   const int t0 = tb * DM_BM;
@@ -271,19 +282,19 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // ---- prologue: A(0) written, B(0) in flight, units of the step after it loaded
-  const int nch = d.nt * NCH;
-  issue_B(0, sB0);
-  load_units(0);
+  const int c_lo = k_lo * NCH, c_hi = k_hi * NCH;  // this part's steps
+  issue_B(c_lo, sB0);
+  load_units(k_lo);
   clear_a(0);
 #pragma unroll
-  for (int part = 0; part < 4; ++part) build_part(part, 0, 0);
+  for (int pt = 0; pt < 4; ++pt) build_part(pt, 0, 0);
   {
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
-    if (NCH == 1) load_units(d.nt > 1 ? 1 : 0);
-    bk_begin(ov, first_entry(0), 0, 0);
-    bk_finish(0, 0, 0);
+    if (NCH == 1) load_units(k_lo + 1 < d.nt ? k_lo + 1 : k_lo);
+    bk_begin(ov, first_entry(k_lo), k_lo, 0);
+    bk_finish(k_lo, 0, 0);
   }
-  int e0_next = first_entry(1 / NCH);  // first backup entry for the chunk step 0 prepares
+  int e0_next = first_entry((c_lo + 1) / NCH);  // first backup entry for the chunk the first step prepares
 
   // step ci: MFMAs of step ci (A and B buffers ci&1) while the A rows of step ci+1 are
   // written into the other A buffer.  The last step rebuilds a chunk nobody reads instead
@@ -293,9 +304,9 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   auto step = [&](int ci, int cb, unsigned char* sBc, unsigned char* sBn, bool load_next)
       __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): B(ci), the units, backup rows landed
-    if (ci > 0) bk_finish(ci / NCH, ci % NCH, cb);  // backup rows of chunk ci (loaded last step)
+    if (ci > c_lo) bk_finish(ci / NCH, ci % NCH, cb);  // backup rows of chunk ci (loaded last step)
     __syncthreads();                     // A(ci), B(ci) complete; step ci-1's buffers free
-    const int cn = ci + 1 < nch ? ci + 1 : nch - 1;
+    const int cn = ci + 1 < c_hi ? ci + 1 : c_hi - 1;
     const int c_next = cn % NCH;
     const uint64_t ov = ballot64(cnt > (uint32_t)W);
     const int e0 = e0_next;
@@ -340,14 +351,15 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  constexpr int UF = NCH < 2 ? 2 : NCH;  // steps per unrolled iteration (nch % UF == 0)
-  for (int base = 0; base < nch; base += UF) {
+  constexpr int UF = NCH < 2 ? 2 : NCH;  // steps per unrolled iteration ((c_hi - c_lo) % UF == 0)
+  for (int base = c_lo; base < c_hi; base += UF) {
 #pragma unroll
     for (int s2 = 0; s2 < UF; ++s2)
       step(base + s2, s2 & 1, (s2 & 1) ? sB1 : sB0, (s2 & 1) ? sB0 : sB1, (s2 + 2) % NCH == 0);
   }
 
-  // ---- y (bf16): C[m = token][n = column]; lane: column l32, rows 8(r/4) + 4lh + r%4
+  // ---- y (bf16), or this part's fp32 sums: C[m = token][n = column]; lane: column l32,
+  // rows 8(r/4) + 4lh + r%4
   if (!active) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -356,8 +368,38 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = t0 + 128 * wt + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (t < T) y[(size_t)t * d.D + d0 + WN * wc + 32 * j + l32] = f32_to_bf16(acc[i][j][r]);
+        const size_t o = (size_t)t * d.D + d0 + WN * wc + 32 * j + l32;
+        if (t < T) {
+          if (S == 1)
+            y[o] = f32_to_bf16(acc[i][j][r]);
+          else
+            dpart[(size_t)split * T * d.D + o] = acc[i][j][r];
+        }
       }
+}
+
+// y = bf16(sum over the S parts of the split kernel), parts added in order (deterministic).
+__global__ __launch_bounds__(256) void down_reduce_kernel(Dims d, const float* __restrict__ part,
+                                                          int S, uint16_t* __restrict__ y,
+                                                          const int32_t* __restrict__ blk_nnz,
+                                                          long long thr) {
+  const int ntb = (d.T + DM_BM - 1) / DM_BM;
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
+  const size_t n4 = (size_t)d.T * d.D / 4;
+  const float4* p4 = reinterpret_cast<const float4*>(part);
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 256) {
+    float4 a = p4[q];
+    for (int sp = 1; sp < S; ++sp) {
+      const float4 v = p4[(size_t)sp * n4 + q];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    reinterpret_cast<uint2*>(y)[q] = make_uint2(lo, hi);
+  }
 }
 
 template <int K, int W>
@@ -366,12 +408,22 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
                               hipStream_t s) {
   const int nd = (d.D + DM_BN - 1) / DM_BN;
   const int ntb = (d.T + DM_BM - 1) / DM_BM;
-  const int total = nd * ntb;
+  const int S = down_split(d);
+  const int total = nd * ntb * S;
   const int per_xcd = (total + 7) / 8;
   hipLaunchKernelGGL((down_mfma_kernel<K, W>), dim3(8 * per_xcd), dim3(64 * DM_NW), 0, s, d, b.counts,
                      static_cast<const uint16_t*>(b.vals), b.cols,
                      static_cast<const uint16_t*>(b.bk_vals), ws.grp_first,
-                     static_cast<const uint16_t*>(Wd), static_cast<uint16_t*>(y), blk_nnz, thr);
+                     static_cast<const uint16_t*>(Wd), static_cast<uint16_t*>(y), ws.dpart, S,
+                     blk_nnz, thr);
+  if (S > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n4 = (size_t)d.T * d.D / 4;
+    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 2048);
+    hipLaunchKernelGGL(down_reduce_kernel, dim3(blocks), dim3(256), 0, s, d, ws.dpart, S,
+                       static_cast<uint16_t*>(y), blk_nnz, thr);
+  }
   return hipGetLastError();
 }
 

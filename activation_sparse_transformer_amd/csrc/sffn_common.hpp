@@ -37,6 +37,7 @@ struct Workspace {
   int32_t* grp_first;   // [nt*ng+1] first backup entry of each (tile, group), canonical order
   int32_t* tile_tot;    // [nt]     overflowing tile-rows per tile (ordering pass)
   float* hsmall;        // [min(T, UP_SMALL_T), F] ReLU output of the decode-shaped up path
+  float* dpart;         // [S, T, D] fp32 partial sums of the split matrix-core down kernel
 };
 
 // Batches of at most this many tokens take the decode-shaped up-projection (one workgroup
@@ -44,6 +45,32 @@ struct Workspace {
 constexpr int UP_SMALL_T = 32;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Split of the matrix-core down-projection over its tiles: with fewer than 256 workgroups of
+// (256 tokens, 256 columns) the tile range is cut into S parts (at most DM_MAX_SPLIT, each at
+// least two tiles), each part's fp32 sums go to dpart and a second kernel adds them in order.
+constexpr int DM_MAX_SPLIT = 16;
+inline int down_split_for(int T, int D, int nt) {
+  const long long base = (long long)((T + 255) / 256) * ((D + 255) / 256);
+  if (base >= 256) return 1;
+  int S = (int)((256 + base - 1) / base);
+  S = S < DM_MAX_SPLIT ? S : DM_MAX_SPLIT;
+  S = S < nt / 2 ? S : nt / 2;
+  return S > 1 ? S : 1;
+}
+inline int down_split(const Dims& d) { return d.bf16 ? down_split_for(d.T, d.D, d.nt) : 1; }
+// dpart floats for a call of T tokens and for every smaller T' (buffers sized for T serve
+// calls with fewer tokens): the largest S(T') T' D over T' <= T
+inline size_t down_part_floats(const Dims& d) {
+  if (!d.bf16) return 0;
+  size_t best = 0;
+  for (long long t1 = 256; t1 - 255 <= d.T; t1 += 256) {  // S is constant on each 256-token block
+    const long long t = t1 < d.T ? t1 : d.T;
+    const int S = down_split_for((int)t, d.D, d.nt);
+    if (S > 1 && (size_t)S * (size_t)t * (size_t)d.D > best) best = (size_t)S * (size_t)t * (size_t)d.D;
+  }
+  return best;
+}
 
 inline size_t workspace_bytes(const Dims& d) {
   size_t n = 0;
@@ -56,6 +83,7 @@ inline size_t workspace_bytes(const Dims& d) {
   n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
   n += align256(sizeof(int32_t) * (size_t)d.nt);
   n += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
+  n += align256(sizeof(float) * down_part_floats(d));
   return n;
 }
 
@@ -79,6 +107,8 @@ inline Workspace carve(void* base, const Dims& d) {
   w.tile_tot = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * (size_t)d.nt);
   w.hsmall = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
+  w.dpart = reinterpret_cast<float*>(p);
   return w;
 }
 

@@ -65,7 +65,7 @@ DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES = 0, 1, 2, 3
 DOWN_GATHER_DENSITY_DEFAULT = 0.0005
 DOWN_MFMA_DENSITY_DEFAULT = 0.005
 DOWN_TILES_MIN_T = 4096
-DOWN_MFMA_MIN_T = 1024
+DOWN_MFMA_MIN_T = 64
 # Largest d_ff / tile a configuration may have (the header's SFFN_MAX_TILES).
 MAX_TILES = 4096
 

@@ -190,9 +190,10 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
  *                     hands its range to the next one down (mfma -> tiles -> gather), and so
  *                     do tiles below SFFN_DOWN_TILES_MIN_T tokens (its 256-token workgroups
  *                     walk every tile in turn and need many tokens to fill the GPU) and mfma
- *                     below SFFN_DOWN_MFMA_MIN_T (decode-shaped batches: it would contract
- *                     whole 256-token blocks and read all of W_down, where the gather reads
- *                     only the rows in use).
+ *                     below SFFN_DOWN_MFMA_MIN_T (a handful of tokens: it contracts whole
+ *                     256-token blocks and reads all of W_down, where the gather reads only
+ *                     the rows in use).  With few tokens the mfma kernel splits the tiles
+ *                     over more workgroups and adds the parts' fp32 sums in a fixed order.
  *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA: always that kernel (tiles and mfma
  *                     fall back as above when the layer does not support them).
  * All accumulate in fp32; they differ only in summation order.  Host only; the setting
@@ -205,7 +206,7 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
 #define SFFN_DOWN_GATHER_DENSITY_DEFAULT 0.0005f
 #define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
 #define SFFN_DOWN_TILES_MIN_T 4096
-#define SFFN_DOWN_MFMA_MIN_T 1024
+#define SFFN_DOWN_MFMA_MIN_T 64
 sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float gather_density,
                                          float mfma_density);
 

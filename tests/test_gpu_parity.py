@@ -235,9 +235,9 @@ def test_down_auto_policy_choice():
         else:
             assert launched == {k: int(k == expect) for k in launched}, launched
     sffn.profile_reset()
-    # a short activation (the first 1000 tokens): the tiles range goes to the gather kernel,
+    # a short activation (the first 48 tokens): the tiles range goes to the gather kernel,
     # and below DOWN_MFMA_MIN_T the matrix-core range too
-    Ts = 1000
+    Ts = 48
     assert Ts < sffn.DOWN_MFMA_MIN_T
     cfg_s = _cfg(sffn, Ts, D, F, K, W, "bf16")
     layer_s = sffn.SparseFFN(cfg_s, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
