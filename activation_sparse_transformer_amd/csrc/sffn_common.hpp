@@ -46,13 +46,14 @@ constexpr int UP_SMALL_T = 32;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-// Split of the matrix-core down-projection over its tiles: with fewer than 256 workgroups of
-// (256 tokens, 256 columns) the tile range is cut into S parts (at most DM_MAX_SPLIT, each at
-// least two tiles), each part's fp32 sums go to dpart and a second kernel adds them in order.
+// Split of the matrix-core down-projection over its tiles: when its workgroups of (256
+// tokens, 256 columns) would fill at most half of the 256 CUs, the tile range is cut into S
+// parts (at most DM_MAX_SPLIT, each at least two tiles), each part's fp32 sums go to dpart
+// and a second kernel adds them in order.
 constexpr int DM_MAX_SPLIT = 16;
 inline int down_split_for(int T, int D, int nt) {
   const long long base = (long long)((T + 255) / 256) * ((D + 255) / 256);
-  if (base >= 256) return 1;
+  if (base > 128) return 1;
   int S = (int)((256 + base - 1) / base);
   S = S < DM_MAX_SPLIT ? S : DM_MAX_SPLIT;
   S = S < nt / 2 ? S : nt / 2;
