@@ -1,13 +1,14 @@
-// Up-projection + bias + ReLU for decode-shaped batches (at most 32 tokens), bf16 layers.
+// Up-projection + bias + ReLU for decode-shaped batches (at most 128 tokens), bf16 layers.
 //
 // With a handful of tokens the layer is bound by reading W_up (upppp.jp TwELL article of
 // 2026-05-11, section "What TwELL and the custom CUDA kernels solve": inference throughput
 // of the sparse FFN), and the 256-neuron workgroups of the fused kernel would leave most
 // CUs idle.  Here a workgroup owns 32 neurons (F/32 workgroups: 256 at d_ff 8192) and all
-// tokens; its 4 waves split d_model into quarters and each runs v_mfma_f32_32x32x16_bf16
-// with A = its 32 W_up rows and B = the token rows, both loaded straight from memory as
-// 16-byte pieces (lane l: row l % 32, columns 8 (l / 32) .. + 7 of each 16-column step).
-// The four partial 32 x 32 sums are added in LDS in a fixed order, the bias is added and
+// tokens, as NTB blocks of 32; its 4 waves split d_model into quarters and each runs
+// v_mfma_f32_32x32x16_bf16 with A = its 32 W_up rows (loaded once per step, used for every
+// token block) and B = the token rows, both loaded straight from memory as 16-byte pieces
+// (lane l: row l % 32, columns 8 (l / 32) .. + 7 of each 16-column step).  Per token block
+// the four partial 32 x 32 sums are added in LDS in a fixed order, the bias is added and
 // h = max(z, 0) is written as fp32 [T, F] for the TwELL pack kernel (the same packing the
 // standalone twell_pack performs); tokens past T are computed from a repeated row and not
 // written.
@@ -20,6 +21,7 @@ typedef float floatx16_s __attribute__((ext_vector_type(16)));
 
 constexpr int US_NB = 32;  // neurons per workgroup
 
+template <int NTB>
 __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ Wu,
                                                        const uint16_t* __restrict__ bu,
@@ -37,35 +39,54 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
   const int nks = D / 16;                          // 16-column steps (D % 16 == 0)
   const int ks0 = wave * nks / 4, ks1 = (wave + 1) * nks / 4;
   const uint16_t* wrow = Wu + (size_t)(n0 + r) * D + 8 * hh;
-  const uint16_t* xrow = x + (size_t)(r < T ? r : 0) * D + 8 * hh;
+  const uint16_t* xrow[NTB];
+#pragma unroll
+  for (int tb = 0; tb < NTB; ++tb) {
+    const int t = 32 * tb + r;
+    xrow[tb] = x + (size_t)(t < T ? t : T - 1) * D + 8 * hh;
+  }
 
-  floatx16_s acc;
+  floatx16_s acc[NTB];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[tb][e] = 0.0f;
+  constexpr int ST = NTB == 1 ? 8 : 4;  // steps whose loads are in flight together
   int ks = ks0;
-  for (; ks + 8 <= ks1; ks += 8) {  // eight steps' loads in flight, then their MFMAs
-    bf16x8_s a[8], b[8];
+  for (; ks + ST <= ks1; ks += ST) {
+    bf16x8_s a[ST], b[ST][NTB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < ST; ++u) {
       a[u] = *reinterpret_cast<const bf16x8_s*>(wrow + (ks + u) * 16);
-      b[u] = *reinterpret_cast<const bf16x8_s*>(xrow + (ks + u) * 16);
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        b[u][tb] = *reinterpret_cast<const bf16x8_s*>(xrow[tb] + (ks + u) * 16);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], acc, 0, 0, 0);
+    for (int u = 0; u < ST; ++u)
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb)
+        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u][tb], acc[tb], 0, 0, 0);
   }
   for (; ks < ks1; ++ks) {
     const bf16x8_s a = *reinterpret_cast<const bf16x8_s*>(wrow + ks * 16);
-    const bf16x8_s b = *reinterpret_cast<const bf16x8_s*>(xrow + ks * 16);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+      const bf16x8_s b = *reinterpret_cast<const bf16x8_s*>(xrow[tb] + ks * 16);
+      acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[tb], 0, 0, 0);
+    }
   }
 
-  // sum the four quarters in a fixed order; element e of lane l is neuron 8(e/4) + 4(l/32)
-  // + e%4 of the block and token l % 32
+  // per token block: sum the four quarters in a fixed order; element e of lane l is neuron
+  // 8(e/4) + 4(l/32) + e%4 of the block and token l % 32 of the token block
 #pragma unroll
-  for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[e];
-  __syncthreads();
-  if (wave == 0) {
-    const int t = r;
+  for (int tb = 0; tb < NTB; ++tb) {
+    if (tb > 0) __syncthreads();  // wave 0 has read the previous block's sums
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[tb][e];
+    __syncthreads();
+    if (wave != 0) continue;
+    const int t = 32 * tb + r;
     float z[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e)
@@ -96,13 +117,19 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
 bool up_small_supported(const Dims& d) {
   return d.bf16 && d.T <= UP_SMALL_T && d.D % 16 == 0 && d.F % US_NB == 0;
 }
+static_assert(UP_SMALL_T <= 128, "at most four 32-token blocks per workgroup");
 
 hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                            const uint16_t* bu, float* h, float* zdump, int32_t* claim,
                            hipStream_t s) {
   if (!up_small_supported(d)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(up_small_kernel, dim3(d.F / US_NB), dim3(256), 0, s, d, x, Wu, bu, h,
-                     zdump, claim);
+  const dim3 grid(d.F / US_NB), block(256);
+  if (d.T <= 32)
+    hipLaunchKernelGGL(up_small_kernel<1>, grid, block, 0, s, d, x, Wu, bu, h, zdump, claim);
+  else if (d.T <= 64)
+    hipLaunchKernelGGL(up_small_kernel<2>, grid, block, 0, s, d, x, Wu, bu, h, zdump, claim);
+  else
+    hipLaunchKernelGGL(up_small_kernel<4>, grid, block, 0, s, d, x, Wu, bu, h, zdump, claim);
   return hipGetLastError();
 }
 

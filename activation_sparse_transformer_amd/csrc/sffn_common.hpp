@@ -42,7 +42,7 @@ struct Workspace {
 
 // Batches of at most this many tokens take the decode-shaped up-projection (one workgroup
 // per 32 neurons, then the TwELL pack kernel) instead of the fused up + pack kernel.
-constexpr int UP_SMALL_T = 32;
+constexpr int UP_SMALL_T = 128;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 

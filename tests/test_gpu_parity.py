@@ -326,8 +326,10 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     ("C1", None, None), ("C1b", None, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
     ("C4", 300, None),
-    # decode-shaped batches (at most 32 tokens: the small-batch up-projection + pack path)
+    # decode-shaped batches (at most 128 tokens: the small-batch up-projection + pack path,
+    # one to four 32-token blocks per workgroup, the last one ragged)
     ("C3", 1, 0.05), ("C3", 7, 0.01), ("C3", 32, 0.05), ("C2", 3, None), ("C4", 5, None),
+    ("C3", 64, 0.05), ("C3", 100, 0.05), ("C2", 128, None), ("C4", 97, None),
 ])
 def test_forward_parity(name, T, rho, policy):
     torch, sffn = need_gpu()
