@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   constexpr int WN = DM_BN / NWC;      // output columns per wave
   constexpr int NJ = WN / 32;          // 32-column MFMA blocks per wave
   constexpr int UL = RW * U / 64;      // 8-slot units per lane
-  static_assert(RW * U % 64 == 0 && RW <= 64, "units must fill whole waves");
+  static_assert(RW == 32 && U % 2 == 0, "a lane owns one row's slot groups l/32, l/32 + 2, ..");
   // A buffers, then 256 B holding the dummy word that padding writes go to; all A writes
   // address this one array, so the compiler sees they never touch the B buffers filled by
   // direct loads (and need not wait for those)
@@ -131,8 +131,10 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
     }
   };
 
-  // ---- TwELL units of tile k for this wave's rows: unit u = lane + 64 j holds slots
-  // 8*(u % U) .. +7 of token tw + u / U.  cnt = count of token tw + lane (lanes < RW).
+  // ---- TwELL units of tile k for this wave's rows: unit j of lane l holds slots 8 g .. +7,
+  // g = l / 32 + 2 j, of token tw + l % 32 (a lane's row is the same for all its units; the
+  // wider ELL widths then need no register spills).  cnt = count of token tw + lane (lanes
+  // < RW).
   uint4 uv[UL];
   uint2 uc[UL];
   uint32_t cnt = 0;
@@ -142,11 +144,10 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
     const size_t row_base = (size_t)k * T;
 #pragma unroll
     for (int j = 0; j < UL; ++j) {
-      const int u = lane + 64 * j;
-      const int tok = tw + u / U;
+      const int tok = tw + (lane & 31);
       const int tk = tok < T ? tok : T - 1;
       const uint32_t m = tok < T ? 0xFFFFFFFFu : 0u;
-      const size_t e0 = (row_base + tk) * W + 8 * (u % U);
+      const size_t e0 = (row_base + tk) * W + 8 * ((lane >> 5) + 2 * j);
       const uint4 v = *reinterpret_cast<const uint4*>(vals + e0);
       uv[j] = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
       uc[j] = *reinterpret_cast<const uint2*>(cols + e0);
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
 #pragma unroll
     for (int j = 0; j < UL; ++j) {
       if ((4 * j) / UL != part) continue;
-      const uint32_t r = (uint32_t)(lane + 64 * j) / U;
+      const uint32_t r = (uint32_t)(lane & 31);
       const uint32_t vv[4] = {uv[j].x, uv[j].y, uv[j].z, uv[j].w};
       const uint32_t cw[2] = {uc[j].x, uc[j].y};
 #pragma unroll
