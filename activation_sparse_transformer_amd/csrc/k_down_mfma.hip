@@ -164,17 +164,18 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
     return buf * ABUF + (wave * RW + r) * AROW + ((cc ^ (((r >> 1) & 7) << 3)) << 1);
   };
 
-  // ---- write step c (of the tile) of the units into A buffer `buf`; the units are split
-  // into four parts (unit j in part 4j/UL) so the writes spread over the four MFMA k-steps
+  // ---- write step c (of the tile) of the units into A buffer `buf`; the 8 UL slots of a
+  // lane are split evenly into four parts (slot q = 8j + e in part 4q / (8 UL)) so the
+  // writes spread over the four MFMA k-steps
   auto build_part = [&](int part, int c, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < UL; ++j) {
-      if ((4 * j) / UL != part) continue;
       const uint32_t r = (uint32_t)(lane & 31);
       const uint32_t vv[4] = {uv[j].x, uv[j].y, uv[j].z, uv[j].w};
       const uint32_t cw[2] = {uc[j].x, uc[j].y};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        if ((4 * (8 * j + e)) / (8 * UL) != part) continue;
         const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
         const uint32_t word = vv[e >> 1];
         const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
