@@ -371,9 +371,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto h_off = [&](int buf, uint32_t r, uint32_t hc) __attribute__((always_inline)) -> uint32_t {
     return buf * HBUF + r * HROW + ((((hc >> 3) ^ (4 * (r & 3))) << 4) | ((hc & 7) << 1));
   };
-  auto build = [&](int ts, int buf) __attribute__((always_inline)) {
-    // clear this wave's segments (4 KB): piece i of the wave is piece i % (SEGB/16) of
-    // segment i / (SEGB/16)
+  // the H block of step ts is built in three pieces spread over the MFMAs of the step before:
+  // clear_h (this wave's segments), build_part (its slots, split evenly over the k-steps:
+  // slot q = 8 unit + e in part 4q / (8 NU)) and build_bk (its backup slices)
+  auto clear_h = [&](int buf) __attribute__((always_inline)) {
+    // this wave's segments (4 KB): piece i of the wave is piece i % (SEGB/16) of segment
+    // i / (SEGB/16)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int pi = lane + 64 * q;
@@ -382,6 +385,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                           pc * 16);
       *p = make_uint4(0, 0, 0, 0);
     }
+  };
+  auto build_part = [&](int part, int ts, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       const int v = lane + 64 * q;
@@ -391,6 +396,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint32_t cw[2] = {uc[q].x, uc[q].y};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        if ((4 * (8 * q + e)) / (8 * NU) != part) continue;
         const uint32_t col = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
         const uint32_t word = vv[e >> 1];
         const bool nz = (e & 1) ? (word > 0xFFFFu) : ((word & 0xFFFFu) != 0u);
@@ -398,6 +404,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         *reinterpret_cast<uint16_t*>(sH + a) = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
       }
     }
+  };
+  auto build_bk = [&](int ts, int buf) __attribute__((always_inline)) {
     // backup slices of the overflowing rows among this wave's segments; entry = first entry
     // of the row's (tile, 32-token group) + its rank among the group's overflowing rows
     const uint64_t ov_all = ballot64(cnt > (uint32_t)W);  // token TS ts + lane
@@ -462,8 +470,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nts = (T + TS - 1) / TS;
   issue_M(0, sM0);
   load_units(0);
-  build(0, 0);
-  if (nts > 1) load_units(1);
+  clear_h(0);
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) build_part(pt, 0, 0);
+  build_bk(0, 0);
+  load_units(nts > 1 ? 1 : 0);
   auto step = [&](int ts, int cb, unsigned char* sMc, unsigned char* sMn) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): M(ts) and the units have landed
     __syncthreads();                     // H(ts), M(ts) complete; step ts-1's buffers free
@@ -475,22 +486,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = tr_frag(sMc, MROW, 128 * wd + 32 * j, kk);
     };
+    // the next step's tiles while these MFMAs run; the last step rebuilds its own tiles into
+    // the other buffers, which nothing reads any more, instead of branching, so each k-step's
+    // MFMAs and build share one basic block
+    const int tn = ts + 1 < nts ? ts + 1 : nts - 1;
     load_frags(0, fa[0], fb[0]);
-    if (ts + 1 < nts) {  // next step's tiles while these MFMAs run
-      issue_M(ts + 1, sMn);
-      build(ts + 1, cb ^ 1);
-      if (ts + 2 < nts) load_units(ts + 2);
-    }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       if (kk + 1 < NKK) load_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (kk == 0) {
+        issue_M(tn, sMn);
+        clear_h(cb ^ 1);
+      }
+      build_part(kk, tn, cb ^ 1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                               acc[i][j], 0, 0, 0);
-      if (do_db) {
+      if constexpr (DB) {  // every wave sums; only the db waves store (no branch here)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           float s = 0.0f;
@@ -499,12 +514,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           dbacc[i] += s;
         }
       }
+      // one MFMA, then a few vector and LDS instructions in its shadow
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x080, 2, 0);  // LDS
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    build_bk(tn, cb ^ 1);
+    load_units(ts + 2 < nts ? ts + 2 : nts - 1);
   };
   for (int ts = 0; ts < nts; ts += 2) {
     step(ts, 0, sM0, sM1);
     if (ts + 1 < nts) step(ts + 1, 1, sM1, sM0);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last step's repeated loads land before LDS goes away
 
   // ---- dW (fp32): C[m = j][n = d]; lane: column l32, rows 8(r/4) + 4lh + r%4
 #pragma unroll
