@@ -5,7 +5,7 @@ The compute lives in ``libsparse_ffn.so`` (hand-written HIP kernels behind a C A
 """
 from .sparse_ffn import (  # noqa: F401
     Config, SparseFFN, TwellBuffers, SffnError, twell_pack, twell_stats, check, buffer_sizes,
-    profile_enable, profile_reset, profile_read, lib, LIB_PATH,
+    profile_enable, profile_only, profile_reset, profile_read, lib, LIB_PATH,
     SFFN_OK, SFFN_ERR_INVALID_ARGUMENT, SFFN_ERR_UNSUPPORTED, SFFN_ERR_BACKUP_OVERFLOW,
     SFFN_ERR_DEVICE, DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES,
     DOWN_GATHER_DENSITY_DEFAULT, DOWN_MFMA_DENSITY_DEFAULT, DOWN_TILES_MIN_T, DOWN_MFMA_MIN_T,

@@ -50,7 +50,15 @@ struct ProfRec {
 };
 struct Prof {
   bool enabled = false;
+  std::vector<std::string> only;  // names to time (empty: all)
   std::vector<ProfRec> recs;
+  bool times(const char* name) const {
+    if (!enabled) return false;
+    if (only.empty()) return true;
+    for (auto& n : only)
+      if (n == name) return true;
+    return false;
+  }
   ~Prof() { clear(); }
   void clear() {
     for (auto& r : recs) {
@@ -66,13 +74,14 @@ thread_local Prof g_prof;
 template <typename Fn>
 sffn_status_t run(const char* name, hipStream_t s, Fn&& f) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (g_prof.enabled) {
+  const bool timed = g_prof.times(name);
+  if (timed) {
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess ||
         hipEventRecord(e0, s) != hipSuccess)
       return dev_fail(hipGetLastError(), "profiling event");
   }
   const hipError_t err = f();
-  if (g_prof.enabled) {
+  if (timed) {
     (void)hipEventRecord(e1, s);
     g_prof.recs.push_back({name, e0, e1});
   }
@@ -431,6 +440,22 @@ sffn_status_t sparse_ffn_check(const twell_buffers_t* buf, void* stream) {
 
 sffn_status_t sffn_profile_enable(int32_t enable) {
   g_prof.enabled = enable != 0;
+  return SFFN_OK;
+}
+
+sffn_status_t sffn_profile_only(const char* names) {
+  g_prof.only.clear();
+  if (!names) return SFFN_OK;
+  std::string cur;
+  for (const char* p = names;; ++p) {
+    if (*p == ',' || *p == '\0') {
+      if (!cur.empty()) g_prof.only.push_back(cur);
+      cur.clear();
+      if (*p == '\0') break;
+    } else {
+      cur += *p;
+    }
+  }
   return SFFN_OK;
 }
 

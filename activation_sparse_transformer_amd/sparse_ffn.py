@@ -87,6 +87,7 @@ _PROTOS = {
     "sparse_ffn_check": ([ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_forward_dump": ([_P, _P, _I32, _P, ctypes.POINTER(BuffersC), _P, _P], ctypes.c_int),
     "sffn_profile_enable": ([_I32], ctypes.c_int),
+    "sffn_profile_only": ([ctypes.c_char_p], ctypes.c_int),
     "sffn_profile_reset": ([], ctypes.c_int),
     "sffn_profile_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
@@ -353,6 +354,12 @@ class SparseFFN:
 
 def profile_enable(on: bool = True):
     _check(lib().sffn_profile_enable(1 if on else 0), "sffn_profile_enable")
+
+
+def profile_only(names=None):
+    """Time only the named kernels while profiling is enabled (None: all of them)."""
+    arg = ",".join(names).encode() if names else None
+    _check(lib().sffn_profile_only(arg), "sffn_profile_only")
 
 
 def profile_reset():

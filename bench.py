@@ -169,7 +169,7 @@ def main():
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
-    def sparse_point(rho, steps, warmup, profile=False):
+    def sparse_point(rho, steps, warmup, profile=False, only=None):
         L = bias_for_density(L0, rho)
         b = bf16_dev(L["b_up"])
         layer = sffn.SparseFFN(cfg, Wu, b, Wd)
@@ -179,27 +179,35 @@ def main():
         torch.cuda.synchronize()
         if profile:
             sffn.profile_reset()
+            sffn.profile_only(only)
             sffn.profile_enable(True)
         ms, wall = time_steps(fn, steps, 0)
         kt = {}
         if profile:
             sffn.profile_enable(False)
-            for k in KERNELS:
+            for k in (only or KERNELS):
                 tot, n = sffn.profile_read(k)
                 kt[k] = tot / max(n, 1)
             sffn.profile_reset()
+            sffn.profile_only(None)
         st = sffn.twell_stats(cfg, act)
         return ms, wall, kt, st, b
 
-    # ---- headline point (timed region, per-kernel HIP events on the launch stream)
+    # ---- headline point: the timed region brackets the up kernel and the down kernels (the
+    # roofline's candidates) with HIP events on the launch stream; the small kernels' times
+    # come from a separate pass that times every launch
     log(f"sparse forward, rho={args.rho}, {args.warmup} warmup + {args.steps} timed steps")
-    ms, wall, kt, st, b0 = sparse_point(args.rho, args.steps, args.warmup, profile=True)
+    down_names = ("down", "down_tiles", "down_mfma")
+    timed_names = ("up_pack",) + down_names
+    ms, wall, kt, st, b0 = sparse_point(args.rho, args.steps, args.warmup, profile=True,
+                                        only=timed_names)
     ms_plain, _, _, _, _ = sparse_point(args.rho, args.steps, 2, profile=False)
+    _, _, kt_all, _, _ = sparse_point(args.rho, max(10, args.steps // 5), 2, profile=True)
+    kt = {**kt_all, **kt}
     log(f"  {ms:.4f} ms/step (profiled), {ms_plain:.4f} ms/step (no events); kernels {kt}")
 
     # ---- which down-projection kernel took the layer: under the auto policy all candidates
     # are launched and all but one return at once (a few microseconds)
-    down_names = ("down", "down_tiles", "down_mfma")
     down_ran = max(down_names, key=lambda k: kt.get(k, 0.0))
     nnz = st["nnz"]
 

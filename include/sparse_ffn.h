@@ -229,6 +229,9 @@ sffn_status_t sparse_ffn_forward_dump(sparse_ffn_t h, const void *x, int32_t T, 
  * events and returns, for a kernel name ("up_pack", "down", "pack", "order", ...), the
  * summed duration in ms and the number of launches since the last reset. */
 sffn_status_t sffn_profile_enable(int32_t enable);
+/* Restrict the timing to the kernels named in `names` (comma-separated, e.g. "up_pack,down");
+ * NULL or "" times every launch again.  Fewer events perturb the timed stream less. */
+sffn_status_t sffn_profile_only(const char *names);
 sffn_status_t sffn_profile_reset(void);
 sffn_status_t sffn_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 

@@ -155,6 +155,8 @@ def test_profile_counters_host_only(sffn):
     sffn.profile_reset()
     ms, n = sffn.profile_read("up_pack")
     assert ms == 0.0 and n == 0
+    sffn.profile_only(["up_pack", "down_mfma"])
+    sffn.profile_only(None)
     sffn.profile_enable(False)
 
 
