@@ -29,9 +29,12 @@
 //     at the start of the next, before its barrier; their first entry comes from the
 //     per-(tile, 32-token group) offsets of the ordering pass.  The barrier at the top of
 //     each step publishes the A and B buffers.
+// With few workgroups (small T) the tile range is split into S parts, one per workgroup
+// group; each part's fp32 sums go to the workspace and down_reduce_kernel adds the parts in
+// order into y.
 // When the layer's stored-nonzero count (the sum of the per-block counts) is at most `thr`
-// the gather kernel takes the layer and every workgroup here returns at once
-// (blk_nnz == nullptr: this kernel runs).
+// the gather kernel takes the layer and every workgroup here (and the reduce) returns at
+// once (blk_nnz == nullptr: this kernel runs).
 #include <algorithm>
 
 #include "sffn_common.hpp"
