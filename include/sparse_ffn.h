@@ -79,13 +79,16 @@ typedef struct {
   int32_t *bk_tile_ptr;  /* [n_t + 1] entries of tile k are e in [ptr[k], ptr[k+1]) */
   int32_t *bk_n;         /* [1] backup entries needed (may exceed the capacity) */
   int32_t *status;       /* [1] device status word: 0, or SFFN_ERR_BACKUP_OVERFLOW */
-  void *workspace;       /* scratch: unordered backup staging, per-group and per-block counters */
+  void *workspace;       /* scratch: unordered backup staging, per-group, per-tile and per-block
+                            counters, the first canonical backup entry of every (tile, group)
+                            (read by sparse_ffn_down and sparse_ffn_backward: keep it with its
+                            TwELL), and fp32 partial sums of the small-batch paths */
 } twell_buffers_t;
 
 /* Byte sizes of each field of twell_buffers_t for T tokens.  Each buffer must be at
  * least this large and 256-byte aligned (torch allocations are).  counts, vals and cols
  * hold 32 tile-rows of padding after [n_t, T(, W)] (read by whole-group and whole-word
- * loads, never used). */
+ * loads, never used).  Buffers sized for T serve any call with fewer tokens. */
 typedef struct {
   size_t counts, vals, cols, bk_tile, bk_tok, bk_vals, bk_tile_ptr, bk_n, status, workspace;
 } twell_buffer_sizes_t;
