@@ -170,12 +170,15 @@ def _ptr(t) -> ctypes.c_void_p:
 
 
 class TwellBuffers:
-    """Device buffers (torch uint8 tensors) of one packed activation of T tokens."""
+    """Device buffers (torch uint8 tensors) of one packed activation.  They are sized for
+    `capacity` tokens and serve any call with fewer; `T` is the token count of the
+    activation they hold (set by the call that packs into them)."""
 
     def __init__(self, cfg: Config, T: int, device="cuda"):
         import torch
         self.cfg = cfg
         self.T = int(T)
+        self.capacity = self.T
         self.sizes = buffer_sizes(cfg, self.T)
         self.t = {n: torch.empty(max(sz, 1), dtype=torch.uint8, device=device)
                   for n, sz in self.sizes.items()}
@@ -183,6 +186,14 @@ class TwellBuffers:
 
     def c(self) -> BuffersC:
         return self._c
+
+    def _hold(self, cfg: Config, T: int):
+        """Checks that these buffers can take a call of T tokens of layer cfg; records T."""
+        if self.cfg != cfg:
+            raise ValueError("TwELL buffers were sized for another layer configuration")
+        if not 1 <= T <= self.capacity:
+            raise ValueError(f"TwELL buffers hold at most {self.capacity} tokens, not {T}")
+        self.T = int(T)
 
     # ---- host copies (for tests and statistics; synchronous)
     def _np(self, name, dtype):
@@ -214,6 +225,7 @@ def twell_pack(cfg: Config, h, out: Optional[TwellBuffers] = None, stream=None) 
     assert h.dtype == torch.float32 and h.is_contiguous() and h.is_cuda
     T = h.shape[0]
     buf = out if out is not None else TwellBuffers(cfg, T, device=h.device)
+    buf._hold(cfg, T)
     c = cfg.c()
     _check(lib().twell_pack(ctypes.byref(c), _ptr(h), int(T), ctypes.byref(buf.c()),
                             _stream_ptr(stream)), "twell_pack")
@@ -278,6 +290,7 @@ class SparseFFN:
         self._check_x(x)
         T = x.shape[0]
         act = act if act is not None else TwellBuffers(self.cfg, T, device=x.device)
+        act._hold(self.cfg, T)
         y = y if y is not None else torch.empty_like(x)
         _check(lib().sparse_ffn_forward(self._h, _ptr(x), int(T), _ptr(y), ctypes.byref(act.c()),
                                         _stream_ptr(stream)), "sparse_ffn_forward")

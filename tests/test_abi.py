@@ -168,3 +168,23 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower().replace("oracle_", ""), f
+
+
+@pytest.mark.parametrize("D,F,K,W,dtype", [
+    (2048, 8192, 128, 32, "bf16"), (1024, 4096, 64, 16, "bf16"), (4096, 16384, 256, 64, "bf16"),
+    (256, 1024, 128, 32, "f32")])
+def test_buffer_sizes_monotone_in_T(sffn, D, F, K, W, dtype):
+    """Every field grows with T, so buffers sized for T serve every call with fewer tokens
+    (the split partial sums of the matrix-core down kernel and the small-batch up buffer
+    included, which are not monotone per call)."""
+    cfg = sffn.Config(d_model=D, d_ff=F, tile=K, ell_width=W, max_tokens=8192,
+                      backup_capacity=1024, dtype=dtype)
+    Ts = sorted(set(list(range(1, 300, 7)) + [128, 129, 255, 256, 257, 511, 512, 513, 1024,
+                                              2048, 2049, 4096, 8191, 8192]))
+    prev = None
+    for T in Ts:
+        s = sffn.buffer_sizes(cfg, T)
+        if prev is not None:
+            for k, v in s.items():
+                assert v >= prev[k], (k, T, v, prev[k])
+        prev = s

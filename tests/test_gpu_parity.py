@@ -394,6 +394,39 @@ def test_determinism_and_homogeneity():
     assert torch.equal(yp.view(torch.int16), y1[perm].view(torch.int16))
 
 
+
+def test_forward_buffers_reused_for_fewer_tokens():
+    """One set of buffers sized for 300 tokens serves calls of 300, 100, 32, 257 and 1
+    tokens in a row (the fused and the small-batch up paths, split and unsplit down
+    kernels): each call's y and TwELL equal those of fresh buffers bit for bit, so no kernel
+    depends on what an earlier, larger call left in the buffers or the workspace."""
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C3"], seed=0, T=300, rho=0.05)
+    c = L["cfg"]
+    cfg = _cfg(sffn, 300, c.D, c.F, c.tile, c.ell_width, c.dtype)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    act = sffn.TwellBuffers(cfg, 300)
+    keys = ("counts", "vals", "cols", "bk_tile", "bk_tok", "bk_vals", "bk_tile_ptr")
+    for T in (300, 100, 32, 257, 1):
+        print(f"[reuse] T={T}", flush=True)
+        xs = x[:T].contiguous()
+        y, a = layer.forward(xs, act=act)
+        assert a is act and act.T == T and act.capacity == 300
+        y_ref, a_ref = layer.forward(xs)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), T
+        h, hr = act.to_host(), a_ref.to_host()
+        for k in keys:
+            assert np.array_equal(h[k].view(np.uint8), hr[k].view(np.uint8)), (T, k)
+        assert h["bk_n"] == hr["bk_n"] and h["status"] == hr["status"] == 0
+        assert sffn.twell_stats(cfg, act)["nnz"] == sffn.twell_stats(cfg, a_ref)["nnz"]
+        yd = layer.down(act)
+        assert torch.equal(yd.view(torch.int16), y_ref.view(torch.int16)), T
+    with pytest.raises(ValueError):
+        layer.forward(x[:1].repeat(301, 1).contiguous(), act=act)
+
+
 def _decode_rows(cfg, host, rows):
     """Dense [len(rows), F] of selected tokens of a device TwELL."""
     K, W, nt = cfg.tile, cfg.ell_width, cfg.n_tiles
@@ -460,3 +493,32 @@ def test_forward_full_size_sampled(name, rho, policy):
     assert np.array_equal((hg != 0)[certain], (z_r > 0)[certain])
     nzc = certain & (z_r > 0)
     assert np.all(np.abs(hg[nzc] - z_r[nzc]) <= (np.abs(z_r[nzc]) * 2.0 ** -8 + band[nzc]) * 1.0001)
+
+
+def test_profile_only_times_named_kernels():
+    """With a name list only those launches are timed and counted; without, all are."""
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C3"], seed=0, T=300, rho=0.05)
+    c = L["cfg"]
+    cfg = _cfg(sffn, 300, c.D, c.F, c.tile, c.ell_width, c.dtype)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    # auto at 300 tokens: block_nnz, then the gather and matrix-core kernels (one returns)
+    names = ("up_pack", "order", "block_nnz", "down", "down_mfma")
+    try:
+        sffn.profile_reset()
+        sffn.profile_enable(True)
+        sffn.profile_only(["up_pack", "down_mfma"])
+        layer.forward(x)
+        got = {n: sffn.profile_read(n) for n in names}
+        assert got["up_pack"][1] == 1 and got["down_mfma"][1] == 1, got
+        assert got["up_pack"][0] > 0 and got["down_mfma"][0] > 0, got
+        assert got["order"][1] == got["block_nnz"][1] == got["down"][1] == 0, got
+        sffn.profile_only(None)
+        sffn.profile_reset()
+        layer.forward(x)
+        assert all(sffn.profile_read(n)[1] == 1 for n in names)
+    finally:
+        sffn.profile_enable(False)
+        sffn.profile_only(None)
+        sffn.profile_reset()
