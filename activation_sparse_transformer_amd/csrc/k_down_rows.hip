@@ -10,57 +10,72 @@
 // work does not depend on the density) takes dense layers.
 //
 // One workgroup per token at a time (NW waves; for few tokens NW = 16 and the workgroups of a
-// token also split its columns into 512-wide chunks, so a short batch still spreads over
-// many CUs); wave w takes a contiguous 1/NW of the tiles, lane l of it tile k = k0 + l: its
+// token also split its columns into 256- or 512-wide chunks, so a short batch still spreads
+// over many CUs); wave w takes a contiguous 1/NW of the tiles, lane l of it tile k = k0 + l: its
 // count, then its slots 8 at a time (16 B values + 8 B columns).  The
 // (row, value) pairs of the lanes are broadcast with readlane in batches of up to 8 (4 for
 // d_model > 2048) whose
 // W_down row loads are all issued before any is used, so a token with many nonzeros (heavy
 // tokens run at 10-20x the mean density) is not a chain of single-row latencies.  Lane L owns
-// output columns c0 + 512q + 8L (q < NQ; c0 = the workgroup's column chunk): every row is
-// read as NQ coalesced 1 KB wave loads.  The waves' partial rows are summed in LDS and y is
-// written as 16-byte stores.
+// the EPL output columns c0 + 64 EPL q + EPL L (q < NQ; c0 = the workgroup's column chunk;
+// EPL = 8, or 4 for the 256-column chunks): every row is read as NQ coalesced wave loads of
+// 128 EPL bytes.  The waves' partial rows are summed in LDS and y is written as 4 EPL-byte
+// stores.
 #include "sffn_common.hpp"
 
 namespace sffn {
 
-template <int NQ, int ROWS_WAVES>
+template <int NQ, int ROWS_WAVES, int EPL = 8>
 __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
     uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr) {
+  static_assert(EPL == 8 || EPL == 4 || EPL == 2, "8, 4 or 2 output columns per lane");
+  constexpr int CW = 64 * EPL;                 // columns of one wave load of a row
   constexpr int ROWS_BATCH = NQ <= 4 ? 8 : 4;  // rows in flight per wave (registers: 4*NQ each)
-  __shared__ __attribute__((aligned(16))) float part[ROWS_WAVES - 1][NQ * 512];
+  __shared__ __attribute__((aligned(16))) float part[ROWS_WAVES - 1][NQ * CW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int T = d.T, D = d.D, K = d.K, W = d.W;
-  const int cb = blockIdx.y * NQ * 512;  // first output column of this workgroup
+  const int cb = blockIdx.y * NQ * CW;  // first output column of this workgroup
   // the layer goes to this kernel only when its stored-nonzero count is at most thr
   if (blk_nnz != nullptr && layer_nnz(blk_nnz, (T + 255) / 256) > thr) return;
   for (int t = blockIdx.x; t < T; t += gridDim.x) {  // workgroup-uniform token loop
-  float acc[NQ][8];
+  float acc[NQ][EPL];
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[q][e] = 0.0f;
+    for (int e = 0; e < EPL; ++e) acc[q][e] = 0.0f;
 
   // a batch of up to ROWS_BATCH (row, value) pairs: loads first, then the FMAs
   int bj[ROWS_BATCH];
   float bv[ROWS_BATCH];
   int nb = 0;
   auto flush = [&]() __attribute__((always_inline)) {
-    uint4 w[ROWS_BATCH][NQ];
+    uint32_t w[ROWS_BATCH][NQ][EPL / 2];  // EPL bf16 of the row per lane and chunk
 #pragma unroll
     for (int i = 0; i < ROWS_BATCH; ++i) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) w[i][q] = make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < EPL / 2; ++e) w[i][q][e] = 0u;
       if (i < nb) {  // wave-uniform
         const uint16_t* wr = Wd + (size_t)bj[i] * D;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-          const int c0 = cb + 512 * q + 8 * lane;
-          if (c0 < D) w[i][q] = *reinterpret_cast<const uint4*>(wr + c0);
+          const int c0 = cb + CW * q + EPL * lane;
+          if (c0 < D) {
+            if constexpr (EPL == 8) {
+              const uint4 u = *reinterpret_cast<const uint4*>(wr + c0);
+              w[i][q][0] = u.x, w[i][q][1] = u.y, w[i][q][2] = u.z, w[i][q][3] = u.w;
+            } else if constexpr (EPL == 4) {
+              const uint2 u = *reinterpret_cast<const uint2*>(wr + c0);
+              w[i][q][0] = u.x, w[i][q][1] = u.y;
+            } else {
+              w[i][q][0] = *reinterpret_cast<const uint32_t*>(wr + c0);
+            }
+          }
         }
       }
     }
@@ -69,9 +84,9 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
       const float v = i < nb ? bv[i] : 0.0f;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const uint32_t ww[4] = {w[i][q].x, w[i][q].y, w[i][q].z, w[i][q].w};
+        const uint32_t* ww = w[i][q];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < EPL / 2; ++e) {
           acc[q][2 * e] = fmaf(v, __uint_as_float(ww[e] << 16), acc[q][2 * e]);
           acc[q][2 * e + 1] = fmaf(v, __uint_as_float(ww[e] & 0xFFFF0000u), acc[q][2 * e + 1]);
         }
@@ -149,30 +164,35 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   if (wave > 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      float4* p = reinterpret_cast<float4*>(&part[wave - 1][512 * q + 8 * lane]);
-      p[0] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-      p[1] = make_float4(acc[q][4], acc[q][5], acc[q][6], acc[q][7]);
+      float* p = &part[wave - 1][CW * q + EPL * lane];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p[e] = acc[q][e];
     }
   }
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int c0 = cb + 512 * q + 8 * lane;
+      const int c0 = cb + CW * q + EPL * lane;
       if (c0 < D) {
 #pragma unroll
         for (int w2 = 0; w2 < ROWS_WAVES - 1; ++w2) {
-          const float4* p = reinterpret_cast<const float4*>(&part[w2][512 * q + 8 * lane]);
-          const float4 a = p[0], c = p[1];
-          acc[q][0] += a.x; acc[q][1] += a.y; acc[q][2] += a.z; acc[q][3] += a.w;
-          acc[q][4] += c.x; acc[q][5] += c.y; acc[q][6] += c.z; acc[q][7] += c.w;
-        }
-        uint32_t o[4];
+          const float* p = &part[w2][CW * q + EPL * lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < EPL; ++e) acc[q][e] += p[e];
+        }
+        uint32_t o[EPL / 2];
+#pragma unroll
+        for (int e = 0; e < EPL / 2; ++e)
           o[e] = (uint32_t)f32_to_bf16(acc[q][2 * e]) |
                  ((uint32_t)f32_to_bf16(acc[q][2 * e + 1]) << 16);
-        *reinterpret_cast<uint4*>(y + (size_t)t * D + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+        uint16_t* yo = y + (size_t)t * D + c0;
+        if constexpr (EPL == 8)
+          *reinterpret_cast<uint4*>(yo) = make_uint4(o[0], o[1], o[2], o[3]);
+        else if constexpr (EPL == 4)
+          *reinterpret_cast<uint2*>(yo) = make_uint2(o[0], o[1]);
+        else
+          *reinterpret_cast<uint32_t*>(yo) = o[0];
       }
     }
   }
@@ -180,7 +200,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   }
 }
 
-// Few tokens: 16 waves per workgroup and one 512-column chunk per workgroup.
+// Few tokens: 16 waves per workgroup and one 256- or 512-column chunk per workgroup.
 constexpr int ROWS_FEW_T = 1024;
 
 bool down_rows_supported(const Dims& d) {
@@ -199,9 +219,17 @@ hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Works
   auto* w = static_cast<const uint16_t*>(Wd);
   auto* yy = static_cast<uint16_t*>(y);
   if (d.T < ROWS_FEW_T) {
-    const dim3 grid(d.T, (d.D + 511) / 512), block(64 * 16);
-    hipLaunchKernelGGL((down_rows_kernel<1, 16>), grid, block, 0, s, d, c, v, b.cols, bk,
-                       ws.grp_first, w, yy, blk_nnz, thr);
+    if (blk_nnz == nullptr) {
+      // the only down kernel of the call: 256-column chunks, twice the workgroups per token
+      const dim3 grid(d.T, (d.D + 255) / 256), block(64 * 16);
+      hipLaunchKernelGGL((down_rows_kernel<1, 16, 4>), grid, block, 0, s, d, c, v, b.cols, bk,
+                         ws.grp_first, w, yy, blk_nnz, thr);
+    } else {
+      // one candidate of the kernel choice: fewer workgroups to start when it returns at once
+      const dim3 grid(d.T, (d.D + 511) / 512), block(64 * 16);
+      hipLaunchKernelGGL((down_rows_kernel<1, 16, 8>), grid, block, 0, s, d, c, v, b.cols, bk,
+                         ws.grp_first, w, yy, blk_nnz, thr);
+    }
     return hipGetLastError();
   }
   const dim3 grid(d.T < 2048 ? d.T : 2048), block(64 * 4);

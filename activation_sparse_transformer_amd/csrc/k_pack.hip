@@ -413,11 +413,15 @@ __global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t
 // Few (tile, group) pairs (decode-shaped batches): one launch instead of two.  Every
 // workgroup scans the counts (one per thread, at most 1024) into LDS, the first one also
 // writes the scan's outputs, and the workgroups then share the moves of the staged entries.
+// With with_blk the last workgroup also writes the stored nonzeros of every 256-token block
+// (blk_nnz, read by the down-projection's kernel choice), which saves the forward pass that
+// launch.
 constexpr int ORDER_SMALL_N = 1024;
 constexpr int ORDER_SMALL_MAX_WG = 128;
 
 template <int K, bool BF16>
-__global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+__global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers_t b, Workspace ws,
+                                                           int with_blk) {
   __shared__ int wsum[16];
   __shared__ int first_s[ORDER_SMALL_N];
   const int tid = threadIdx.x;
@@ -448,6 +452,28 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
       *b.status = tot > d.cap ? (int)SFFN_ERR_BACKUP_OVERFLOW : 0;
     }
   }
+  if (with_blk && blockIdx.x == gridDim.x - 1) {
+    // thread i sums tiles i/256, i/256 + 4, ... of token i%256 of each block
+    for (int tb = 0; tb * 256 < d.T; ++tb) {
+      const int t = tb * 256 + (tid & 255);
+      int sum = 0;
+      if (t < d.T) {
+#pragma unroll 16
+        for (int k = tid >> 8; k < d.nt; k += 4) sum += b.counts[(size_t)k * d.T + t];
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      __syncthreads();  // wsum's previous readers are done
+      if (lane == 0) wsum[wv] = sum;
+      __syncthreads();
+      if (tid == 0) {
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) v += wsum[w];
+        ws.blk_nnz[tb] = v;
+      }
+    }
+  }
   __syncthreads();
   // the copy: entry e of the staging goes to first(tile, group) + its rank in the group.
   // A slice is LPE 16-byte pieces (slices start 16-byte aligned), so a wave moves EPW
@@ -476,14 +502,17 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
   }
 }
 
+bool order_writes_blk_nnz(const Dims& d) { return d.nt * d.ng <= ORDER_SMALL_N; }
+
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                        hipStream_t s) {
-  if (d.nt * d.ng <= ORDER_SMALL_N) {
+                        hipStream_t s, bool with_blk) {
+  if (order_writes_blk_nnz(d)) {
     // workgroups for the copy: 64 staged entries each, of at most min(cap, n_t T)
     const long long most = std::min<long long>((long long)d.cap, (long long)d.nt * d.T);
     const int nwg = (int)std::min<long long>(ORDER_SMALL_MAX_WG, std::max<long long>(1, (most + 63) / 64));
 #define SFFN_ORDER_SMALL(KK, BB) \
-  hipLaunchKernelGGL((order_small_kernel<KK, BB>), dim3(nwg), dim3(1024), 0, s, d, b, ws)
+  hipLaunchKernelGGL((order_small_kernel<KK, BB>), dim3(nwg), dim3(1024), 0, s, d, b, ws, \
+                     with_blk ? 1 : 0)
     if (d.bf16) {
       if (d.K == 64) SFFN_ORDER_SMALL(64, true);
       else if (d.K == 128) SFFN_ORDER_SMALL(128, true);

@@ -239,14 +239,40 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
   return SFFN_OK;
 }
 
+// The down-projection's kernel choice.  Forced policies name one kernel (an unsupported one
+// falls back to the next one down).  Under the auto policy the layer's stored nonzeros n
+// decide: gather for n <= thr_g, tiles for thr_g < n <= thr_m, mfma for n > thr_m; an
+// unsupported kernel's range goes to the next one down, and with a single candidate no count
+// is needed.
+struct DownPlan {
+  int32_t policy;
+  long long thr_g, thr_m, all;
+  bool needs_count;  // auto with several candidates: the per-block counts are read
+};
+
+static DownPlan plan_down(const sparse_ffn* hd, const Dims& d) {
+  DownPlan p{hd->down_policy, 0, 0, 0, false};
+  if (p.policy == SFFN_DOWN_MFMA && !down_mfma_supported(d)) p.policy = SFFN_DOWN_TILES;
+  if (p.policy == SFFN_DOWN_TILES && !down_lds_supported(d)) p.policy = SFFN_DOWN_GATHER;
+  if (p.policy != SFFN_DOWN_AUTO) return p;
+  const double cells = (double)d.T * (double)d.F;
+  p.thr_g = (long long)((double)hd->down_gather_density * cells);
+  p.thr_m = (long long)((double)hd->down_mfma_density * cells);
+  p.all = (long long)cells + 1;  // above any count
+  if (!down_mfma_supported(d) || d.T < SFFN_DOWN_MFMA_MIN_T) p.thr_m = p.all;
+  if (!down_lds_supported(d) || d.T < SFFN_DOWN_TILES_MIN_T) p.thr_g = p.thr_m;
+  p.needs_count = p.thr_g < p.all;
+  return p;
+}
+
 // Down-projection of a packed activation.  The gather kernel is the per-token row gather
 // for bf16 layers (the staged-tile gather for fp32 layers and d_model > 4096); under the auto
 // policy the kernel is chosen by the layer's stored nonzeros, counted and compared on the
 // device: every candidate is launched with its range and all but one return at once.
+// blk_ready: ws.blk_nnz already holds this TwELL's per-block counts (written by the ordering
+// pass of the same call).
 static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
-                               const Workspace& ws, void* y, hipStream_t s) {
-  const bool mfma_ok = down_mfma_supported(d);
-  const bool tiles_ok = down_lds_supported(d);
+                               const Workspace& ws, void* y, hipStream_t s, bool blk_ready) {
   const bool rows_ok = down_rows_supported(d);
   auto gather = [&](const int32_t* blk, long long thr) {
     if (rows_ok)
@@ -261,25 +287,16 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
     return run("down_mfma", s,
                [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, blk, thr, s); });
   };
-  int32_t policy = hd->down_policy;
-  if (policy == SFFN_DOWN_MFMA && !mfma_ok) policy = SFFN_DOWN_TILES;
-  if (policy == SFFN_DOWN_TILES && !tiles_ok) policy = SFFN_DOWN_GATHER;
-  if (policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
-  if (policy == SFFN_DOWN_TILES) return tiles(nullptr, 0, 0);
-  if (policy == SFFN_DOWN_MFMA) return mfma(nullptr, 0);
-  // auto: stored nonzeros n of the layer; gather for n <= thr_g, tiles for thr_g < n <= thr_m,
-  // mfma for n > thr_m.  An unsupported kernel's range goes to the next one down.
-  const double cells = (double)d.T * (double)d.F;
-  long long thr_g = (long long)((double)hd->down_gather_density * cells);
-  long long thr_m = (long long)((double)hd->down_mfma_density * cells);
-  const long long all = (long long)cells + 1;  // above any count
-  if (!mfma_ok || d.T < SFFN_DOWN_MFMA_MIN_T) thr_m = all;
-  if (!tiles_ok || d.T < SFFN_DOWN_TILES_MIN_T) thr_g = thr_m;
-  if (thr_g >= all) return gather(nullptr, 0);  // one candidate: no count needed
-  SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
-  SFFN_TRY_INNER(gather(ws.blk_nnz, thr_g));
-  if (thr_m > thr_g) SFFN_TRY_INNER(tiles(ws.blk_nnz, thr_g, thr_m));
-  if (thr_m < all) SFFN_TRY_INNER(mfma(ws.blk_nnz, thr_m));
+  const DownPlan p = plan_down(hd, d);
+  if (p.policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
+  if (p.policy == SFFN_DOWN_TILES) return tiles(nullptr, 0, 0);
+  if (p.policy == SFFN_DOWN_MFMA) return mfma(nullptr, 0);
+  if (!p.needs_count) return gather(nullptr, 0);
+  if (!blk_ready)
+    SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
+  SFFN_TRY_INNER(gather(ws.blk_nnz, p.thr_g));
+  if (p.thr_m > p.thr_g) SFFN_TRY_INNER(tiles(ws.blk_nnz, p.thr_g, p.thr_m));
+  if (p.thr_m < p.all) SFFN_TRY_INNER(mfma(ws.blk_nnz, p.thr_m));
   return SFFN_OK;
 }
 
@@ -316,8 +333,10 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
                                 static_cast<const float*>(hd->b_up), *act, ws, z, s);
     }));
   }
-  SFFN_TRY(run("order", s, [&] { return launch_order(d, *act, ws, s); }));
-  return down_impl(hd, d, *act, ws, y, s);
+  // the one-launch ordering of few pairs also writes the counts the kernel choice reads
+  const bool blk = plan_down(hd, d).needs_count && order_writes_blk_nnz(d);
+  SFFN_TRY(run("order", s, [&] { return launch_order(d, *act, ws, s, blk); }));
+  return down_impl(hd, d, *act, ws, y, s, blk);
 }
 
 sffn_status_t sparse_ffn_forward(sparse_ffn_t hd, const void* x, int32_t T, void* y,
@@ -340,7 +359,7 @@ sffn_status_t sparse_ffn_down(sparse_ffn_t hd, const twell_buffers_t* act, int32
   const Dims d = make_dims(&hd->cfg, T);
   const Workspace ws = carve(act->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return down_impl(hd, d, *act, ws, y, s);
+  return down_impl(hd, d, *act, ws, y, s, false);
 }
 
 sffn_status_t sparse_ffn_backward(sparse_ffn_t hd, const void* x, const void* dy, int32_t T,
