@@ -13,8 +13,8 @@
 // token also split its columns into 256- or 512-wide chunks, so a short batch still spreads
 // over many CUs); wave w takes a contiguous 1/NW of the tiles, lane l of it tile k = k0 + l: its
 // count, then its slots 8 at a time (16 B values + 8 B columns).  The
-// (row, value) pairs of the lanes are broadcast with readlane in batches of up to 8 (4 for
-// d_model > 2048) whose
+// (row, value) pairs of the lanes are gathered with readlane into batches (slot i in lane i;
+// 32 pairs for the 256-column chunks, 8 up to d_model 2048 and 4 above otherwise) whose
 // W_down row loads are all issued before any is used, so a token with many nonzeros (heavy
 // tokens run at 10-20x the mean density) is not a chain of single-row latencies.  Lane L owns
 // the EPL output columns c0 + 64 EPL q + EPL L (q < NQ; c0 = the workgroup's column chunk;
@@ -33,7 +33,8 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr) {
   static_assert(EPL == 8 || EPL == 4 || EPL == 2, "8, 4 or 2 output columns per lane");
   constexpr int CW = 64 * EPL;                 // columns of one wave load of a row
-  constexpr int ROWS_BATCH = NQ <= 4 ? 8 : 4;  // rows in flight per wave (registers: 4*NQ each)
+  // rows in flight per wave (registers: NQ EPL / 2 each; at most 64, one lane per slot)
+  constexpr int ROWS_BATCH = (NQ == 1 && EPL <= 4) ? 32 : (NQ <= 4 ? 8 : 4);
   __shared__ __attribute__((aligned(16))) float part[ROWS_WAVES - 1][NQ * CW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -48,9 +49,10 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[q][e] = 0.0f;
 
-  // a batch of up to ROWS_BATCH (row, value) pairs: loads first, then the FMAs
-  int bj[ROWS_BATCH];
-  float bv[ROWS_BATCH];
+  // a batch of up to ROWS_BATCH (row, value) pairs, slot i in lane i of bjl and bvl: the row
+  // loads first, then the FMAs
+  int bjl = 0;
+  uint32_t bvl = 0u;
   int nb = 0;
   auto flush = [&]() __attribute__((always_inline)) {
     uint32_t w[ROWS_BATCH][NQ][EPL / 2];  // EPL bf16 of the row per lane and chunk
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
 #pragma unroll
         for (int e = 0; e < EPL / 2; ++e) w[i][q][e] = 0u;
       if (i < nb) {  // wave-uniform
-        const uint16_t* wr = Wd + (size_t)bj[i] * D;
+        const uint16_t* wr = Wd + (size_t)__builtin_amdgcn_readlane(bjl, i) * D;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           const int c0 = cb + CW * q + EPL * lane;
@@ -81,7 +83,8 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     }
 #pragma unroll
     for (int i = 0; i < ROWS_BATCH; ++i) {
-      const float v = i < nb ? bv[i] : 0.0f;
+      const float v = i < nb ? __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)bvl, i) << 16)
+                             : 0.0f;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const uint32_t* ww = w[i][q];
@@ -99,13 +102,10 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     while (act != 0) {
       const int b = __builtin_ctzll(act);
       act &= act - 1;
-      // nb is wave-uniform, so the batch slots stay in registers after unrolling
-#pragma unroll
-      for (int i = 0; i < ROWS_BATCH; ++i)
-        if (i == nb) {
-          bj[i] = __builtin_amdgcn_readlane(jl, b);
-          bv[i] = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)vl, b) << 16);
-        }
+      const int j = __builtin_amdgcn_readlane(jl, b);
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)vl, b);
+      bjl = lane == nb ? j : bjl;
+      bvl = lane == nb ? v : bvl;
       if (++nb == ROWS_BATCH) flush();
     }
   };
