@@ -15,15 +15,18 @@
 // Two forms, by measurement on MI355X at d_model 2048:
 //  * up to 64 tokens (one or two token blocks): 4 waves, each over a quarter of d_model in
 //    batches of 8 (4) steps whose loads are in flight together;
-//  * 65 to 128 tokens (four token blocks, four times the token-row loads per W_up piece):
-//    8 waves, each over an eighth of d_model, with all W_up pieces of a chunk of steps in
-//    flight at once (16 KB per wave) and the token rows loaded one line of four steps ahead.
+//  * 65 to 128 tokens (four token blocks, four times the token-row bytes per W_up piece):
+//    8 waves, each over an eighth of d_model in groups of four steps, with the W_up pieces of
+//    two groups in flight at once and the token rows of the next group loaded as whole
+//    128-byte lines and staged through the wave's own LDS (a token row's 32 bytes per step,
+//    loaded straight into the MFMA layout, would cost a line fetch from L2 each).
 #include "sffn_common.hpp"
 
 namespace sffn {
 
 typedef __bf16 bf16x8_s __attribute__((ext_vector_type(8)));
 typedef float floatx16_s __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_s __attribute__((ext_vector_type(4)));
 
 constexpr int US_NB = 32;  // neurons per workgroup
 
@@ -122,49 +125,60 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
 
 constexpr int US8_NW = 8;  // waves of the 8-wave form
 
-// Steps c .. c + n - 1 (1 <= n <= CH) of one wave of the 8-wave form: all CH W_up pieces
-// are loaded first.  A token row's 128-byte line holds four steps, so its pieces are loaded
-// four steps at a time (the four loads of a line together), one group ahead of the MFMAs
-// (all at once for one token block).
-template <int NTB, int CH>
-__device__ __forceinline__ void up_small_chunk(floatx16_s (&acc)[NTB], const uint16_t* wrow,
-                                               const uint16_t* const (&xrow)[NTB], int c,
-                                               int n) {
-  static_assert(CH % 4 == 0, "whole groups of four steps");
-  constexpr int NG = CH / 4;
-  constexpr int GA = NTB == 1 ? NG : 1;  // groups loaded ahead of the one in the MFMAs
-  bf16x8_s a[CH], b[CH][NTB];
-  auto ldb = [&](int g) {
+// groups of four steps per chunk (two: the 8 W_up pieces, two sets of token-row lines and the
+// accumulators fill the 256 registers of a wave at two waves per SIMD)
+constexpr int US8_NGC = 2;
+
+// Groups g0 .. g0 + n - 1 (1 <= n <= NGC) of one wave of the 8-wave form.  A group is
+// four 16-column steps: 64 columns, one 128-byte line of every token row.  The W_up pieces of
+// the whole chunk are loaded first.  The 128 token rows of a group are loaded as whole lines
+// (8 lanes per row, 8 rows per load), one group ahead of the MFMAs, and written to the wave's
+// own 16 KB of LDS (row t at t * 128 bytes, 16-byte piece p at (p ^ (t & 7)) * 16), from
+// which each step reads its MFMA operand (lane l: row 32 tb + l % 32, piece 2 j + l / 32).
+// Groups past n repeat a valid address and multiply a zero A.
+template <int NGC>
+__device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[4], const uint16_t* wrow,
+                                                const uint16_t* xl, const int* toff, char* xs,
+                                                int g0, int n, int lane) {
+  bf16x8_s a[4 * NGC];
 #pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
+  for (int st = 0; st < 4 * NGC; ++st) {
+    const int g = st >> 2, gc = g < n ? g : n - 1;
+    a[st] = *reinterpret_cast<const bf16x8_s*>(wrow + ((g0 + gc) * 4 + (st & 3)) * 16);
+  }
+  u32x4_s xr0[16], xr1[16];  // token-row lines of even and odd groups
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sl = 4 * g + j;
-        b[sl][tb] =
-            *reinterpret_cast<const bf16x8_s*>(xrow[tb] + (c + (sl < n ? sl : n - 1)) * 16);
-      }
-  };
-#pragma unroll
-  for (int s = 0; s < CH; ++s)
-    a[s] = *reinterpret_cast<const bf16x8_s*>(wrow + (c + (s < n ? s : n - 1)) * 16);
-#pragma unroll
-  for (int g = 0; g < (GA < NG ? GA : NG); ++g) ldb(g);
-  // keep the scheduler from sinking these loads back next to their MFMAs
+  for (int i = 0; i < 16; ++i) xr0[i] = *reinterpret_cast<const u32x4_s*>(xl + toff[i] + g0 * 64);
+  // keep the scheduler from sinking these loads back next to their uses
   __builtin_amdgcn_sched_barrier(0);
   const bf16x8_s zero = {};
+  const int wp = lane & 7;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if (g + GA < NG) {
-      ldb(g + GA);
+  for (int g = 0; g < NGC; ++g) {
+    u32x4_s(&cur)[16] = (g & 1) ? xr1 : xr0;
+    u32x4_s(&nxt)[16] = (g & 1) ? xr0 : xr1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 8 * i + (lane >> 3);
+      *reinterpret_cast<u32x4_s*>(xs + t * 128 + ((wp ^ (t & 7)) << 4)) = cur[i];
+    }
+    if (g + 1 < NGC) {
+      const int gc = g + 1 < n ? g + 1 : n - 1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        nxt[i] = *reinterpret_cast<const u32x4_s*>(xl + toff[i] + (g0 + gc) * 64);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int s = 4 * g + j;
-      const bf16x8_s av = s < n ? a[s] : zero;
+      const bf16x8_s av = g < n ? a[4 * g + j] : zero;
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb)
-        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[s][tb], acc[tb], 0, 0, 0);
+      for (int tb = 0; tb < 4; ++tb) {
+        const int R = 32 * tb + (lane & 31), P = 2 * j + (lane >> 5);
+        const bf16x8_s b =
+            *reinterpret_cast<const bf16x8_s*>(xs + R * 128 + ((P ^ (R & 7)) << 4));
+        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[tb], 0, 0, 0);
+      }
     }
   }
 }
@@ -174,8 +188,10 @@ __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
     Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
     const uint16_t* __restrict__ bu, float* __restrict__ h, float* __restrict__ zdump,
     int32_t* __restrict__ claim) {
+  static_assert(NTB == 4, "the 8-wave form stages 128 token rows");
   constexpr int US_NW = US8_NW;
-  // partial sums: [wave][token block][element][lane]
+  // wave w's 16 KB: first its staged token rows, then its partial sums
+  // [wave][token block][element][lane] (the same bytes, after its last MFMA)
   __shared__ __attribute__((aligned(16))) float red[US_NW * NTB * 16 * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -184,33 +200,29 @@ __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
   // the backup staging counter the pack kernel (the next launch) claims from
   if (blockIdx.x == 0 && threadIdx.x == 0) *claim = 0;
   const int r = lane & 31, hh = lane >> 5;
-  const int nks = D / 16;                          // 16-column steps (D % 16 == 0)
-  const int ks0 = wave * nks / US_NW, ks1 = (wave + 1) * nks / US_NW;
+  const int ngr = D / 64;                          // groups of four steps (D % 64 == 0)
+  const int g0 = wave * ngr / US_NW, g1 = (wave + 1) * ngr / US_NW;
   const uint16_t* wrow = Wu + (size_t)(n0 + r) * D + 8 * hh;
-  const uint16_t* xrow[NTB];
+  // token-row loads: load i of lane l reads row 8 i + l / 8 (rows past T repeat row T - 1),
+  // 16-byte piece l % 8 of the group's line
+  const uint16_t* xl = x + 8 * (lane & 7);
+  int toff[16];
 #pragma unroll
-  for (int tb = 0; tb < NTB; ++tb) {
-    const int t = 32 * tb + r;
-    xrow[tb] = x + (size_t)(t < T ? t : T - 1) * D + 8 * hh;
+  for (int i = 0; i < 16; ++i) {
+    const int t = 8 * i + (lane >> 3);
+    toff[i] = (t < T ? t : T - 1) * D;
   }
+  char* xs = reinterpret_cast<char*>(red) + wave * 16384;
 
   floatx16_s acc[NTB];
 #pragma unroll
   for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[tb][e] = 0.0f;
-  // chunks of CH steps (W_up pieces in flight per wave: 16 KB at CH 16), the last one
-  // partly filled
-  constexpr int CH = NTB == 4 ? 8 : 16;
-  int c = ks0;
-  for (; c + CH <= ks1; c += CH) up_small_chunk<NTB, CH>(acc, wrow, xrow, c, CH);
-  const int rest = ks1 - c;
-  if (rest > 8)
-    up_small_chunk<NTB, 16>(acc, wrow, xrow, c, rest);
-  else if (rest > 4)
-    up_small_chunk<NTB, 8>(acc, wrow, xrow, c, rest);
-  else if (rest > 0)
-    up_small_chunk<NTB, 4>(acc, wrow, xrow, c, rest);
+  int g = g0;
+  for (; g + US8_NGC <= g1; g += US8_NGC)
+    up_small8_chunk<US8_NGC>(acc, wrow, xl, toff, xs, g, US8_NGC, lane);
+  if (g < g1) up_small8_chunk<US8_NGC>(acc, wrow, xl, toff, xs, g, g1 - g, lane);
 
   // element e of lane l is neuron 8(e/4) + 4(l/32) + e%4 of the block and token l % 32 of
   // the token block
@@ -264,9 +276,11 @@ hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
     hipLaunchKernelGGL(up_small_kernel<1>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump, claim);
   else if (d.T <= 64)
     hipLaunchKernelGGL(up_small_kernel<2>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump, claim);
-  else
+  else if (d.D % 64 == 0)
     hipLaunchKernelGGL(up_small8_kernel<4>, grid, dim3(US8_NW * 64), 0, s, d, x, Wu, bu, h,
                        zdump, claim);
+  else
+    hipLaunchKernelGGL(up_small_kernel<4>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump, claim);
   return hipGetLastError();
 }
 
