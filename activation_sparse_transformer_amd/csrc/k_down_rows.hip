@@ -121,13 +121,20 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
   const int mmax = __builtin_amdgcn_readfirstlane(mx);
   const size_t row = ((size_t)(own ? k : 0) * T + t) * W;
+  // slots s0 .. s0+7 of this lane's tile-row (rows are W bytes / 2W bytes, W % 8 == 0), the
+  // next eight loaded while these are added
+  uint4 v4n = make_uint4(0, 0, 0, 0);
+  uint2 c2n = make_uint2(0, 0);
+  if (0u < m) {
+    v4n = *reinterpret_cast<const uint4*>(vals + row);
+    c2n = *reinterpret_cast<const uint2*>(cols + row);
+  }
   for (int s0 = 0; s0 < mmax; s0 += 8) {
-    // slots s0 .. s0+7 of this lane's tile-row (rows are W bytes / 2W bytes, W % 8 == 0)
-    uint4 v4 = make_uint4(0, 0, 0, 0);
-    uint2 c2 = make_uint2(0, 0);
-    if ((uint32_t)s0 < m) {
-      v4 = *reinterpret_cast<const uint4*>(vals + row + s0);
-      c2 = *reinterpret_cast<const uint2*>(cols + row + s0);
+    const uint4 v4 = v4n;
+    const uint2 c2 = c2n;
+    if ((uint32_t)(s0 + 8) < m) {
+      v4n = *reinterpret_cast<const uint4*>(vals + row + s0 + 8);
+      c2n = *reinterpret_cast<const uint2*>(cols + row + s0 + 8);
     }
     const uint32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
     const uint32_t cc[2] = {c2.x, c2.y};
@@ -152,11 +159,14 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     const int rank = __builtin_popcountll(ov & ((1ull << (t - g * GROUP)) - 1ull));
     const int e = ld_uniform(grp_first + kb * d.ng + g) + rank;
     if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
+    // the slice's K <= 256 values, all loaded before any is added
     const uint16_t* sl = bk_vals + (size_t)e * K;
-    for (int c0 = 0; c0 < K; c0 += 64) {
-      const uint32_t v = sl[c0 + lane];
-      add_lanes(ballot64(v != 0u), kb * K + c0 + lane, v);
-    }
+    uint32_t sv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sv[q] = 64 * q < K ? (uint32_t)sl[64 * q + lane] : 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (64 * q < K) add_lanes(ballot64(sv[q] != 0u), kb * K + 64 * q + lane, sv[q]);
   }
   if (nb > 0) flush();
 
