@@ -322,7 +322,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // every workgroup scans the tile totals into tile offsets in LDS; together they write
 // grp_first (tile offset + group offset: the first canonical entry of every (tile, group)),
 // the first one bk_tile_ptr, bk_n and the status word, and every staged entry goes to
-// grp_first[tile, group] + its rank inside the group.
+// grp_first[tile, group] + its rank inside the group.  With with_blk, workgroup i also
+// writes the stored nonzeros of 256-token blocks i, i + gridDim.x, ... (blk_nnz, read by the
+// down-projection's kernel choice), which saves the forward pass that launch.
 constexpr int ORDER_COPY_MAX_NT = SFFN_MAX_TILES;  // tile offsets the copy kernel's LDS holds
 
 __global__ __launch_bounds__(1024) void order_tile_kernel(Dims d, Workspace ws) {
@@ -352,9 +354,11 @@ __global__ __launch_bounds__(1024) void order_tile_kernel(Dims d, Workspace ws) 
 }
 
 template <int K, bool BF16>
-__global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+__global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t b, Workspace ws,
+                                                         int with_blk) {
   __shared__ int toff[ORDER_COPY_MAX_NT + 1];
   __shared__ int wsum[4];
+  __shared__ int bsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // tile offsets: exclusive scan of the tile totals, 256 at a time
   int carry = 0;
@@ -389,6 +393,23 @@ __global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t
   }
   for (int q = blockIdx.x * 256 + tid; q < N; q += gridDim.x * 256)
     ws.grp_first[q] = toff[q / d.ng] + ws.ov_grp[q];
+  if (with_blk) {
+    // thread i sums every tile's count of token i of the block (coalesced rows of counts)
+    for (int tb = blockIdx.x; tb * 256 < d.T; tb += gridDim.x) {
+      const int t = tb * 256 + tid;
+      int sum = 0;
+      if (t < d.T) {
+#pragma unroll 16
+        for (int k = 0; k < d.nt; ++k) sum += b.counts[(size_t)k * d.T + t];
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      __syncthreads();  // bsum's previous readers are done
+      if (lane == 0) bsum[wv] = sum;
+      __syncthreads();
+      if (tid == 0) ws.blk_nnz[tb] = bsum[0] + bsum[1] + bsum[2] + bsum[3];
+    }
+  }
   // the copy
   const int n_staged = min(*ws.claim, d.cap);
   const int gw = blockIdx.x * 4 + wv;
@@ -502,11 +523,9 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
   }
 }
 
-bool order_writes_blk_nnz(const Dims& d) { return d.nt * d.ng <= ORDER_SMALL_N; }
-
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s, bool with_blk) {
-  if (order_writes_blk_nnz(d)) {
+  if (d.nt * d.ng <= ORDER_SMALL_N) {
     // workgroups for the copy: 64 staged entries each, of at most min(cap, n_t T)
     const long long most = std::min<long long>((long long)d.cap, (long long)d.nt * d.T);
     const int nwg = (int)std::min<long long>(ORDER_SMALL_MAX_WG, std::max<long long>(1, (most + 63) / 64));
@@ -533,7 +552,8 @@ hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace
   int blocks = (d.cap + 3) / 4;
   blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
 #define SFFN_ORDER(KK, BB) \
-  hipLaunchKernelGGL((order_copy_kernel<KK, BB>), dim3(blocks), dim3(256), 0, s, d, b, ws)
+  hipLaunchKernelGGL((order_copy_kernel<KK, BB>), dim3(blocks), dim3(256), 0, s, d, b, ws, \
+                     with_blk ? 1 : 0)
   if (d.bf16) {
     if (d.K == 64) SFFN_ORDER(64, true);
     else if (d.K == 128) SFFN_ORDER(128, true);

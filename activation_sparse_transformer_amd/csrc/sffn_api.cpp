@@ -333,8 +333,8 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
                                 static_cast<const float*>(hd->b_up), *act, ws, z, s);
     }));
   }
-  // the one-launch ordering of few pairs also writes the counts the kernel choice reads
-  const bool blk = plan_down(hd, d).needs_count && order_writes_blk_nnz(d);
+  // the ordering pass also writes the counts the kernel choice reads
+  const bool blk = plan_down(hd, d).needs_count;
   SFFN_TRY(run("order", s, [&] { return launch_order(d, *act, ws, s, blk); }));
   return down_impl(hd, d, *act, ws, y, s, blk);
 }

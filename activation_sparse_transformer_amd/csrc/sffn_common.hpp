@@ -154,11 +154,9 @@ __device__ __forceinline__ long long layer_nnz(const int32_t* blk_nnz, int n) {
 hipError_t launch_zero_claim(const Workspace& ws, hipStream_t s);
 hipError_t launch_pack(const Dims& d, const float* h, const twell_buffers_t& b,
                        const Workspace& ws, hipStream_t s);
-// with_blk: also write ws.blk_nnz where the one-launch ordering of few pairs runs.
+// with_blk: also write ws.blk_nnz (the per-256-token-block stored nonzeros).
 hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s, bool with_blk = false);
-// True if launch_order(..., with_blk = true) writes ws.blk_nnz (the one-launch ordering).
-bool order_writes_blk_nnz(const Dims& d);
 hipError_t launch_stats(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s);
 hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, const float* bu,
