@@ -347,6 +347,20 @@ def test_forward_heavy_rows_force_backup(policy):
     _forward_case(torch, sffn, L, policy=policy)
 
 
+
+@pytest.mark.parametrize("T", [32, 48])
+@pytest.mark.parametrize("policy", ["auto", "gather"])
+def test_forward_heavy_rows_short_batch(T, policy):
+    """Decode-shaped batch of the 1.5B-like layer with two 3x-scaled token rows: most of their
+    tile-rows overflow into the backup, and below 64 tokens the row gather (256-column chunks)
+    is the only down kernel."""
+    torch, sffn = need_gpu()
+    print(f"[forward-heavy-short] T={T} {policy}", flush=True)
+    L = make_layer(CONFIGS["C3"].replace(heavy_frac=2.0 / T), seed=0, T=T, rho=0.05)
+    assert len(L["heavy"]) == 2
+    _forward_case(torch, sffn, L, policy=policy)
+
+
 def test_forward_edge_all_zero_all_positive():
     torch, sffn = need_gpu()
     base = CONFIGS["C3"].replace(heavy_frac=0.0)
