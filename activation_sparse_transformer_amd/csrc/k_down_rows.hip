@@ -9,11 +9,12 @@
 // d_model 2048), so this kernel wins when few rows are used; the matrix-core kernel (whose
 // work does not depend on the density) takes dense layers.
 //
-// One workgroup per token at a time (NW waves; for few tokens NW = 16 and the workgroups of a
-// token also split its columns into 256- or 512-wide chunks, so a short batch still spreads
-// over many CUs); wave w takes a contiguous 1/NW of the tiles, lane l of it tile k = k0 + l: its
-// count, then its slots 8 at a time (16 B values + 8 B columns).  The
-// (row, value) pairs of the lanes are gathered with readlane into batches (slot i in lane i;
+// One workgroup per token at a time (NW waves; for few tokens, when the gather is the call's
+// only down kernel, NW = 16 and the workgroups of a token also split its columns into 256-wide
+// chunks, so a short batch still spreads over many CUs); wave w takes a contiguous 1/NW of the
+// tiles, lane l of it tile k = k0 + l: its count, then its slots 8 at a time (16 B values +
+// 8 B columns).  The (row, value) pairs of the lanes are gathered with readlane into batches
+// (slot i in lane i;
 // 32 pairs for the 256-column chunks, 8 up to d_model 2048 and 4 above otherwise) whose
 // W_down row loads are all issued before any is used, so a token with many nonzeros (heavy
 // tokens run at 10-20x the mean density) is not a chain of single-row latencies.  Lane L owns
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   }
 }
 
-// Few tokens: 16 waves per workgroup and one 256- or 512-column chunk per workgroup.
+// Few tokens, gather alone: 16 waves per workgroup and one 256-column chunk per workgroup.
 constexpr int ROWS_FEW_T = 1024;
 
 bool down_rows_supported(const Dims& d) {
@@ -228,20 +229,16 @@ hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Works
   auto* bk = static_cast<const uint16_t*>(b.bk_vals);
   auto* w = static_cast<const uint16_t*>(Wd);
   auto* yy = static_cast<uint16_t*>(y);
-  if (d.T < ROWS_FEW_T) {
-    if (blk_nnz == nullptr) {
-      // the only down kernel of the call: 256-column chunks, twice the workgroups per token
-      const dim3 grid(d.T, (d.D + 255) / 256), block(64 * 16);
-      hipLaunchKernelGGL((down_rows_kernel<1, 16, 4>), grid, block, 0, s, d, c, v, b.cols, bk,
-                         ws.grp_first, w, yy, blk_nnz, thr);
-    } else {
-      // one candidate of the kernel choice: fewer workgroups to start when it returns at once
-      const dim3 grid(d.T, (d.D + 511) / 512), block(64 * 16);
-      hipLaunchKernelGGL((down_rows_kernel<1, 16, 8>), grid, block, 0, s, d, c, v, b.cols, bk,
-                         ws.grp_first, w, yy, blk_nnz, thr);
-    }
+  if (d.T < ROWS_FEW_T && blk_nnz == nullptr) {
+    // the only down kernel of the call: 16-wave workgroups over 256-column chunks
+    const dim3 grid(d.T, (d.D + 255) / 256), block(64 * 16);
+    hipLaunchKernelGGL((down_rows_kernel<1, 16, 4>), grid, block, 0, s, d, c, v, b.cols, bk,
+                       ws.grp_first, w, yy, blk_nnz, thr);
     return hipGetLastError();
   }
+  // many tokens, or one candidate of the kernel choice (which usually returns at once, so its
+  // waves should be few; when it runs, the layer holds very few nonzeros per token): 4-wave
+  // workgroups over whole tokens
   const dim3 grid(d.T < 2048 ? d.T : 2048), block(64 * 4);
   switch ((d.D + 511) / 512) {
 #define SFFN_ROWS(NQ)                                                                      \

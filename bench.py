@@ -413,7 +413,7 @@ def main():
     # rows the stored nonzeros select; sparse (auto policy and each down kernel) vs dense
     decode = []
     if not args.no_decode:
-        for Td in (1, 8, 32, 128, 256):
+        for Td in (1, 8, 32, 64, 128, 256):
             cfg_d = sffn.Config(d_model=D, d_ff=F, tile=c.tile, ell_width=c.ell_width,
                                 max_tokens=Td, backup_capacity=max(64, c.n_tiles * Td // 8),
                                 dtype="bf16")

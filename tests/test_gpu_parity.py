@@ -255,6 +255,47 @@ def test_down_auto_policy_choice():
     assert np.array_equal(outs[("auto", 0.0)], outs[("gather", 0.0)])
 
 
+
+@pytest.mark.parametrize("T", [64, 300])
+def test_down_gather_candidate_runs(T):
+    """Auto policy with every count in the gather's range, at token counts where the gather is
+    launched as one candidate of the kernel choice (4-wave workgroups over whole tokens): it
+    runs, writes every row and matches the oracle; the matrix-core candidate returns."""
+    torch, sffn = need_gpu()
+    print(f"[down-candidate] T={T}", flush=True)
+    D, F, K, W = 256, 1024, 128, 32
+    h = make_hidden(T, F, 0.05, seed=T, heavy_rows=(1, T // 2), heavy_density=0.6)
+    from gen import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(5)
+    Wd_bits = f32_to_bf16_bits((rng.standard_normal((F, D)) / np.sqrt(F)).astype(np.float32))
+    Wd_ref = bf16_bits_to_f32(Wd_bits).astype(np.float64)
+    cfg = _cfg(sffn, T, D, F, K, W, "bf16")
+    Wd_dev = torch.from_numpy(Wd_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    layer = sffn.SparseFFN(cfg, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
+                           torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
+    buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
+    layer.set_down_policy("auto", 1.0, 1.0)
+    y = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    try:
+        sffn.profile_reset()
+        sffn.profile_enable(True)
+        layer.down(buf, y=y)
+        sffn.profile_enable(False)
+        assert sffn.profile_read("down")[1] == 1 and sffn.profile_read("down_mfma")[1] == 1
+    finally:
+        sffn.profile_enable(False)
+        sffn.profile_reset()
+    yh = y_to_host(torch, y)
+    assert not np.isnan(yh).any(), "rows not written"
+    # the bf16 TwELL stores the activations rounded to bf16
+    h_ref = oracle.bf16_value(oracle.round_bf16(h.astype(np.float64)))
+    y_ref = oracle.down_sparse(oracle.pack(h_ref, K, W), Wd_ref)
+    assert_y_close(yh, y_ref, "bf16", f"gather candidate T={T}")
+    layer.set_down_policy("gather")
+    y2 = layer.down(buf)
+    assert_y_close(y_to_host(torch, y2), y_ref, "bf16", f"gather alone T={T}")
+
+
 def test_down_policy_arguments():
     torch, sffn = need_gpu()
     cfg = _cfg(sffn, 64, 128, 256, 128, 16, "bf16")
