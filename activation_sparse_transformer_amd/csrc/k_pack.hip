@@ -568,18 +568,39 @@ hipError_t launch_order(const Dims& d, const twell_buffers_t& b, const Workspace
 }
 
 // ---------------------------------------------------------------------------------------
-// Statistics: one workgroup reduces the counts array.
-__global__ __launch_bounds__(1024) void stats_kernel(Dims d, twell_buffers_t b, Workspace ws) {
-  __shared__ long long red[5][16];
+// Statistics: a grid of workgroups reduces the counts array into ws.stats (cleared by the
+// launcher first); integer sums and a maximum, so the order of the atomic updates does not
+// change the result.
+constexpr int STATS_WG = 256;
+
+__global__ __launch_bounds__(256) void stats_kernel(Dims d, twell_buffers_t b, Workspace ws) {
+  __shared__ unsigned long long red[5][4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t n = (size_t)d.nt * d.T;
-  long long nnz = 0, slots = 0, over = 0, bnz = 0, mx = 0;
-  for (size_t q = tid; q < n; q += 1024) {
-    const long long c = b.counts[q];
+  const int W = d.W;
+  unsigned long long nnz = 0, slots = 0, over = 0, bnz = 0, mx = 0;
+  // eight counts (16 bytes) per load where the run is aligned; the tail one by one
+  const size_t n8 = n / 8;
+  const uint4* c8 = reinterpret_cast<const uint4*>(b.counts);
+  for (size_t q = (size_t)blockIdx.x * 256 + tid; q < n8; q += (size_t)gridDim.x * 256) {
+    const uint4 v = c8[q];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned long long c = (w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      nnz += c;
+      slots += c < (unsigned)W ? c : (unsigned)W;
+      over += c > (unsigned)W ? 1 : 0;
+      bnz += c > (unsigned)W ? c - W : 0;
+      mx = c > mx ? c : mx;
+    }
+  }
+  for (size_t q = n8 * 8 + (size_t)blockIdx.x * 256 + tid; q < n; q += (size_t)gridDim.x * 256) {
+    const unsigned long long c = b.counts[q];
     nnz += c;
-    slots += c < d.W ? c : d.W;
-    over += c > d.W ? 1 : 0;
-    bnz += c > d.W ? c - d.W : 0;
+    slots += c < (unsigned)W ? c : (unsigned)W;
+    over += c > (unsigned)W ? 1 : 0;
+    bnz += c > (unsigned)W ? c - W : 0;
     mx = c > mx ? c : mx;
   }
 #pragma unroll
@@ -588,7 +609,7 @@ __global__ __launch_bounds__(1024) void stats_kernel(Dims d, twell_buffers_t b, 
     slots += __shfl_xor(slots, o);
     over += __shfl_xor(over, o);
     bnz += __shfl_xor(bnz, o);
-    const long long m2 = __shfl_xor(mx, o);
+    const unsigned long long m2 = __shfl_xor(mx, o);
     mx = m2 > mx ? m2 : mx;
   }
   if (lane == 0) {
@@ -596,21 +617,29 @@ __global__ __launch_bounds__(1024) void stats_kernel(Dims d, twell_buffers_t b, 
   }
   __syncthreads();
   if (tid == 0) {
-    long long a[5] = {0, 0, 0, 0, 0};
-    for (int w = 0; w < 16; ++w) {
+    unsigned long long a[5] = {0, 0, 0, 0, 0};
+    for (int w = 0; w < 4; ++w) {
       for (int j = 0; j < 4; ++j) a[j] += red[j][w];
       a[4] = red[4][w] > a[4] ? red[4][w] : a[4];
     }
-    for (int j = 0; j < 5; ++j) ws.stats[j] = a[j];
-    ws.stats[5] = *b.bk_n;
-    ws.stats[6] = *b.status;
-    ws.stats[7] = 0;
+    unsigned long long* st = reinterpret_cast<unsigned long long*>(ws.stats);
+    for (int j = 0; j < 4; ++j)
+      if (a[j]) atomicAdd(st + j, a[j]);
+    if (a[4]) atomicMax(st + 4, a[4]);
+    if (blockIdx.x == 0) {
+      ws.stats[5] = *b.bk_n;
+      ws.stats[6] = *b.status;
+    }
   }
 }
 
 hipError_t launch_stats(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                         hipStream_t s) {
-  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, s, d, b, ws);
+  hipError_t e = hipMemsetAsync(ws.stats, 0, 8 * sizeof(long long), s);
+  if (e != hipSuccess) return e;
+  const size_t n8 = ((size_t)d.nt * d.T) / 8;
+  const int grid = (int)std::max<size_t>(1, std::min<size_t>(STATS_WG, (n8 + 255) / 256));
+  hipLaunchKernelGGL(stats_kernel, dim3(grid), dim3(256), 0, s, d, b, ws);
   return hipGetLastError();
 }
 

@@ -11,9 +11,10 @@
 //     neurons [128*wn, 128*wn+128) x tokens [wt*BM/2, (wt+1)*BM/2) of the tile.
 //   * v_mfma_f32_32x32x16_bf16 with A = W_up rows (neurons) and B = x rows (tokens): both
 //     operands are contiguous along d_model, so both are read from LDS as 16-byte rows.
-//   * BK = 64; global -> register prefetch of the next k-slice while the current one is
-//     multiplied; LDS double buffer; 16-byte chunks XOR-swizzled by row so the 32 rows a
-//     wave reads at one column land in distinct banks.
+//   * d_model is consumed in slices of BK columns (32 for 128- and 256-column tiles, 64 for
+//     64-column tiles) through a ring of NS LDS stages filled by direct global -> LDS loads
+//     issued NS - 1 stages ahead; 16-byte chunks XOR-swizzled by row so the rows a wave
+//     reads at one column land in distinct banks.
 //   * workgroups are ordered in groups of 8 token blocks and dispatched so that the
 //     workgroups sharing an XCD's L2 cover a compact patch of the output.
 //
@@ -256,11 +257,23 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
         for (int i = 0; i < 4; ++i) acc[a][bb][4 * q + i] += bv[i];
     }
 
-  // staging: vals [NTWG][2 wt][32 tok][W] bf16, cols [NTWG][2][32][W] u8
-  uint16_t* st_vals = reinterpret_cast<uint16_t*>(sA0);  // <= 32 KB
-  uint8_t* st_cols = reinterpret_cast<uint8_t*>(sA1);     // <= 16 KB
-  const int st_vwords = NTWG * 2 * 32 * W / 2;             // 32-bit words of st_vals
-  const int st_cwords = NTWG * 2 * 32 * W / 4;             // 32-bit words of st_cols
+  // Staging of one 32-token block: region r = (tile slot js, token half w2), r = 2 js + w2,
+  // holds [32 tok][W] values (bf16) and [32 tok][W] columns (u8), W <= K.  Columns: all
+  // regions in sA1.  Values: with three ring stages (16 KB stages) the regions of w2 = 0 go
+  // to sA0 and those of w2 = 1 to sA2, NTWG * 32 * W * 2 bytes each; with two stages (32 KB)
+  // all regions fit in sA0.
+  static_assert(NS > 2 ? (NTWG * 32 * K * 2 <= (int)sizeof(sA0) && NTWG * 32 * K * 2 <= (int)sizeof(sA2))
+                       : (NTWG * 2 * 32 * K * 2 <= (int)sizeof(sA0)),
+                "TwELL value staging exceeds its LDS stage at W = K");
+  static_assert(NTWG * 2 * 32 * K <= (int)sizeof(sA1), "TwELL column staging exceeds sA1 at W = K");
+  uint8_t* st_cols = reinterpret_cast<uint8_t*>(sA1);
+  auto st_vals = [&](int js, int w2) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (NS > 2)
+      return reinterpret_cast<uint16_t*>(w2 ? sA2 : sA0) + js * 32 * W;
+    else
+      return reinterpret_cast<uint16_t*>(sA0) + (js * 2 + w2) * 32 * W;
+  };
+  const int st_cwords = NTWG * 2 * 32 * W / 4;  // 32-bit words of st_cols in use
 
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
@@ -271,7 +284,14 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
 
     // (1) clear the staging block
     __syncthreads();
-    for (int q = tid; q < st_vwords; q += 256) reinterpret_cast<uint32_t*>(st_vals)[q] = 0u;
+    if constexpr (NS > 2) {
+      for (int q = tid; q < NTWG * 32 * W / 2; q += 256) {
+        reinterpret_cast<uint32_t*>(sA0)[q] = 0u;
+        reinterpret_cast<uint32_t*>(sA2)[q] = 0u;
+      }
+    } else {
+      for (int q = tid; q < NTWG * 2 * 32 * W / 2; q += 256) reinterpret_cast<uint32_t*>(sA0)[q] = 0u;
+    }
     for (int q = tid; q < st_cwords; q += 256) reinterpret_cast<uint32_t*>(st_cols)[q] = 0u;
 
     // (2) positive mask of this lane's 64 elements
@@ -374,9 +394,8 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
         else col = wn * 128 + nl;
         const uint16_t zb = f32_to_bf16(z);
         if (nz && rank < W) {
-          const int sidx = ((jslot[j] * 2 + wt) * 32 + l32) * W + rank;
-          st_vals[sidx] = zb;
-          st_cols[sidx] = (uint8_t)col;
+          st_vals(jslot[j], wt)[l32 * W + rank] = zb;
+          st_cols[((jslot[j] * 2 + wt) * 32 + l32) * W + rank] = (uint8_t)col;
         }
         stbuf[i] = (nz && rank >= W) ? zb : (uint16_t)0;
       }
@@ -417,15 +436,16 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
         if (nv == 0) continue;
         const int kt_g = n0 / K + js;
         const size_t gbase = ((size_t)kt_g * T + tb0) * (size_t)W;
-        const int sbase = (js * 2 + w2) * 32 * W;
+        const int sbase = (js * 2 + w2) * 32 * W;  // region of st_cols
+        const uint16_t* sv = st_vals(js, w2);
         const int n_el = nv * W;
         uint16_t* gv = static_cast<uint16_t*>(b.vals) + gbase;
         uint8_t* gc = b.cols + gbase;
         if ((W & 7) == 0) {
           for (int q = tid; q < n_el / 8; q += 256)
-            reinterpret_cast<uint4*>(gv)[q] = reinterpret_cast<const uint4*>(st_vals + sbase)[q];
+            reinterpret_cast<uint4*>(gv)[q] = reinterpret_cast<const uint4*>(sv)[q];
         } else {
-          for (int q = tid; q < n_el; q += 256) gv[q] = st_vals[sbase + q];
+          for (int q = tid; q < n_el; q += 256) gv[q] = sv[q];
         }
         if ((W & 15) == 0) {
           for (int q = tid; q < n_el / 16; q += 256)

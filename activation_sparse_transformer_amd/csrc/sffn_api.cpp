@@ -204,6 +204,17 @@ sffn_status_t twell_buffer_sizes(const sffn_config_t* cfg, int32_t T, twell_buff
   return SFFN_OK;
 }
 
+sffn_status_t twell_buffer_bytes(const sffn_config_t* cfg, int32_t T,
+                                 size_t out_bytes[SFFN_N_BUFFERS]) {
+  if (!out_bytes) return fail(SFFN_ERR_INVALID_ARGUMENT, "out_bytes is NULL");
+  twell_buffer_sizes_t z;
+  SFFN_TRY(twell_buffer_sizes(cfg, T, &z));
+  const size_t v[SFFN_N_BUFFERS] = {z.counts, z.vals, z.cols, z.bk_tile, z.bk_tok,
+                                    z.bk_vals, z.bk_tile_ptr, z.bk_n, z.status, z.workspace};
+  for (int i = 0; i < SFFN_N_BUFFERS; ++i) out_bytes[i] = v[i];
+  return SFFN_OK;
+}
+
 sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* W_up, const void* b_up,
                                 const void* W_down, sparse_ffn_t* out) {
   SFFN_TRY(check_layer_cfg(cfg));

@@ -74,6 +74,8 @@ _PROTOS = {
     "sffn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sffn_last_error": ([], ctypes.c_char_p),
     "twell_buffer_sizes": ([ctypes.POINTER(ConfigC), _I32, ctypes.POINTER(SizesC)], ctypes.c_int),
+    "twell_buffer_bytes": ([ctypes.POINTER(ConfigC), _I32, ctypes.POINTER(ctypes.c_size_t)],
+                           ctypes.c_int),
     "sparse_ffn_create": ([ctypes.POINTER(ConfigC), _P, _P, _P, ctypes.POINTER(_P)], ctypes.c_int),
     "sparse_ffn_destroy": ([_P], ctypes.c_int),
     "twell_pack": ([ctypes.POINTER(ConfigC), _P, _I32, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
@@ -157,6 +159,14 @@ def buffer_sizes(cfg: Config, T: int) -> dict:
     c = cfg.c()
     _check(lib().twell_buffer_sizes(ctypes.byref(c), int(T), ctypes.byref(out)), "twell_buffer_sizes")
     return {n: int(getattr(out, n)) for n in BUFFER_FIELDS}
+
+
+def buffer_bytes(cfg: Config, T: int) -> list:
+    """twell_buffer_bytes: the same sizes as buffer_sizes, as a list in field order."""
+    out = (ctypes.c_size_t * len(BUFFER_FIELDS))()
+    c = cfg.c()
+    _check(lib().twell_buffer_bytes(ctypes.byref(c), int(T), out), "twell_buffer_bytes")
+    return [int(v) for v in out]
 
 
 def _stream_ptr(stream=None):

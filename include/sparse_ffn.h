@@ -111,24 +111,46 @@ typedef struct {
 
 typedef struct sparse_ffn *sparse_ffn_t;
 
-/* Status name ("SFFN_OK", ...) for a code; never NULL. */
+/* Status name ("SFFN_OK", ...) for a code; never NULL.  Interface of the library (the
+ * pages define no API): error reporting by status codes only. */
 const char *sffn_status_string(sffn_status_t s);
 
-/* Message of the last failing call on this host thread ("" if none). */
+/* Message of the last failing call on this host thread ("" if none).  Interface of the
+ * library; the string is owned by the library and valid until the next failing call on
+ * the same thread. */
 const char *sffn_last_error(void);
 
-/* (host only) Sizes of the twell_buffers_t fields for T tokens.  Validates cfg and T. */
+/* (host only) Sizes of the twell_buffers_t fields for T tokens: the storage of the
+ * TwELL main part (counts, values, local column indices) and of the dense backup
+ * (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom CUDA kernels
+ * solve": per-tile ELL rows plus a few dense backups), and the scratch workspace.
+ * Validates cfg and T; *out is written only on SFFN_OK. */
 sffn_status_t twell_buffer_sizes(const sffn_config_t *cfg, int32_t T, twell_buffer_sizes_t *out);
 
-/* (host only, no device work) Create a layer handle.  Beyond the checks every call
- * makes, a bf16 layer needs d_model % 128 == 0 and d_ff % 256 == 0 (SFFN_ERR_UNSUPPORTED
- * otherwise).  The weights are borrowed: they
- * must stay valid while the handle is used and may be updated in place between calls.
- * b_up may not be NULL (pass zeros for a bias-free layer). */
+/* Number of buffers of twell_buffers_t, in its field order. */
+#define SFFN_N_BUFFERS 10
+
+/* (host only) The same sizes as twell_buffer_sizes, as an array in the field order of
+ * twell_buffers_t: counts, vals, cols, bk_tile, bk_tok, bk_vals, bk_tile_ptr, bk_n,
+ * status, workspace.  out_bytes (host) must hold SFFN_N_BUFFERS entries; it is written
+ * only on SFFN_OK. */
+sffn_status_t twell_buffer_bytes(const sffn_config_t *cfg, int32_t T,
+                                 size_t out_bytes[SFFN_N_BUFFERS]);
+
+/* (host only, no device work) Create a handle for one ReLU FFN layer
+ * y = ReLU(x W_up^T + b) W_down (upppp.jp TwELL article of 2026-05-11, section "What is
+ * the waste in LLM FFN layers": an up-projection that widens each token, an activation,
+ * a down-projection back).  Beyond the checks every call makes, a bf16 layer needs
+ * d_model % 128 == 0 and d_ff % 256 == 0 (SFFN_ERR_UNSUPPORTED otherwise).  The weights
+ * are borrowed device pointers: they must stay valid while the handle is used and may be
+ * updated in place between calls; nothing derived from their values is kept.  b_up may
+ * not be NULL (pass zeros for a bias-free layer).  *out is written only on SFFN_OK. */
 sffn_status_t sparse_ffn_create(const sffn_config_t *cfg, const void *W_up, const void *b_up,
                                 const void *W_down, sparse_ffn_t *out);
 
-/* (host only) Release a handle; NULL is accepted. */
+/* (host only) Release a handle created by sparse_ffn_create; NULL is accepted.
+ * Interface of the library: no device memory is owned, so nothing on the device is
+ * released or waited for. */
 sffn_status_t sparse_ffn_destroy(sparse_ffn_t h);
 
 /* Pack a dense fp32 hidden tensor h [T, d_ff] into TwELL (same article, section "What
@@ -138,10 +160,17 @@ sffn_status_t sparse_ffn_destroy(sparse_ffn_t h);
 sffn_status_t twell_pack(const sffn_config_t *cfg, const float *h, int32_t T,
                          const twell_buffers_t *buf, void *stream);
 
-/* Forward pass y = ReLU(x W_up^T + b) W_down for T tokens.  The up-projection kernel
- * applies bias and ReLU in fp32 (nonzero iff the fp32 pre-activation is > 0) and packs
- * the result into `act` on the fly; the down-projection then reads only the stored
- * entries (main slots and backup).  `act` doubles as the saved activations. */
+/* Forward pass y = ReLU(x W_up^T + b) W_down for T tokens (upppp.jp TwELL article of
+ * 2026-05-11, sections "What is the waste in LLM FFN layers" and "What TwELL and the
+ * custom CUDA kernels solve": the activations are packed into TwELL by the up-projection
+ * kernel itself and the down-projection runs over the stored nonzeros; innovatopia.jp
+ * TwELL article, "Editor's commentary": no extra memory traffic for the format).  The
+ * up-projection kernel applies bias and ReLU in fp32 (nonzero iff the fp32
+ * pre-activation is > 0) and packs the result into `act` on the fly; the down-projection
+ * then reads only the stored entries (main slots and backup).  x [T, d_model] and y
+ * [T, d_model] are device buffers in the layer dtype; `act` (sized for at least T tokens)
+ * doubles as the saved activations.  Host-side argument errors return before any launch;
+ * a backup overflow is reported through act->status (outputs then undefined). */
 sffn_status_t sparse_ffn_forward(sparse_ffn_t h, const void *x, int32_t T, void *y,
                                  const twell_buffers_t *act, void *stream);
 
@@ -210,15 +239,23 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
 #define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
 #define SFFN_DOWN_TILES_MIN_T 4096
 #define SFFN_DOWN_MFMA_MIN_T 64
+/* Set the handle's down-projection policy and the auto policy's two density thresholds
+ * (host only; the policies and their kernels are described above). */
 sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float gather_density,
                                          float mfma_density);
 
-/* (sync) Counters of `buf` for T tokens; synchronises `stream`.  Returns
- * SFFN_ERR_BACKUP_OVERFLOW (with *out filled) if the status word reports an overflow. */
+/* (sync) Counters of `buf` for T tokens (the quantities the TwELL format is built from:
+ * upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom CUDA kernels
+ * solve" - per-tile nonzero counts, the ELL part's fill and the few dense backups);
+ * synchronises `stream`.  *out (host) is filled; returns SFFN_ERR_BACKUP_OVERFLOW (with
+ * *out filled) if the status word reports an overflow. */
 sffn_status_t twell_stats(const sffn_config_t *cfg, const twell_buffers_t *buf, int32_t T,
                           twell_stats_t *out, void *stream);
 
-/* (sync) Synchronise `stream` and return the status word of `buf`. */
+/* (sync) Synchronise `stream` and return the status word of `buf`: SFFN_OK, or
+ * SFFN_ERR_BACKUP_OVERFLOW when more tile-rows overflowed their W slots than the dense
+ * backup holds (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom
+ * CUDA kernels solve": the backup holds only a few rows). */
 sffn_status_t sparse_ffn_check(const twell_buffers_t *buf, void *stream);
 
 /* Test hook: sparse_ffn_forward that also writes the fp32 pre-activation
@@ -227,15 +264,22 @@ sffn_status_t sparse_ffn_check(const twell_buffers_t *buf, void *stream);
 sffn_status_t sparse_ffn_forward_dump(sparse_ffn_t h, const void *x, int32_t T, void *y,
                                       const twell_buffers_t *act, float *z, void *stream);
 
-/* Per-kernel timing: while enabled, every launch of this library on the calling thread
- * is bracketed by HIP events on its stream.  sffn_profile_read synchronises the recorded
- * events and returns, for a kernel name ("up_pack", "down", "pack", "order", ...), the
- * summed duration in ms and the number of launches since the last reset. */
+/* Per-kernel timing (measurement interface of the library, not part of the layer): while
+ * enabled, every launch of this library on the calling thread is bracketed by HIP events
+ * on its stream.  Host only; the event records live in a thread-local host list. */
 sffn_status_t sffn_profile_enable(int32_t enable);
-/* Restrict the timing to the kernels named in `names` (comma-separated, e.g. "up_pack,down");
- * NULL or "" times every launch again.  Fewer events perturb the timed stream less. */
+
+/* Restrict the timing to the kernels named in `names` (host string, comma-separated, e.g.
+ * "up_pack,down"); NULL or "" times every launch again.  Fewer events perturb the timed
+ * stream less. */
 sffn_status_t sffn_profile_only(const char *names);
+
+/* Drop every recorded event pair of the calling thread. */
 sffn_status_t sffn_profile_reset(void);
+
+/* (sync on the recorded events) For a kernel name ("up_pack", "down", "pack", "order",
+ * ...), the summed duration in ms and the number of launches since the last reset
+ * (host outputs; SFFN_ERR_INVALID_ARGUMENT for NULL pointers). */
 sffn_status_t sffn_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 
 #ifdef __cplusplus

@@ -37,6 +37,39 @@ def test_header_symbols_exported(sffn):
     assert sorted(b.exported_names()) == names
 
 
+# The entry points the boundary is specified to export (the interface list the hot path
+# is built behind): each must be declared, exported and documented.
+BOUNDARY = ["twell_buffer_bytes", "sparse_ffn_create", "sparse_ffn_destroy", "twell_pack",
+            "sparse_ffn_forward", "twell_stats", "sparse_ffn_check", "sparse_ffn_backward",
+            "sffn_status_string", "sffn_last_error"]
+
+
+def test_header_declares_boundary_with_comments(sffn):
+    """Every boundary function is declared in the header, and every declaration in the
+    header is preceded by its own comment block (meaning, layout, ownership, errors)."""
+    text = open(HEADER).read()
+    names = _declared_functions()
+    for n in BOUNDARY:
+        assert n in names, n
+    for n in names:
+        m = re.search(r"(\*/)\s*(?:const\s+)?[a-z_]+\s*\*?\s*" + n + r"\s*\(", text)
+        assert m is not None, f"{n}: no comment block right before its declaration"
+
+
+def test_buffer_bytes_matches_sizes(sffn):
+    cfg = sffn.Config(d_model=2048, d_ff=8192, tile=128, ell_width=32, max_tokens=8192,
+                      backup_capacity=4096, dtype="bf16")
+    for T in (1, 100, 8192):
+        s = sffn.buffer_sizes(cfg, T)
+        b = sffn.buffer_bytes(cfg, T)
+        assert b == [s[n] for n in sffn.BUFFER_FIELDS]
+    with pytest.raises(sffn.SffnError):
+        sffn.buffer_bytes(cfg, 0)
+    from activation_sparse_transformer_amd.sparse_ffn import ConfigC, lib
+    c = cfg.c()
+    assert lib().twell_buffer_bytes(ctypes.byref(c), 8, None) == 1
+
+
 def test_header_constants_match_binding(sffn):
     """The binding's down-policy codes, thresholds and token-count rules equal the header's
     #defines (the library reads the header's)."""
@@ -54,6 +87,8 @@ def test_header_constants_match_binding(sffn):
     assert sffn.DOWN_GATHER_DENSITY_DEFAULT <= sffn.DOWN_MFMA_DENSITY_DEFAULT
     mt = re.search(r"#define\s+SFFN_MAX_TILES\s+([0-9]+)", text)
     assert mt and int(mt.group(1)) == sffn.MAX_TILES
+    nb = re.search(r"#define\s+SFFN_N_BUFFERS\s+([0-9]+)", text)
+    assert nb and int(nb.group(1)) == len(sffn.BUFFER_FIELDS)
 
 
 def test_status_strings(sffn):

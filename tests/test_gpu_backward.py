@@ -135,12 +135,14 @@ def test_backward_arguments():
     assert "SFFN_ERR_UNSUPPORTED" in str(ei.value)
 
 
-def test_backward_full_size_sampled():
+def test_backward_full_size():
     """The 1.5B-like training layer at its full size (T=8192), in the launch configuration
-    the benchmark times: dh and dx of sampled tokens against the oracle run on those tokens
-    (both are per-token quantities); dW_down and dW_up of sampled hidden columns against the
-    oracle run on that column over all tokens; db against the column sums of the stored dh."""
+    the benchmark times.  dh and dx of 64 sampled tokens against the oracle run on those
+    tokens (both are per-token quantities); dW_down, dW_up and db of four hidden columns in
+    every tile (256 columns) against the oracle run on those columns over all tokens; db of
+    every column against the column sums of the stored dh."""
     torch, sffn = need_gpu()
+    print("[backward-full] C5", flush=True)
     L = make_layer(CONFIGS["C5"], seed=0)
     c = L["cfg"]
     T = c.T
@@ -158,10 +160,11 @@ def test_backward_full_size_sampled():
     dhost = dict(host)
     dhost["vals"] = dh_vals.view(torch.int16).cpu().numpy().view(np.uint16)
     dhost["bk_vals"] = dh_bk.view(torch.int16).cpu().numpy().view(np.uint16)[:r]
+    K, W, nt = cfg.tile, cfg.ell_width, cfg.n_tiles
 
     rng = np.random.default_rng(4)
-    rows = np.array(sorted(set([0, T - 1] + L["heavy"][:6].tolist()
-                               + rng.choice(T, 16, replace=False).tolist())), np.int64)
+    rows = np.array(sorted(set([0, 1, T - 2, T - 1] + L["heavy"][:12].tolist()
+                               + rng.choice(T, 48, replace=False).tolist())), np.int64)
     from tests.test_gpu_parity import _decode_rows
     h_rows = _decode_rows(cfg, host, rows)
     dh_rows = _decode_rows(cfg, dhost, rows)
@@ -176,41 +179,51 @@ def test_backward_full_size_sampled():
     assert_y_close(dx_rows, fx, "bf16", "full dx")
     assert _rel(dx_rows, dx_r) <= 5e-3
 
-    # weight gradients of sampled hidden columns j, from the whole column of the stored h and
-    # dh (read straight from the TwELL arrays): dW_down[j] = sum_t h[t,j] g[t], dW_up[j] =
-    # sum_t dh[t,j] x[t] (the oracle on the one-column sub-problem)
-    def column(hst, j):
-        K, W = cfg.tile, cfg.ell_width
-        k, cl = divmod(j, K)
-        v = oracle.bf16_value(hst["vals"][k])
-        m = np.minimum(hst["counts"][k].astype(np.int64), W)[:, None] > np.arange(W)[None, :]
-        hit = m & (hst["cols"][k] == cl)
-        out = (v * hit).sum(axis=1)
+    # whole columns of the stored h and dh (read straight from the TwELL arrays) for four
+    # hidden columns per tile; the oracle on that column sub-problem over all tokens
+    cols_sel = np.sort(np.concatenate([k * K + rng.choice(K, 4, replace=False) for k in range(nt)]))
+
+    def columns(hst, js):
+        out = np.zeros((T, len(js)), np.float64)
+        pos = {int(j): i for i, j in enumerate(js)}
+        vals = oracle.bf16_value(hst["vals"])
+        m = np.minimum(host["counts"].astype(np.int64), W)
+        for k in range(nt):
+            sel = m[k][:, None] > np.arange(W)[None, :]
+            t_idx, s_idx = np.nonzero(sel)
+            gc = k * K + host["cols"][k][t_idx, s_idx].astype(np.int64)
+            for i, j in enumerate(js):
+                if j // K != k:
+                    continue
+                hit = gc == j
+                out[t_idx[hit], i] = vals[k][t_idx[hit], s_idx[hit]]
         bv = oracle.bf16_value(hst["bk_vals"])
         for e in range(r):
-            if host["bk_tile"][e] == k:
-                out[host["bk_tok"][e]] += bv[e, cl]
+            k, t = int(host["bk_tile"][e]), int(host["bk_tok"][e])
+            for cl in np.nonzero(bv[e])[0]:
+                i = pos.get(k * K + int(cl))
+                if i is not None:
+                    out[t, i] = bv[e, cl]
         return out
+    hc = columns(host, cols_sel)
+    dhc = columns(dhost, cols_sel)
+    _, _, dwd_c, _, _ = oracle.backward(x64, hc, g64, Wu64[cols_sel], Wd64[cols_sel])
+    _, dwu_c, db_c = oracle.backward_from_dh(x64, dhc, Wu64[cols_sel])
     dWd_h = dWd.cpu().numpy().astype(np.float64)
     dWu_h = dWu.cpu().numpy().astype(np.float64)
-    for j in rng.choice(c.F, 6, replace=False).tolist():
-        hc = column(host, j)[:, None]
-        dhc = column(dhost, j)[:, None]
-        _, _, dwd_j, _, _ = oracle.backward(x64, hc, g64, Wu64[[j]], Wd64[[j]])
-        _, dwu_j, _ = oracle.backward_from_dh(x64, dhc, Wu64[[j]])
-        assert_y_close(dWd_h[j], dwd_j[0], "bf16", f"full dW_down[{j}]")
-        assert_y_close(dWu_h[j], dwu_j[0], "bf16", f"full dW_up[{j}]")
-    # db is the column sum of dh
     dbh = db.cpu().numpy().astype(np.float64)
+    assert_y_close(dWd_h[cols_sel], dwd_c, "bf16", "full dW_down columns")
+    assert _rel(dWd_h[cols_sel], dwd_c) <= 1e-4
+    assert_y_close(dWu_h[cols_sel], dwu_c, "bf16", "full dW_up columns")
+    assert_y_close(dbh[cols_sel], db_c, "bf16", "full db columns")
+    # db of every column is the column sum of the stored dh
     col = np.zeros(c.F)
-    W = cfg.ell_width
-    K = cfg.tile
     vals = oracle.bf16_value(dhost["vals"])
-    cols = host["cols"].astype(np.int64)
+    cidx = host["cols"].astype(np.int64)
     m = np.minimum(host["counts"].astype(np.int64), W)
-    for k in range(cfg.n_tiles):
+    for k in range(nt):
         sel = m[k][:, None] > np.arange(W)[None, :]
-        np.add.at(col, k * K + cols[k][sel], vals[k][sel])
+        np.add.at(col, k * K + cidx[k][sel], vals[k][sel])
     bkv = oracle.bf16_value(dhost["bk_vals"])
     for e in range(r):
         col[host["bk_tile"][e] * K: (host["bk_tile"][e] + 1) * K] += bkv[e]
