@@ -355,6 +355,28 @@ sffn_status_t sparse_ffn_forward(sparse_ffn_t hd, const void* x, int32_t T, void
   return forward_impl(hd, x, T, y, act, nullptr, stream);
 }
 
+sffn_status_t sparse_ffn_forward_noalloc(sparse_ffn_t hd, const void* x, int32_t T, void* y,
+                                         const twell_buffers_t* act, void* stream) {
+  if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
+  SFFN_TRY(check_T(&hd->cfg, T));
+  if (!x || !y) return fail(SFFN_ERR_INVALID_ARGUMENT, "x or y is NULL");
+  SFFN_TRY(check_bufs(act, false));
+  const Dims d = make_dims(&hd->cfg, T);
+  const size_t need = workspace_bytes(d, true);
+  if (need > (size_t)SFFN_NOALLOC_SCRATCH_BYTES)
+    return fail(SFFN_ERR_UNSUPPORTED,
+                "this call needs " + std::to_string(need) +
+                    " bytes of workspace, more than the no-allocation scratch holds (" +
+                    std::to_string((size_t)SFFN_NOALLOC_SCRATCH_BYTES) + ")");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  const hipError_t e = noalloc_scratch(s, &scratch);
+  if (e != hipSuccess) return dev_fail(e, "no-allocation scratch lookup");
+  twell_buffers_t a = *act;
+  a.workspace = scratch;
+  return forward_impl(hd, x, T, y, &a, nullptr, stream);
+}
+
 sffn_status_t sparse_ffn_forward_dump(sparse_ffn_t hd, const void* x, int32_t T, void* y,
                                       const twell_buffers_t* act, float* z, void* stream) {
   if (!z) return fail(SFFN_ERR_INVALID_ARGUMENT, "z is NULL");

@@ -73,7 +73,9 @@ inline size_t down_part_floats(const Dims& d) {
   return best;
 }
 
-inline size_t workspace_bytes(const Dims& d) {
+// this_call_only: size the split partial sums for a call of exactly d.T tokens (the
+// workspace is used by that call alone) instead of for every T' <= d.T.
+inline size_t workspace_bytes(const Dims& d, bool this_call_only = false) {
   size_t n = 0;
   n += align256(sizeof(int32_t));
   n += align256(sizeof(int32_t) * (size_t)d.nt * d.ng);
@@ -84,9 +86,16 @@ inline size_t workspace_bytes(const Dims& d) {
   n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
   n += align256(sizeof(int32_t) * (size_t)d.nt);
   n += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
-  n += align256(sizeof(float) * down_part_floats(d));
+  const int S = down_split(d);
+  n += align256(sizeof(float) * (this_call_only ? (S > 1 ? (size_t)S * d.T * d.D : 0)
+                                                : down_part_floats(d)));
   return n;
 }
+
+// Callers that cannot allocate device memory: the forward variant that takes its
+// workspace from a fixed array inside the library (one per device).  Returns the device
+// address of the calling stream's device's array (looked up once per device).
+hipError_t noalloc_scratch(hipStream_t s, void** out);
 
 inline Workspace carve(void* base, const Dims& d) {
   char* p = static_cast<char*>(base);

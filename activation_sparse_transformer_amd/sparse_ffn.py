@@ -87,6 +87,7 @@ _PROTOS = {
     "twell_stats": ([ctypes.POINTER(ConfigC), ctypes.POINTER(BuffersC), _I32,
                      ctypes.POINTER(StatsC), _P], ctypes.c_int),
     "sparse_ffn_check": ([ctypes.POINTER(BuffersC), _P], ctypes.c_int),
+    "sparse_ffn_forward_noalloc": ([_P, _P, _I32, _P, ctypes.POINTER(BuffersC), _P], ctypes.c_int),
     "sparse_ffn_forward_dump": ([_P, _P, _I32, _P, ctypes.POINTER(BuffersC), _P, _P], ctypes.c_int),
     "sffn_profile_enable": ([_I32], ctypes.c_int),
     "sffn_profile_only": ([ctypes.c_char_p], ctypes.c_int),
@@ -304,6 +305,23 @@ class SparseFFN:
         y = y if y is not None else torch.empty_like(x)
         _check(lib().sparse_ffn_forward(self._h, _ptr(x), int(T), _ptr(y), ctypes.byref(act.c()),
                                         _stream_ptr(stream)), "sparse_ffn_forward")
+        return y, act
+
+    def forward_noalloc(self, x, act: TwellBuffers, y, stream=None, workspace=False):
+        """sparse_ffn_forward_noalloc: the forward with its workspace in the library's fixed
+        device scratch.  act (TwELL and backup outputs) and y are the caller's; act's own
+        workspace is passed as NULL unless `workspace` is set (it is ignored either way)."""
+        self._check_x(x)
+        T = x.shape[0]
+        act._hold(self.cfg, T)
+        if tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype or not y.is_contiguous():
+            raise ValueError("y must be a contiguous tensor shaped and typed like x")
+        c = act.c()
+        b = BuffersC(*[getattr(c, n) for n in BUFFER_FIELDS])
+        if not workspace:
+            b.workspace = None
+        _check(lib().sparse_ffn_forward_noalloc(self._h, _ptr(x), int(T), _ptr(y), ctypes.byref(b),
+                                                _stream_ptr(stream)), "sparse_ffn_forward_noalloc")
         return y, act
 
     def forward_dump(self, x, stream=None):

@@ -258,6 +258,24 @@ sffn_status_t twell_stats(const sffn_config_t *cfg, const twell_buffers_t *buf, 
  * CUDA kernels solve": the backup holds only a few rows). */
 sffn_status_t sparse_ffn_check(const twell_buffers_t *buf, void *stream);
 
+/* Size of the fixed device scratch of sparse_ffn_forward_noalloc (bytes, per device). */
+#define SFFN_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sparse_ffn_forward with its workspace
+ * taken from a fixed scratch array inside the library instead of act->workspace, which is
+ * ignored (may be NULL).  Same kernels and results as sparse_ffn_forward; no device memory
+ * is allocated or freed.  Every device the library runs on holds one such array of
+ * SFFN_NOALLOC_SCRATCH_BYTES until the process ends; calls on one device share it and keep
+ * the last call's contents, so calls that overlap on one device (other streams, other host
+ * threads) race, and the workspace-dependent state of a call (the per-group backup offsets
+ * that sparse_ffn_down and sparse_ffn_backward read) does not outlive the next call: the
+ * TwELL and backup written into act stay complete and canonical.  Returns
+ * SFFN_ERR_UNSUPPORTED, before any launch, when the call's workspace (twell_buffer_sizes'
+ * workspace for exactly these T tokens) exceeds the scratch. */
+sffn_status_t sparse_ffn_forward_noalloc(sparse_ffn_t h, const void *x, int32_t T, void *y,
+                                         const twell_buffers_t *act, void *stream);
+
 /* Test hook: sparse_ffn_forward that also writes the fp32 pre-activation
  * z = x W_up^T + b [T, d_ff] (before ReLU) exactly as the up-projection kernel computed
  * it, so its TwELL can be checked against a pack of the same z. */
