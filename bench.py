@@ -103,6 +103,48 @@ def average_power(path, run, seconds):
     return (sum(keep) / len(keep) if keep else float("nan")), calls, elapsed
 
 
+def down_roofline(st, T, D, F, K, esz, ms, kernel):
+    """Roofline of a down-projection launch on the method's own work: flops = one
+    multiply-add per stored main slot and output column plus the dense [1 x K] x [K x D]
+    product of every backup entry (2 slots_used D + 2 K D R); HBM bytes = the TwELL main
+    part and backup read once, W_down read once, y written once.  `kernel` is "mfma" (a
+    matrix-core kernel: flops against the bf16 MFMA peak) or "alu" (vector kernel: against
+    the vector peak).  The binding roofline is the one with the larger floor time."""
+    R = int(st["overflow_tile_rows"])
+    flops = 2.0 * float(st["slots_used"]) * D + 2.0 * K * D * R
+    hbm_bytes = float(st["bytes_main"] + st["bytes_backup"]) + F * D * esz + T * D * esz
+    sec = ms * 1e-3
+    peak_c = PEAK_BF16_TFLOPS if kernel == "mfma" else PEAK_VALU_TFLOPS
+    tflops = flops / sec / 1e12 if sec > 0 else 0.0
+    gbs = hbm_bytes / sec / 1e9 if sec > 0 else 0.0
+    floor_c = flops / (peak_c * 1e12)
+    floor_m = hbm_bytes / (PEAK_HBM_GBS * 1e9)
+    out = {"algorithmic_flops": flops, "algorithmic_bytes": hbm_bytes,
+           "tflops": round(tflops, 3), f"{kernel}_frac": round(tflops / peak_c, 5),
+           "hbm_gbs": round(gbs, 2), "hbm_frac": round(gbs / PEAK_HBM_GBS, 5),
+           "dense_equiv_tflops": round(2.0 * T * F * D / sec / 1e12, 2) if sec > 0 else 0.0,
+           "floor_us": {kernel: round(floor_c * 1e6, 3), "hbm": round(floor_m * 1e6, 3)}}
+    out["bound"] = "hbm" if floor_m >= floor_c else kernel
+    return out
+
+
+def parity_metrics(y, ref):
+    """max |y - ref| / (1 + |ref|) and the relative Frobenius error (fp64)."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(y - ref)
+    nr = float(np.linalg.norm(ref))
+    return {"max_rel_elem": float((d / (1.0 + np.abs(ref))).max()) if d.size else 0.0,
+            "rel_frobenius": float(np.linalg.norm(y - ref) / nr) if nr > 0 else float(np.linalg.norm(y))}
+
+
+def spread(ms_list):
+    """median, p10 and p90 of per-step times (ms)."""
+    a = np.sort(np.asarray(ms_list, np.float64))
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "n": int(a.size)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,11 +153,14 @@ def main():
     ap.add_argument("--rho", type=float, default=0.05, help="density of the headline point")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the per-point oracle checks")
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward timing")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / GEMM ceilings")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times): the reference "
                          "kernel that scales hardware byte counters to bytes")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="target seconds of one CPU oracle run (each path is run 3 times)")
     ap.add_argument("--energy-seconds", type=float, default=2.0,
                     help="seconds of repeated forwards per energy measurement (0: skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shaped points")
@@ -144,6 +189,9 @@ def main():
     def bf16_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    def bf16_host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
     x = bf16_dev(L0["x"])
     Wu = bf16_dev(L0["W_up"])
     Wd = bf16_dev(L0["W_down"])
@@ -169,6 +217,41 @@ def main():
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
 
+    def per_step(fn, steps, warmup):
+        """Per-step times (ms) from events around each step: median, p10, p90."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return spread([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+
+    rng_rows = np.random.default_rng(7)
+
+    def sample_rows(Tn, heavy, n):
+        """First, last, up to 16 heavy and random token rows (sorted, unique)."""
+        r = set([0, Tn - 1]) | set(np.asarray(heavy, np.int64)[:16].tolist())
+        r |= set(rng_rows.choice(Tn, min(n, Tn), replace=False).tolist())
+        return np.array(sorted(r), np.int64)
+
+    # Per-point parity: the GPU's y of sampled rows is kept here (host copy); the CPU leg at
+    # the end runs the oracle on the same rows and fills in each point's "parity" entry.
+    pending = []
+
+    def point_parity(target, Lp, yt, rows, K, W):
+        if args.no_parity or args.no_cpu:
+            target["parity"] = None
+            return
+        yb = bf16_host(yt[torch.from_numpy(rows).to(dev)]).copy()
+        pending.append((target, Lp, yb, rows, K, W))
+
+    down_names = sffn_down_names()
+    timed_names = ("up_pack",) + down_names
+
     def sparse_point(rho, steps, warmup, profile=False, only=None):
         L = bias_for_density(L0, rho)
         b = bf16_dev(L["b_up"])
@@ -190,26 +273,30 @@ def main():
                 kt[k] = tot / max(n, 1)
             sffn.profile_reset()
             sffn.profile_only(None)
+        assert sffn.check(act) == sffn.SFFN_OK, "backup overflow in a timed point"
         st = sffn.twell_stats(cfg, act)
-        return ms, wall, kt, st, b
+        return ms, wall, kt, st, b, L, layer
+
+    def down_of(kt):
+        name = max(down_names, key=lambda k: kt.get(k, 0.0))
+        return name, ("alu" if name in ("down", "down_tiles") else "mfma")
 
     # ---- headline point: the timed region brackets the up kernel and the down kernels (the
     # roofline's candidates) with HIP events on the launch stream; the small kernels' times
     # come from a separate pass that times every launch
     log(f"sparse forward, rho={args.rho}, {args.warmup} warmup + {args.steps} timed steps")
-    down_names = ("down", "down_tiles", "down_mfma")
-    timed_names = ("up_pack",) + down_names
-    ms, wall, kt, st, b0 = sparse_point(args.rho, args.steps, args.warmup, profile=True,
-                                        only=timed_names)
-    ms_plain, _, _, _, _ = sparse_point(args.rho, args.steps, 2, profile=False)
-    _, _, kt_all, _, _ = sparse_point(args.rho, max(10, args.steps // 5), 2, profile=True)
+    ms, wall, kt, st, b0, Lh, layer_h = sparse_point(args.rho, args.steps, args.warmup, profile=True,
+                                                    only=timed_names)
+    ms_plain, _, _, _, _, _, _ = sparse_point(args.rho, args.steps, 2, profile=False)
+    _, _, kt_all, _, _, _, _ = sparse_point(args.rho, max(10, args.steps // 5), 2, profile=True)
     kt = {**kt_all, **kt}
-    log(f"  {ms:.4f} ms/step (profiled), {ms_plain:.4f} ms/step (no events); kernels {kt}")
-
-    # ---- which down-projection kernel took the layer: under the auto policy all candidates
-    # are launched and all but one return at once (a few microseconds)
-    down_ran = max(down_names, key=lambda k: kt.get(k, 0.0))
+    sp_steps = per_step(lambda: layer_h.forward(x, act=act, y=y), max(20, args.steps), 3)
+    log(f"  {ms:.4f} ms/step (profiled), {ms_plain:.4f} ms/step (no events), per step {sp_steps}; "
+        f"kernels {kt}")
+    down_ran, down_kind = down_of(kt)
     nnz = st["nnz"]
+    head = {}
+    point_parity(head, Lh, y, sample_rows(T, Lh["heavy"], 512), c.tile, c.ell_width)
 
     # ---- dense bf16 FFN baseline (hipBLASLt through torch), same inputs and stream
     def dense():
@@ -217,7 +304,30 @@ def main():
         return torch.matmul(h, Wd)
     log("dense bf16 FFN baseline")
     ms_dense, _ = time_steps(dense, args.steps, args.warmup)
-    log(f"  {ms_dense:.4f} ms/step")
+    dn_steps = per_step(dense, max(20, args.steps), 3)
+    log(f"  {ms_dense:.4f} ms/step, per step {dn_steps}")
+
+    # ---- measured ceilings on this GPU: a plain device copy (HBM) and hipBLASLt GEMMs of the
+    # layer's two shapes (dense bf16 MFMA)
+    ceilings = None
+    if not args.no_ceilings:
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        cp_ms, _ = time_steps(lambda: dst.copy_(src), 20, 3)
+        h_b = torch.randn((T, F), device=dev).to(torch.bfloat16)
+        g_up, _ = time_steps(lambda: torch.matmul(x, Wu.t()), 20, 3)
+        g_dn, _ = time_steps(lambda: torch.matmul(h_b, Wd), 20, 3)
+        fl = 2.0 * T * D * F
+        ceilings = {"copy_gbs": round(2 * nb / (cp_ms * 1e-3) / 1e9, 1),
+                    "copy_bytes": 2 * nb,
+                    "gemm_up_shape_tflops": round(fl / (g_up * 1e-3) / 1e12, 1),
+                    "gemm_down_shape_tflops": round(fl / (g_dn * 1e-3) / 1e12, 1),
+                    "gemm_up_ms": round(g_up, 5), "gemm_down_ms": round(g_dn, 5),
+                    "shapes": f"[{T},{D}]x[{D},{F}] and [{T},{F}]x[{F},{D}] bf16 (torch.matmul)"}
+        del src, dst, h_b
+        torch.cuda.empty_cache()
+        log(f"  ceilings {ceilings}")
 
     # ---- training step of the same layer (1.5B-like training layer): forward + backward over
     # TwELL, against the dense bf16 FFN forward + its backward matmuls
@@ -274,18 +384,26 @@ def main():
         log(f"  sparse {ms_tr:.4f} ms (backward {ms_bwd:.4f}), dense {ms_dtr:.4f} ms; {ktr}")
         del bout
 
-    # ---- density sweep
+    # ---- density sweep: per point the kernel times, the down kernel's roofline on the
+    # method's work, and the oracle check of sampled rows
     sweep = []
     if not args.no_sweep:
         for rho in (0.002, 0.005, 0.01, 0.05, 0.10, 0.20):
-            m, _, k2, s2, _ = sparse_point(rho, max(10, args.steps // 2), 3, profile=True)
-            sweep.append({"rho_target": rho, "density": round(s2["density"], 5),
-                          "overflow_tile_rows": int(s2["overflow_tile_rows"]),
-                          "ms_per_step": round(m, 4), "tokens_per_s": round(T / (m * 1e-3), 1),
-                          "dense_tokens_per_s": round(T / (ms_dense * 1e-3), 1),
-                          "speedup_vs_dense": round(ms_dense / m, 4),
-                          "kernel_ms": {k: round(v, 4) for k, v in k2.items()}})
+            m, _, k2, s2, _, Lr, layer_r = sparse_point(rho, max(10, args.steps // 2), 3, profile=True)
+            dn, kind = down_of(k2)
+            pt = {"rho_target": rho, "density": round(s2["density"], 5),
+                  "nnz": int(s2["nnz"]), "slots_used": int(s2["slots_used"]),
+                  "overflow_tile_rows": int(s2["overflow_tile_rows"]),
+                  "ms_per_step": round(m, 4), "tokens_per_s": round(T / (m * 1e-3), 1),
+                  "dense_tokens_per_s": round(T / (ms_dense * 1e-3), 1),
+                  "speedup_vs_dense": round(ms_dense / m, 4),
+                  "kernel_ms": {k: round(v, 4) for k, v in k2.items()},
+                  "down_kernel": dn,
+                  "down_roofline": down_roofline(s2, T, D, F, c.tile, 2, k2[dn], kind)}
+            point_parity(pt, Lr, y, sample_rows(T, Lr["heavy"], 96), c.tile, c.ell_width)
+            sweep.append(pt)
             log(f"  sweep rho={rho}: {m:.4f} ms, density {s2['density']:.4f}, {k2}")
+            del layer_r
 
     # ---- per-kernel rates and the roofline of the dominant kernel
     src_hash = kernel_source_hash()
@@ -301,24 +419,16 @@ def main():
 
     up_ms, dn_ms = kt["up_pack"], kt[down_ran]
     up_flops = 2.0 * T * D * F
-    dense_flops = 2.0 * T * F * D              # the matrix-core kernel's dense-equivalent work
-    sparse_flops = 2.0 * nnz * D               # one MAC per stored nonzero per output column
-    rate = lambda fl, ms: fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+    rate = lambda fl, ms_: fl / (ms_ * 1e-3) / 1e12 if ms_ > 0 else 0.0
+    dn_roof = down_roofline(st, T, D, F, c.tile, 2, dn_ms, down_kind)
     kernels = {
         "up_pack": {"ms": round(up_ms, 5), "tflops": round(rate(up_flops, up_ms), 2),
                     "frac_mfma_peak": round(rate(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4)},
-        "order": {"ms": round(kt["order"], 5)}, "zero": {"ms": round(kt["zero"], 5)},
-        "block_nnz": {"ms": round(kt["block_nnz"], 5)},
-        "down_launches_ms": {k: round(kt[k], 5) for k in down_names},
+        "order": {"ms": round(kt.get("order", 0.0), 5)}, "zero": {"ms": round(kt.get("zero", 0.0), 5)},
+        "block_nnz": {"ms": round(kt.get("block_nnz", 0.0), 5)},
+        "down_launches_ms": {k: round(kt.get(k, 0.0), 5) for k in down_names},
+        "down": {"kernel": down_ran, "ms": round(dn_ms, 5), **dn_roof},
     }
-    if down_ran == "down_mfma":
-        kernels["down"] = {"kernel": "down_mfma", "ms": round(dn_ms, 5),
-                           "dense_equiv_tflops": round(rate(dense_flops, dn_ms), 2),
-                           "frac_mfma_peak": round(rate(dense_flops, dn_ms) / PEAK_BF16_TFLOPS, 4)}
-    else:
-        kernels["down"] = {"kernel": down_ran, "ms": round(dn_ms, 5), "nnz": int(nnz),
-                           "tflops": round(rate(sparse_flops, dn_ms), 2),
-                           "frac_valu_peak": round(rate(sparse_flops, dn_ms) / PEAK_VALU_TFLOPS, 4)}
     if up_ms >= dn_ms:
         roofline = {"bound": "mfma", "achieved": round(rate(up_flops, up_ms), 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -326,21 +436,26 @@ def main():
                     "traffic": traffic_of("up_pack"),
                     "kernel": "up_pack_bf16_kernel (fused up-projection + bias + ReLU + TwELL pack)",
                     "avg_launch_ms": round(up_ms, 5), "algorithmic_flops_per_launch": up_flops}
-    elif down_ran == "down_mfma":
-        roofline = {"bound": "mfma", "achieved": round(rate(dense_flops, dn_ms), 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(rate(dense_flops, dn_ms) / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_of("down_mfma"),
-                    "kernel": "down_mfma_kernel (TwELL tiles rebuilt in LDS, MFMA down-projection)",
-                    "avg_launch_ms": round(dn_ms, 5), "algorithmic_flops_per_launch": dense_flops}
     else:
         kname = {"down": "down_rows_kernel (per-token W_down row gather)",
-                 "down_tiles": "down_lds_kernel (W_down tiles in LDS, bf16 dot products)"}[down_ran]
-        roofline = {"bound": "alu", "achieved": round(rate(sparse_flops, dn_ms), 2),
-                    "peak": PEAK_VALU_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(rate(sparse_flops, dn_ms) / PEAK_VALU_TFLOPS, 4),
-                    "traffic": traffic_of(down_ran), "kernel": kname,
-                    "avg_launch_ms": round(dn_ms, 5), "algorithmic_flops_per_launch": sparse_flops}
+                 "down_tiles": "down_lds_kernel (W_down tiles in LDS, bf16 dot products)",
+                 "down_mfma": "down_mfma_kernel (TwELL tiles rebuilt in LDS, MFMA down-projection)",
+                 "down_union": "down_union_kernel (column-union compacted MFMA down-projection)"}.get(
+            down_ran, down_ran)
+        if dn_roof["bound"] == "hbm":
+            roofline = {"bound": "hbm", "achieved": dn_roof["hbm_gbs"], "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": dn_roof["hbm_frac"]}
+        else:
+            pk = PEAK_BF16_TFLOPS if down_kind == "mfma" else PEAK_VALU_TFLOPS
+            roofline = {"bound": down_kind, "achieved": dn_roof["tflops"], "peak": pk,
+                        "unit": "TFLOP/s", "frac": dn_roof[f"{down_kind}_frac"]}
+        roofline.update({"traffic": traffic_of(down_ran), "kernel": kname,
+                         "avg_launch_ms": round(dn_ms, 5),
+                         "algorithmic_flops_per_launch": dn_roof["algorithmic_flops"],
+                         "algorithmic_bytes_per_launch": dn_roof["algorithmic_bytes"],
+                         f"{down_kind}_frac": dn_roof[f"{down_kind}_frac"],
+                         "hbm_frac": dn_roof["hbm_frac"],
+                         "dense_equiv_tflops": dn_roof["dense_equiv_tflops"]})
 
     # ---- energy per token of the headline forward, sparse and dense (board power sampled
     # every 10 ms while the forward runs back to back)
@@ -393,17 +508,29 @@ def main():
             layer_c = sffn.SparseFFN(cfg_c, Wuc, bc, Wdc)
             act_c = sffn.TwellBuffers(cfg_c, cc.T)
             yc = torch.empty_like(xc)
+            sffn.profile_reset()
+            sffn.profile_enable(True)
             ms_c, _ = time_steps(lambda: layer_c.forward(xc, act=act_c, y=yc), max(10, args.steps // 2), 3)
+            sffn.profile_enable(False)
+            kc = {k: sffn.profile_read(k)[0] / max(sffn.profile_read(k)[1], 1) for k in KERNELS}
+            sffn.profile_reset()
             ms_cd, _ = time_steps(lambda: torch.matmul(Fn.relu(Fn.linear(xc, Wuc, bc)), Wdc),
                                   max(10, args.steps // 2), 3)
+            assert sffn.check(act_c) == sffn.SFFN_OK
             stc = sffn.twell_stats(cfg_c, act_c)
-            layers.append({"layer": cc.name, "T": cc.T, "d_model": cc.D, "d_ff": cc.F,
-                           "tile": cc.tile, "ell_width": cc.ell_width,
-                           "density": round(stc["density"], 5),
-                           "overflow_tile_rows": int(stc["overflow_tile_rows"]),
-                           "ms_sparse": round(ms_c, 5), "ms_dense": round(ms_cd, 5),
-                           "tokens_per_s": round(cc.T / (ms_c * 1e-3), 1),
-                           "speedup_vs_dense": round(ms_cd / ms_c, 4)})
+            dn_c, kind_c = down_of(kc)
+            lp = {"layer": cc.name, "T": cc.T, "d_model": cc.D, "d_ff": cc.F,
+                  "tile": cc.tile, "ell_width": cc.ell_width,
+                  "density": round(stc["density"], 5),
+                  "overflow_tile_rows": int(stc["overflow_tile_rows"]),
+                  "ms_sparse": round(ms_c, 5), "ms_dense": round(ms_cd, 5),
+                  "tokens_per_s": round(cc.T / (ms_c * 1e-3), 1),
+                  "speedup_vs_dense": round(ms_cd / ms_c, 4),
+                  "kernel_ms": {k: round(v, 4) for k, v in kc.items()},
+                  "down_kernel": dn_c,
+                  "down_roofline": down_roofline(stc, cc.T, cc.D, cc.F, cc.tile, 2, kc[dn_c], kind_c)}
+            point_parity(lp, Lc, yc, sample_rows(cc.T, Lc["heavy"], 96), cc.tile, cc.ell_width)
+            layers.append(lp)
             log(f"  layer {cc.name}: sparse {ms_c:.4f} ms, dense {ms_cd:.4f} ms, "
                 f"density {stc['density']:.4f}")
             del layer_c, act_c, xc, Wuc, bc, Wdc, yc
@@ -422,11 +549,14 @@ def main():
             yd = torch.empty_like(xd)
             layer_d = sffn.SparseFFN(cfg_d, Wu, b0, Wd)
             pt = {"T": Td}
-            for pol in ("auto", "gather", "mfma"):
+            for pol in decode_policies():
                 layer_d.set_down_policy(pol)
                 ms_d, _ = time_steps(lambda: layer_d.forward(xd, act=act_d, y=yd), 50, 10)
+                assert sffn.check(act_d) == sffn.SFFN_OK
                 pt[f"ms_{pol}"] = round(ms_d, 5)
             layer_d.set_down_policy("auto")
+            layer_d.forward(xd, act=act_d, y=yd)
+            assert sffn.check(act_d) == sffn.SFFN_OK
             ms_dd, _ = time_steps(lambda: torch.matmul(Fn.relu(Fn.linear(xd, Wu, b0)), Wd), 50, 10)
             hs = act_d.to_host()
             used = np.zeros(F, bool)
@@ -446,33 +576,64 @@ def main():
                        "weight_bytes_sparse": sp_bytes, "weight_bytes_dense": dn_bytes,
                        "hbm_gbs_sparse": round(sp_bytes / (pt["ms_auto"] * 1e-3) / 1e9, 1),
                        "hbm_gbs_dense": round(dn_bytes / (ms_dd * 1e-3) / 1e9, 1)})
+            Ld = {k: (v[:Td] if k in ("x", "x_f32") else v) for k, v in Lh.items()}
+            point_parity(pt, Ld, yd, np.arange(Td, dtype=np.int64), c.tile, c.ell_width)
             decode.append(pt)
             log(f"  decode T={Td}: {pt}")
             del layer_d, act_d
 
-    # ---- CPU fp64 oracle on a bounded sample of the same workload
+    # ---- CPU fp64 oracle on bounded samples of the same workload, the sparse path (up-projection,
+    # ReLU, TwELL pack, sparse down-projection, per token) and the dense FFN; median of 3 runs each
     cpu = None
     if not args.no_cpu:
-        import oracle
-        x64 = L0["x_f32"].astype(np.float64)
-        Wu64 = L0["W_up_f32"].astype(np.float64)
-        b64 = oracle.bf16_value(b0.view(torch.int16).cpu().numpy().view(np.uint16))
-        Wd64 = L0["W_down_f32"].astype(np.float64)
-        threads = oracle.num_threads()
+        import oracle as orc  # the CPU fp64 oracle: this leg only
+        for target, Lp, yb, rows, K, W in pending:
+            x64, Wu64, b64, Wd64 = (Lp[k].astype(np.float64)
+                                    for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+            y_st, _ = orc.ffn_rows(x64, Wu64, b64, Wd64, rows, K, W, round_h=True)
+            y_pl, _ = orc.ffn_rows(x64, Wu64, b64, Wd64, rows, K, W, round_h=False)
+            yh = orc.bf16_value(yb)
+            a = parity_metrics(yh, y_st)
+            target["parity"] = {"rows": int(len(rows)), "vs_oracle_bf16_activations": a,
+                                "vs_plain_fp64_ffn": parity_metrics(yh, y_pl),
+                                "within_tolerance": bool(a["max_rel_elem"] <= 1e-2 and
+                                                         a["rel_frobenius"] <= 5e-3)}
+        log(f"parity of {len(pending)} points checked against the oracle; headline {head.get('parity')}")
+        x64 = Lh["x_f32"].astype(np.float64)
+        Wu64 = Lh["W_up_f32"].astype(np.float64)
+        b64 = Lh["b_up_f32"].astype(np.float64)
+        Wd64 = Lh["W_down_f32"].astype(np.float64)
+        threads = orc.num_threads()
         n = max(threads, 16)
-        rows = np.arange(n, dtype=np.int64)
         t0 = time.perf_counter()
-        oracle.ffn_rows(x64, Wu64, b64, Wd64, rows, c.tile, c.ell_width, round_h=True)
+        orc.ffn_rows(x64, Wu64, b64, Wd64, np.arange(n, dtype=np.int64), c.tile, c.ell_width, round_h=True)
         t1 = time.perf_counter() - t0
         n2 = int(min(T, max(n, n * args.cpu_seconds / max(t1, 1e-3))))
         rows = np.linspace(0, T - 1, n2).astype(np.int64)
-        log(f"CPU oracle: {n2} tokens on {threads} threads")
-        t0 = time.perf_counter()
-        oracle.ffn_rows(x64, Wu64, b64, Wd64, rows, c.tile, c.ell_width, round_h=True)
-        t2 = time.perf_counter() - t0
-        cpu = {"value": round(n2 / t2, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"{n2} of {T} tokens of the same layer (per-token fp64 up-projection, "
-                         f"ReLU, TwELL-order sparse down-projection), {t2:.1f} s"}
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            orc.ffn_rows(x64, Wu64, b64, Wd64, rows, c.tile, c.ell_width, round_h=True)
+            ts.append(time.perf_counter() - t0)
+        t_sp = float(np.median(ts))
+        nd = max(threads, n2 // 2)
+        rows_d = np.linspace(0, T - 1, nd).astype(np.int64)
+        td = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            orc.ffn_dense(x64[rows_d], Wu64, b64, Wd64)
+            td.append(time.perf_counter() - t0)
+        t_dn = float(np.median(td))
+        log(f"CPU oracle: sparse path {n2} tokens {t_sp:.2f} s, dense FFN {nd} tokens {t_dn:.2f} s, "
+            f"{threads} threads")
+        cpu = {"value": round(n2 / t_sp, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n2} of {T} tokens of the same layer through the oracle's sparse path "
+                         f"(per-token fp64 up-projection, ReLU, TwELL pack, sparse down-projection), "
+                         f"median of 3 runs ({', '.join(f'{v:.2f}' for v in ts)} s)",
+               "dense_ffn_tokens_per_s": round(nd / t_dn, 2),
+               "dense_sample": f"{nd} tokens through the oracle's dense FFN, median of 3 runs "
+                               f"({', '.join(f'{v:.2f}' for v in td)} s)",
+               "label": f"CPU fp64 oracle, {threads} threads - reference baseline, not the target"}
 
     tok_s = T / (ms * 1e-3)
     out = {
@@ -487,12 +648,16 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense_bf16": {"ms_per_step": round(ms_dense, 5), "tokens_per_s": round(T / (ms_dense * 1e-3), 1),
-                       "speedup_sparse_vs_dense": round(ms_dense / ms, 4)},
+                       "speedup_sparse_vs_dense": round(ms_dense / ms, 4), "per_step_ms": dn_steps},
+        "per_step_ms": sp_steps,
         "ms_per_step_without_kernel_events": round(ms_plain, 5),
+        "parity": head.get("parity"),
         "measured": {"density": round(st["density"], 5), "nnz": int(nnz),
+                     "slots_used": int(st["slots_used"]),
                      "overflow_tile_rows": int(st["overflow_tile_rows"]),
                      "ell_fill": round(st["ell_fill"], 4)},
         "kernels": kernels,
+        "ceilings": ceilings,
         "effective_tflops_dense_equiv": round(4.0 * T * D * F / (ms * 1e-3) / 1e12, 2),
         "train": train,
         "energy": energy,
@@ -512,6 +677,15 @@ def main():
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n
     print(json.dumps(out), flush=True)
+
+
+def sffn_down_names():
+    """Event names of the library's down-projection launches."""
+    return ("down", "down_tiles", "down_mfma")
+
+
+def decode_policies():
+    return ("auto", "gather", "mfma")
 
 
 if __name__ == "__main__":

@@ -52,3 +52,30 @@ def test_traffic_counters_name_their_sources():
         assert tuple(ent["sources"]) == bench.KERNEL_SOURCES[name]
         assert len(ent["source_hash"]) == 16
         assert abs(ent["bytes_per_launch"] - ent["fetch_bytes"] - ent["write_bytes"]) <= 1
+
+
+def test_down_roofline_method_work():
+    """The down kernel's roofline counts one multiply-add per stored main slot and output
+    column plus K x D per backup entry, and reads TwELL + backup + W_down once + writes y."""
+    st = {"slots_used": 1000, "overflow_tile_rows": 3, "bytes_main": 5000, "bytes_backup": 800}
+    T, D, F, K = 64, 256, 1024, 128
+    r = bench.down_roofline(st, T, D, F, K, 2, 0.01, "mfma")
+    assert r["algorithmic_flops"] == 2.0 * 1000 * 256 + 2.0 * 128 * 256 * 3
+    assert r["algorithmic_bytes"] == 5000 + 800 + F * D * 2 + T * D * 2
+    assert abs(r["tflops"] - r["algorithmic_flops"] / 1e-5 / 1e12) < 1e-3
+    assert abs(r["hbm_frac"] - r["algorithmic_bytes"] / 1e-5 / 8e12) < 1e-5
+    # bytes dominate at 2500 TFLOP/s: the HBM floor binds
+    assert r["bound"] == "hbm"
+    v = bench.down_roofline(st, T, D, F, K, 2, 0.01, "alu")
+    assert "alu_frac" in v and v["floor_us"]["alu"] > r["floor_us"]["mfma"]
+
+
+def test_parity_metrics_and_spread():
+    import numpy as np
+    ref = np.array([[1.0, -2.0], [0.0, 4.0]])
+    y = ref + np.array([[0.02, 0.0], [0.0, -0.05]])
+    m = bench.parity_metrics(y, ref)
+    assert abs(m["max_rel_elem"] - max(0.02 / 2.0, 0.05 / 5.0)) < 1e-12
+    assert abs(m["rel_frobenius"] - np.linalg.norm([0.02, 0.05]) / np.linalg.norm(ref)) < 1e-12
+    s = bench.spread([3.0, 1.0, 2.0, 4.0, 5.0])
+    assert s["median"] == 3.0 and s["n"] == 5 and s["p10"] < s["median"] < s["p90"]
