@@ -424,11 +424,17 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
   if (S > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t n4 = (size_t)d.T * d.D / 4;
-    const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 2048);
-    hipLaunchKernelGGL(down_reduce_kernel, dim3(blocks), dim3(256), 0, s, d, ws.dpart, S,
-                       static_cast<uint16_t*>(y), blk_nnz, thr);
+    return launch_down_reduce(d, ws, y, S, blk_nnz, thr, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
+                              const int32_t* blk_nnz, long long thr, hipStream_t s) {
+  const size_t n4 = (size_t)d.T * d.D / 4;
+  const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 2048);
+  hipLaunchKernelGGL(down_reduce_kernel, dim3(blocks), dim3(256), 0, s, d, ws.dpart, S,
+                     static_cast<uint16_t*>(y), blk_nnz, thr);
   return hipGetLastError();
 }
 

@@ -94,6 +94,19 @@ __global__ __launch_bounds__(256) void pack_kernel(Dims d, const float* __restri
     for (int c = 0; c < C; ++c) cnt += __popcll(ballot64(v[i][c] != 0.0f));
     if (lane == i) cnt_lane = cnt;
   }
+  // Column union of the group: lane = column c*64 + lane, any token nonzero there.
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) any |= v[i][c] != 0.0f;
+    const uint64_t um = ballot64(any);
+    if (lane == 0) {
+      uint32_t* dst = ws.umask + ((int64_t)k * d.ng + g) * (K / 32) + 2 * c;
+      dst[0] = (uint32_t)um;
+      dst[1] = (uint32_t)(um >> 32);
+    }
+  }
   // One staging claim for all of the group's overflowing tile-rows.
   const uint64_t om = ballot64(lane < GROUP && cnt_lane > W);
   const int n_ov = __popcll(om);
@@ -192,10 +205,12 @@ __global__ __launch_bounds__(512) void pack_small_kernel(Dims d, const float* __
   constexpr int C = K / 64;
   __shared__ int cnt_s[GROUP];
   __shared__ int base_s;
+  __shared__ uint32_t um_s[K / 32];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int k = blockIdx.x / d.ng;
   const int g = blockIdx.x - k * d.ng;
+  if (threadIdx.x < K / 32) um_s[threadIdx.x] = 0u;
   const int i0 = wv * PS_TPW;  // first row of the group this wave owns
   const int t0 = g * GROUP + i0;
   const int T = d.T, W = d.W;
@@ -216,6 +231,18 @@ __global__ __launch_bounds__(512) void pack_small_kernel(Dims d, const float* __
     if (lane == 0) cnt_s[i0 + i] = cnt;  // rows past T hold zeros: count 0
   }
   __syncthreads();
+  // column union of the group: each wave ORs in its 4 tokens
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < PS_TPW; ++i) any |= v[i][c] != 0.0f;
+    const uint64_t um = ballot64(any);
+    if (lane == 0) {
+      if ((uint32_t)um) atomicOr(&um_s[2 * c], (uint32_t)um);
+      if ((uint32_t)(um >> 32)) atomicOr(&um_s[2 * c + 1], (uint32_t)(um >> 32));
+    }
+  }
   const int cnt_lane = lane < GROUP ? cnt_s[lane] : 0;
   const uint64_t om = ballot64(lane < GROUP && cnt_lane > W);
   const int n_ov = __popcll(om);
@@ -224,6 +251,7 @@ __global__ __launch_bounds__(512) void pack_small_kernel(Dims d, const float* __
     ws.ov_grp[(int64_t)k * d.ng + g] = n_ov;
   }
   __syncthreads();
+  if (threadIdx.x < K / 32) ws.umask[((int64_t)k * d.ng + g) * (K / 32) + threadIdx.x] = um_s[threadIdx.x];
   const int base = base_s;
 
 #pragma unroll

@@ -309,6 +309,30 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
     const uint32_t pm_hi = __shfl_xor((uint32_t)(own >> 32), 32);
     const uint64_t pm = ((uint64_t)pm_hi << 32) | pm_lo;
 
+    // column union of the block's 32 tokens (one token group): element e = 16 a + 4 q + i
+    // of this lane is wave-local neuron 32 a + 8 q + 4 lh + i, so nibble q of the a-th
+    // 16 bits of `own` goes to bits 8 q + 4 lh of column word a; OR over all 64 lanes
+    {
+      uint32_t cw[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t f = (uint32_t)(own >> (16 * a)) & 0xFFFFu;
+        const uint32_t sp = (f & 0xFu) | ((f & 0xF0u) << 4) | ((f & 0xF00u) << 8) | ((f & 0xF000u) << 12);
+        cw[a] = sp << (4 * lh);
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) cw[a] |= __shfl_xor(cw[a], o);
+      if (lane == 0 && tokblk < T) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int n = n0 + wn * 128 + 32 * a;  // first neuron of word a
+          ws.umask[((size_t)(n / K) * d.ng + g) * (K / 32) + (n % K) / 32] = cw[a];
+        }
+      }
+    }
+
     // (3) per tile part: count, rank base, overflow
     // tile part j of this wave covers own/partner bits tmask[j]
     uint64_t tmask[TPW];

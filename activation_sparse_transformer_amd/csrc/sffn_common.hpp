@@ -36,6 +36,7 @@ struct Workspace {
   int32_t* blk_nnz;     // [nblk]   stored nonzeros per 256-token block (down-path choice)
   int32_t* grp_first;   // [nt*ng+1] first backup entry of each (tile, group), canonical order
   int32_t* tile_tot;    // [nt]     overflowing tile-rows per tile (ordering pass)
+  uint32_t* umask;      // [nt*ng*K/32] per (tile, group): columns with a nonzero in any token
   float* hsmall;        // [min(T, UP_SMALL_T), F] ReLU output of the decode-shaped up path
   float* dpart;         // [S, T, D] fp32 partial sums of the split matrix-core down kernel
 };
@@ -45,6 +46,15 @@ struct Workspace {
 constexpr int UP_SMALL_T = 128;
 
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Column unions of the packed activation: for every tile k and token group g, K bits
+// (K/32 words, bit b of word w = local column 32 w + b) telling which columns of the tile
+// hold a nonzero in at least one token of the group (main slots and backup alike).  Every
+// kernel that writes a TwELL writes them; the matrix-core down-projection contracts each
+// token block only over the union of its groups' columns.
+inline size_t umask_bytes(const Dims& d) {
+  return sizeof(uint32_t) * (size_t)d.nt * d.ng * (d.K / 32);
+}
 
 // Split of the matrix-core down-projection over its tiles: when its workgroups of (256
 // tokens, 256 columns) would fill at most half of the 256 CUs, the tile range is cut into S
@@ -85,6 +95,7 @@ inline size_t workspace_bytes(const Dims& d, bool this_call_only = false) {
   n += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
   n += align256(sizeof(int32_t) * (size_t)d.nt);
+  n += align256(umask_bytes(d));
   n += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
   const int S = down_split(d);
   n += align256(sizeof(float) * (this_call_only ? (S > 1 ? (size_t)S * d.T * d.D : 0)
@@ -116,6 +127,8 @@ inline Workspace carve(void* base, const Dims& d) {
   p += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
   w.tile_tot = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * (size_t)d.nt);
+  w.umask = reinterpret_cast<uint32_t*>(p);
+  p += align256(umask_bytes(d));
   w.hsmall = reinterpret_cast<float*>(p);
   p += align256(sizeof(float) * (size_t)(d.T < UP_SMALL_T ? d.T : UP_SMALL_T) * d.F);
   w.dpart = reinterpret_cast<float*>(p);
@@ -212,5 +225,13 @@ hipError_t launch_backward_part(int which, const Dims& d, const twell_buffers_t&
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                             hipStream_t s);
+// The matrix-core down-projection over the column unions of 64-token blocks (the same
+// shapes as launch_down_mfma; reads ws.umask, written by the kernel that produced the TwELL).
+hipError_t launch_down_union(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                             hipStream_t s);
+// y = bf16 of the sum of the S fp32 parts in ws.dpart (split matrix-core kernels).
+hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
+                              const int32_t* blk_nnz, long long thr, hipStream_t s);
 
 }  // namespace sffn

@@ -61,7 +61,7 @@ class StatsC(ctypes.Structure):
 
 
 # Down-projection policies (mirror the header's SFFN_DOWN_* values).
-DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES = 0, 1, 2, 3
+DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES, DOWN_UNION = 0, 1, 2, 3, 4
 DOWN_GATHER_DENSITY_DEFAULT = 0.0005
 DOWN_MFMA_DENSITY_DEFAULT = 0.005
 DOWN_TILES_MIN_T = 4096
@@ -345,7 +345,7 @@ class SparseFFN:
         vector kernel up to `mfma_density`, the matrix cores above), or always "gather",
         "tiles" or "mfma"."""
         code = {"auto": DOWN_AUTO, "gather": DOWN_GATHER, "mfma": DOWN_MFMA,
-                "tiles": DOWN_TILES}.get(policy)
+                "tiles": DOWN_TILES, "union": DOWN_UNION}.get(policy)
         if code is None:
             raise ValueError(f"unknown down policy {policy!r}")
         _check(lib().sparse_ffn_set_down_policy(self._h, code, float(gather_density),

@@ -147,7 +147,7 @@ DOWN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union"])
 @pytest.mark.parametrize("T,D,F,K,W,dtype,density", DOWN_CASES)
 def test_down_from_pack(T, D, F, K, W, dtype, density, policy):
     torch, sffn = need_gpu()
@@ -362,7 +362,7 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     return rel
 
 
-@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union"])
 @pytest.mark.parametrize("name,T,rho", [
     ("C1", None, None), ("C1b", None, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
@@ -379,7 +379,7 @@ def test_forward_parity(name, T, rho, policy):
     _forward_case(torch, sffn, L, policy=policy)
 
 
-@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union"])
 def test_forward_heavy_rows_force_backup(policy):
     """2B-like layer at a reduced T with heavy rows: the backup is in use."""
     torch, sffn = need_gpu()
@@ -390,7 +390,7 @@ def test_forward_heavy_rows_force_backup(policy):
 
 
 @pytest.mark.parametrize("T", [32, 48])
-@pytest.mark.parametrize("policy", ["auto", "gather"])
+@pytest.mark.parametrize("policy", ["auto", "gather", "union"])
 def test_forward_heavy_rows_short_batch(T, policy):
     """Decode-shaped batch of the 1.5B-like layer with two 3x-scaled token rows: most of their
     tile-rows overflow into the backup, and below 64 tokens the row gather (256-column chunks)
@@ -414,16 +414,35 @@ def test_forward_wide_ell(name, W, rho, T):
     _forward_case(torch, sffn, L)
 
 
-def test_forward_edge_all_zero_all_positive():
+@pytest.mark.parametrize("policy", ["auto", "union"])
+def test_forward_edge_all_zero_all_positive(policy):
     torch, sffn = need_gpu()
     base = CONFIGS["C3"].replace(heavy_frac=0.0)
     for label, bias in (("all-zero", -1e4), ("all-positive", 1e4)):
-        print(f"[forward-edge] {label}", flush=True)
+        print(f"[forward-edge] {label} {policy}", flush=True)
         L = make_layer(base, seed=0, T=100)
         from gen import f32_to_bf16_bits, bf16_bits_to_f32
         L["b_up"] = f32_to_bf16_bits(np.full(base.F, bias, np.float32))
         L["b_up_f32"] = bf16_bits_to_f32(L["b_up"])
-        _forward_case(torch, sffn, L, check_pattern=(label == "all-zero"))
+        _forward_case(torch, sffn, L, check_pattern=(label == "all-zero"), policy=policy)
+
+
+def test_union_dense_steps_equal_dense_kernel():
+    """Where every 64-column step of every 64-token block is contracted densely (20% density:
+    unions of more than 48 columns), the union kernel sums the same products in the same
+    order as the dense matrix-core kernel: y is identical bit for bit."""
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C3"].replace(heavy_frac=0.0), seed=0, T=520, rho=0.3)
+    c = L["cfg"]
+    cfg = _cfg(sffn, c.T, c.D, c.F, c.tile, c.ell_width, c.dtype)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    layer.set_down_policy("union")
+    y_u, act = layer.forward(x)
+    layer.set_down_policy("mfma")
+    y_m = layer.down(act)
+    torch.cuda.synchronize()
+    assert torch.equal(y_u.view(torch.int16), y_m.view(torch.int16))
 
 
 def test_forward_capacity_overflow_reported():
@@ -536,8 +555,10 @@ def _plain_bound_report(yh, y_plain, heavy, what):
 
 @pytest.mark.parametrize("name,rho,policy", [
     ("C2", None, "auto"), ("C3", 0.01, "auto"), ("C3", 0.05, "auto"), ("C3", 0.05, "gather"),
-    ("C3", 0.05, "tiles"), ("C3", 0.05, "mfma"), ("C3", 0.10, "auto"), ("C3", 0.20, "auto"),
-    ("C4", None, "auto"), ("C4", None, "gather"), ("C4", None, "tiles")])
+    ("C3", 0.05, "tiles"), ("C3", 0.05, "mfma"), ("C3", 0.05, "union"), ("C3", 0.01, "union"),
+    ("C3", 0.002, "union"), ("C3", 0.10, "auto"), ("C3", 0.20, "auto"), ("C3", 0.20, "union"),
+    ("C2", None, "union"), ("C4", None, "auto"), ("C4", None, "gather"), ("C4", None, "tiles"),
+    ("C4", None, "union")])
 def test_forward_full_size(name, rho, policy):
     """Full layer sizes, in the launch configuration the benchmark times: every token row
     against the oracle (activations stored in bf16 as the TwELL holds them), every row
