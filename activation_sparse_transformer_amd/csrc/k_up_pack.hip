@@ -41,6 +41,10 @@ constexpr int UP_GM = 8;    // token blocks per ordering group
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// s_waitcnt immediate waiting for at most n vector-memory operations in flight (gfx9
+// encoding: vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait values).
+constexpr int vmcnt_enc(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // BK: d_model slice per LDS stage.  WPE: waves per SIMD the kernel is built for; with 2
 // (BK = 32, 128 tokens, 48 KB of LDS, at most 256 registers), two workgroups share a CU and
 // one's pack epilogue runs while the other's MFMA loop keeps the matrix cores busy.
@@ -151,7 +155,7 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
   // and the next stage's first fragments are read, all before that k-step's MFMAs.
   constexpr int KS = BK / 16;
   constexpr int LPS = ALD + BLD;  // direct loads per wave per stage
-  static_assert(LPS * (NS - 1) <= 15, "vmcnt immediate");
+  static_assert(LPS * (NS - 1) <= 63, "vmcnt immediate");
   const int nk = D / BK;          // D % 128 == 0
   bf16x8_t fa[2][4], fb[2][NB];
   auto mfmas = [&](int c) __attribute__((always_inline)) {
@@ -201,7 +205,7 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // the next stage is in once only the NS - 2 stages after it may still be loading
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 2)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_enc(LPS * (NS - 2)));
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this stage's reads are done
         // a plain barrier: the workgroup fence of __syncthreads would also wait for the
         // loads still in flight (they write LDS); the clobber keeps memory accesses in place
@@ -219,7 +223,7 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
   issue(0, sA0, sB0);
   issue(1 < nk ? 1 : 0, sA1, sB1);
   if constexpr (NS > 2) issue(2 < nk ? 2 : nk - 1, sA2, sB2);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 1)));  // stage 0 is in
+  __builtin_amdgcn_s_waitcnt(vmcnt_enc(LPS * (NS - 1)));  // stage 0 is in
   __asm__ volatile("s_barrier" ::: "memory");
   load_frags(sA0, sB0, 0, fa[0], fb[0]);
   const int nring = nk / NS * NS;
