@@ -26,7 +26,8 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = OUT) -> str:
+    """Compile every source with ``extra`` flags added and link the library into ``out``."""
     srcs = sources()
     tmpdir = tempfile.mkdtemp(prefix="sffn_build_")
     try:
@@ -41,15 +42,15 @@ def build(verbose: bool = False, extra=()) -> str:
         jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
         with ThreadPoolExecutor(jobs) as ex:
             list(ex.map(compile_one, cmds))
-        tmp = OUT + ".tmp"
+        tmp = out + ".tmp"
         link = [HIPCC, f"--offload-arch={ARCH}", "-fPIC", "-shared", *objs, "-o", tmp]
         if verbose:
             print(" ".join(link), flush=True)
         subprocess.check_call(link)
-        os.replace(tmp, OUT)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return OUT
+    return out
 
 
 if __name__ == "__main__":

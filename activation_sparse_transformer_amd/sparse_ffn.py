@@ -14,7 +14,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsparse_ffn.so")
+# SFFN_LIB names another build of the same sources (the host-sanitizer test uses it)
+LIB_PATH = os.environ.get("SFFN_LIB") or os.path.join(_HERE, "libsparse_ffn.so")
 
 SFFN_OK = 0
 SFFN_ERR_INVALID_ARGUMENT = 1

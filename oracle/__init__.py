@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SFFN_ORACLE_LIB names another build of the same source (the sanitizer test uses it)
+_LIB_PATH = os.environ.get("SFFN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _P = ctypes.c_void_p

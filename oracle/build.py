@@ -13,14 +13,16 @@ SRC = os.path.join(HERE, "oracle.cpp")
 OUT = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = OUT, extra=()) -> str:
+    """Compile oracle.cpp into ``out``; ``extra`` flags go after the standard ones (the
+    sanitizer test builds an instrumented copy elsewhere this way)."""
     cmd = ["g++", "-std=c++17", "-O2", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-fno-fast-math", SRC, "-o", OUT + ".tmp"]
+           "-ffp-contract=off", "-fno-fast-math", *extra, SRC, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(OUT + ".tmp", OUT)
-    return OUT
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
