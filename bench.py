@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MAC (dot2) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # launches of one forward, by the names the library's event timing uses
-KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_tiles", "down_mfma")
+KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_tiles", "down_mfma", "down_union")
 TRAIN_KERNELS = KERNELS + ("bwd_dh", "bwd_dw_down", "bwd_dw_up", "bwd_dx")
 
 
@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "down_mfma": ("k_down_mfma.hip", "sffn_common.hpp"),
     "down_tiles": ("k_down_lds.hip", "sffn_common.hpp"),
     "down": ("k_down_rows.hip", "sffn_common.hpp"),
+    "down_union": ("k_down_union.hip", "sffn_common.hpp"),
 }
 
 
@@ -152,6 +153,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rho", type=float, default=0.05, help="density of the headline point")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-policies", default="auto",
+                    help="comma-separated down policies the density sweep runs, each at every "
+                         "density (auto, gather, tiles, mfma, union)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the per-point oracle checks")
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward timing")
@@ -252,10 +256,11 @@ def main():
     down_names = sffn_down_names()
     timed_names = ("up_pack",) + down_names
 
-    def sparse_point(rho, steps, warmup, profile=False, only=None):
+    def sparse_point(rho, steps, warmup, profile=False, only=None, policy="auto"):
         L = bias_for_density(L0, rho)
         b = bf16_dev(L["b_up"])
         layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+        layer.set_down_policy(policy)
         fn = lambda: layer.forward(x, act=act, y=y)
         for _ in range(warmup):
             fn()
@@ -388,10 +393,12 @@ def main():
     # method's work, and the oracle check of sampled rows
     sweep = []
     if not args.no_sweep:
-        for rho in (0.002, 0.005, 0.01, 0.05, 0.10, 0.20):
-            m, _, k2, s2, _, Lr, layer_r = sparse_point(rho, max(10, args.steps // 2), 3, profile=True)
+        for rho, pol in [(r, p) for p in args.sweep_policies.split(",")
+                         for r in (0.002, 0.005, 0.01, 0.05, 0.10, 0.20)]:
+            m, _, k2, s2, _, Lr, layer_r = sparse_point(rho, max(10, args.steps // 2), 3,
+                                                        profile=True, policy=pol)
             dn, kind = down_of(k2)
-            pt = {"rho_target": rho, "density": round(s2["density"], 5),
+            pt = {"rho_target": rho, "policy": pol, "density": round(s2["density"], 5),
                   "nnz": int(s2["nnz"]), "slots_used": int(s2["slots_used"]),
                   "overflow_tile_rows": int(s2["overflow_tile_rows"]),
                   "ms_per_step": round(m, 4), "tokens_per_s": round(T / (m * 1e-3), 1),
@@ -402,7 +409,7 @@ def main():
                   "down_roofline": down_roofline(s2, T, D, F, c.tile, 2, k2[dn], kind)}
             point_parity(pt, Lr, y, sample_rows(T, Lr["heavy"], 96), c.tile, c.ell_width)
             sweep.append(pt)
-            log(f"  sweep rho={rho}: {m:.4f} ms, density {s2['density']:.4f}, {k2}")
+            log(f"  sweep rho={rho} {pol}: {m:.4f} ms, density {s2['density']:.4f}, {k2}")
             del layer_r
 
     # ---- per-kernel rates and the roofline of the dominant kernel
@@ -681,7 +688,7 @@ def main():
 
 def sffn_down_names():
     """Event names of the library's down-projection launches."""
-    return ("down", "down_tiles", "down_mfma")
+    return ("down", "down_tiles", "down_mfma", "down_union")
 
 
 def decode_policies():
