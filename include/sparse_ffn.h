@@ -4,9 +4,12 @@
  * layers"): y = ReLU(x W_up^T + b) W_down, applied to each token on its own.  Most hidden
  * activations are zero, so the library packs them into TwELL (same article, section "What
  * TwELL and the custom CUDA kernels solve": hidden columns split into tiles, an ELL layout
- * inside each tile, plus a few dense backups for what does not fit) and runs the
- * down-projection over the stored nonzeros only.  The dense hidden tensor never reaches
- * device memory on the forward path.
+ * inside each tile, plus a few dense backups for what does not fit).  The down-projection
+ * reads only that packed form: its vector kernels multiply the stored nonzeros only, its
+ * matrix-core kernels rebuild each tile in on-chip memory and contract it there.  On the
+ * forward path of more than 128 tokens the dense hidden tensor never reaches device memory;
+ * a batch of at most 128 tokens keeps its fp32 hidden rows (T x d_ff) in the workspace
+ * between the small-batch up-projection and the pack.
  *
  * Conventions
  *   - Pointers are DEVICE pointers unless marked (host).  Row-major layouts.
