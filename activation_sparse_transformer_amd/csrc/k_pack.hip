@@ -38,53 +38,22 @@ __device__ __forceinline__ void store_val(void* base, size_t idx, float v) {
   }
 }
 
-// Values source of the pack: MODE_H reads a dense fp32 hidden tensor; MODE_UP computes
-// h = ReLU(x W_up^T + b) in fp32 on the fly (the fused forward of fp32 layers).
+// Values source of the pack: MODE_H reads a dense fp32 hidden tensor (pack_kernel); MODE_UP
+// computes h = ReLU(x W_up^T + b) in fp32 on the fly (up_pack_f32_kernel, the fused forward
+// of fp32 layers).
 enum { MODE_H = 0, MODE_UP = 1 };
 
-// One wave per (tile k, token group g).  4 waves per workgroup.
-template <int K, bool BF16, int MODE>
-__global__ __launch_bounds__(256) void pack_kernel(Dims d, const float* __restrict__ h,
-                                                   const float* __restrict__ x,
-                                                   const float* __restrict__ Wu,
-                                                   const float* __restrict__ bu,
-                                                   twell_buffers_t b, Workspace ws,
-                                                   float* __restrict__ zdump) {
+// The pack of one (tile k, token group g) by one wave, from the group's values v: lane l
+// holds column c*64 + l of token t0 + i in v[i][c] (0 for tokens past T).  Writes the main
+// slots, their padding, the counts, the group's column union and overflow count, and stages
+// the remainder of overflowing tile-rows under one claim.
+template <int K, bool BF16>
+__device__ __forceinline__ void pack_pair(const Dims& d, int k, int g, const float (&v)[GROUP][K / 64],
+                                          const twell_buffers_t& b, const Workspace& ws) {
   constexpr int C = K / 64;
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= d.nt * d.ng) return;  // uniform per wave
-  const int k = wave / d.ng;
-  const int g = wave - k * d.ng;
   const int t0 = g * GROUP;
   const int T = d.T, W = d.W;
-
-  float v[GROUP][C];
-#pragma unroll
-  for (int i = 0; i < GROUP; ++i) {
-    const int t = t0 + i;
-    const bool valid = t < T;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int64_t n = (int64_t)k * K + c * 64 + lane;
-      float val = 0.0f;
-      if (valid) {
-        if constexpr (MODE == MODE_H) {
-          val = h[(int64_t)t * d.F + n];
-        } else {
-          const float* xr = x + (int64_t)t * d.D;
-          const float* wr = Wu + n * d.D;
-          float acc = 0.0f;
-          for (int i2 = 0; i2 < d.D; ++i2) acc = fmaf(xr[i2], wr[i2], acc);
-          acc += bu[n];
-          if (zdump) zdump[(int64_t)t * d.F + n] = acc;
-          val = acc > 0.0f ? acc : 0.0f;
-        }
-      }
-      v[i][c] = val;
-    }
-  }
-
   // Phase 1: true count of every tile-row of the group; lane i keeps token i's count.
   int cnt_lane = 0;
 #pragma unroll
@@ -158,14 +127,149 @@ __global__ __launch_bounds__(256) void pack_kernel(Dims d, const float* __restri
   }
 }
 
+
+// One wave per (tile k, token group g).  4 waves per workgroup.  The values come from a
+// dense fp32 hidden tensor h [T, F].
+template <int K, bool BF16>
+__global__ __launch_bounds__(256) void pack_kernel(Dims d, const float* __restrict__ h,
+                                                   twell_buffers_t b, Workspace ws) {
+  constexpr int C = K / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= d.nt * d.ng) return;  // uniform per wave
+  const int k = wave / d.ng;
+  const int g = wave - k * d.ng;
+  const int t0 = g * GROUP;
+  float v[GROUP][C];
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    const int t = t0 + i;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      v[i][c] = t < d.T ? h[(int64_t)t * d.F + (int64_t)k * K + c * 64 + lane] : 0.0f;
+  }
+  pack_pair<K, BF16>(d, k, g, v, b, ws);
+}
+
+// Fused up-projection + ReLU + pack of fp32 layers (small test-sized layers): one workgroup
+// of 4 waves per (tile k, token group g).  Wave w sums the d_model quarter
+// [w D/4, (w+1) D/4) of z[t, n] = x[t, :] . W_up[n, :] for the group's 32 tokens and the
+// tile's K neurons: slices of DCH columns of the tile's W_up rows and of the group's x rows
+// are copied into the wave's own LDS region with 16-byte loads (rows padded to DCH + 4
+// floats, so the lanes' 16-byte reads of 16 consecutive rows fall in distinct banks), and
+// every lane keeps its K/64 neurons x 32 tokens of sums in registers (x values are LDS
+// broadcasts).  The four partial sums meet in LDS and are added in wave order; wave 0 adds
+// the bias, applies ReLU and packs.
+template <int K, bool BF16>
+__global__ __launch_bounds__(256) void up_pack_f32_kernel(Dims d, const float* __restrict__ x,
+                                                          const float* __restrict__ Wu,
+                                                          const float* __restrict__ bu,
+                                                          twell_buffers_t b, Workspace ws,
+                                                          float* __restrict__ zdump) {
+  constexpr int C = K / 64;
+  constexpr int DCH = K >= 256 ? 16 : 32;        // d_model columns per staged slice
+  constexpr int SWS = DCH + 4;                   // padded row stride (floats)
+  constexpr int WREG = (K + GROUP) * SWS;        // one wave's staging (floats)
+  constexpr int PART = 3 * GROUP * K;            // waves 1-3's partial sums (floats)
+  constexpr int SBUF = 4 * WREG > PART ? 4 * WREG : PART;
+  __shared__ __attribute__((aligned(16))) float sbuf[SBUF];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int k = blockIdx.x / d.ng;
+  const int g = blockIdx.x - k * d.ng;
+  const int t0 = g * GROUP;
+  const int T = d.T, D = d.D;
+  float* sW = sbuf + wave * WREG;
+  float* sX = sW + K * SWS;
+  const int dq = D / 4;  // D % 64 == 0
+  const int dlo = wave * dq, dhi = dlo + dq;
+
+  float acc[GROUP][C];
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i)
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[i][c] = 0.0f;
+  for (int dc = dlo; dc < dhi; dc += DCH) {
+    // this wave's slice: K rows of W_up and 32 rows of x, columns dc .. dc+DCH-1 (16-byte
+    // pieces; columns past the quarter and rows past T are zero)
+    for (int p = lane; p < K * DCH / 4; p += 64) {
+      const int r = p / (DCH / 4), q = p - r * (DCH / 4);
+      const int c0 = dc + 4 * q;
+      const float4 w = c0 < dhi ? *reinterpret_cast<const float4*>(Wu + ((int64_t)k * K + r) * D + c0)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(sW + r * SWS + 4 * q) = w;
+    }
+    for (int p = lane; p < GROUP * DCH / 4; p += 64) {
+      const int i = p / (DCH / 4), q = p - i * (DCH / 4);
+      const int c0 = dc + 4 * q, t = t0 + i;
+      const float4 xv = (c0 < dhi && t < T) ? *reinterpret_cast<const float4*>(x + (int64_t)t * D + c0)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(sX + i * SWS + 4 * q) = xv;
+    }
+    // (one wave writes and reads its own region: program order suffices)
+#pragma unroll
+    for (int dd = 0; dd < DCH; dd += 4) {
+      float4 w[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) w[c] = *reinterpret_cast<const float4*>(sW + (c * 64 + lane) * SWS + dd);
+#pragma unroll
+      for (int i = 0; i < GROUP; ++i) {
+        const float4 xv = *reinterpret_cast<const float4*>(sX + i * SWS + dd);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          float a = acc[i][c];
+          a = fmaf(xv.x, w[c].x, a);
+          a = fmaf(xv.y, w[c].y, a);
+          a = fmaf(xv.z, w[c].z, a);
+          a = fmaf(xv.w, w[c].w, a);
+          acc[i][c] = a;
+        }
+      }
+    }
+  }
+  // partial sums of waves 1-3 into LDS (over the staging), then wave 0 adds them in order
+  __syncthreads();
+  if (wave > 0) {
+    float* pw = sbuf + (wave - 1) * GROUP * K;
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i)
+#pragma unroll
+      for (int c = 0; c < C; ++c) pw[i * K + c * 64 + lane] = acc[i][c];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  float v[GROUP][C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int64_t n = (int64_t)k * K + c * 64 + lane;
+    const float bias = bu[n];
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+      float z = acc[i][c];
+#pragma unroll
+      for (int w2 = 0; w2 < 3; ++w2) z += sbuf[w2 * GROUP * K + i * K + c * 64 + lane];
+      z += bias;
+      const int t = t0 + i;
+      if (zdump && t < T) zdump[(int64_t)t * d.F + n] = z;
+      v[i][c] = (t < T && z > 0.0f) ? z : 0.0f;
+    }
+  }
+  pack_pair<K, BF16>(d, k, g, v, b, ws);
+}
+
 template <int K, bool BF16, int MODE>
 static hipError_t launch_pack_t(const Dims& d, const float* h, const float* x, const float* Wu,
                                 const float* bu, const twell_buffers_t& b, const Workspace& ws,
                                 float* zdump, hipStream_t s) {
-  const int waves = d.nt * d.ng;
-  const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((pack_kernel<K, BF16, MODE>), dim3(blocks), dim3(256), 0, s, d, h, x, Wu,
-                     bu, b, ws, zdump);
+  if constexpr (MODE == MODE_UP) {
+    hipLaunchKernelGGL((up_pack_f32_kernel<K, BF16>), dim3(d.nt * d.ng), dim3(256), 0, s, d, x,
+                       Wu, bu, b, ws, zdump);
+  } else {
+    const int waves = d.nt * d.ng;
+    const int blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((pack_kernel<K, BF16>), dim3(blocks), dim3(256), 0, s, d, h, b, ws);
+  }
   return hipGetLastError();
 }
 

@@ -541,4 +541,18 @@ sffn_status_t sffn_profile_read(const char* kernel, double* total_ms, int64_t* l
   return SFFN_OK;
 }
 
+sffn_status_t sffn_probe_gather_fma(const void* W, int32_t F, int32_t d, const int32_t* rows,
+                                    const void* vals, int32_t T, int32_t n, void* y,
+                                    void* stream) {
+  if (!W || !y || (n > 0 && (!rows || !vals)))
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "probe: NULL pointer");
+  if (F < 1 || d < 8 || d % 8 != 0 || T < 1 || n < 0)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "probe: need F >= 1, d >= 8, d % 8 == 0, T >= 1, n >= 0");
+  if ((long long)T * n >= (1ll << 31) || (long long)F * d >= (1ll << 40))
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "probe: sizes out of range");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run("probe_gather_fma", s,
+             [&] { return sffn::launch_gather_fma_probe(W, F, d, rows, vals, T, n, y, s); });
+}
+
 }  // extern "C"

@@ -230,6 +230,9 @@ hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Works
 hipError_t launch_down_union(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                              hipStream_t s);
+// y[t] = sum_j vals[t, j] W[rows[t, j]] (bf16 W, vals, y; fp32 sums): the measurement probe.
+hipError_t launch_gather_fma_probe(const void* W, int F, int D, const int32_t* rows,
+                                   const void* vals, int T, int n, void* y, hipStream_t s);
 // y = bf16 of the sum of the S fp32 parts in ws.dpart (split matrix-core kernels).
 hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
                               const int32_t* blk_nnz, long long thr, hipStream_t s);

@@ -95,6 +95,7 @@ _PROTOS = {
     "sffn_profile_reset": ([], ctypes.c_int),
     "sffn_profile_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
+    "sffn_probe_gather_fma": ([_P, _I32, _I32, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -406,6 +407,26 @@ def profile_only(names=None):
 
 def profile_reset():
     _check(lib().sffn_profile_reset(), "sffn_profile_reset")
+
+
+def probe_gather_fma(W, rows, vals, y=None, stream=None):
+    """y[t] = sum_j vals[t, j] W[rows[t, j]] (the library's measurement probe of a vector
+    down-projection's gather-multiply-add).  W [F, d] bf16, rows [T, n] int32, vals [T, n]
+    bf16, y [T, d] bf16; device tensors.  Returns y."""
+    import torch
+    F, d = W.shape
+    T, n = rows.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.bfloat16, device=W.device)
+    for t_, name in ((W, "W"), (rows, "rows"), (vals, "vals"), (y, "y")):
+        if not t_.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if rows.dtype != torch.int32 or vals.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise ValueError("W and vals bf16, rows int32")
+    _check(lib().sffn_probe_gather_fma(_ptr(W), int(F), int(d), _ptr(rows), _ptr(vals), int(T),
+                                       int(n), _ptr(y), _stream_ptr(stream)),
+           "sffn_probe_gather_fma")
+    return y
 
 
 def profile_read(kernel: str):

@@ -14,6 +14,7 @@ are reported next to it.  Prints ONE JSON line on stdout; progress goes to stder
 """
 import argparse
 import hashlib
+import subprocess
 import json
 import os
 import sys
@@ -331,6 +332,24 @@ def main():
                     "gemm_up_ms": round(g_up, 5), "gemm_down_ms": round(g_dn, 5),
                     "shapes": f"[{T},{D}]x[{D},{F}] and [{T},{F}]x[{F},{D}] bf16 (torch.matmul)"}
         del src, dst, h_b
+        # the gather-multiply-add of a vector down-projection alone (the library's probe): per
+        # token n random rows of this layer's W_down with bf16 weights, n = the stored nonzeros
+        # per token at 0.37% (where the vector tile kernel runs) and at the headline density
+        rng_p = np.random.default_rng(11)
+        gf = []
+        for npt in (max(1, int(round(0.0037 * F))), max(1, int(round(nnz / T)))):
+            rows_p = torch.from_numpy(rng_p.integers(0, F, (T, npt)).astype(np.int32)).to(dev)
+            vals_p = torch.randn((T, npt), device=dev).to(torch.bfloat16)
+            y_p = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+            pm, _ = time_steps(lambda: sffn.probe_gather_fma(Wd, rows_p, vals_p, y_p), 20, 3)
+            fl_p = 2.0 * T * npt * D
+            gf.append({"rows_per_token": npt, "ms": round(pm, 5),
+                       "tflops": round(fl_p / (pm * 1e-3) / 1e12, 2),
+                       "gathered_gbs": round(T * npt * D * 2 / (pm * 1e-3) / 1e9, 1)})
+            del rows_p, vals_p, y_p
+        ceilings["gather_fma"] = gf
+        ceilings["gather_fma_note"] = ("y[t] = sum_j v[t,j] W_down[r[t,j]] with random rows, fp32 FMA "
+                                       "on the vector units, one 16-byte load per lane and row")
         torch.cuda.empty_cache()
         log(f"  ceilings {ceilings}")
 
@@ -524,6 +543,16 @@ def main():
             ms_cd, _ = time_steps(lambda: torch.matmul(Fn.relu(Fn.linear(xc, Wuc, bc)), Wdc),
                                   max(10, args.steps // 2), 3)
             assert sffn.check(act_c) == sffn.SFFN_OK
+            gemm_c = None
+            if not args.no_ceilings:
+                h_c = torch.randn((cc.T, cc.F), device=dev).to(torch.bfloat16)
+                g_u, _ = time_steps(lambda: torch.matmul(xc, Wuc.t()), 10, 2)
+                g_d, _ = time_steps(lambda: torch.matmul(h_c, Wdc), 10, 2)
+                fl_c = 2.0 * cc.T * cc.D * cc.F
+                gemm_c = {"up_shape_tflops": round(fl_c / (g_u * 1e-3) / 1e12, 1),
+                          "down_shape_tflops": round(fl_c / (g_d * 1e-3) / 1e12, 1),
+                          "up_ms": round(g_u, 5), "down_ms": round(g_d, 5)}
+                del h_c
             stc = sffn.twell_stats(cfg_c, act_c)
             dn_c, kind_c = down_of(kc)
             lp = {"layer": cc.name, "T": cc.T, "d_model": cc.D, "d_ff": cc.F,
@@ -535,6 +564,7 @@ def main():
                   "speedup_vs_dense": round(ms_cd / ms_c, 4),
                   "kernel_ms": {k: round(v, 4) for k, v in kc.items()},
                   "down_kernel": dn_c,
+                  "gemm_ceiling": gemm_c,
                   "down_roofline": down_roofline(stc, cc.T, cc.D, cc.F, cc.tile, 2, kc[dn_c], kind_c)}
             point_parity(lp, Lc, yc, sample_rows(cc.T, Lc["heavy"], 96), cc.tile, cc.ell_width)
             layers.append(lp)
@@ -589,6 +619,36 @@ def main():
             log(f"  decode T={Td}: {pt}")
             del layer_d, act_d
 
+    # ---- the tiny fp32 layer (T=64, d_model 256, d_ff 1024, tile 128, W 32, 10%) is launch-bound,
+    # so it is reported as latency: each forward timed on its own (events around it), median and
+    # spread of 200 calls, against the dense fp32 FFN; the oracle's time for the same 64 tokens
+    latency_tiny, tiny_case = None, None
+    if not args.no_layers:
+        Lt = make_layer(CONFIGS["C1"], seed=0)
+        ct = Lt["cfg"]
+        f32d = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        xt, Wut, bt, Wdt = (f32d(Lt[k]) for k in ("x", "W_up", "b_up", "W_down"))
+        cfg_t = sffn.Config(d_model=ct.D, d_ff=ct.F, tile=ct.tile, ell_width=ct.ell_width,
+                            max_tokens=ct.T, backup_capacity=ct.n_tiles * ct.T, dtype="f32")
+        layer_t = sffn.SparseFFN(cfg_t, Wut, bt, Wdt)
+        act_t = sffn.TwellBuffers(cfg_t, ct.T)
+        yt = torch.empty_like(xt)
+        lt = per_step(lambda: layer_t.forward(xt, act=act_t, y=yt), 200, 10)
+        ld = per_step(lambda: torch.matmul(Fn.relu(Fn.linear(xt, Wut, bt)), Wdt), 200, 10)
+        assert sffn.check(act_t) == sffn.SFFN_OK
+        stt = sffn.twell_stats(cfg_t, act_t)
+        us = lambda d_: {k: (round(v * 1e3, 2) if k != "n" else v) for k, v in d_.items()}
+        latency_tiny = {"layer": ct.name, "T": ct.T, "d_model": ct.D, "d_ff": ct.F,
+                        "tile": ct.tile, "ell_width": ct.ell_width, "dtype": "f32",
+                        "density": round(stt["density"], 5), "sparse_us": us(lt),
+                        "dense_fp32_us": us(ld),
+                        "speedup_vs_dense_median": round(ld["median"] / lt["median"], 4)}
+        torch.cuda.synchronize()
+        tiny_case = (latency_tiny, Lt, yt.cpu().numpy().astype(np.float64))
+        log(f"  tiny fp32 layer latency: sparse {latency_tiny['sparse_us']} us, "
+            f"dense {latency_tiny['dense_fp32_us']} us")
+        del layer_t, act_t
+
     # ---- CPU fp64 oracle on bounded samples of the same workload, the sparse path (up-projection,
     # ReLU, TwELL pack, sparse down-projection, per token) and the dense FFN; median of 3 runs each
     cpu = None
@@ -606,6 +666,21 @@ def main():
                                 "within_tolerance": bool(a["max_rel_elem"] <= 1e-2 and
                                                          a["rel_frobenius"] <= 5e-3)}
         log(f"parity of {len(pending)} points checked against the oracle; headline {head.get('parity')}")
+        if tiny_case is not None:
+            lat, Lt, yt_h = tiny_case
+            xt64, Wut64, bt64, Wdt64 = (Lt[k].astype(np.float64) for k in ("x", "W_up", "b_up", "W_down"))
+            rows_t = np.arange(lat["T"], dtype=np.int64)
+            tt = []
+            for _ in range(20):
+                t0 = time.perf_counter()
+                y_t, _ = orc.ffn_rows(xt64, Wut64, bt64, Wdt64, rows_t, lat["tile"], lat["ell_width"])
+                tt.append(time.perf_counter() - t0)
+            a = parity_metrics(yt_h, y_t)
+            lat["parity"] = {"rows": int(lat["T"]), "vs_oracle": a,
+                             "within_tolerance": bool(a["max_rel_elem"] <= 1e-4 and
+                                                      a["rel_frobenius"] <= 1e-5)}
+            lat["cpu_oracle_us"] = {"median": round(float(np.median(tt)) * 1e6, 1), "runs": 20,
+                                    "threads": orc.num_threads()}
         x64 = Lh["x_f32"].astype(np.float64)
         Wu64 = Lh["W_up_f32"].astype(np.float64)
         b64 = Lh["b_up_f32"].astype(np.float64)
@@ -671,7 +746,8 @@ def main():
         "decode": decode,
         "layers": layers,
         "device": {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
-                   "torch": torch.__version__},
+                   "torch": torch.__version__, **machine_info()},
+        "latency_tiny": latency_tiny,
         "sweep": sweep,
         "kernel_source_hash": src_hash,
     }
@@ -684,6 +760,29 @@ def main():
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n
     print(json.dumps(out), flush=True)
+
+
+def machine_info():
+    """Host CPU model and thread counts, and the GPU's current clocks as amd-smi reports them
+    (best effort: absent tools or fields give None)."""
+    info = {"cpu_model": None, "host_threads_affinity": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "gpu_clocks": None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True, text=True,
+                           timeout=20)
+        if r.returncode == 0:
+            info["gpu_clocks"] = " ".join(r.stdout.split())[:600]
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return info
 
 
 def sffn_down_names():

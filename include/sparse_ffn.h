@@ -309,6 +309,22 @@ sffn_status_t sffn_profile_reset(void);
  * (host outputs; SFFN_ERR_INVALID_ARGUMENT for NULL pointers). */
 sffn_status_t sffn_profile_read(const char *kernel, double *total_ms, int64_t *launches);
 
+/* Measurement probe (interface of the library, for the benchmark's ceilings):
+ *   y[t, :] = sum_j vals[t, j] W[rows[t, j], :]   for t < T, j < n
+ * in fp32, rounded to nearest-even into bf16 y.  This is the gather-multiply-add a vector
+ * down-projection performs for each stored nonzero - only the W_down rows that a token's
+ * nonzero activations select contribute (upppp.jp TwELL article of 2026-05-11, section
+ * "What is the waste in LLM FFN layers") - with the row lists given instead of decoded from
+ * TwELL, so its rate bounds the vector down kernels on the same rows.  W [F, d] bf16
+ * (d = d_model), rows [T, n] int32 (a row outside [0, F) reads row 0 or F-1), vals [T, n]
+ * bf16, y [T, d] bf16, all device.  F >= 1, d >= 8 with d % 8 == 0, T >= 1, n >= 0 (n = 0:
+ * y = 0, rows and vals may be NULL); SFFN_ERR_INVALID_ARGUMENT otherwise (and for NULL
+ * pointers).  Async on `stream`; timed as
+ * "probe_gather_fma" by the profiling calls. */
+sffn_status_t sffn_probe_gather_fma(const void *W, int32_t F, int32_t d, const int32_t *rows,
+                                    const void *vals, int32_t T, int32_t n, void *y,
+                                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

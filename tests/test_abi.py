@@ -186,6 +186,22 @@ def test_null_arguments_rejected_before_launch(sffn):
     assert b"NULL" in L.sffn_last_error()
 
 
+def test_probe_arguments_rejected_before_launch(sffn):
+    """The gather-multiply-add probe checks its pointers and sizes on the host."""
+    from activation_sparse_transformer_amd.sparse_ffn import lib
+    L = lib()
+    d_ = ctypes.c_void_p(0x1000)
+    assert L.sffn_probe_gather_fma(None, 16, 64, d_, d_, 4, 3, d_, None) == 1
+    assert L.sffn_probe_gather_fma(d_, 16, 64, None, d_, 4, 3, d_, None) == 1
+    assert L.sffn_probe_gather_fma(d_, 16, 64, d_, d_, 4, 3, None, None) == 1
+    assert L.sffn_probe_gather_fma(d_, 16, 60, d_, d_, 4, 3, d_, None) == 1   # d % 8
+    assert L.sffn_probe_gather_fma(d_, 0, 64, d_, d_, 4, 3, d_, None) == 1    # F
+    assert L.sffn_probe_gather_fma(d_, 16, 64, d_, d_, 0, 3, d_, None) == 1   # T
+    assert L.sffn_probe_gather_fma(d_, 16, 64, d_, d_, 4, -1, d_, None) == 1  # n
+    assert b"probe" in L.sffn_last_error()
+    assert L.sffn_probe_gather_fma(d_, 16, 64, d_, None, 4, 3, d_, None) == 1   # vals, n > 0
+
+
 def test_profile_counters_host_only(sffn):
     sffn.profile_enable(True)
     sffn.profile_reset()

@@ -609,6 +609,31 @@ def test_forward_full_size(name, rho, policy):
     assert np.all(np.abs(hg[nzc] - zs[nzc]) <= (np.abs(zs[nzc]) * 2.0 ** -8 + bs[nzc]) * 1.0001)
 
 
+@pytest.mark.parametrize("F,d,T,n", [(300, 520, 7, 37), (64, 8, 3, 1), (1024, 2048, 5, 0),
+                                     (8192, 2048, 33, 430)])
+def test_probe_gather_fma(F, d, T, n):
+    """The measurement probe computes y[t] = sum_j vals[t, j] W[rows[t, j]] (rows outside
+    [0, F) read the first or last row), against an fp64 numpy sum of the same bf16 values."""
+    torch, sffn = need_gpu()
+    from gen import f32_to_bf16_bits, bf16_bits_to_f32
+    print(f"[probe] F={F} d={d} T={T} n={n}", flush=True)
+    rng = np.random.default_rng(3)
+    W_bits = f32_to_bf16_bits(rng.standard_normal((F, d)).astype(np.float32))
+    v_bits = f32_to_bf16_bits(rng.standard_normal((T, n)).astype(np.float32))
+    rows = rng.integers(0, F, (T, n)).astype(np.int32)
+    if n >= 2:
+        rows[0, 0], rows[-1, -1] = -5, F + 3
+    W = torch.from_numpy(W_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    vals = torch.from_numpy(v_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    y = sffn.probe_gather_fma(W, torch.from_numpy(rows).cuda(), vals)
+    torch.cuda.synchronize()
+    yh = bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    Wf = bf16_bits_to_f32(W_bits).astype(np.float64)
+    vf = bf16_bits_to_f32(v_bits).astype(np.float64)
+    ref = np.einsum("tj,tjd->td", vf, Wf[np.clip(rows, 0, F - 1)]) if n else np.zeros((T, d))
+    assert np.all(np.abs(yh - ref) <= 1e-2 * (1.0 + np.abs(ref)))
+
+
 def test_profile_only_times_named_kernels():
     """With a name list only those launches are timed and counted; without, all are."""
     torch, sffn = need_gpu()
