@@ -232,12 +232,23 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
           }
         }
       } else if constexpr (FAST && !BF16) {
+        // Slot quads, as above: one 16-byte read of four values and one of four columns,
+        // then the four W_down reads together (slots past m add exact zeros)
         const float* vrow = reinterpret_cast<const float*>(tv + i * W * 4);
         const uint8_t* crow = tc + i * W;
-        for (int s = 0; s < m; ++s) {
-          const float v = vrow[s];
-          const uint32_t c = crow[s];
-          acc[i][0] = fmaf(v, __uint_as_float(wl[c * 64 + lane]), acc[i][0]);
+        for (int s = 0; s < m; s += 4) {
+          const float4 vq = *reinterpret_cast<const float4*>(vrow + s);
+          const uint32_t cq = *reinterpret_cast<const uint32_t*>(crow + s);
+          const float w0 = __uint_as_float(wl[(cq & 0xFFu) * 64 + lane]);
+          const float w1 = __uint_as_float(wl[((cq >> 8) & 0xFFu) * 64 + lane]);
+          const float w2 = __uint_as_float(wl[((cq >> 16) & 0xFFu) * 64 + lane]);
+          const float w3 = __uint_as_float(wl[(cq >> 24) * 64 + lane]);
+          float a = acc[i][0];
+          a = fmaf(vq.x, w0, a);
+          a = fmaf(vq.y, w1, a);
+          a = fmaf(vq.z, w2, a);
+          a = fmaf(vq.w, w3, a);
+          acc[i][0] = a;
         }
       } else {
         // generic slot layout (any W): scalar reads straight from the TwELL arrays
