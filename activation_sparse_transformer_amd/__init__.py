@@ -5,6 +5,7 @@ The compute lives in ``libsparse_ffn.so`` (hand-written HIP kernels behind a C A
 """
 from .sparse_ffn import (  # noqa: F401
     Config, SparseFFN, TwellBuffers, SffnError, twell_pack, twell_stats, check, buffer_sizes,
+    count_histogram, choose_ell_width,
     buffer_bytes, BUFFER_FIELDS,
     profile_enable, profile_only, profile_reset, profile_read, probe_gather_fma, lib, LIB_PATH,
     SFFN_OK, SFFN_ERR_INVALID_ARGUMENT, SFFN_ERR_UNSUPPORTED, SFFN_ERR_BACKUP_OVERFLOW,

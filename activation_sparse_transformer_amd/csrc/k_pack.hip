@@ -775,4 +775,31 @@ hipError_t launch_stats(const Dims& d, const twell_buffers_t& b, const Workspace
   return hipGetLastError();
 }
 
+// Count histogram: each workgroup bins its share of the counts in LDS (32-bit), then adds
+// its bins into the cleared 64-bit global bins.
+__global__ __launch_bounds__(256) void hist_kernel(Dims d, const uint16_t* __restrict__ counts,
+                                                   unsigned long long* __restrict__ hist) {
+  __shared__ uint32_t bins[SFFN_HIST_BINS];
+  for (int i = threadIdx.x; i < d.K + 1; i += 256) bins[i] = 0;
+  __syncthreads();
+  const size_t n = (size_t)d.nt * d.T;
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n; q += (size_t)gridDim.x * 256) {
+    const int c = counts[q];
+    atomicAdd(&bins[c <= d.K ? c : d.K], 1u);  // (a count never exceeds the tile width)
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < d.K + 1; i += 256)
+    if (bins[i] != 0) atomicAdd(&hist[i], (unsigned long long)bins[i]);
+}
+
+hipError_t launch_hist(const Dims& d, const twell_buffers_t& b, const Workspace& ws, hipStream_t s) {
+  hipError_t e = hipMemsetAsync(ws.hist, 0, sizeof(long long) * SFFN_HIST_BINS, s);
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)d.nt * d.T;
+  const int grid = (int)std::max<size_t>(1, std::min<size_t>(STATS_WG, (n + 255) / 256));
+  hipLaunchKernelGGL(hist_kernel, dim3(grid), dim3(256), 0, s, d, b.counts,
+                     reinterpret_cast<unsigned long long*>(ws.hist));
+  return hipGetLastError();
+}
+
 }  // namespace sffn

@@ -482,6 +482,60 @@ sffn_status_t twell_stats(const sffn_config_t* cfg, const twell_buffers_t* buf, 
   return SFFN_OK;
 }
 
+sffn_status_t twell_count_histogram(const sffn_config_t* cfg, const twell_buffers_t* buf,
+                                    int32_t T, int64_t* hist, void* stream) {
+  SFFN_TRY(check_cfg(cfg));
+  SFFN_TRY(check_T(cfg, T));
+  SFFN_TRY(check_bufs(buf, true));
+  if (!hist) return fail(SFFN_ERR_INVALID_ARGUMENT, "hist is NULL");
+  const Dims d = make_dims(cfg, T);
+  const Workspace ws = carve(buf->workspace, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SFFN_TRY(run("hist", s, [&] { return launch_hist(d, *buf, ws, s); }));
+  long long host[SFFN_HIST_BINS];
+  hipError_t e = hipMemcpyAsync(host, ws.hist, sizeof(long long) * (d.K + 1),
+                                hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return dev_fail(e, "histogram copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return dev_fail(e, "histogram sync");
+  for (int c = 0; c <= d.K; ++c) hist[c] = host[c];
+  return SFFN_OK;
+}
+
+sffn_status_t twell_choose_ell_width(const sffn_config_t* cfg, const int64_t* hist,
+                                     const int32_t* candidates, int32_t n_candidates,
+                                     int32_t* W_out, int64_t* bytes_out) {
+  SFFN_TRY(check_cfg(cfg));
+  if (!hist || !W_out) return fail(SFFN_ERR_INVALID_ARGUMENT, "hist or W_out is NULL");
+  const int K = cfg->tile;
+  const int64_t esz = cfg->dtype == SFFN_BF16 ? 2 : 4;
+  if (candidates != nullptr && n_candidates < 1)
+    return fail(SFFN_ERR_INVALID_ARGUMENT, "empty candidate list");
+  int64_t R = 0;
+  for (int c = 0; c <= K; ++c) {
+    if (hist[c] < 0) return fail(SFFN_ERR_INVALID_ARGUMENT, "negative histogram bin");
+    R += hist[c];
+  }
+  // over[W] = tile-rows with count > W
+  std::vector<int64_t> over(K + 1, 0);
+  for (int w = K - 1; w >= 0; --w) over[w] = over[w + 1] + hist[w + 1];
+  const int n = candidates ? n_candidates : K;
+  int best_w = 0;
+  int64_t best = 0;
+  for (int i = 0; i < n; ++i) {
+    const int w = candidates ? candidates[i] : i + 1;
+    if (w < 1 || w > K) return fail(SFFN_ERR_INVALID_ARGUMENT, "candidate width outside [1, tile]");
+    const int64_t bytes = R * (2 + (int64_t)w * (esz + 1)) + over[w] * (esz * K + 8);
+    if (best_w == 0 || bytes < best || (bytes == best && w < best_w)) {
+      best = bytes;
+      best_w = w;
+    }
+  }
+  *W_out = best_w;
+  if (bytes_out) *bytes_out = best;
+  return SFFN_OK;
+}
+
 sffn_status_t sparse_ffn_check(const twell_buffers_t* buf, void* stream) {
   if (!buf || !buf->status) return fail(SFFN_ERR_INVALID_ARGUMENT, "status buffer is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -33,6 +33,7 @@ struct Workspace {
   int32_t* stage_key;   // [2*cap]  (tile, token | rank_in_group << 24)
   void* stage_vals;     // [cap*K]  dtype
   long long* stats;     // [8]      stats reduction output
+  long long* hist;      // [SFFN_HIST_BINS] count histogram (twell_count_histogram)
   int32_t* blk_nnz;     // [nblk]   stored nonzeros per 256-token block (down-path choice)
   int32_t* grp_first;   // [nt*ng+1] first backup entry of each (tile, group), canonical order
   int32_t* tile_tot;    // [nt]     overflowing tile-rows per tile (ordering pass)
@@ -92,6 +93,7 @@ inline size_t workspace_bytes(const Dims& d, bool this_call_only = false) {
   n += align256(sizeof(int32_t) * 2 * (size_t)(d.cap > 0 ? d.cap : 1));
   n += align256((size_t)d.esz * (size_t)(d.cap > 0 ? d.cap : 1) * d.K);
   n += align256(sizeof(long long) * 8);
+  n += align256(sizeof(long long) * SFFN_HIST_BINS);
   n += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   n += align256(sizeof(int32_t) * ((size_t)d.nt * d.ng + 1));
   n += align256(sizeof(int32_t) * (size_t)d.nt);
@@ -121,6 +123,8 @@ inline Workspace carve(void* base, const Dims& d) {
   p += align256((size_t)d.esz * (size_t)(d.cap > 0 ? d.cap : 1) * d.K);
   w.stats = reinterpret_cast<long long*>(p);
   p += align256(sizeof(long long) * 8);
+  w.hist = reinterpret_cast<long long*>(p);
+  p += align256(sizeof(long long) * SFFN_HIST_BINS);
   w.blk_nnz = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * (size_t)((d.T + 255) / 256));
   w.grp_first = reinterpret_cast<int32_t*>(p);
@@ -233,6 +237,8 @@ hipError_t launch_down_union(const Dims& d, const twell_buffers_t& b, const Work
 // y[t] = sum_j vals[t, j] W[rows[t, j]] (bf16 W, vals, y; fp32 sums): the measurement probe.
 hipError_t launch_gather_fma_probe(const void* W, int F, int D, const int32_t* rows,
                                    const void* vals, int T, int n, void* y, hipStream_t s);
+// hist[c] = number of tile-rows with count c (c = 0 .. K), into ws.hist (cleared first).
+hipError_t launch_hist(const Dims& d, const twell_buffers_t& b, const Workspace& ws, hipStream_t s);
 // y = bf16 of the sum of the S fp32 parts in ws.dpart (split matrix-core kernels).
 hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
                               const int32_t* blk_nnz, long long thr, hipStream_t s);

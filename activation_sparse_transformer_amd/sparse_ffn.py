@@ -96,6 +96,12 @@ _PROTOS = {
     "sffn_profile_read": ([ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
     "sffn_probe_gather_fma": ([_P, _I32, _I32, _P, _P, _I32, _I32, _P, _P], ctypes.c_int),
+    "twell_count_histogram": ([ctypes.POINTER(ConfigC), ctypes.POINTER(BuffersC), _I32,
+                               ctypes.POINTER(ctypes.c_int64), _P], ctypes.c_int),
+    "twell_choose_ell_width": ([ctypes.POINTER(ConfigC), ctypes.POINTER(ctypes.c_int64),
+                                ctypes.POINTER(ctypes.c_int32), _I32,
+                                ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)],
+                               ctypes.c_int),
 }
 
 _lib = None
@@ -255,6 +261,34 @@ def twell_stats(cfg: Config, buf: TwellBuffers, stream=None, raise_on_overflow=T
     d = {n: getattr(out, n) for n, _ in StatsC._fields_}
     d["status"] = st
     return d
+
+
+def count_histogram(cfg: Config, buf: TwellBuffers, stream=None) -> np.ndarray:
+    """hist[c] = tile-rows of `buf` holding c nonzeros, c = 0 .. tile (computed on the device)."""
+    out = (ctypes.c_int64 * (cfg.tile + 1))()
+    c = cfg.c()
+    _check(lib().twell_count_histogram(ctypes.byref(c), ctypes.byref(buf.c()), int(buf.T), out,
+                                       _stream_ptr(stream)), "twell_count_histogram")
+    return np.array(out[:], dtype=np.int64)
+
+
+def choose_ell_width(cfg: Config, hist, candidates=None):
+    """(W, bytes): the ELL width with the fewest stored bytes for a count histogram (host)."""
+    h = np.ascontiguousarray(hist, dtype=np.int64)
+    if h.size != cfg.tile + 1:
+        raise ValueError(f"histogram needs tile + 1 = {cfg.tile + 1} bins")
+    c = cfg.c()
+    w = ctypes.c_int32()
+    nb = ctypes.c_int64()
+    if candidates is None:
+        cand, n = None, 0
+    else:
+        arr = np.ascontiguousarray(candidates, dtype=np.int32)
+        cand, n = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(arr.size)
+    _check(lib().twell_choose_ell_width(ctypes.byref(c), h.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                        cand, n, ctypes.byref(w), ctypes.byref(nb)),
+           "twell_choose_ell_width")
+    return int(w.value), int(nb.value)
 
 
 def check(buf: TwellBuffers, stream=None) -> int:

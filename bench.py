@@ -303,6 +303,20 @@ def main():
     nnz = st["nnz"]
     head = {}
     point_parity(head, Lh, y, sample_rows(T, Lh["heavy"], 512), c.tile, c.ell_width)
+    # the headline activation's tile-row count histogram and the ELL width with the fewest
+    # stored bytes for it (any width, and among the widths the matrix-core kernels take)
+    hist = sffn.count_histogram(cfg, act)
+    w_any, b_any = sffn.choose_ell_width(cfg, hist)
+    w_k, b_k = sffn.choose_ell_width(cfg, hist, [16, 32, 48, 64])
+    _, b_cfg = sffn.choose_ell_width(cfg, hist, [c.ell_width])
+    cum = np.cumsum(hist) / max(int(hist.sum()), 1)
+    width_choice = {"configured_w": c.ell_width, "bytes_at_configured_w": b_cfg,
+                    "best_w": w_any, "bytes_at_best_w": b_any,
+                    "best_kernel_w": w_k, "bytes_at_best_kernel_w": b_k,
+                    "count_quantiles": {q: int(np.searchsorted(cum, q)) for q in (0.5, 0.9, 0.99, 0.999)},
+                    "max_count": int(np.nonzero(hist)[0].max()) if hist.any() else 0,
+                    "rule": "bytes(W) = rows (2 + W (esz + 1)) + rows_over_W (esz K + 8)"}
+    log(f"  ELL width from the count histogram: {width_choice}")
 
     # ---- dense bf16 FFN baseline (hipBLASLt through torch), same inputs and stream
     def dense():
@@ -740,6 +754,7 @@ def main():
                      "ell_fill": round(st["ell_fill"], 4)},
         "kernels": kernels,
         "ceilings": ceilings,
+        "ell_width_choice": width_choice,
         "effective_tflops_dense_equiv": round(4.0 * T * D * F / (ms * 1e-3) / 1e12, 2),
         "train": train,
         "energy": energy,

@@ -261,6 +261,35 @@ sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t h, int32_t policy, float g
 sffn_status_t twell_stats(const sffn_config_t *cfg, const twell_buffers_t *buf, int32_t T,
                           twell_stats_t *out, void *stream);
 
+/* Bins of a count histogram: counts 0 .. tile, tile <= 256. */
+#define SFFN_HIST_BINS 257
+
+/* (sync) Histogram of the tile-row counts of `buf` for T tokens: hist[c] = the number of
+ * tile-rows (k, t) that hold c nonzeros, c = 0 .. cfg->tile (host array of cfg->tile + 1
+ * entries, written on SFFN_OK).  The per-tile nonzero counts are what the TwELL format is
+ * laid out from (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom
+ * CUDA kernels solve": per-tile ELL rows sized to the nonzeros, with a few dense backups for
+ * the rows that do not fit); twell_choose_ell_width picks a width from it.  Computed on the
+ * device; synchronises `stream`. */
+sffn_status_t twell_count_histogram(const sffn_config_t *cfg, const twell_buffers_t *buf,
+                                    int32_t T, int64_t *hist, void *stream);
+
+/* (host only) The ELL width W that stores a packed activation with count histogram `hist`
+ * (cfg->tile + 1 host entries, as twell_count_histogram writes it) in the fewest bytes
+ * (same section: the hybrid form keeps memory overhead minimal): with R = sum_c hist[c]
+ * tile-rows and O(W) = sum_{c > W} hist[c] of them overflowing,
+ *   bytes(W) = R (2 + W (esz + 1)) + O(W) (esz tile + 8)
+ * (a tile-row's count, its W value and column slots; an overflowing row's dense backup slice
+ * and its tile and token indices; esz = bytes per value of cfg->dtype), the same accounting
+ * as twell_stats' bytes_main and bytes_backup.  The minimum is taken over the n_candidates
+ * widths in `candidates` (host; each in [1, tile]; NULL: every W in [1, tile]); ties go to
+ * the smaller W.  cfg->ell_width is not used.  *W_out and *bytes_out (host; bytes_out may be
+ * NULL) are written on SFFN_OK; SFFN_ERR_INVALID_ARGUMENT for NULL pointers, negative bins,
+ * an empty or out-of-range candidate list. */
+sffn_status_t twell_choose_ell_width(const sffn_config_t *cfg, const int64_t *hist,
+                                     const int32_t *candidates, int32_t n_candidates,
+                                     int32_t *W_out, int64_t *bytes_out);
+
 /* (sync) Synchronise `stream` and return the status word of `buf`: SFFN_OK, or
  * SFFN_ERR_BACKUP_OVERFLOW when more tile-rows overflowed their W slots than the dense
  * backup holds (upppp.jp TwELL article of 2026-05-11, section "What TwELL and the custom

@@ -260,3 +260,37 @@ def stats(tw: TwELL) -> dict:
         "ell_fill": slots / float(nt * T * W) if nt * T * W else 0.0,
         "row_nnz": c.sum(axis=0),
     }
+
+
+def count_histogram(tw: TwELL) -> np.ndarray:
+    """hist[c] = number of tile-rows (k, t) of the TwELL with c stored nonzeros, c = 0..K
+    (the per-tile nonzero counts the format is laid out from: upppp.jp TwELL article of
+    2026-05-11, section "What TwELL and the custom CUDA kernels solve")."""
+    return np.bincount(tw.counts.astype(np.int64).ravel(), minlength=tw.K + 1).astype(np.int64)
+
+
+def twell_bytes(tw: TwELL, esz: int) -> int:
+    """Bytes of a packed activation as stored: every tile-row's count (2 bytes) and its W
+    value and column slots, plus each backup entry's dense K-value slice and its tile and
+    token indices (4 bytes each) - the storage of the hybrid form's sparse main part and
+    dense backups (same section)."""
+    assert tw.n_backup == tw.bk_vals.shape[0], "measured on a TwELL whose backup fits"
+    return (tw.counts.size * 2 + tw.vals.size * esz + tw.cols.size * 1
+            + tw.bk_vals.size * esz + tw.bk_tile.size * 4 + tw.bk_tok.size * 4)
+
+
+def choose_ell_width(hist, K: int, esz: int, candidates=None):
+    """The ELL width with the fewest stored bytes for a count histogram: for each candidate
+    W, every tile-row stores its count and W slots, and a row with more than W nonzeros
+    also stores a backup entry; the smallest total wins, ties to the smaller W.  Returns
+    (W, bytes)."""
+    hist = np.asarray(hist, np.int64)
+    rows = int(hist.sum())
+    best = None
+    for W in (range(1, K + 1) if candidates is None else candidates):
+        n_over = int(hist[W + 1:].sum())
+        total = rows * 2 + rows * W * (esz + 1) + n_over * (K * esz + 8)
+        if best is None or total < best[1] or (total == best[1] and W < best[0]):
+            best = (int(W), int(total))
+    return best
+

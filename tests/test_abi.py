@@ -240,3 +240,33 @@ def test_buffer_sizes_monotone_in_T(sffn, D, F, K, W, dtype):
             for k, v in s.items():
                 assert v >= prev[k], (k, T, v, prev[k])
         prev = s
+
+
+def test_choose_ell_width_matches_oracle(sffn):
+    """The library's width choice (host code) equals the oracle's on random and edge
+    histograms, with and without a candidate list; bad arguments are refused."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(0)
+    for K, dtype in ((64, "bf16"), (128, "bf16"), (256, "f32"), (128, "f32")):
+        cfg = sffn.Config(d_model=256, d_ff=4 * K, tile=K, ell_width=8, max_tokens=64,
+                          backup_capacity=16, dtype=dtype)
+        esz = 2 if dtype == "bf16" else 4
+        for trial in range(25):
+            lam = rng.uniform(0.5, K * 0.7)
+            hist = np.bincount(np.minimum(rng.poisson(lam, 5000), K), minlength=K + 1).astype(np.int64)
+            if trial % 5 == 0:
+                hist[K] += rng.integers(0, 300)  # dense tile-rows
+            assert sffn.choose_ell_width(cfg, hist) == oracle.choose_ell_width(hist, K, esz)
+            cands = [w for w in (16, 32, 48, 64) if w <= K]
+            assert sffn.choose_ell_width(cfg, hist, cands) == oracle.choose_ell_width(hist, K, esz, cands)
+        zero = np.zeros(K + 1, np.int64)
+        assert sffn.choose_ell_width(cfg, zero) == oracle.choose_ell_width(zero, K, esz)
+        with pytest.raises(sffn.SffnError):
+            sffn.choose_ell_width(cfg, zero, [0])
+        with pytest.raises(sffn.SffnError):
+            sffn.choose_ell_width(cfg, zero, [K + 1])
+        bad = zero.copy()
+        bad[3] = -1
+        with pytest.raises(sffn.SffnError):
+            sffn.choose_ell_width(cfg, bad)

@@ -634,6 +634,28 @@ def test_probe_gather_fma(F, d, T, n):
     assert np.all(np.abs(yh - ref) <= 1e-2 * (1.0 + np.abs(ref)))
 
 
+@pytest.mark.parametrize("T,F,K,W,dtype,density", [(300, 1024, 128, 16, "bf16", 0.08),
+                                                     (8192, 8192, 128, 32, "bf16", 0.05),
+                                                     (77, 512, 64, 8, "f32", 0.3),
+                                                     (130, 1024, 256, 16, "bf16", 0.03)])
+def test_count_histogram_and_width(T, F, K, W, dtype, density):
+    """The device count histogram of a packed activation equals the oracle's, bit for bit,
+    and the width chosen from it is the oracle's."""
+    torch, sffn = need_gpu()
+    print(f"[hist] T={T} F={F} K={K} W={W} {dtype} {density}", flush=True)
+    h = make_hidden(T, F, density, seed=2, heavy_rows=(0, T - 1), heavy_density=0.6)
+    cap = (F // K) * T
+    cfg = _cfg(sffn, T, 256, F, K, W, dtype, cap)
+    act = sffn.TwellBuffers(cfg, T)
+    sffn.twell_pack(cfg, torch.from_numpy(h).cuda(), act)
+    hist = sffn.count_histogram(cfg, act)
+    tw = oracle.pack(h.astype(np.float64), K, W)
+    ref = oracle.count_histogram(tw)
+    assert np.array_equal(hist, ref)
+    esz = 2 if dtype == "bf16" else 4
+    assert sffn.choose_ell_width(cfg, hist) == oracle.choose_ell_width(ref, K, esz)
+
+
 def test_profile_only_times_named_kernels():
     """With a name list only those launches are timed and counted; without, all are."""
     torch, sffn = need_gpu()

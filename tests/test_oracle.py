@@ -492,3 +492,40 @@ def test_generator_density_c3_sample(rho):
     _, counts = oracle.ffn_rows(x, Wu, b, Wd, rows, cfg.tile, cfg.ell_width)
     dens = counts.sum() / float(len(rows) * cfg.F)
     assert abs(dens - rho) < max(0.003, 0.15 * rho)
+
+
+@pytest.mark.parametrize("T,F,K,density,heavy,esz", [
+    (40, 256, 64, 0.05, (), 2), (40, 256, 64, 0.3, (3, 17), 2), (33, 512, 128, 0.02, (0,), 4),
+    (20, 256, 128, 0.9, (), 2), (25, 512, 256, 0.1, (5,), 2)])
+def test_choose_ell_width_is_the_smallest_packing(T, F, K, density, heavy, esz):
+    """The width chosen from the count histogram is the one whose actual packing - the
+    oracle's pack at every width, its arrays measured - takes the fewest bytes (ties to the
+    smaller width), and the histogram counts every tile-row once."""
+    h = make_hidden(T, F, density, seed=5, heavy_rows=heavy, heavy_density=0.7)
+    tw1 = oracle.pack(h, K, 1)
+    hist = oracle.count_histogram(tw1)
+    assert hist.sum() == (F // K) * T and hist.size == K + 1
+    assert np.array_equal(hist, np.bincount(((h != 0).reshape(T, F // K, K).sum(axis=2)).ravel(),
+                                            minlength=K + 1))
+    measured = [oracle.twell_bytes(oracle.pack(h, K, W), esz) for W in range(1, K + 1)]
+    W_best = 1 + int(np.argmin(measured))  # argmin takes the first (smallest W) of ties
+    assert oracle.choose_ell_width(hist, K, esz) == (W_best, measured[W_best - 1])
+    cands = [16, 32, 48, 64]
+    cands = [c for c in cands if c <= K]
+    wc, bc = oracle.choose_ell_width(hist, K, esz, cands)
+    assert bc == min(measured[c - 1] for c in cands) and wc == min(
+        c for c in cands if measured[c - 1] == bc)
+
+
+def test_choose_ell_width_special_cases():
+    """Every tile-row with the same count c: the width c when ELL slots are cheaper than a
+    dense backup slice (c (esz + 1) < esz K + 8), else width 1 with every row in the backup;
+    all rows empty: width 1."""
+    K, esz = 128, 2
+    for c, expect in ((5, 5), (40, 40), (88, 88), (89, 1), (128, 1)):
+        hist = np.zeros(K + 1, np.int64)
+        hist[c] = 1000
+        assert oracle.choose_ell_width(hist, K, esz)[0] == expect, c
+    hist = np.zeros(K + 1, np.int64)
+    hist[0] = 7
+    assert oracle.choose_ell_width(hist, K, esz) == (1, 7 * (2 + 3))
