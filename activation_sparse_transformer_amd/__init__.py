@@ -9,7 +9,7 @@ from .sparse_ffn import (  # noqa: F401
     buffer_bytes, BUFFER_FIELDS,
     profile_enable, profile_only, profile_reset, profile_read, probe_gather_fma, lib, LIB_PATH,
     SFFN_OK, SFFN_ERR_INVALID_ARGUMENT, SFFN_ERR_UNSUPPORTED, SFFN_ERR_BACKUP_OVERFLOW,
-    SFFN_ERR_DEVICE, DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES, DOWN_UNION,
+    SFFN_ERR_DEVICE, DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES, DOWN_UNION, DOWN_SPARSE,
     DOWN_GATHER_DENSITY_DEFAULT, DOWN_MFMA_DENSITY_DEFAULT, DOWN_TILES_MIN_T, DOWN_MFMA_MIN_T,
     MAX_TILES,
 )

@@ -263,7 +263,8 @@ struct DownPlan {
 
 static DownPlan plan_down(const sparse_ffn* hd, const Dims& d) {
   DownPlan p{hd->down_policy, 0, 0, 0, false};
-  if ((p.policy == SFFN_DOWN_MFMA || p.policy == SFFN_DOWN_UNION) && !down_mfma_supported(d))
+  if ((p.policy == SFFN_DOWN_MFMA || p.policy == SFFN_DOWN_UNION ||
+       p.policy == SFFN_DOWN_SPARSE) && !down_mfma_supported(d))
     p.policy = SFFN_DOWN_TILES;
   if (p.policy == SFFN_DOWN_TILES && !down_lds_supported(d)) p.policy = SFFN_DOWN_GATHER;
   if (p.policy != SFFN_DOWN_AUTO) return p;
@@ -303,7 +304,12 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
     return run("down_union", s,
                [&] { return launch_down_union(d, act, ws, hd->W_down, y, blk, thr, s); });
   };
+  auto sparse = [&](const int32_t* blk, long long thr) {
+    return run("down_sparse", s,
+               [&] { return launch_down_sparse(d, act, ws, hd->W_down, y, blk, thr, s); });
+  };
   const DownPlan p = plan_down(hd, d);
+  if (p.policy == SFFN_DOWN_SPARSE) return sparse(nullptr, 0);
   if (p.policy == SFFN_DOWN_UNION) return unionk(nullptr, 0);
   if (p.policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
   if (p.policy == SFFN_DOWN_TILES) return tiles(nullptr, 0, 0);
@@ -435,7 +441,7 @@ sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float 
                                          float mfma_density) {
   if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
   if (policy != SFFN_DOWN_AUTO && policy != SFFN_DOWN_GATHER && policy != SFFN_DOWN_MFMA &&
-      policy != SFFN_DOWN_TILES && policy != SFFN_DOWN_UNION)
+      policy != SFFN_DOWN_TILES && policy != SFFN_DOWN_UNION && policy != SFFN_DOWN_SPARSE)
     return fail(SFFN_ERR_INVALID_ARGUMENT, "unknown down-projection policy");
   if (!(gather_density >= 0.0f && gather_density <= mfma_density && mfma_density <= 1.0f))
     return fail(SFFN_ERR_INVALID_ARGUMENT,

@@ -234,6 +234,11 @@ hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Works
 hipError_t launch_down_union(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                              hipStream_t s);
+// The down-projection on the 2:4 structured-sparse matrix cores (the same shapes as
+// launch_down_mfma): each stored nonzero at its rank within its four-column group.
+hipError_t launch_down_sparse(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                              hipStream_t s);
 // y[t] = sum_j vals[t, j] W[rows[t, j]] (bf16 W, vals, y; fp32 sums): the measurement probe.
 hipError_t launch_gather_fma_probe(const void* W, int F, int D, const int32_t* rows,
                                    const void* vals, int T, int n, void* y, hipStream_t s);

@@ -62,7 +62,7 @@ class StatsC(ctypes.Structure):
 
 
 # Down-projection policies (mirror the header's SFFN_DOWN_* values).
-DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES, DOWN_UNION = 0, 1, 2, 3, 4
+DOWN_AUTO, DOWN_GATHER, DOWN_MFMA, DOWN_TILES, DOWN_UNION, DOWN_SPARSE = 0, 1, 2, 3, 4, 5
 DOWN_GATHER_DENSITY_DEFAULT = 0.0005
 DOWN_MFMA_DENSITY_DEFAULT = 0.005
 DOWN_TILES_MIN_T = 4096
@@ -379,9 +379,10 @@ class SparseFFN:
         """Choice of the down-projection kernel: "auto" (by the layer's stored density,
         decided on the device: the per-token gather up to `gather_density`, the LDS-tile
         vector kernel up to `mfma_density`, the matrix cores above), or always "gather",
-        "tiles" or "mfma"."""
+        "tiles", "mfma", "union" (matrix cores over each 64-token block's column union) or
+        "sparse" (the 2:4 structured-sparse matrix-core instruction)."""
         code = {"auto": DOWN_AUTO, "gather": DOWN_GATHER, "mfma": DOWN_MFMA,
-                "tiles": DOWN_TILES, "union": DOWN_UNION}.get(policy)
+                "tiles": DOWN_TILES, "union": DOWN_UNION, "sparse": DOWN_SPARSE}.get(policy)
         if code is None:
             raise ValueError(f"unknown down policy {policy!r}")
         _check(lib().sparse_ffn_set_down_policy(self._h, code, float(gather_density),

@@ -33,7 +33,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MAC (dot2) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # launches of one forward, by the names the library's event timing uses
-KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_tiles", "down_mfma", "down_union")
+KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_tiles", "down_mfma", "down_union",
+           "down_sparse")
 TRAIN_KERNELS = KERNELS + ("bwd_dh", "bwd_dw_down", "bwd_dw_up", "bwd_dx")
 
 
@@ -49,6 +50,7 @@ KERNEL_SOURCES = {
     "down_tiles": ("k_down_lds.hip", "sffn_common.hpp"),
     "down": ("k_down_rows.hip", "sffn_common.hpp"),
     "down_union": ("k_down_union.hip", "sffn_common.hpp"),
+    "down_sparse": ("k_down_sparse.hip", "sffn_common.hpp"),
 }
 
 
@@ -156,7 +158,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--sweep-policies", default="auto",
                     help="comma-separated down policies the density sweep runs, each at every "
-                         "density (auto, gather, tiles, mfma, union)")
+                         "density (auto, gather, tiles, mfma, union, sparse)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the per-point oracle checks")
     ap.add_argument("--no-train", action="store_true", help="skip the forward+backward timing")
@@ -480,7 +482,8 @@ def main():
         kname = {"down": "down_rows_kernel (per-token W_down row gather)",
                  "down_tiles": "down_lds_kernel (W_down tiles in LDS, bf16 dot products)",
                  "down_mfma": "down_mfma_kernel (TwELL tiles rebuilt in LDS, MFMA down-projection)",
-                 "down_union": "down_union_kernel (column-union compacted MFMA down-projection)"}.get(
+                 "down_union": "down_union_kernel (column-union compacted MFMA down-projection)",
+                 "down_sparse": "down_sparse_kernel (2:4 structured-sparse MFMA down-projection)"}.get(
             down_ran, down_ran)
         if dn_roof["bound"] == "hbm":
             roofline = {"bound": "hbm", "achieved": dn_roof["hbm_gbs"], "peak": PEAK_HBM_GBS,
@@ -802,7 +805,7 @@ def machine_info():
 
 def sffn_down_names():
     """Event names of the library's down-projection launches."""
-    return ("down", "down_tiles", "down_mfma", "down_union")
+    return ("down", "down_tiles", "down_mfma", "down_union", "down_sparse")
 
 
 def decode_policies():

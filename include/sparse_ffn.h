@@ -220,7 +220,11 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
  *   union:  the matrix-core contraction of each 64-token block over only the columns where
  *           one of its tokens has a stored nonzero (the block's column union, per 64-column
  *           step; a step whose union leaves no 16-column k-step to skip runs densely), so
- *           the matrix-core work falls with the density (same shapes as mfma).
+ *           the matrix-core work falls with the density (same shapes as mfma);
+ *   sparse: the 2:4 structured-sparse matrix-core instruction: each stored nonzero goes to
+ *           its rank within its four-column group, ranks 0-1 in one compressed plane and
+ *           2-3 in a second that is contracted only where it holds a value, so a step costs
+ *           half a dense one where no group has three nonzeros (same shapes as mfma).
  * Policies:
  *   SFFN_DOWN_AUTO:   by the layer's stored density (stored nonzeros / (T d_ff)): gather up to
  *                     gather_density, tiles up to mfma_density, mfma above; the count is taken
@@ -233,9 +237,9 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
  *                     256-token blocks and reads all of W_down, where the gather reads only
  *                     the rows in use).  With few tokens the mfma kernel splits the tiles
  *                     over more workgroups and adds the parts' fp32 sums in a fixed order.
- *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA, SFFN_DOWN_UNION: always that
- *                     kernel (tiles, mfma and union fall back as above when the layer does
- *                     not support them).
+ *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA, SFFN_DOWN_UNION, SFFN_DOWN_SPARSE:
+ *                     always that kernel (tiles, mfma, union and sparse fall back as above
+ *                     when the layer does not support them).
  * All accumulate in fp32; they differ only in summation order.  Host only; the setting
  * belongs to the handle.  SFFN_ERR_INVALID_ARGUMENT for an unknown policy or thresholds
  * outside 0 <= gather_density <= mfma_density <= 1. */
@@ -244,6 +248,7 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
 #define SFFN_DOWN_MFMA 2
 #define SFFN_DOWN_TILES 3
 #define SFFN_DOWN_UNION 4
+#define SFFN_DOWN_SPARSE 5
 #define SFFN_DOWN_GATHER_DENSITY_DEFAULT 0.0005f
 #define SFFN_DOWN_MFMA_DENSITY_DEFAULT 0.005f
 #define SFFN_DOWN_TILES_MIN_T 4096

@@ -77,7 +77,7 @@ def test_header_constants_match_binding(sffn):
     defs = dict(re.findall(r"#define\s+(SFFN_DOWN_[A-Z_]+)\s+([0-9.]+)f?", text))
     want = {"SFFN_DOWN_AUTO": sffn.DOWN_AUTO, "SFFN_DOWN_GATHER": sffn.DOWN_GATHER,
             "SFFN_DOWN_MFMA": sffn.DOWN_MFMA, "SFFN_DOWN_TILES": sffn.DOWN_TILES,
-            "SFFN_DOWN_UNION": sffn.DOWN_UNION,
+            "SFFN_DOWN_UNION": sffn.DOWN_UNION, "SFFN_DOWN_SPARSE": sffn.DOWN_SPARSE,
             "SFFN_DOWN_GATHER_DENSITY_DEFAULT": sffn.DOWN_GATHER_DENSITY_DEFAULT,
             "SFFN_DOWN_MFMA_DENSITY_DEFAULT": sffn.DOWN_MFMA_DENSITY_DEFAULT,
             "SFFN_DOWN_TILES_MIN_T": sffn.DOWN_TILES_MIN_T,

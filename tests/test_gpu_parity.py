@@ -147,7 +147,7 @@ DOWN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union", "sparse"])
 @pytest.mark.parametrize("T,D,F,K,W,dtype,density", DOWN_CASES)
 def test_down_from_pack(T, D, F, K, W, dtype, density, policy):
     torch, sffn = need_gpu()
@@ -362,7 +362,7 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     return rel
 
 
-@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union", "sparse"])
 @pytest.mark.parametrize("name,T,rho", [
     ("C1", None, None), ("C1b", None, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
@@ -379,7 +379,7 @@ def test_forward_parity(name, T, rho, policy):
     _forward_case(torch, sffn, L, policy=policy)
 
 
-@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union"])
+@pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union", "sparse"])
 def test_forward_heavy_rows_force_backup(policy):
     """2B-like layer at a reduced T with heavy rows: the backup is in use."""
     torch, sffn = need_gpu()
@@ -390,7 +390,7 @@ def test_forward_heavy_rows_force_backup(policy):
 
 
 @pytest.mark.parametrize("T", [32, 48])
-@pytest.mark.parametrize("policy", ["auto", "gather", "union"])
+@pytest.mark.parametrize("policy", ["auto", "gather", "union", "sparse"])
 def test_forward_heavy_rows_short_batch(T, policy):
     """Decode-shaped batch of the 1.5B-like layer with two 3x-scaled token rows: most of their
     tile-rows overflow into the backup, and below 64 tokens the row gather (256-column chunks)
@@ -414,7 +414,7 @@ def test_forward_wide_ell(name, W, rho, T):
     _forward_case(torch, sffn, L)
 
 
-@pytest.mark.parametrize("policy", ["auto", "union"])
+@pytest.mark.parametrize("policy", ["auto", "union", "sparse"])
 def test_forward_edge_all_zero_all_positive(policy):
     torch, sffn = need_gpu()
     base = CONFIGS["C3"].replace(heavy_frac=0.0)
@@ -558,7 +558,8 @@ def _plain_bound_report(yh, y_plain, heavy, what):
     ("C3", 0.05, "tiles"), ("C3", 0.05, "mfma"), ("C3", 0.05, "union"), ("C3", 0.01, "union"),
     ("C3", 0.002, "union"), ("C3", 0.10, "auto"), ("C3", 0.20, "auto"), ("C3", 0.20, "union"),
     ("C2", None, "union"), ("C4", None, "auto"), ("C4", None, "gather"), ("C4", None, "tiles"),
-    ("C4", None, "union")])
+    ("C4", None, "union"), ("C3", 0.05, "sparse"), ("C3", 0.01, "sparse"), ("C3", 0.002, "sparse"),
+    ("C3", 0.20, "sparse"), ("C2", None, "sparse"), ("C4", None, "sparse")])
 def test_forward_full_size(name, rho, policy):
     """Full layer sizes, in the launch configuration the benchmark times: every token row
     against the oracle (activations stored in bf16 as the TwELL holds them), every row
