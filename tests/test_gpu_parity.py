@@ -456,6 +456,75 @@ def test_forward_capacity_overflow_reported():
     assert sffn.check(act) == sffn.SFFN_ERR_BACKUP_OVERFLOW
 
 
+@pytest.mark.parametrize("T", [1, 32])
+def test_forward_small_batch_capacity(T):
+    """Decode-shaped batches (the small-batch up-projection, pack and one-launch ordering, the
+    split row gather): with a 3x token in the batch, a backup capacity of exactly the rows it
+    needs gives the same y and TwELL as a large one, one row fewer and none at all are
+    reported as overflow."""
+    torch, sffn = need_gpu()
+    L = make_layer(CONFIGS["C3"].replace(heavy_frac=1.0 / T), seed=0, T=T, rho=0.05)
+    c = L["cfg"]
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    big = _cfg(sffn, T, c.D, c.F, c.tile, c.ell_width, c.dtype, c.n_tiles * T)
+    y0, a0 = sffn.SparseFFN(big, Wu, b, Wd).forward(x)
+    assert sffn.check(a0) == sffn.SFFN_OK
+    h0 = a0.to_host()
+    R = int(h0["bk_n"])
+    assert R > 0, "the 3x token overflows some tile-rows"
+    print(f"[small-capacity] T={T} R={R}", flush=True)
+    exact = _cfg(sffn, T, c.D, c.F, c.tile, c.ell_width, c.dtype, R)
+    y1, a1 = sffn.SparseFFN(exact, Wu, b, Wd).forward(x)
+    assert sffn.check(a1) == sffn.SFFN_OK
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+    h1 = a1.to_host()
+    for k in ("counts", "vals", "cols", "bk_tile", "bk_tok", "bk_vals", "bk_tile_ptr"):
+        assert np.array_equal(h1[k].view(np.uint8), h0[k].view(np.uint8)), k
+    for cap in (R - 1, 0):
+        cfg = _cfg(sffn, T, c.D, c.F, c.tile, c.ell_width, c.dtype, cap)
+        _, a = sffn.SparseFFN(cfg, Wu, b, Wd).forward(x)
+        assert sffn.check(a) == sffn.SFFN_ERR_BACKUP_OVERFLOW, cap
+
+
+@pytest.mark.parametrize("T", [32, 300])
+def test_forward_graph_replay(T):
+    """The forward records into a HIP graph (it allocates nothing and records no memset):
+    three replays, each after an eager forward of other inputs into the same buffers, give the
+    eager result bit for bit (y and the whole TwELL + backup)."""
+    torch, sffn = need_gpu()
+    print(f"[graph] T={T}", flush=True)
+    L = make_layer(CONFIGS["C3"], seed=0, T=T, rho=0.05)
+    c = L["cfg"]
+    cfg = _cfg(sffn, T, c.D, c.F, c.tile, c.ell_width, c.dtype)
+    x, Wu, b, Wd = layer_to_dev(torch, L)
+    layer = sffn.SparseFFN(cfg, Wu, b, Wd)
+    act = sffn.TwellBuffers(cfg, T)
+    y = torch.empty_like(x)
+    layer.forward(x, act=act, y=y)
+    torch.cuda.synchronize()
+    y_ref, h_ref = y.clone(), act.to_host()
+    keys = ("counts", "vals", "cols", "bk_tile", "bk_tok", "bk_vals", "bk_tile_ptr")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x, act=act, y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, act=act, y=y)
+    x_other = torch.flip(x, dims=[0]).contiguous()
+    for r in range(3):
+        layer.forward(x_other, act=act, y=y)  # eager work on the same buffers in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert sffn.check(act) == sffn.SFFN_OK
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), r
+        h = act.to_host()
+        for k in keys:
+            assert np.array_equal(h[k].view(np.uint8), h_ref[k].view(np.uint8)), (r, k)
+
+
 def test_determinism_and_homogeneity():
     torch, sffn = need_gpu()
     L = make_layer(CONFIGS["C3"], seed=0, T=257, rho=0.05)
