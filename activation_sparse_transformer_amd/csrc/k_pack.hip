@@ -19,14 +19,6 @@
 
 namespace sffn {
 
-__global__ void zero_claim_kernel(int32_t* claim) {
-  if (threadIdx.x == 0) *claim = 0;
-}
-
-hipError_t launch_zero_claim(const Workspace& ws, hipStream_t s) {
-  hipLaunchKernelGGL(zero_claim_kernel, dim3(1), dim3(64), 0, s, ws.claim);
-  return hipGetLastError();
-}
 
 // Store one value of the TwELL value array in the layer dtype.
 template <bool BF16>
@@ -94,8 +86,8 @@ __device__ __forceinline__ void pack_pair(const Dims& d, int k, int g, const flo
     if (t >= T) break;
     const int cnt = __builtin_amdgcn_readlane(cnt_lane, i);
     const bool over = cnt > W;
-    const int slot = base + lr;
-    const bool stage = over && slot < d.cap;
+    const bool stage = over && d.cap > 0;
+    const int slot = stage ? stage_slot((uint32_t)base + (uint32_t)lr, d.cap) : 0;
     const size_t row = ((size_t)k * T + t) * (size_t)W;
     int prefix = 0;
 #pragma unroll
@@ -365,8 +357,8 @@ __global__ __launch_bounds__(512) void pack_small_kernel(Dims d, const float* __
     const int cnt = __builtin_amdgcn_readlane(cnt_lane, i0 + i);
     const bool over = cnt > W;
     const int lr = __popcll(om & ((1ull << (i0 + i)) - 1));  // rank among the group's overflows
-    const int slot = base + lr;
-    const bool stage = over && slot < d.cap;
+    const bool stage = over && d.cap > 0;
+    const int slot = stage ? stage_slot((uint32_t)base + (uint32_t)lr, d.cap) : 0;
     const size_t row = ((size_t)k * T + t) * (size_t)W;
     int prefix = 0;
 #pragma unroll
@@ -542,12 +534,14 @@ __global__ __launch_bounds__(256) void order_copy_kernel(Dims d, twell_buffers_t
       if (tid == 0) ws.blk_nnz[tb] = bsum[0] + bsum[1] + bsum[2] + bsum[3];
     }
   }
-  // the copy
-  const int n_staged = min(*ws.claim, d.cap);
+  // the copy: the producers claimed positions first .. first + total - 1 (slots modulo cap)
+  const int n_staged = min(total, d.cap);
+  const uint32_t first_pos = (uint32_t)*ws.claim - (uint32_t)total;
   const int gw = blockIdx.x * 4 + wv;
   const int nw = gridDim.x * 4;
   constexpr int WORDS = K * (BF16 ? 2 : 4) / 4;  // 32-bit words per slice
-  for (int e = gw; e < n_staged; e += nw) {
+  for (int i = gw; i < n_staged; i += nw) {
+    const int e = stage_slot(first_pos + (uint32_t)i, d.cap);
     const int kk = ws.stage_key[2 * e];
     const int tw = ws.stage_key[2 * e + 1];
     const int t = tw & 0xFFFFFF, lr = tw >> 24;
@@ -631,13 +625,16 @@ __global__ __launch_bounds__(1024) void order_small_kernel(Dims d, twell_buffers
   // the copy: entry e of the staging goes to first(tile, group) + its rank in the group.
   // A slice is LPE 16-byte pieces (slices start 16-byte aligned), so a wave moves EPW
   // entries at once and the grid 16 EPW per workgroup.
-  const int n_staged = min(*ws.claim, d.cap);
+  // the producers claimed positions first .. first + tot - 1 (slots modulo cap)
+  const int n_staged = min(tot, d.cap);
+  const uint32_t first_pos = (uint32_t)*ws.claim - (uint32_t)tot;
   constexpr int LPE = K * (BF16 ? 2 : 4) / 16;  // lanes per entry: 8 .. 64
   constexpr int EPW = 64 / LPE;
   const int sub = lane / LPE, q = lane - sub * LPE;
   for (int e0 = (blockIdx.x * 16 + wv) * EPW; e0 < n_staged; e0 += gridDim.x * 16 * EPW) {
-    const int e = e0 + sub;
-    if (e < n_staged) {
+    const int i = e0 + sub;
+    if (i < n_staged) {
+      const int e = stage_slot(first_pos + (uint32_t)i, d.cap);
       const int kk = ws.stage_key[2 * e];
       const int tw = ws.stage_key[2 * e + 1];
       const int t = tw & 0xFFFFFF, lr = tw >> 24;

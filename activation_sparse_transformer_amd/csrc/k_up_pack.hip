@@ -393,8 +393,8 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
     bool stage[TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      slot[j] = claim_base[jslot[j]][wt] + lrank[j];
-      stage[j] = tot[j] > W && slot[j] < d.cap;
+      stage[j] = tot[j] > W && d.cap > 0;
+      slot[j] = stage[j] ? stage_slot((uint32_t)claim_base[jslot[j]][wt] + (uint32_t)lrank[j], d.cap) : 0;
     }
     int run[TPW];
 #pragma unroll

@@ -35,15 +35,12 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
                                                        const uint16_t* __restrict__ Wu,
                                                        const uint16_t* __restrict__ bu,
                                                        float* __restrict__ h,
-                                                       float* __restrict__ zdump,
-                                                       int32_t* __restrict__ claim) {
+                                                       float* __restrict__ zdump) {
   __shared__ __attribute__((aligned(16))) float red[4][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int D = d.D, T = d.T, F = d.F;
   const int n0 = blockIdx.x * US_NB;
-  // the backup staging counter the pack kernel (the next launch) claims from
-  if (blockIdx.x == 0 && threadIdx.x == 0) *claim = 0;
   const int r = lane & 31, hh = lane >> 5;
   const int nks = D / 16;                          // 16-column steps (D % 16 == 0)
   const int ks0 = wave * nks / 4, ks1 = (wave + 1) * nks / 4;
@@ -186,8 +183,7 @@ __device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[4], const uint
 template <int NTB>
 __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
     Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
-    const uint16_t* __restrict__ bu, float* __restrict__ h, float* __restrict__ zdump,
-    int32_t* __restrict__ claim) {
+    const uint16_t* __restrict__ bu, float* __restrict__ h, float* __restrict__ zdump) {
   static_assert(NTB == 4, "the 8-wave form stages 128 token rows");
   constexpr int US_NW = US8_NW;
   // wave w's 16 KB: first its staged token rows, then its partial sums
@@ -197,8 +193,6 @@ __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int D = d.D, T = d.T, F = d.F;
   const int n0 = blockIdx.x * US_NB;
-  // the backup staging counter the pack kernel (the next launch) claims from
-  if (blockIdx.x == 0 && threadIdx.x == 0) *claim = 0;
   const int r = lane & 31, hh = lane >> 5;
   const int ngr = D / 64;                          // groups of four steps (D % 64 == 0)
   const int g0 = wave * ngr / US_NW, g1 = (wave + 1) * ngr / US_NW;
@@ -268,19 +262,19 @@ bool up_small_supported(const Dims& d) {
 static_assert(UP_SMALL_T <= 128, "at most four 32-token blocks per workgroup");
 
 hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
-                           const uint16_t* bu, float* h, float* zdump, int32_t* claim,
+                           const uint16_t* bu, float* h, float* zdump,
                            hipStream_t s) {
   if (!up_small_supported(d)) return hipErrorInvalidValue;
   const dim3 grid(d.F / US_NB);
   if (d.T <= 32)
-    hipLaunchKernelGGL(up_small_kernel<1>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump, claim);
+    hipLaunchKernelGGL(up_small_kernel<1>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   else if (d.T <= 64)
-    hipLaunchKernelGGL(up_small_kernel<2>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump, claim);
+    hipLaunchKernelGGL(up_small_kernel<2>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   else if (d.D % 64 == 0)
     hipLaunchKernelGGL(up_small8_kernel<4>, grid, dim3(US8_NW * 64), 0, s, d, x, Wu, bu, h,
-                       zdump, claim);
+                       zdump);
   else
-    hipLaunchKernelGGL(up_small_kernel<4>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump, claim);
+    hipLaunchKernelGGL(up_small_kernel<4>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   return hipGetLastError();
 }
 

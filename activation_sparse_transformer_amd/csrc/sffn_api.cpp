@@ -244,7 +244,6 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
   const Dims d = make_dims(cfg, T);
   const Workspace ws = carve(buf->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SFFN_TRY(run("zero", s, [&] { return launch_zero_claim(ws, s); }));
   SFFN_TRY(run("pack", s, [&] { return launch_pack(d, h, *buf, ws, s); }));
   SFFN_TRY(run("order", s, [&] { return launch_order(d, *buf, ws, s); }));
   return SFFN_OK;
@@ -333,23 +332,20 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
   const Workspace ws = carve(act->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (up_small_supported(d)) {
-    // decode-shaped batch: up-projection over many small workgroups (it also clears the
-    // staging claim), then the pack kernel
+    // decode-shaped batch: up-projection over many small workgroups, then the pack kernel
     SFFN_TRY(run("up_small", s, [&] {
       return launch_up_small(d, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(hd->W_up),
-                             static_cast<const uint16_t*>(hd->b_up), ws.hsmall, z, ws.claim, s);
+                             static_cast<const uint16_t*>(hd->b_up), ws.hsmall, z, s);
     }));
     SFFN_TRY(run("pack", s, [&] { return launch_pack(d, ws.hsmall, *act, ws, s); }));
   } else if (d.bf16) {
-    SFFN_TRY(run("zero", s, [&] { return launch_zero_claim(ws, s); }));
     SFFN_TRY(run("up_pack", s, [&] {
       return launch_up_pack_bf16(d, static_cast<const uint16_t*>(x),
                                  static_cast<const uint16_t*>(hd->W_up),
                                  static_cast<const uint16_t*>(hd->b_up), *act, ws, z, s);
     }));
   } else {
-    SFFN_TRY(run("zero", s, [&] { return launch_zero_claim(ws, s); }));
     SFFN_TRY(run("up_pack", s, [&] {
       return launch_up_pack_f32(d, static_cast<const float*>(x),
                                 static_cast<const float*>(hd->W_up),

@@ -28,7 +28,7 @@ struct Dims {
 
 // Workspace carving.  Regions are 256-byte aligned.
 struct Workspace {
-  int32_t* claim;       // [1]      staging slots claimed so far
+  int32_t* claim;       // [1]      staging claim counter (any start value, see stage_slot)
   int32_t* ov_grp;      // [nt*ng]  overflowing tile-rows per (tile, group)
   int32_t* stage_key;   // [2*cap]  (tile, token | rank_in_group << 24)
   void* stage_vals;     // [cap*K]  dtype
@@ -165,6 +165,11 @@ __device__ __forceinline__ T ld_uniform(const T* p) {
   typedef const __attribute__((address_space(4))) T* cptr;
   return *(cptr)(uintptr_t)p;
 }
+// Staging slot of claimed position p.  Producers claim consecutive positions from
+// ws.claim with atomicAdd; the counter is never cleared (it starts wherever the previous
+// call left it), so slots run modulo the staging capacity, and the ordering pass recovers
+// the first position as the final counter minus the total it scans.  cap > 0.
+__device__ __forceinline__ int stage_slot(uint32_t p, int cap) { return (int)(p % (uint32_t)cap); }
 // Sum of the n per-block counts (the layer's stored nonzeros), the same in every lane.
 __device__ __forceinline__ long long layer_nnz(const int32_t* blk_nnz, int n) {
   long long s = 0;
@@ -177,7 +182,6 @@ __device__ __forceinline__ long long layer_nnz(const int32_t* blk_nnz, int n) {
 
 // ---------------------------------------------------------------- launchers
 // Each returns the launch's hipError_t (hipGetLastError after the launch).
-hipError_t launch_zero_claim(const Workspace& ws, hipStream_t s);
 hipError_t launch_pack(const Dims& d, const float* h, const twell_buffers_t& b,
                        const Workspace& ws, hipStream_t s);
 // with_blk: also write ws.blk_nnz (the per-256-token-block stored nonzeros).
@@ -189,10 +193,10 @@ hipError_t launch_up_pack_f32(const Dims& d, const float* x, const float* Wu, co
                               const twell_buffers_t& b, const Workspace& ws, float* zdump,
                               hipStream_t s);
 // Decode-shaped up-projection: h = max(x W_up^T + b, 0) as fp32 [T, F] (T <= UP_SMALL_T),
-// and z = x W_up^T + b into zdump if it is not null; also sets the staging claim to 0.
+// and z = x W_up^T + b into zdump if it is not null.
 bool up_small_supported(const Dims& d);
 hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
-                           const uint16_t* bu, float* h, float* zdump, int32_t* claim,
+                           const uint16_t* bu, float* h, float* zdump,
                            hipStream_t s);
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,

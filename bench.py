@@ -33,8 +33,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PEAK_VALU_TFLOPS = 157.3      # MI355X vector: 256 CU x 4 SIMD x 16 lanes x 2 MAC (dot2) x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # launches of one forward, by the names the library's event timing uses
-KERNELS = ("zero", "up_pack", "order", "block_nnz", "down", "down_tiles", "down_mfma", "down_union",
-           "down_sparse")
+KERNELS = ("up_pack", "up_small", "pack", "order", "block_nnz", "down", "down_tiles", "down_mfma",
+           "down_union", "down_sparse")
 TRAIN_KERNELS = KERNELS + ("bwd_dh", "bwd_dw_down", "bwd_dw_up", "bwd_dx")
 
 
@@ -466,7 +466,7 @@ def main():
     kernels = {
         "up_pack": {"ms": round(up_ms, 5), "tflops": round(rate(up_flops, up_ms), 2),
                     "frac_mfma_peak": round(rate(up_flops, up_ms) / PEAK_BF16_TFLOPS, 4)},
-        "order": {"ms": round(kt.get("order", 0.0), 5)}, "zero": {"ms": round(kt.get("zero", 0.0), 5)},
+        "order": {"ms": round(kt.get("order", 0.0), 5)},
         "block_nnz": {"ms": round(kt.get("block_nnz", 0.0), 5)},
         "down_launches_ms": {k: round(kt.get(k, 0.0), 5) for k in down_names},
         "down": {"kernel": down_ran, "ms": round(dn_ms, 5), **dn_roof},
