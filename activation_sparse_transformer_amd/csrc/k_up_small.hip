@@ -14,7 +14,13 @@
 //
 // Two forms, by measurement on MI355X at d_model 2048:
 //  * up to 64 tokens (one or two token blocks): 4 waves, each over a quarter of d_model in
-//    batches of 8 (4) steps whose loads are in flight together;
+//    batches of 8 (4) steps whose loads are in flight together.  Where the quarters fit LDS
+//    (d_model <= 2048, a multiple of 512), each wave first copies its 32 W_up rows x D/4
+//    columns into its own LDS region with contiguous 1 KB direct loads (16-byte piece s of row
+//    rr at slot s ^ (rr % 16), so the fragment reads of 16 rows hit distinct banks): read in
+//    the MFMA layout straight from memory, each load used 32 bytes of 32 lines, and W_up
+//    streamed at 6.3 TB/s against 11.3 TB/s for whole-row loads (a probe over the 1.5B-like
+//    layer's W_up, cache-resident as in the forward);
 //  * 65 to 128 tokens (four token blocks, four times the token-row bytes per W_up piece):
 //    8 waves, each over an eighth of d_model in groups of four steps, with the W_up pieces of
 //    two groups in flight at once and the token rows of the next group loaded as whole
@@ -30,13 +36,17 @@ typedef unsigned int u32x4_s __attribute__((ext_vector_type(4)));
 
 constexpr int US_NB = 32;  // neurons per workgroup
 
-template <int NTB>
+constexpr int US_STG_MAXQ = 512;  // d_model columns of a wave's quarter when W_up is staged
+
+template <int NTB, bool STG>
 __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ Wu,
                                                        const uint16_t* __restrict__ bu,
                                                        float* __restrict__ h,
                                                        float* __restrict__ zdump) {
   __shared__ __attribute__((aligned(16))) float red[4][16][64];
+  // STG: each wave's 32 W_up rows x D/4 columns (16-byte pieces, swizzled by row)
+  __shared__ __attribute__((aligned(16))) uint4 sw[STG ? 4 : 1][STG ? 32 * US_STG_MAXQ / 8 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int D = d.D, T = d.T, F = d.F;
@@ -58,7 +68,38 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[tb][e] = 0.0f;
   constexpr int ST = NTB == 1 ? 8 : 4;  // steps whose loads are in flight together
-  int ks = ks0;
+  if constexpr (STG) {
+    // D % 512 == 0 and D <= 2048: the quarter is q = D/4 columns, ppr = q/8 pieces per row
+    // (a multiple of 16), q/16 steps (a multiple of 8)
+    const int q = D / 4, ppr = q / 8, c0 = wave * q;
+    uint4* my = sw[wave];
+    typedef __attribute__((address_space(3))) void* lds_ptr_s;
+    // slot p = 64 i + lane of the region: row p / ppr, logical piece (p % ppr) ^ (row % 16)
+    for (int i = 0; i < 32 * ppr / 64; ++i) {
+      const int p = i * 64 + lane;
+      const int rr = p / ppr, sl = p - rr * ppr;
+      __builtin_amdgcn_global_load_lds(Wu + (size_t)(n0 + rr) * D + c0 + 8 * (sl ^ (rr & 15)),
+                                       (lds_ptr_s)(my + i * 64), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the wave's own region is in
+    for (int k2 = 0; k2 < q / 16; k2 += ST) {
+      bf16x8_s a[ST], b[ST][NTB];
+#pragma unroll
+      for (int u = 0; u < ST; ++u) {
+        const int sp = 2 * (k2 + u) + hh;  // logical piece of this lane's 8 columns
+        a[u] = __builtin_bit_cast(bf16x8_s, my[r * ppr + (sp ^ (r & 15))]);
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          b[u][tb] = *reinterpret_cast<const bf16x8_s*>(xrow[tb] + c0 + (k2 + u) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < ST; ++u)
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u][tb], acc[tb], 0, 0, 0);
+    }
+  }
+  int ks = STG ? ks1 : ks0;
   for (; ks + ST <= ks1; ks += ST) {
     bf16x8_s a[ST], b[ST][NTB];
 #pragma unroll
@@ -256,6 +297,9 @@ __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
   }
 }
 
+// W_up staged through LDS: the four quarters of d_model fit the 32 KB regions
+static bool up_small_staged(const Dims& d) { return d.D % 512 == 0 && d.D / 4 <= US_STG_MAXQ; }
+
 bool up_small_supported(const Dims& d) {
   return d.bf16 && d.T <= UP_SMALL_T && d.D % 16 == 0 && d.F % US_NB == 0;
 }
@@ -266,15 +310,20 @@ hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                            hipStream_t s) {
   if (!up_small_supported(d)) return hipErrorInvalidValue;
   const dim3 grid(d.F / US_NB);
-  if (d.T <= 32)
-    hipLaunchKernelGGL(up_small_kernel<1>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
+  const bool stg = up_small_staged(d);
+  if (d.T <= 32 && stg)
+    hipLaunchKernelGGL((up_small_kernel<1, true>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
+  else if (d.T <= 32)
+    hipLaunchKernelGGL((up_small_kernel<1, false>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
+  else if (d.T <= 64 && stg)
+    hipLaunchKernelGGL((up_small_kernel<2, true>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   else if (d.T <= 64)
-    hipLaunchKernelGGL(up_small_kernel<2>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
+    hipLaunchKernelGGL((up_small_kernel<2, false>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   else if (d.D % 64 == 0)
     hipLaunchKernelGGL(up_small8_kernel<4>, grid, dim3(US8_NW * 64), 0, s, d, x, Wu, bu, h,
                        zdump);
   else
-    hipLaunchKernelGGL(up_small_kernel<4>, grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
+    hipLaunchKernelGGL((up_small_kernel<4, false>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   return hipGetLastError();
 }
 
