@@ -197,12 +197,15 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   uint2 bkv[4];
   uint32_t bkr[4];
   int bk_e0 = 0, bk_n = 0;
+  // only the 4-row groups that hold one of the wave's bk_n rows are loaded and written (a
+  // wave usually has one to three: the rest of a batch of 16 would only delay the barrier)
   auto bk_load = [&](int k, int c, int first) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int rr = first + 4 * q + (lane >> 4);
       bkv[q] = make_uint2(0, 0);
       bkr[q] = 0;
+      if (first + 4 * q >= bk_n) continue;  // wave-uniform
       if (rr < bk_n && bk_e0 + rr < d.cap) {
         bkr[q] = pos[rr];
         bkv[q] = *reinterpret_cast<const uint2*>(bk_vals + (size_t)(bk_e0 + rr) * K + c * KC +
@@ -210,9 +213,10 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
       }
     }
   };
-  auto bk_write = [&](int buf) __attribute__((always_inline)) {
+  auto bk_write = [&](int buf, int first) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      if (first + 4 * q >= bk_n) continue;  // wave-uniform
       const uint32_t w2[2] = {bkv[q].x, bkv[q].y};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -239,10 +243,10 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   // writes the first batch, then any further batches
   auto bk_finish = [&](int k, int c, int buf) __attribute__((always_inline)) {
     if (bk_n == 0) return;
-    bk_write(buf);
+    bk_write(buf, 0);
     for (int first = 16; first < bk_n; first += 16) {
       bk_load(k, c, first);
-      bk_write(buf);
+      bk_write(buf, first);
     }
   };
 

@@ -297,6 +297,7 @@ __global__ __launch_bounds__(64 * SP_NW) __attribute__((amdgpu_waves_per_eu(SP_N
     uint32_t f0 = 0, f1 = 0;
 #pragma unroll 1
     for (int q = 0; q < 4; ++q) {
+      if (first + 4 * q >= bk_n) break;  // wave-uniform: the 4-row groups in use
       const int rr = first + 4 * q + (lane >> 4);
       const bool ok = rr < bk_n && bk_e0 + rr < d.cap;
       const uint32_t row = ok ? pos[rr] : 0u;

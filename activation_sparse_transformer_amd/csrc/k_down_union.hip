@@ -237,7 +237,8 @@ down_union_kernel(Dims d, const uint16_t* __restrict__ counts, const uint16_t* _
     return __builtin_amdgcn_readfirstlane(m);
   };
 
-  // ---- backup slices of the wave's overflowing rows (as the dense matrix-core kernel)
+  // ---- backup slices of the wave's overflowing rows (as the dense matrix-core kernel: only
+  // the 4-row groups that hold one of the wave's rows)
   uint2 bkv[4];
   uint32_t bkr[4];
   int bk_e0 = 0, bk_n = 0;
@@ -247,6 +248,7 @@ down_union_kernel(Dims d, const uint16_t* __restrict__ counts, const uint16_t* _
       const int rr = first + 4 * q + (lane >> 4);
       bkv[q] = make_uint2(0, 0);
       bkr[q] = 0;
+      if (first + 4 * q >= bk_n) continue;  // wave-uniform
       if (rr < bk_n && bk_e0 + rr < d.cap) {
         bkr[q] = pos[rr];
         bkv[q] = *reinterpret_cast<const uint2*>(bk_vals + (size_t)(bk_e0 + rr) * K + c * KC +
@@ -254,9 +256,10 @@ down_union_kernel(Dims d, const uint16_t* __restrict__ counts, const uint16_t* _
       }
     }
   };
-  auto bk_write = [&](int buf, const uint8_t* tab) __attribute__((always_inline)) {
+  auto bk_write = [&](int buf, const uint8_t* tab, int first) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      if (first + 4 * q >= bk_n) continue;  // wave-uniform
       const uint32_t w2[2] = {bkv[q].x, bkv[q].y};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -283,10 +286,10 @@ down_union_kernel(Dims d, const uint16_t* __restrict__ counts, const uint16_t* _
     if (bk_n == 0) return;
     const uint8_t* tab = sColPos[ring(ci)][ugw];
     const int k = ci / NCH, c = ci % NCH;
-    bk_write(buf, tab);
+    bk_write(buf, tab, 0);
     for (int first = 16; first < bk_n; first += 16) {
       bk_load(k, c, first);
-      bk_write(buf, tab);
+      bk_write(buf, tab, first);
     }
   };
 
