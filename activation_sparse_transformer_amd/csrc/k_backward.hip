@@ -405,19 +405,57 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
+  // backup slices of the overflowing rows among this wave's segments; entry = first entry of
+  // the row's (tile, 32-token group) + its rank among the group's overflowing rows.  The
+  // slices of the first BKP such rows of the next step are loaded when the step starts (so
+  // they land during its MFMAs) and written at its end; further rows are loaded there.
+  constexpr int BKP = 2;
+  uint32_t bkw[BKP][VPL / 2];
+  int bkt[BKP];
+  uint64_t bk_ovall = 0, bk_rest = 0;
+  auto bk_entry = [&](int ts, int tt) __attribute__((always_inline)) -> int {
+    const int gb = tt & ~(GROUP - 1);
+    const uint64_t below = bk_ovall & ((1ull << tt) - 1ull) & ~((1ull << gb) - 1ull);
+    return ld_uniform(grp_first + (k0 + seg_tl) * d.ng + (ts * TS + gb) / GROUP) +
+           __builtin_popcountll(below);
+  };
+  auto bk_prefetch = [&](int ts) __attribute__((always_inline)) {
+    bk_ovall = ballot64(cnt > (uint32_t)W);  // token TS ts + lane
+    uint64_t ov = (bk_ovall >> seg_t0) & ((1ull << SPW) - 1ull);
+#pragma unroll
+    for (int j = 0; j < BKP; ++j) {
+#pragma unroll
+      for (int v = 0; v < VPL / 2; ++v) bkw[j][v] = 0u;
+      bkt[j] = -1;
+      if (ov == 0) continue;  // wave-uniform
+      const int tt = seg_t0 + __builtin_ctzll(ov);
+      ov &= ov - 1;
+      const int e = bk_entry(ts, tt);
+      if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
+      bkt[j] = tt;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(Hbk + (size_t)e * K + VPL * lane);
+#pragma unroll
+      for (int v = 0; v < VPL / 2; ++v) bkw[j][v] = src[v];
+    }
+    bk_rest = ov;
+  };
   auto build_bk = [&](int ts, int buf) __attribute__((always_inline)) {
-    // backup slices of the overflowing rows among this wave's segments; entry = first entry
-    // of the row's (tile, 32-token group) + its rank among the group's overflowing rows
-    const uint64_t ov_all = ballot64(cnt > (uint32_t)W);  // token TS ts + lane
-    uint64_t ov = (ov_all >> seg_t0) & ((1ull << SPW) - 1ull);
+#pragma unroll
+    for (int j = 0; j < BKP; ++j) {
+      if (bkt[j] < 0) continue;  // wave-uniform
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const uint16_t hv = (uint16_t)(bkw[j][v >> 1] >> (16 * (v & 1)));
+        const uint32_t a = hv ? h_off(buf, bkt[j], seg_tl * K + VPL * lane + v) : trash;
+        *reinterpret_cast<uint16_t*>(sH + a) = hv;
+      }
+    }
+    uint64_t ov = bk_rest;
     while (ov != 0) {
       const int i = __builtin_ctzll(ov);
       ov &= ov - 1;
       const int tt = seg_t0 + i;  // token row of the step
-      const int gb = tt & ~(GROUP - 1);
-      const uint64_t below = ov_all & ((1ull << tt) - 1ull) & ~((1ull << gb) - 1ull);
-      const int e = ld_uniform(grp_first + (k0 + seg_tl) * d.ng + (ts * TS + gb) / GROUP) +
-                    __builtin_popcountll(below);
+      const int e = bk_entry(ts, tt);
       if (e >= d.cap) continue;  // capacity exceeded: the status word reports it
       const uint16_t* src = Hbk + (size_t)e * K + VPL * lane;
       uint16_t hv[VPL];
@@ -473,6 +511,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   clear_h(0);
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) build_part(pt, 0, 0);
+  bk_prefetch(0);
   build_bk(0, 0);
   load_units(nts > 1 ? 1 : 0);
   auto step = [&](int ts, int cb, unsigned char* sMc, unsigned char* sMn) __attribute__((always_inline)) {
@@ -490,6 +529,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // the other buffers, which nothing reads any more, instead of branching, so each k-step's
     // MFMAs and build share one basic block
     const int tn = ts + 1 < nts ? ts + 1 : nts - 1;
+    bk_prefetch(tn);  // the units of step tn are in
     load_frags(0, fa[0], fb[0]);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
