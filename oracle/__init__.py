@@ -49,6 +49,12 @@ def _load():
     lib.oracle_backward.restype = None
     lib.oracle_backward_from_dh.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P]
     lib.oracle_backward_from_dh.restype = None
+    lib.oracle_dh_rows.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int32, _P]
+    lib.oracle_dh_rows.restype = None
+    lib.oracle_dx_rows.argtypes = [_P, _P, _I, _I, _I, _P]
+    lib.oracle_dx_rows.restype = None
+    lib.oracle_dw.argtypes = [_P, _P, _I, _I, _I, _P, _P]
+    lib.oracle_dw.restype = None
     lib.oracle_ffn_rows.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int32, _P, _P, _P]
     lib.oracle_ffn_rows.restype = None
     lib.oracle_round_bf16.argtypes = [_P, _I, _P]
@@ -224,6 +230,41 @@ def backward_from_dh(x, dh, W_up):
     lib.oracle_backward_from_dh(_ptr(x), _ptr(dh), _ptr(W_up), T, D, F, _ptr(dx), _ptr(dWu),
                                 _ptr(db))
     return dx, dWu, db
+
+
+def dh_rows(h, g, W_down, round_dh=False) -> np.ndarray:
+    """O9's dh of given token rows: [h != 0] * (g W_down^T), bf16-rounded with round_dh.
+    The same values oracle.backward returns as dh, without the weight gradients."""
+    lib = _load()
+    h = _c(h, np.float64); g = _c(g, np.float64); W_down = _c(W_down, np.float64)
+    T, F = h.shape
+    D = g.shape[1]
+    dh = np.empty((T, F))
+    lib.oracle_dh_rows(_ptr(h), _ptr(g), _ptr(W_down), T, D, F, 1 if round_dh else 0, _ptr(dh))
+    return dh
+
+
+def dx_rows(dh, W_up) -> np.ndarray:
+    """O9's dx = dh W_up of given rows of dh [T, F] (zero dh entries skipped)."""
+    lib = _load()
+    dh = _c(dh, np.float64); W_up = _c(W_up, np.float64)
+    T, F = dh.shape
+    D = W_up.shape[1]
+    dx = np.empty((T, D))
+    lib.oracle_dx_rows(_ptr(dh), _ptr(W_up), T, D, F, _ptr(dx))
+    return dx
+
+
+def dw(a, b):
+    """O9's weight-gradient sums over tokens: (a^T b [F, D], column sums of a [F]) for
+    a [T, F] and b [T, D]: (h, g) gives dW_down, (dh, x) gives dW_up and db."""
+    lib = _load()
+    a = _c(a, np.float64); b = _c(b, np.float64)
+    T, F = a.shape
+    D = b.shape[1]
+    out = np.empty((F, D)); cs = np.empty(F)
+    lib.oracle_dw(_ptr(a), _ptr(b), T, D, F, _ptr(out), _ptr(cs))
+    return out, cs
 
 
 def round_bf16(a) -> np.ndarray:

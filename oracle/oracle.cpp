@@ -238,6 +238,65 @@ void oracle_backward(const double* x, const double* h, const double* g,
   }
 }
 
+// O9's per-token half for many tokens at once, without the weight gradients: dh and dx of
+// every given row (Page A, "What TwELL and the custom CUDA kernels solve": the backward runs
+// from the stored hybrid form; the ReLU mask is the set of stored positions h != 0).
+//   dh[t,j] = [h[t,j] != 0] * sum_d g[t,d] W_down[j,d]   (bf16-rounded with round_dh)
+// Both sums run in ascending index order, as in oracle_backward; only the products with a
+// zero dh (which add nothing) are skipped, so the work follows the stored nonzeros.
+void oracle_dh_rows(const double* h, const double* g, const double* W_down, int64_t T,
+                    int64_t D, int64_t F, int32_t round_dh, double* dh) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < F; ++j) {
+      double v = 0.0;
+      if (h[t * F + j] != 0.0) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += g[t * D + d] * W_down[j * D + d];
+        v = round_dh ? round_to_bf16_value(acc) : acc;
+      }
+      dh[(size_t)(t * F + j)] = v;
+    }
+}
+
+//   dx[t,:] = sum_j dh[t,j] W_up[j,:]   (rows of a given dh [T, F])
+void oracle_dx_rows(const double* dh, const double* W_up, int64_t T, int64_t D, int64_t F,
+                    double* dx) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    double* r = dx + t * D;
+    for (int64_t d = 0; d < D; ++d) r[d] = 0.0;
+    for (int64_t j = 0; j < F; ++j) {
+      const double gv = dh[(size_t)(t * F + j)];
+      if (gv == 0.0) continue;
+      const double* w = W_up + j * D;
+      for (int64_t d = 0; d < D; ++d) r[d] += gv * w[d];
+    }
+  }
+}
+
+// O9's weight gradients as sums over the tokens of the stored activations:
+//   dW[j,:] = sum_t a[t,j] b[t,:]   and   colsum[j] = sum_t a[t,j]   (ascending t)
+// with (a, b) = (h, g) for dW_down and (dh, x) for dW_up and db (Page A, "What TwELL and
+// the custom CUDA kernels solve": training from the hybrid form).  Tokens with a[t,j] == 0
+// add nothing and are skipped, so the work follows the stored nonzeros.  colsum may be null.
+void oracle_dw(const double* a, const double* b, int64_t T, int64_t D, int64_t F, double* dW,
+               double* colsum) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t j = 0; j < F; ++j) {
+    double* u = dW + j * D;
+    for (int64_t d = 0; d < D; ++d) u[d] = 0.0;
+    double s = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double av = a[(size_t)(t * F + j)];
+      if (av == 0.0) continue;
+      for (int64_t d = 0; d < D; ++d) u[d] += av * b[t * D + d];
+      s += av;
+    }
+    if (colsum) colsum[j] = s;
+  }
+}
+
 // The dh-consuming half of O9 for a given dh [T, F] (as a layer stores it): dW_up, db and
 // dx exactly as oracle_backward computes them from its own dh.
 //   dW_up[j,:] = sum_t dh[t,j] x[t,:];  db[j] = sum_t dh[t,j];  dx[t,:] = sum_j dh[t,j] W_up[j,:]

@@ -137,10 +137,9 @@ def test_backward_arguments():
 
 def test_backward_full_size():
     """The 1.5B-like training layer at its full size (T=8192), in the launch configuration
-    the benchmark times.  dh and dx of 64 sampled tokens against the oracle run on those
-    tokens (both are per-token quantities); dW_down, dW_up and db of four hidden columns in
-    every tile (256 columns) against the oracle run on those columns over all tokens; db of
-    every column against the column sums of the stored dh."""
+    the benchmark times, compared with the oracle everywhere: dh and dx of every token (dh at
+    the stored positions of the activation, dx from that dh), and every entry of dW_down,
+    dW_up and db (sums over all tokens of the stored activations and of the stored dh)."""
     torch, sffn = need_gpu()
     print("[backward-full] C5", flush=True)
     L = make_layer(CONFIGS["C5"], seed=0)
@@ -160,71 +159,32 @@ def test_backward_full_size():
     dhost = dict(host)
     dhost["vals"] = dh_vals.view(torch.int16).cpu().numpy().view(np.uint16)
     dhost["bk_vals"] = dh_bk.view(torch.int16).cpu().numpy().view(np.uint16)[:r]
-    K, W, nt = cfg.tile, cfg.ell_width, cfg.n_tiles
-
-    rng = np.random.default_rng(4)
-    rows = np.array(sorted(set([0, 1, T - 2, T - 1] + L["heavy"][:12].tolist()
-                               + rng.choice(T, 48, replace=False).tolist())), np.int64)
+    rows = np.arange(T, dtype=np.int64)
     from tests.test_gpu_parity import _decode_rows
     h_rows = _decode_rows(cfg, host, rows)
     dh_rows = _decode_rows(cfg, dhost, rows)
     x64, Wu64, Wd64 = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "W_down_f32"))
     g64 = oracle.bf16_value(g_bits)
-    dx_r, _, _, _, dh_r = oracle.backward(x64[rows], h_rows, g64[rows], Wu64, Wd64, round_dh=True)
+    dh_r = oracle.dh_rows(h_rows, g64, Wd64, round_dh=True)
     mask = h_rows != 0
     assert not np.any(dh_rows[~mask])
     assert_y_close(dh_rows[mask], dh_r[mask], "bf16", "full dh")
-    fx, _, _ = oracle.backward_from_dh(x64[rows], dh_rows, Wu64)
-    dx_rows = y_to_host(torch, dx[torch.from_numpy(rows).cuda()])
-    assert_y_close(dx_rows, fx, "bf16", "full dx")
-    assert _rel(dx_rows, dx_r) <= 5e-3
+    dx_rows = y_to_host(torch, dx)
+    assert_y_close(dx_rows, oracle.dx_rows(dh_rows, Wu64), "bf16", "full dx")
+    assert _rel(dx_rows, oracle.dx_rows(dh_r, Wu64)) <= 5e-3
+    del dh_r
 
-    # whole columns of the stored h and dh (read straight from the TwELL arrays) for four
-    # hidden columns per tile; the oracle on that column sub-problem over all tokens
-    cols_sel = np.sort(np.concatenate([k * K + rng.choice(K, 4, replace=False) for k in range(nt)]))
-
-    def columns(hst, js):
-        out = np.zeros((T, len(js)), np.float64)
-        pos = {int(j): i for i, j in enumerate(js)}
-        vals = oracle.bf16_value(hst["vals"])
-        m = np.minimum(host["counts"].astype(np.int64), W)
-        for k in range(nt):
-            sel = m[k][:, None] > np.arange(W)[None, :]
-            t_idx, s_idx = np.nonzero(sel)
-            gc = k * K + host["cols"][k][t_idx, s_idx].astype(np.int64)
-            for i, j in enumerate(js):
-                if j // K != k:
-                    continue
-                hit = gc == j
-                out[t_idx[hit], i] = vals[k][t_idx[hit], s_idx[hit]]
-        bv = oracle.bf16_value(hst["bk_vals"])
-        for e in range(r):
-            k, t = int(host["bk_tile"][e]), int(host["bk_tok"][e])
-            for cl in np.nonzero(bv[e])[0]:
-                i = pos.get(k * K + int(cl))
-                if i is not None:
-                    out[t, i] = bv[e, cl]
-        return out
-    hc = columns(host, cols_sel)
-    dhc = columns(dhost, cols_sel)
-    _, _, dwd_c, _, _ = oracle.backward(x64, hc, g64, Wu64[cols_sel], Wd64[cols_sel])
-    _, dwu_c, db_c = oracle.backward_from_dh(x64, dhc, Wu64[cols_sel])
+    # every entry of the weight gradients: dW_down = H^T g over the stored activations,
+    # dW_up = dH^T x and db = the column sums of dH over the stored dh
     dWd_h = dWd.cpu().numpy().astype(np.float64)
     dWu_h = dWu.cpu().numpy().astype(np.float64)
     dbh = db.cpu().numpy().astype(np.float64)
-    assert_y_close(dWd_h[cols_sel], dwd_c, "bf16", "full dW_down columns")
-    assert _rel(dWd_h[cols_sel], dwd_c) <= 1e-4
-    assert_y_close(dWu_h[cols_sel], dwu_c, "bf16", "full dW_up columns")
-    assert_y_close(dbh[cols_sel], db_c, "bf16", "full db columns")
-    # db of every column is the column sum of the stored dh
-    col = np.zeros(c.F)
-    vals = oracle.bf16_value(dhost["vals"])
-    cidx = host["cols"].astype(np.int64)
-    m = np.minimum(host["counts"].astype(np.int64), W)
-    for k in range(nt):
-        sel = m[k][:, None] > np.arange(W)[None, :]
-        np.add.at(col, k * K + cidx[k][sel], vals[k][sel])
-    bkv = oracle.bf16_value(dhost["bk_vals"])
-    for e in range(r):
-        col[host["bk_tile"][e] * K: (host["bk_tile"][e] + 1) * K] += bkv[e]
-    assert_y_close(dbh, col, "bf16", "full db")
+    wd_ref, _ = oracle.dw(h_rows, g64)
+    del h_rows
+    assert_y_close(dWd_h, wd_ref, "bf16", "full dW_down")
+    assert _rel(dWd_h, wd_ref) <= 1e-4
+    del wd_ref
+    wu_ref, db_ref = oracle.dw(dh_rows, x64)
+    assert_y_close(dWu_h, wu_ref, "bf16", "full dW_up")
+    assert _rel(dWu_h, wu_ref) <= 1e-4
+    assert_y_close(dbh, db_ref, "bf16", "full db")

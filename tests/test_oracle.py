@@ -442,6 +442,52 @@ def test_backward_bf16_storage_model():
     assert np.all(np.abs(dx1 - dx0) <= bound)
 
 
+def test_backward_rows_match_backward_and_matmul():
+    """dh_rows / dx_rows (the per-token half of O9 over many rows, zero products skipped):
+    bit for bit the dh and dx of oracle.backward, with and without the bf16 storage of dh;
+    against numpy's matmul, dh = mask * (g W_down^T) and dx = dh W_up within fp64 rounding;
+    a row with no stored activation has dh = 0 and dx = 0."""
+    L = make_layer(CONFIGS["C1b"], seed=0, T=32)
+    x, Wu, b, Wd = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+    g = np.random.default_rng(9).standard_normal((32, x.shape[1]))
+    h = oracle.up_relu(x, Wu, b)
+    h[3] = 0.0
+    for rd in (False, True):
+        dx, _, _, _, dh = oracle.backward(x, h, g, Wu, Wd, round_dh=rd)
+        dh_r = oracle.dh_rows(h, g, Wd, round_dh=rd)
+        dx_r = oracle.dx_rows(dh_r, Wu)
+        assert np.array_equal(dh_r, dh) and np.array_equal(dx_r, dx)
+        assert not np.any(dh_r[3]) and not np.any(dx_r[3])
+    exact = (g @ Wd.T) * (h != 0)
+    dh0 = oracle.dh_rows(h, g, Wd)
+    assert np.allclose(dh0, exact, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(dh0 != 0, (h != 0) & (exact != 0))
+    assert np.allclose(oracle.dx_rows(dh0, Wu), dh0 @ Wu, rtol=1e-12, atol=1e-12)
+    # a row's result does not depend on the other rows
+    assert np.array_equal(oracle.dh_rows(h[5:9], g[5:9], Wd), dh0[5:9])
+    assert np.array_equal(oracle.dx_rows(dh0[5:9], Wu), oracle.dx_rows(dh0, Wu)[5:9])
+
+
+def test_weight_gradients_match_backward_and_matmul():
+    """oracle.dw (the token sums of O9 with zero products skipped): bit for bit the dW_down,
+    dW_up and db of oracle.backward; against numpy, a^T b and the column sums within fp64
+    rounding; a hidden column that never fires has zero gradients."""
+    L = make_layer(CONFIGS["C1b"], seed=0, T=32)
+    x, Wu, b, Wd = (L[k].astype(np.float64) for k in ("x_f32", "W_up_f32", "b_up_f32", "W_down_f32"))
+    g = np.random.default_rng(10).standard_normal((32, x.shape[1]))
+    h = oracle.up_relu(x, Wu, b)
+    h[:, 7] = 0.0
+    for rd in (False, True):
+        _, dWu, dWd, db, dh = oracle.backward(x, h, g, Wu, Wd, round_dh=rd)
+        wd, hs = oracle.dw(h, g)
+        wu, cs = oracle.dw(dh, x)
+        assert np.array_equal(wd, dWd) and np.array_equal(wu, dWu) and np.array_equal(cs, db)
+        assert not np.any(wd[7]) and not np.any(wu[7]) and cs[7] == 0.0
+    assert np.allclose(wd, h.T @ g, rtol=1e-12, atol=1e-12)
+    assert np.allclose(hs, h.sum(axis=0), rtol=1e-12, atol=1e-12)
+    assert np.allclose(wu, dh.T @ x, rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 def test_pins_catch_planted_mistakes(golden_dir, monkeypatch):
     """Plant plausible mistakes in the Python twin and check the pins reject them."""
