@@ -289,6 +289,8 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
   auto gather = [&](const int32_t* blk, long long thr) {
     if (rows_ok)
       return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, blk, thr, s); });
+    if (down_rows_f32_supported(d) && blk == nullptr)
+      return run("down", s, [&] { return launch_down_rows_f32(d, act, ws, hd->W_down, y, s); });
     return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, blk, thr, s); });
   };
   auto tiles = [&](const int32_t* blk, long long lo, long long hi) {
@@ -337,6 +339,14 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
       return launch_up_small(d, static_cast<const uint16_t*>(x),
                              static_cast<const uint16_t*>(hd->W_up),
                              static_cast<const uint16_t*>(hd->b_up), ws.hsmall, z, s);
+    }));
+    SFFN_TRY(run("pack", s, [&] { return launch_pack(d, ws.hsmall, *act, ws, s); }));
+  } else if (up_small_f32_supported(d)) {
+    // the same for fp32 layers
+    SFFN_TRY(run("up_small", s, [&] {
+      return launch_up_small_f32(d, static_cast<const float*>(x),
+                                 static_cast<const float*>(hd->W_up),
+                                 static_cast<const float*>(hd->b_up), ws.hsmall, z, s);
     }));
     SFFN_TRY(run("pack", s, [&] { return launch_pack(d, ws.hsmall, *act, ws, s); }));
   } else if (d.bf16) {

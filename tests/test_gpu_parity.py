@@ -144,6 +144,11 @@ DOWN_CASES = [
     (33, 256, 512, 64, 16, "bf16", 0.1),
     # 128-column tiles with 16 slots: two 8-slot units per row in the decode-once rebuild
     (200, 256, 1024, 128, 16, "bf16", 0.1),
+    # fp32 layers of at most 128 tokens (the per-token row gather over 256-column chunks):
+    # a partial last chunk, overflowing rows at every tile size, fewer tiles than waves
+    (100, 320, 1024, 128, 32, "f32", 0.1),
+    (17, 192, 512, 64, 8, "f32", 0.3),
+    (3, 256, 768, 256, 40, "f32", 0.2),
 ]
 
 
@@ -364,7 +369,7 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
 
 @pytest.mark.parametrize("policy", ["gather", "tiles", "mfma", "union", "sparse"])
 @pytest.mark.parametrize("name,T,rho", [
-    ("C1", None, None), ("C1b", None, None),
+    ("C1", None, None), ("C1b", None, None), ("C1", 1, None), ("C1b", 100, None),
     ("C2", 300, None), ("C3", 300, 0.01), ("C3", 300, 0.05), ("C3", 300, 0.20),
     ("C4", 300, None),
     # decode-shaped batches (at most 128 tokens: the small-batch up-projection + pack path,
