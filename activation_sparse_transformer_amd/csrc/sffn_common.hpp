@@ -60,12 +60,14 @@ inline size_t umask_bytes(const Dims& d) {
 // Split of the matrix-core down-projection over its tiles: when its workgroups of (256
 // tokens, 256 columns) would fill at most half of the 256 CUs, the tile range is cut into S
 // parts (at most DM_MAX_SPLIT, each at least two tiles), each part's fp32 sums go to dpart
-// and a second kernel adds them in order.
+// and a second kernel adds them in order.  S parts of `base` workgroups stay within the 256
+// CUs (one workgroup per CU fits in LDS): one more part would start a second round of
+// workgroups, each with fewer tiles, and take longer than S parts of more tiles.
 constexpr int DM_MAX_SPLIT = 16;
 inline int down_split_for(int T, int D, int nt) {
   const long long base = (long long)((T + 255) / 256) * ((D + 255) / 256);
   if (base > 128) return 1;
-  int S = (int)((256 + base - 1) / base);
+  int S = (int)(256 / base);
   S = S < DM_MAX_SPLIT ? S : DM_MAX_SPLIT;
   S = S < nt / 2 ? S : nt / 2;
   return S > 1 ? S : 1;
@@ -198,6 +200,10 @@ bool up_small_supported(const Dims& d);
 hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                            const uint16_t* bu, float* h, float* zdump,
                            hipStream_t s);
+// The same for fp32 layers (fp32 x, W_up, b).
+bool up_small_f32_supported(const Dims& d);
+hipError_t launch_up_small_f32(const Dims& d, const float* x, const float* Wu, const float* bu,
+                               float* h, float* zdump, hipStream_t s);
 hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);
@@ -216,6 +222,11 @@ bool down_rows_supported(const Dims& d);
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
                             hipStream_t s);
+// One workgroup per (token, 256 output columns) over the W_down rows its nonzeros select
+// (fp32 layers, T <= UP_SMALL_T).
+bool down_rows_f32_supported(const Dims& d);
+hipError_t launch_down_rows_f32(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
+                                const void* Wd, void* y, hipStream_t s);
 // 256 tokens per workgroup over W_down tiles staged in LDS, bf16 dot products (bf16, even
 // W <= 128).  With blk_nnz it runs only when the layer's stored nonzeros are in (lo, hi].
 bool down_lds_supported(const Dims& d);
