@@ -53,7 +53,8 @@ __global__ __launch_bounds__(64 * DL_WAVES) void down_lds_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint32_t* __restrict__ vals2,
     const uint32_t* __restrict__ cols4, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long lo, long long hi) {
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long lo, long long hi,
+    DownHint hint) {
   constexpr int DC = 64 * CPL;              // output columns per workgroup
   constexpr int ROWB = DC * 2;              // bytes per staged W_down row
   constexpr int STAGE = K * DC;             // bf16 elements of one staged W_down slice
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(64 * DL_WAVES) void down_lds_kernel(
     const long long n = layer_nnz(blk_nnz, (T + 255) / 256);
     if (n <= lo || n > hi) return;
   }
+  note_choice(hint, (T + 255) / 256, blockIdx.x == 0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
@@ -315,22 +317,22 @@ template <int K, int CPL>
 static void launch_lds_k(const Dims& d, dim3 grid, dim3 block, hipStream_t s,
                          const uint16_t* c, const uint32_t* v, const uint32_t* cl,
                          const uint16_t* bk, const int32_t* gf, const uint16_t* w, uint16_t* yy,
-                         const int32_t* blk_nnz, long long lo, long long hi) {
+                         const int32_t* blk_nnz, long long lo, long long hi, const DownHint& hint) {
   const int hw = d.W / 2;
   if (hw <= 8)
     hipLaunchKernelGGL((down_lds_kernel<K, CPL, 8>), grid, block, 0, s, d, c, v, cl, bk, gf, w,
-                       yy, blk_nnz, lo, hi);
+                       yy, blk_nnz, lo, hi, hint);
   else if (hw <= 16)
     hipLaunchKernelGGL((down_lds_kernel<K, CPL, 16>), grid, block, 0, s, d, c, v, cl, bk, gf, w,
-                       yy, blk_nnz, lo, hi);
+                       yy, blk_nnz, lo, hi, hint);
   else
     hipLaunchKernelGGL((down_lds_kernel<K, CPL, 32>), grid, block, 0, s, d, c, v, cl, bk, gf, w,
-                       yy, blk_nnz, lo, hi);
+                       yy, blk_nnz, lo, hi, hint);
 }
 
 hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                            const void* Wd, void* y, const int32_t* blk_nnz, long long lo,
-                           long long hi, hipStream_t s) {
+                           long long hi, hipStream_t s, const DownHint& hint) {
   if (!down_lds_supported(d)) return hipErrorInvalidValue;
   auto* c = b.counts;
   auto* v = static_cast<const uint32_t*>(b.vals);
@@ -344,9 +346,9 @@ hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Worksp
   const int per_xcd = (nTB * nDC + 7) / 8;
   const dim3 grid(8 * per_xcd), block(64 * DL_WAVES);
   switch (d.K) {
-    case 64: launch_lds_k<64, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi); break;
-    case 128: launch_lds_k<128, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi); break;
-    case 256: launch_lds_k<256, 2>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi); break;
+    case 64: launch_lds_k<64, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi, hint); break;
+    case 128: launch_lds_k<128, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi, hint); break;
+    case 256: launch_lds_k<256, 2>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi, hint); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -34,7 +34,8 @@
 // order into y.
 // When the layer's stored-nonzero count (the sum of the per-block counts) is at most `thr`
 // the gather kernel takes the layer and every workgroup here (and the reduce) returns at
-// once (blk_nnz == nullptr: this kernel runs).
+// once (blk_nnz == nullptr: this kernel runs).  Workgroup 0 of a running launch records the
+// kernel the count selects through `hint`.
 #include <algorithm>
 
 #include "sffn_common.hpp"
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
     uint16_t* __restrict__ y, float* __restrict__ dpart, int S, const int32_t* __restrict__ blk_nnz,
-    long long thr) {
+    long long thr, DownHint hint) {
   constexpr int KC = DM_KC;
   constexpr int NCH = K / KC;          // steps per tile
   constexpr int U = W / 8;             // 8-slot units per tile-row
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   const int Pl = P - split * nd * ntb;
   const int tb = Pl / nd;
   if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
+  note_choice(hint, ntb, blockIdx.x == 0);
   const int dchunk = Pl - tb * nd;
   // tiles [k_lo, k_hi) of this part (in pairs for 64-column tiles, whose one-step tiles run
   // two per unrolled iteration)
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(256) void down_reduce_kernel(Dims d, const float* _
 template <int K, int W>
 static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                               const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
-                              hipStream_t s) {
+                              hipStream_t s, const DownHint& hint) {
   const int nd = (d.D + DM_BN - 1) / DM_BN;
   const int ntb = (d.T + DM_BM - 1) / DM_BM;
   const int S = down_split(d);
@@ -424,7 +426,7 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
                      static_cast<const uint16_t*>(b.vals), b.cols,
                      static_cast<const uint16_t*>(b.bk_vals), ws.grp_first,
                      static_cast<const uint16_t*>(Wd), static_cast<uint16_t*>(y), ws.dpart, S,
-                     blk_nnz, thr);
+                     blk_nnz, thr, hint);
   if (S > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -445,12 +447,12 @@ hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S
 template <int K>
 static hipError_t launch_dm_k(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                               const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
-                              hipStream_t s) {
+                              hipStream_t s, const DownHint& hint) {
   switch (d.W) {
-    case 16: return launch_dm_t<K, 16>(d, b, ws, Wd, y, blk_nnz, thr, s);
-    case 32: return launch_dm_t<K, 32>(d, b, ws, Wd, y, blk_nnz, thr, s);
-    case 48: return launch_dm_t<K, 48>(d, b, ws, Wd, y, blk_nnz, thr, s);
-    case 64: return launch_dm_t<K, 64>(d, b, ws, Wd, y, blk_nnz, thr, s);
+    case 16: return launch_dm_t<K, 16>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+    case 32: return launch_dm_t<K, 32>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+    case 48: return launch_dm_t<K, 48>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+    case 64: return launch_dm_t<K, 64>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
   }
   return hipErrorInvalidValue;
 }
@@ -461,11 +463,11 @@ bool down_mfma_supported(const Dims& d) {
 
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
-                            hipStream_t s) {
+                            hipStream_t s, const DownHint& hint) {
   if (!down_mfma_supported(d)) return hipErrorInvalidValue;
-  if (d.K == 64) return launch_dm_k<64>(d, b, ws, Wd, y, blk_nnz, thr, s);
-  if (d.K == 128) return launch_dm_k<128>(d, b, ws, Wd, y, blk_nnz, thr, s);
-  return launch_dm_k<256>(d, b, ws, Wd, y, blk_nnz, thr, s);
+  if (d.K == 64) return launch_dm_k<64>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+  if (d.K == 128) return launch_dm_k<128>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+  return launch_dm_k<256>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
 }
 
 }  // namespace sffn

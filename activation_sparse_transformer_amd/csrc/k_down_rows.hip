@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr) {
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr, DownHint hint) {
   static_assert(EPL == 8 || EPL == 4 || EPL == 2, "8, 4 or 2 output columns per lane");
   constexpr int CW = 64 * EPL;                 // columns of one wave load of a row
   // rows in flight per wave (registers: NQ EPL / 2 each; at most 64, one lane per slot)
@@ -43,6 +43,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   const int cb = blockIdx.y * NQ * CW;  // first output column of this workgroup
   // the layer goes to this kernel only when its stored-nonzero count is at most thr
   if (blk_nnz != nullptr && layer_nnz(blk_nnz, (T + 255) / 256) > thr) return;
+  note_choice(hint, (T + 255) / 256, blockIdx.x == 0 && blockIdx.y == 0);
   for (int t = blockIdx.x; t < T; t += gridDim.x) {  // workgroup-uniform token loop
   float acc[NQ][EPL];
 #pragma unroll
@@ -220,31 +221,32 @@ bool down_rows_supported(const Dims& d) {
 
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
-                            hipStream_t s) {
+                            hipStream_t s, const DownHint& hint) {
   if (!down_rows_supported(d)) return hipErrorInvalidValue;
-  // at most 2048 workgroups (x), each looping over tokens: a skipped launch (the layer went to
-  // the matrix cores) then costs little
+  // from ROWS_FEW_T tokens at most 2048 workgroups (x), each looping over tokens: a skipped
+  // launch (the layer went to the matrix cores) then costs little
   auto* c = b.counts;
   auto* v = static_cast<const uint16_t*>(b.vals);
   auto* bk = static_cast<const uint16_t*>(b.bk_vals);
   auto* w = static_cast<const uint16_t*>(Wd);
   auto* yy = static_cast<uint16_t*>(y);
-  if (d.T < ROWS_FEW_T && blk_nnz == nullptr) {
-    // the only down kernel of the call: 16-wave workgroups over 256-column chunks
+  if (d.T < ROWS_FEW_T) {
+    // few tokens: 16-wave workgroups over 256-column chunks, also as a candidate of the kernel
+    // choice (the auto policy launches the candidates only until a call has recorded the
+    // kernel its count selects), so that the gather's sums do not depend on how it was
+    // launched
     const dim3 grid(d.T, (d.D + 255) / 256), block(64 * 16);
     hipLaunchKernelGGL((down_rows_kernel<1, 16, 4>), grid, block, 0, s, d, c, v, b.cols, bk,
-                       ws.grp_first, w, yy, blk_nnz, thr);
+                       ws.grp_first, w, yy, blk_nnz, thr, hint);
     return hipGetLastError();
   }
-  // many tokens, or one candidate of the kernel choice (which usually returns at once, so its
-  // waves should be few; when it runs, the layer holds very few nonzeros per token): 4-wave
-  // workgroups over whole tokens
+  // many tokens: 4-wave workgroups over whole tokens
   const dim3 grid(d.T < 2048 ? d.T : 2048), block(64 * 4);
   switch ((d.D + 511) / 512) {
 #define SFFN_ROWS(NQ)                                                                      \
   case NQ:                                                                                 \
     hipLaunchKernelGGL((down_rows_kernel<NQ, 4>), grid, block, 0, s, d, c, v, b.cols, bk,   \
-                       ws.grp_first, w, yy, blk_nnz, thr);                                 \
+                       ws.grp_first, w, yy, blk_nnz, thr, hint);                           \
     break;
     SFFN_ROWS(1) SFFN_ROWS(2) SFFN_ROWS(3) SFFN_ROWS(4)
     SFFN_ROWS(5) SFFN_ROWS(6) SFFN_ROWS(7) SFFN_ROWS(8)

@@ -5,6 +5,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -21,6 +22,14 @@ struct sparse_ffn {
   int32_t down_policy = SFFN_DOWN_AUTO;
   float down_gather_density = SFFN_DOWN_GATHER_DENSITY_DEFAULT;
   float down_mfma_density = SFFN_DOWN_MFMA_DENSITY_DEFAULT;
+  // Auto policy: the kernel the last running down kernel found the layer's count to select
+  // (0 gather, 1 tiles, 2 matrix cores, -1 none yet), in one word of pinned host memory that
+  // the kernels write; set up by the first auto call that may allocate, reset by a policy
+  // change.
+  int* hint_host = nullptr;
+  int* hint_dev = nullptr;
+  bool hint_failed = false;
+  std::mutex hint_mu;
 };
 
 namespace {
@@ -231,6 +240,7 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* W_up, cons
 }
 
 sffn_status_t sparse_ffn_destroy(sparse_ffn_t h) {
+  if (h && h->hint_host) (void)hipHostFree(h->hint_host);
   delete h;
   return SFFN_OK;
 }
@@ -283,23 +293,52 @@ static DownPlan plan_down(const sparse_ffn* hd, const Dims& d) {
 // device: every candidate is launched with its range and all but one return at once.
 // blk_ready: ws.blk_nnz already holds this TwELL's per-block counts (written by the ordering
 // pass of the same call).
-static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
-                               const Workspace& ws, void* y, hipStream_t s, bool blk_ready) {
+// The hint word of a handle, set up on first use by a call that may allocate (not one that
+// promised not to, and not while the stream is being captured): device address or null.
+static int* hint_word(sparse_ffn* hd, hipStream_t s, bool may_alloc) {
+  std::lock_guard<std::mutex> lock(hd->hint_mu);
+  if (hd->hint_dev || hd->hint_failed || !may_alloc) return hd->hint_dev;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return nullptr;
+  void* hp = nullptr;
+  void* dp = nullptr;
+  if (hipHostMalloc(&hp, sizeof(int), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    hd->hint_failed = true;
+    return nullptr;
+  }
+  *static_cast<volatile int*>(hp) = -1;
+  if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipHostFree(hp);
+    hd->hint_failed = true;
+    return nullptr;
+  }
+  hd->hint_host = static_cast<int*>(hp);
+  hd->hint_dev = static_cast<int*>(dp);
+  return hd->hint_dev;
+}
+
+static sffn_status_t down_impl(sparse_ffn* hd, const Dims& d, const twell_buffers_t& act,
+                               const Workspace& ws, void* y, hipStream_t s, bool blk_ready,
+                               bool may_alloc) {
   const bool rows_ok = down_rows_supported(d);
+  DownHint hint;  // where the kernel that runs records its choice (auto policy only)
   auto gather = [&](const int32_t* blk, long long thr) {
     if (rows_ok)
-      return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, blk, thr, s); });
+      return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, blk, thr, s, hint); });
     if (down_rows_f32_supported(d) && blk == nullptr)
       return run("down", s, [&] { return launch_down_rows_f32(d, act, ws, hd->W_down, y, s); });
     return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, blk, thr, s); });
   };
   auto tiles = [&](const int32_t* blk, long long lo, long long hi) {
     return run("down_tiles", s,
-               [&] { return launch_down_lds(d, act, ws, hd->W_down, y, blk, lo, hi, s); });
+               [&] { return launch_down_lds(d, act, ws, hd->W_down, y, blk, lo, hi, s, hint); });
   };
   auto mfma = [&](const int32_t* blk, long long thr) {
     return run("down_mfma", s,
-               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, blk, thr, s); });
+               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, blk, thr, s, hint); });
   };
   auto unionk = [&](const int32_t* blk, long long thr) {
     return run("down_union", s,
@@ -318,6 +357,19 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
   if (!p.needs_count) return gather(nullptr, 0);
   if (!blk_ready)
     SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
+  // Every candidate gives the layer's result at any density (the choice is speed only), so
+  // once a call has recorded the kernel its count selects, the next call launches that one
+  // alone (and records its own count's choice for the call after it).  The first call, a
+  // recorded kernel that is no candidate for this call's shape, or no hint word: every
+  // candidate is launched and the count decides on the device.
+  int* hw = rows_ok ? hint_word(hd, s, may_alloc) : nullptr;
+  if (hw) {
+    hint = DownHint{hw, ws.blk_nnz, p.thr_g, p.thr_m};
+    const int h = __atomic_load_n(hd->hint_host, __ATOMIC_RELAXED);
+    if (h == 0) return gather(nullptr, 0);
+    if (h == 1 && p.thr_m > p.thr_g) return tiles(nullptr, 0, 0);
+    if (h == 2 && p.thr_m < p.all) return mfma(nullptr, 0);
+  }
   SFFN_TRY_INNER(gather(ws.blk_nnz, p.thr_g));
   if (p.thr_m > p.thr_g) SFFN_TRY_INNER(tiles(ws.blk_nnz, p.thr_g, p.thr_m));
   if (p.thr_m < p.all) SFFN_TRY_INNER(mfma(ws.blk_nnz, p.thr_m));
@@ -325,7 +377,8 @@ static sffn_status_t down_impl(const sparse_ffn* hd, const Dims& d, const twell_
 }
 
 static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, void* y,
-                                  const twell_buffers_t* act, float* z, void* stream) {
+                                  const twell_buffers_t* act, float* z, void* stream,
+                                  bool may_alloc = true) {
   if (!hd) return fail(SFFN_ERR_INVALID_ARGUMENT, "handle is NULL");
   SFFN_TRY(check_T(&hd->cfg, T));
   if (!x || !y) return fail(SFFN_ERR_INVALID_ARGUMENT, "x or y is NULL");
@@ -365,7 +418,7 @@ static sffn_status_t forward_impl(sparse_ffn_t hd, const void* x, int32_t T, voi
   // the ordering pass also writes the counts the kernel choice reads
   const bool blk = plan_down(hd, d).needs_count;
   SFFN_TRY(run("order", s, [&] { return launch_order(d, *act, ws, s, blk); }));
-  return down_impl(hd, d, *act, ws, y, s, blk);
+  return down_impl(hd, d, *act, ws, y, s, blk, may_alloc);
 }
 
 sffn_status_t sparse_ffn_forward(sparse_ffn_t hd, const void* x, int32_t T, void* y,
@@ -392,7 +445,7 @@ sffn_status_t sparse_ffn_forward_noalloc(sparse_ffn_t hd, const void* x, int32_t
   if (e != hipSuccess) return dev_fail(e, "no-allocation scratch lookup");
   twell_buffers_t a = *act;
   a.workspace = scratch;
-  return forward_impl(hd, x, T, y, &a, nullptr, stream);
+  return forward_impl(hd, x, T, y, &a, nullptr, stream, false);
 }
 
 sffn_status_t sparse_ffn_forward_dump(sparse_ffn_t hd, const void* x, int32_t T, void* y,
@@ -410,7 +463,7 @@ sffn_status_t sparse_ffn_down(sparse_ffn_t hd, const twell_buffers_t* act, int32
   const Dims d = make_dims(&hd->cfg, T);
   const Workspace ws = carve(act->workspace, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return down_impl(hd, d, *act, ws, y, s, false);
+  return down_impl(hd, d, *act, ws, y, s, false, true);
 }
 
 sffn_status_t sparse_ffn_backward(sparse_ffn_t hd, const void* x, const void* dy, int32_t T,
@@ -455,6 +508,10 @@ sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float 
   hd->down_policy = policy;
   hd->down_gather_density = gather_density;
   hd->down_mfma_density = mfma_density;
+  {
+    std::lock_guard<std::mutex> lock(hd->hint_mu);
+    if (hd->hint_host) __atomic_store_n(hd->hint_host, -1, __ATOMIC_RELAXED);
+  }
   return SFFN_OK;
 }
 

@@ -182,6 +182,27 @@ __device__ __forceinline__ long long layer_nnz(const int32_t* blk_nnz, int n) {
 }
 #endif
 
+// Where a down kernel records the kernel the layer's count selects for the next call of the
+// auto policy: dst (a word of pinned host memory, or null) gets 0 (gather, count <= thr_g),
+// 1 (tiles, count <= thr_m) or 2 (matrix cores) from the per-block counts blk.
+struct DownHint {
+  int* dst = nullptr;
+  const int32_t* blk = nullptr;
+  long long thr_g = 0, thr_m = 0;
+};
+#if defined(__HIPCC__)
+// Called by every thread of a kernel that runs; wave 0 of the workgroup for which `first`
+// holds (wave-uniform) reads the counts and one lane stores the choice (system scope: the
+// host reads it).
+__device__ __forceinline__ void note_choice(const DownHint& h, int n_blocks, bool first) {
+  if (h.dst == nullptr || !first || threadIdx.x >= 64) return;
+  const long long n = layer_nnz(h.blk, n_blocks);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(h.dst, n <= h.thr_g ? 0 : (n <= h.thr_m ? 1 : 2), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+}
+#endif
+
 // ---------------------------------------------------------------- launchers
 // Each returns the launch's hipError_t (hipGetLastError after the launch).
 hipError_t launch_pack(const Dims& d, const float* h, const twell_buffers_t& b,
@@ -211,7 +232,8 @@ hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t*
 // matrix-core kernel.  With blk_nnz (per-256-token-block stored-nonzero counts from
 // launch_block_nnz) each is launched with its range of the layer's total and reads the
 // total at entry: the one whose range holds it runs, the others return at once.
-// blk_nnz == nullptr runs the kernel launched.
+// blk_nnz == nullptr runs the kernel launched.  The kernel that runs records, through `hint`,
+// the kernel the count selects (the next auto call launches only that one).
 hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* blk_nnz,
                             hipStream_t s);
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
@@ -221,7 +243,7 @@ bool down_mfma_supported(const Dims& d);
 bool down_rows_supported(const Dims& d);
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
-                            hipStream_t s);
+                            hipStream_t s, const DownHint& hint = DownHint());
 // One workgroup per (token, 256 output columns) over the W_down rows its nonzeros select
 // (fp32 layers, T <= UP_SMALL_T).
 bool down_rows_f32_supported(const Dims& d);
@@ -232,7 +254,7 @@ hipError_t launch_down_rows_f32(const Dims& d, const twell_buffers_t& b, const W
 bool down_lds_supported(const Dims& d);
 hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                            const void* Wd, void* y, const int32_t* blk_nnz, long long lo,
-                           long long hi, hipStream_t s);
+                           long long hi, hipStream_t s, const DownHint& hint = DownHint());
 bool backward_supported(const Dims& d);
 // One part of the backward weights pass: which = 0: dh at the stored positions of `act`
 // (into dh_vals / dh_bk); 1: dW_down = H^T g; 2: dW_up = dH^T x and, if db is not null,
@@ -243,7 +265,7 @@ hipError_t launch_backward_part(int which, const Dims& d, const twell_buffers_t&
                                 float* dW_down, float* db, hipStream_t s);
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
                             const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
-                            hipStream_t s);
+                            hipStream_t s, const DownHint& hint = DownHint());
 // The matrix-core down-projection over the column unions of 64-token blocks (the same
 // shapes as launch_down_mfma; reads ws.umask, written by the kernel that produced the TwELL).
 hipError_t launch_down_union(const Dims& d, const twell_buffers_t& b, const Workspace& ws,

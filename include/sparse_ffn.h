@@ -24,7 +24,9 @@
  *     message in sffn_last_error().  Device-side overflow of the backup capacity is
  *     reported through the buffers' status word: outputs of that call are then undefined,
  *     and twell_stats / sparse_ffn_check return SFFN_ERR_BACKUP_OVERFLOW.
- *   - The library allocates no device memory.  Every device buffer is the caller's.
+ *   - The library allocates no device memory.  Every device buffer is the caller's.  (A
+ *     handle under the auto down policy keeps one word of pinned host memory: see
+ *     sparse_ffn_set_down_policy.)
  *
  * TwELL layout written by twell_pack and sparse_ffn_forward (n_t = d_ff / tile tiles,
  * "tile-row (k, t)" = token t restricted to the tile's columns [k*tile, (k+1)*tile)):
@@ -146,14 +148,16 @@ sffn_status_t twell_buffer_bytes(const sffn_config_t *cfg, int32_t T,
  * a down-projection back).  Beyond the checks every call makes, a bf16 layer needs
  * d_model % 128 == 0 and d_ff % 256 == 0 (SFFN_ERR_UNSUPPORTED otherwise).  The weights
  * are borrowed device pointers: they must stay valid while the handle is used and may be
- * updated in place between calls; nothing derived from their values is kept.  b_up may
- * not be NULL (pass zeros for a bias-free layer).  *out is written only on SFFN_OK. */
+ * updated in place between calls; nothing derived from their values is kept (the auto
+ * down policy keeps one word about the last call's density, see sparse_ffn_set_down_policy).
+ * b_up may not be NULL (pass zeros for a bias-free layer).  *out is written only on SFFN_OK. */
 sffn_status_t sparse_ffn_create(const sffn_config_t *cfg, const void *W_up, const void *b_up,
                                 const void *W_down, sparse_ffn_t *out);
 
 /* (host only) Release a handle created by sparse_ffn_create; NULL is accepted.
  * Interface of the library: no device memory is owned, so nothing on the device is
- * released or waited for. */
+ * released or waited for; the auto down policy's word of pinned host memory, if one was
+ * allocated, is freed (no call of the handle may still be running on the device). */
 sffn_status_t sparse_ffn_destroy(sparse_ffn_t h);
 
 /* Pack a dense fp32 hidden tensor h [T, d_ff] into TwELL (same article, section "What
@@ -237,6 +241,16 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
  *                     256-token blocks and reads all of W_down, where the gather reads only
  *                     the rows in use).  With few tokens the mfma kernel splits the tiles
  *                     over more workgroups and adds the parts' fp32 sums in a fixed order.
+ *                     Every candidate is correct at any density, so the choice is one of
+ *                     speed: the first auto call on a handle (and the first after any
+ *                     sparse_ffn_set_down_policy) launches every candidate and the count
+ *                     decides on the device; the kernel that runs also writes which kernel its
+ *                     count selects into a 4-byte word of pinned host memory that the handle
+ *                     keeps (allocated by the first auto forward or down call, never by
+ *                     sparse_ffn_forward_noalloc or under stream capture, freed by
+ *                     sparse_ffn_destroy), and each later call launches that kernel alone.  A
+ *                     change of density thus changes the kernel one call later; the result is
+ *                     the kernel's that ran.
  *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA, SFFN_DOWN_UNION, SFFN_DOWN_SPARSE:
  *                     always that kernel (tiles, mfma, union and sparse fall back as above
  *                     when the layer does not support them).

@@ -264,8 +264,8 @@ def test_down_auto_policy_choice():
 @pytest.mark.parametrize("T", [64, 300])
 def test_down_gather_candidate_runs(T):
     """Auto policy with every count in the gather's range, at token counts where the gather is
-    launched as one candidate of the kernel choice (4-wave workgroups over whole tokens): it
-    runs, writes every row and matches the oracle; the matrix-core candidate returns."""
+    launched as one candidate of the kernel choice: it runs, writes every row and matches the
+    oracle; the matrix-core candidate returns."""
     torch, sffn = need_gpu()
     print(f"[down-candidate] T={T}", flush=True)
     D, F, K, W = 256, 1024, 128, 32
@@ -299,6 +299,64 @@ def test_down_gather_candidate_runs(T):
     layer.set_down_policy("gather")
     y2 = layer.down(buf)
     assert_y_close(y_to_host(torch, y2), y_ref, "bf16", f"gather alone T={T}")
+
+
+def test_down_auto_policy_follows_the_last_count():
+    """Auto policy over calls on one handle: the first call launches every candidate and the
+    count decides on the device; the kernel that runs records its choice, and the next call
+    launches that kernel alone.  When the density changes, the call after the change still
+    runs the recorded kernel (a correct result at any density, equal to that kernel's forced
+    result bit for bit) and records the new choice, which the call after it follows."""
+    torch, sffn = need_gpu()
+    from gen import f32_to_bf16_bits, bf16_bits_to_f32
+    T, D, F, K, W = 300, 256, 1024, 128, 32
+    rng = np.random.default_rng(8)
+    Wd_bits = f32_to_bf16_bits((rng.standard_normal((F, D)) / np.sqrt(F)).astype(np.float32))
+    Wd64 = bf16_bits_to_f32(Wd_bits).astype(np.float64)
+    cfg = _cfg(sffn, T, D, F, K, W, "bf16")
+    Wd_dev = torch.from_numpy(Wd_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    layer = sffn.SparseFFN(cfg, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
+                           torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
+    dense = make_hidden(T, F, 0.05, seed=21)
+    sparse = make_hidden(T, F, 0.0003, seed=22)   # below the gather's 0.05% of T x F
+    assert 0 < np.count_nonzero(sparse) <= 0.0005 * T * F < np.count_nonzero(dense)
+    bufs = {k: sffn.twell_pack(cfg, to_dev_f32(torch, h)) for k, h in (("dense", dense), ("sparse", sparse))}
+    refs = {}
+    for k, h in (("dense", dense), ("sparse", sparse)):
+        h_ref = oracle.bf16_value(oracle.round_bf16(h.astype(np.float64)))
+        refs[k] = oracle.down_sparse(oracle.pack(h_ref, K, W), Wd64)
+    forced = {}
+    for pol in ("gather", "mfma"):
+        layer.set_down_policy(pol)
+        forced[pol] = {k: y_to_host(torch, layer.down(b)) for k, b in bufs.items()}
+    layer.set_down_policy("auto")
+
+    def call(which):
+        sffn.profile_reset()
+        sffn.profile_enable(True)
+        try:
+            yh = y_to_host(torch, layer.down(bufs[which]))
+            launched = (sffn.profile_read("down")[1], sffn.profile_read("down_mfma")[1])
+        finally:
+            sffn.profile_enable(False)
+            sffn.profile_reset()
+        assert_y_close(yh, refs[which], "bf16", f"auto {which}")
+        return yh, launched
+
+    steps = [("dense", (1, 1), "mfma"),    # first call: both candidates, the count decides
+             ("dense", (0, 1), "mfma"),    # recorded: the matrix cores alone
+             ("sparse", (0, 1), "mfma"),   # density changed: the recorded kernel runs once more
+             ("sparse", (1, 0), "gather"),  # and the new choice is followed
+             ("dense", (1, 0), "gather"),
+             ("dense", (0, 1), "mfma")]
+    for which, launched_expect, kernel in steps:
+        yh, launched = call(which)
+        assert launched == launched_expect, (which, launched)
+        assert np.array_equal(yh, forced[kernel][which]), (which, kernel)
+    # a policy change forgets the recorded choice
+    layer.set_down_policy("auto")
+    yh, launched = call("sparse")
+    assert launched == (1, 1) and np.array_equal(yh, forced["gather"]["sparse"])
 
 
 def test_down_policy_arguments():
@@ -754,9 +812,15 @@ def test_profile_only_times_named_kernels():
         assert got["order"][1] == got["down"][1] == 0, got
         sffn.profile_only(None)
         sffn.profile_reset()
+        # the first call's count selected the matrix cores: this call launches only them
+        layer.forward(x)
+        assert all(sffn.profile_read(n)[1] == 1 for n in ("up_pack", "order", "down_mfma"))
+        assert sffn.profile_read("down")[1] == 0 and sffn.profile_read("block_nnz")[1] == 0
+        # a policy change forgets the recorded choice: every candidate again
+        layer.set_down_policy("auto")
+        sffn.profile_reset()
         layer.forward(x)
         assert all(sffn.profile_read(n)[1] == 1 for n in names)
-        assert sffn.profile_read("block_nnz")[1] == 0
     finally:
         sffn.profile_enable(False)
         sffn.profile_only(None)
