@@ -169,24 +169,30 @@ up_pack_bf16_kernel(Dims d, const uint16_t* __restrict__ x, const uint16_t* __re
   // at a stage's end, the direct loads of the freed buffer and their address arithmetic)
   // placed between them, so the matrix pipe is fed while those issue.
   constexpr int NFR = 4 + NB;  // fragment reads per k-step
+  constexpr int NM = 4 * NB;   // MFMAs per k-step
+  // (64-token workgroups have fewer MFMAs than reads or loads to place between them: the
+  // rest follow without one)
+  constexpr int NPR = NFR < NM ? NFR : NM;            // (MFMA, read) pairs
+  constexpr int NPL = LPS < NM - 1 ? LPS : NM - 1;    // (MFMA, direct load) pairs
   auto order_step = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NFR; ++i) {
+    for (int i = 0; i < NPR; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - NFR, 0);
+    if constexpr (NM > NPR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NPR, 0);
+    if constexpr (NFR > NPR) __builtin_amdgcn_sched_group_barrier(0x100, NFR - NPR, 0);
   };
   auto order_boundary = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (i < NPL) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (load addresses)
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (direct load)
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);  // the next stage's first reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - LPS - 1, 0);
+    if constexpr (NM - NPL - 1 > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - NPL - 1, 0);
   };
   // Every stage runs the same instructions: the last one also waits, reloads (the last
   // stage again, into a buffer nothing reads) and reads fragments it does not use.  With
@@ -507,11 +513,18 @@ hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t*
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s) {
   // 128-token workgroups, two per CU (BK = 32); K = 64 keeps one per CU (its staging of
-  // four tiles needs the larger LDS stages)
+  // four tiles needs the larger LDS stages).  When the 128-token workgroups would not cover
+  // the CUs (a few hundred tokens), 64-token ones: twice the workgroups, each with half the
+  // MFMAs for the same W_up slice.
+  const bool few = (long long)(d.F / UP_BN) * ((d.T + 127) / 128) < 256;
   switch (d.K) {
     case 64: return launch_up_t<64, 2>(d, x, Wu, bu, b, ws, zdump, s);
-    case 128: return launch_up_t<128, 2, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s);
-    case 256: return launch_up_t<256, 2, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s);
+    case 128:
+      return few ? launch_up_t<128, 1, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s)
+                 : launch_up_t<128, 2, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s);
+    case 256:
+      return few ? launch_up_t<256, 1, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s)
+                 : launch_up_t<256, 2, 32, 2, 3>(d, x, Wu, bu, b, ws, zdump, s);
   }
   return hipErrorInvalidValue;
 }
