@@ -24,7 +24,7 @@ struct sparse_ffn {
   float down_mfma_density = SFFN_DOWN_MFMA_DENSITY_DEFAULT;
   // Auto policy: the kernel the last running down kernel found the layer's count to select
   // (0 gather, 1 tiles, 2 matrix cores, -1 none yet), in one word of pinned host memory that
-  // the kernels write; set up by the first auto call that may allocate, reset by a policy
+  // the kernels write; taken by the first auto call that may allocate, reset by a policy
   // change.
   int* hint_host = nullptr;
   int* hint_dev = nullptr;
@@ -240,8 +240,7 @@ sffn_status_t sparse_ffn_create(const sffn_config_t* cfg, const void* W_up, cons
 }
 
 sffn_status_t sparse_ffn_destroy(sparse_ffn_t h) {
-  if (h && h->hint_host) (void)hipHostFree(h->hint_host);
-  delete h;
+  delete h;  // its hint word, if any, stays with the library (never reused)
   return SFFN_OK;
 }
 
@@ -293,6 +292,41 @@ static DownPlan plan_down(const sparse_ffn* hd, const Dims& d) {
 // device: every candidate is launched with its range and all but one return at once.
 // blk_ready: ws.blk_nnz already holds this TwELL's per-block counts (written by the ordering
 // pass of the same call).
+// Hint words come from pages of pinned host memory that the library keeps until the process
+// ends; a word is never given to a second handle, so a kernel still writing one (or a graph
+// recorded with it and replayed later) never writes memory that was freed or reused.
+namespace {
+constexpr int HINT_PAGE_WORDS = 1024;
+std::mutex g_hint_mu;
+int* g_hint_page = nullptr;      // host address of the current page
+int* g_hint_page_dev = nullptr;  // its device address
+int g_hint_used = HINT_PAGE_WORDS;
+}  // namespace
+
+static bool new_hint_word(int** host, int** dev) {
+  std::lock_guard<std::mutex> lock(g_hint_mu);
+  if (g_hint_used == HINT_PAGE_WORDS) {
+    void* hp = nullptr;
+    void* dp = nullptr;
+    if (hipHostMalloc(&hp, sizeof(int) * HINT_PAGE_WORDS, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipHostFree(hp);  // nothing has used it yet
+      return false;
+    }
+    g_hint_page = static_cast<int*>(hp);
+    g_hint_page_dev = static_cast<int*>(dp);
+    g_hint_used = 0;
+  }
+  *host = g_hint_page + g_hint_used;
+  *dev = g_hint_page_dev + g_hint_used;
+  ++g_hint_used;
+  return true;
+}
+
 // The hint word of a handle, set up on first use by a call that may allocate (not one that
 // promised not to, and not while the stream is being captured): device address or null.
 static int* hint_word(sparse_ffn* hd, hipStream_t s, bool may_alloc) {
@@ -301,22 +335,15 @@ static int* hint_word(sparse_ffn* hd, hipStream_t s, bool may_alloc) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
     return nullptr;
-  void* hp = nullptr;
-  void* dp = nullptr;
-  if (hipHostMalloc(&hp, sizeof(int), hipHostMallocDefault) != hipSuccess) {
-    (void)hipGetLastError();
+  int* hp = nullptr;
+  int* dp = nullptr;
+  if (!new_hint_word(&hp, &dp)) {
     hd->hint_failed = true;
     return nullptr;
   }
-  *static_cast<volatile int*>(hp) = -1;
-  if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) {
-    (void)hipGetLastError();
-    (void)hipHostFree(hp);
-    hd->hint_failed = true;
-    return nullptr;
-  }
-  hd->hint_host = static_cast<int*>(hp);
-  hd->hint_dev = static_cast<int*>(dp);
+  __atomic_store_n(hp, -1, __ATOMIC_RELAXED);
+  hd->hint_host = hp;
+  hd->hint_dev = dp;
   return hd->hint_dev;
 }
 

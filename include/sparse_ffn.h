@@ -156,8 +156,9 @@ sffn_status_t sparse_ffn_create(const sffn_config_t *cfg, const void *W_up, cons
 
 /* (host only) Release a handle created by sparse_ffn_create; NULL is accepted.
  * Interface of the library: no device memory is owned, so nothing on the device is
- * released or waited for; the auto down policy's word of pinned host memory, if one was
- * allocated, is freed (no call of the handle may still be running on the device). */
+ * released or waited for (the auto down policy's word of pinned host memory stays with the
+ * library and is never given to another handle, so work of the handle still running, or a
+ * recorded graph replayed later, writes only that word). */
 sffn_status_t sparse_ffn_destroy(sparse_ffn_t h);
 
 /* Pack a dense fp32 hidden tensor h [T, d_ff] into TwELL (same article, section "What
@@ -246,9 +247,9 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
  *                     sparse_ffn_set_down_policy) launches every candidate and the count
  *                     decides on the device; the kernel that runs also writes which kernel its
  *                     count selects into a 4-byte word of pinned host memory that the handle
- *                     keeps (allocated by the first auto forward or down call, never by
- *                     sparse_ffn_forward_noalloc or under stream capture, freed by
- *                     sparse_ffn_destroy), and each later call launches that kernel alone.  A
+ *                     takes from pages the library keeps until the process ends (by the first
+ *                     auto forward or down call, never by sparse_ffn_forward_noalloc or under
+ *                     stream capture), and each later call launches that kernel alone.  A
  *                     change of density thus changes the kernel one call later; the result is
  *                     the kernel's that ran.
  *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA, SFFN_DOWN_UNION, SFFN_DOWN_SPARSE:
