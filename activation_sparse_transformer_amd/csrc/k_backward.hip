@@ -33,6 +33,7 @@ typedef __bf16 bf16x8_b __attribute__((ext_vector_type(8)));
 typedef short short4_b __attribute__((ext_vector_type(4)));
 typedef short short8_b __attribute__((ext_vector_type(8)));
 typedef float floatx16_b __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_b __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_vptr_b;
 typedef __attribute__((address_space(3))) short4_b* lds_s4ptr_b;
 
@@ -546,12 +547,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                               acc[i][j], 0, 0, 0);
       if constexpr (DB) {  // every wave sums; only the db waves store (no branch here)
+        // the fragment's 8 values in pairs against (1, 1): four dot2 instructions (fp32
+        // accumulation) instead of eight conversions and eight adds
+        const bf16x2_b ones = __builtin_bit_cast(bf16x2_b, 0x3F803F80u);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          float s = 0.0f;
+          const uint4 u = __builtin_bit_cast(uint4, fa[kk & 1][i]);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s += (float)fa[kk & 1][i][e];
-          dbacc[i] += s;
+          for (int q = 0; q < 4; ++q)
+            dbacc[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_b, w[q]), ones,
+                                                       dbacc[i], false);
         }
       }
       // one MFMA, then a few vector and LDS instructions in its shadow
