@@ -36,7 +36,6 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 constexpr int DOWN_NW = 16;   // waves per workgroup
 constexpr int DOWN_TPW = 16;  // tokens per wave
 constexpr int DOWN_BT = DOWN_NW * DOWN_TPW;
-static_assert(DOWN_BT == DK_BLOCK, "a workgroup's tokens are one block of the kernel choice");
 constexpr int DOWN_LDS = 160 * 1024;  // the whole LDS of a CU: one workgroup per CU
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -87,7 +86,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
     const uint8_t* __restrict__ cols, const int32_t* __restrict__ bk_tile_ptr,
     const int32_t* __restrict__ bk_tok, const void* __restrict__ bk_vals,
     const void* __restrict__ Wd_, void* __restrict__ y_, int tv_bytes, int tc_bytes,
-    DownChoice ch) {
+    const int32_t* __restrict__ blk_nnz, long long thr) {
   constexpr int DCL = BF16 ? 2 : 1;   // output columns per lane
   constexpr int DC = 64 * DCL;        // output columns per workgroup
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -111,8 +110,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
   // token blocks, so each TwELL block is fetched once into that XCD's L2 and the W_down
   // tile loads spread over every memory channel
   const int tb = P / nd;
-  note_choice(ch, T, d.F, blockIdx.x == 0);
-  if (!dk_takes(ch, DK_GATHER, tb, T, d.F)) return;  // another kernel's block
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) > thr) return;  // the matrix cores' layer
   const int dchunk = P - tb * nd;
   const int d0 = dchunk * DC;
   const int tw0 = tb * DOWN_BT + wv * DOWN_TPW;  // first token of this wave
@@ -302,7 +300,7 @@ __global__ __launch_bounds__(DOWN_NW * 64) void down_kernel(
 
 template <int K, bool BF16, bool FAST>
 static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                                const DownChoice& ch, hipStream_t s) {
+                                const int32_t* blk_nnz, long long thr, hipStream_t s) {
   constexpr int DC = BF16 ? 128 : 64;
   const int esz = BF16 ? 2 : 4;
   const int nd = d.D / DC;
@@ -315,32 +313,32 @@ static hipError_t launch_down_t(const Dims& d, const twell_buffers_t& b, const v
   if (lds > DOWN_LDS) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((down_kernel<K, BF16, FAST>), dim3(8 * per_xcd), dim3(DOWN_NW * 64), 0, s, d,
                      b.counts, b.vals, b.cols, b.bk_tile_ptr, b.bk_tok, b.bk_vals, Wd, y, tv, tc,
-                     ch);
+                     blk_nnz, thr);
   return hipGetLastError();
 }
 
 template <int K, bool BF16>
 static hipError_t launch_down_k(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                                const DownChoice& ch, hipStream_t s) {
+                                const int32_t* blk_nnz, long long thr, hipStream_t s) {
   // The LDS fast path needs 16-byte aligned TwELL rows and room for two stages.
   const int esz = BF16 ? 2 : 4;
   const size_t lds_fast = 2 * (size_t)K * 256 +
                           2 * (size_t)DOWN_NW * (((DOWN_TPW * d.W * esz + 15) & ~15) +
                                                  ((DOWN_TPW * d.W + 15) & ~15));
-  if (d.W % 16 == 0 && lds_fast <= DOWN_LDS) return launch_down_t<K, BF16, true>(d, b, Wd, y, ch, s);
-  return launch_down_t<K, BF16, false>(d, b, Wd, y, ch, s);
+  if (d.W % 16 == 0 && lds_fast <= DOWN_LDS) return launch_down_t<K, BF16, true>(d, b, Wd, y, blk_nnz, thr, s);
+  return launch_down_t<K, BF16, false>(d, b, Wd, y, blk_nnz, thr, s);
 }
 
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                       const DownChoice& ch, hipStream_t s) {
+                       const int32_t* blk_nnz, long long thr, hipStream_t s) {
   if (d.bf16) {
-    if (d.K == 64) return launch_down_k<64, true>(d, b, Wd, y, ch, s);
-    if (d.K == 128) return launch_down_k<128, true>(d, b, Wd, y, ch, s);
-    return launch_down_k<256, true>(d, b, Wd, y, ch, s);
+    if (d.K == 64) return launch_down_k<64, true>(d, b, Wd, y, blk_nnz, thr, s);
+    if (d.K == 128) return launch_down_k<128, true>(d, b, Wd, y, blk_nnz, thr, s);
+    return launch_down_k<256, true>(d, b, Wd, y, blk_nnz, thr, s);
   }
-  if (d.K == 64) return launch_down_k<64, false>(d, b, Wd, y, ch, s);
-  if (d.K == 128) return launch_down_k<128, false>(d, b, Wd, y, ch, s);
-  return launch_down_k<256, false>(d, b, Wd, y, ch, s);
+  if (d.K == 64) return launch_down_k<64, false>(d, b, Wd, y, blk_nnz, thr, s);
+  if (d.K == 128) return launch_down_k<128, false>(d, b, Wd, y, blk_nnz, thr, s);
+  return launch_down_k<256, false>(d, b, Wd, y, blk_nnz, thr, s);
 }
 
 // Stored nonzeros (true tile-row counts) of every 256-token block: 1024 threads per block;

@@ -35,7 +35,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int DL_WAVES = 16;
 constexpr int DL_TPW = 16;                 // tokens per wave: half a 32-token group
 constexpr int DL_BM = DL_WAVES * DL_TPW;   // 256 tokens per workgroup
-static_assert(DL_BM == DK_BLOCK, "a workgroup's tokens are one block of the kernel choice");
 
 // a * b + c for a, b < 2^24 and a result below 2^32, as a 24-bit multiply-add: a 32-bit
 // multiply-add is selected as v_mad_u64_u32, whose unused high addend register can be one a
@@ -54,7 +53,8 @@ __global__ __launch_bounds__(64 * DL_WAVES) void down_lds_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint32_t* __restrict__ vals2,
     const uint32_t* __restrict__ cols4, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, DownChoice ch) {
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long lo, long long hi,
+    DownHint hint) {
   constexpr int DC = 64 * CPL;              // output columns per workgroup
   constexpr int ROWB = DC * 2;              // bytes per staged W_down row
   constexpr int STAGE = K * DC;             // bf16 elements of one staged W_down slice
@@ -68,7 +68,12 @@ __global__ __launch_bounds__(64 * DL_WAVES) void down_lds_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sW1[STAGE];
 
   const int T = d.T, D = d.D, W = d.W, nt = d.nt;
-  note_choice(ch, T, d.F, blockIdx.x == 0);
+  // the layer goes to this kernel only when its stored-nonzero count is in (lo, hi]
+  if (blk_nnz != nullptr) {
+    const long long n = layer_nnz(blk_nnz, (T + 255) / 256);
+    if (n <= lo || n > hi) return;
+  }
+  note_choice(hint, (T + 255) / 256, blockIdx.x == 0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
@@ -81,7 +86,6 @@ __global__ __launch_bounds__(64 * DL_WAVES) void down_lds_kernel(
   const int P = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (P >= total) return;
   const int chunk = P / nTB, tb = P - chunk * nTB;
-  if (!dk_takes(ch, DK_TILES, tb, T, d.F)) return;  // another kernel's block
   const int d0 = chunk * DC;
   const int tg = tb * DL_BM + (wave >> 1) * GROUP;  // first token of this wave's group
   const int half = (wave & 1) * DL_TPW;              // this wave's tokens: tg + half + j
@@ -313,21 +317,22 @@ template <int K, int CPL>
 static void launch_lds_k(const Dims& d, dim3 grid, dim3 block, hipStream_t s,
                          const uint16_t* c, const uint32_t* v, const uint32_t* cl,
                          const uint16_t* bk, const int32_t* gf, const uint16_t* w, uint16_t* yy,
-                         const DownChoice& ch) {
+                         const int32_t* blk_nnz, long long lo, long long hi, const DownHint& hint) {
   const int hw = d.W / 2;
   if (hw <= 8)
     hipLaunchKernelGGL((down_lds_kernel<K, CPL, 8>), grid, block, 0, s, d, c, v, cl, bk, gf, w,
-                       yy, ch);
+                       yy, blk_nnz, lo, hi, hint);
   else if (hw <= 16)
     hipLaunchKernelGGL((down_lds_kernel<K, CPL, 16>), grid, block, 0, s, d, c, v, cl, bk, gf, w,
-                       yy, ch);
+                       yy, blk_nnz, lo, hi, hint);
   else
     hipLaunchKernelGGL((down_lds_kernel<K, CPL, 32>), grid, block, 0, s, d, c, v, cl, bk, gf, w,
-                       yy, ch);
+                       yy, blk_nnz, lo, hi, hint);
 }
 
 hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                           const void* Wd, void* y, const DownChoice& ch, hipStream_t s) {
+                           const void* Wd, void* y, const int32_t* blk_nnz, long long lo,
+                           long long hi, hipStream_t s, const DownHint& hint) {
   if (!down_lds_supported(d)) return hipErrorInvalidValue;
   auto* c = b.counts;
   auto* v = static_cast<const uint32_t*>(b.vals);
@@ -341,9 +346,9 @@ hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Worksp
   const int per_xcd = (nTB * nDC + 7) / 8;
   const dim3 grid(8 * per_xcd), block(64 * DL_WAVES);
   switch (d.K) {
-    case 64: launch_lds_k<64, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, ch); break;
-    case 128: launch_lds_k<128, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, ch); break;
-    case 256: launch_lds_k<256, 2>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, ch); break;
+    case 64: launch_lds_k<64, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi, hint); break;
+    case 128: launch_lds_k<128, 4>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi, hint); break;
+    case 256: launch_lds_k<256, 2>(d, grid, block, s, c, v, cl, bk, ws.grp_first, w, yy, blk_nnz, lo, hi, hint); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

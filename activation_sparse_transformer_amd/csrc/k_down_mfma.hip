@@ -32,9 +32,10 @@
 // With few workgroups (small T) the tile range is split into S parts, one per workgroup
 // group; each part's fp32 sums go to the workspace and down_reduce_kernel adds the parts in
 // order into y.
-// Under the auto policy a workgroup whose 256-token block the kernel choice gives to another
-// kernel returns at once (the reduce skips those blocks too); workgroup 0 records the kernels
-// the blocks select.
+// When the layer's stored-nonzero count (the sum of the per-block counts) is at most `thr`
+// the gather kernel takes the layer and every workgroup here (and the reduce) returns at
+// once (blk_nnz == nullptr: this kernel runs).  Workgroup 0 of a running launch records the
+// kernel the count selects through `hint`.
 #include <algorithm>
 
 #include "sffn_common.hpp"
@@ -52,16 +53,14 @@ constexpr int DM_BM = 256;  // tokens per workgroup
 constexpr int DM_BN = 256;  // output columns per workgroup
 constexpr int DM_KC = 64;   // hidden columns per contraction step
 constexpr int DM_NW = 8;    // waves per workgroup: 2 along the tokens x DM_NW / 2 along the columns
-static_assert(DM_BM == DK_BLOCK, "a workgroup's tokens are one block of the kernel choice");
-// token blocks of a split layer: at most 128 workgroups of (256 tokens, 256 columns) are split
-constexpr int DM_SPLIT_MAX_BLOCKS = 128;
 
 template <int K, int W>
 __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_NW / 4, DM_NW / 4))) void down_mfma_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, float* __restrict__ dpart, int S, DownChoice ch) {
+    uint16_t* __restrict__ y, float* __restrict__ dpart, int S, const int32_t* __restrict__ blk_nnz,
+    long long thr, DownHint hint) {
   constexpr int KC = DM_KC;
   constexpr int NCH = K / KC;          // steps per tile
   constexpr int U = W / 8;             // 8-slot units per tile-row
@@ -100,8 +99,8 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
   const int split = P / (nd * ntb);
   const int Pl = P - split * nd * ntb;
   const int tb = Pl / nd;
-  note_choice(ch, T, d.F, blockIdx.x == 0);
-  if (!dk_takes(ch, DK_MFMA, tb, T, d.F)) return;  // another kernel's block
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
+  note_choice(hint, ntb, blockIdx.x == 0);
   const int dchunk = Pl - tb * nd;
   // tiles [k_lo, k_hi) of this part (in pairs for 64-column tiles, whose one-step tiles run
   // two per unrolled iteration)
@@ -390,22 +389,16 @@ __global__ __launch_bounds__(64 * DM_NW) __attribute__((amdgpu_waves_per_eu(DM_N
       }
 }
 
-// y = bf16(sum over the S parts of the split kernel), parts added in order (deterministic),
-// for the token blocks the matrix cores took.
+// y = bf16(sum over the S parts of the split kernel), parts added in order (deterministic).
 __global__ __launch_bounds__(256) void down_reduce_kernel(Dims d, const float* __restrict__ part,
                                                           int S, uint16_t* __restrict__ y,
-                                                          DownChoice ch) {
-  // the blocks of this kernel (a split layer has at most 128 of them: 256 / S workgroups)
-  __shared__ uint8_t mine[DM_SPLIT_MAX_BLOCKS];
+                                                          const int32_t* __restrict__ blk_nnz,
+                                                          long long thr) {
   const int ntb = (d.T + DM_BM - 1) / DM_BM;
-  for (int b = (int)threadIdx.x; b < ntb && b < DM_SPLIT_MAX_BLOCKS; b += 256)
-    mine[b] = dk_takes(ch, DK_MFMA, b, d.T, d.F) ? 1 : 0;
-  __syncthreads();
-  const uint32_t d4 = (uint32_t)(d.D / 4);
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, ntb) <= thr) return;  // the gather kernel's layer
   const size_t n4 = (size_t)d.T * d.D / 4;
   const float4* p4 = reinterpret_cast<const float4*>(part);
   for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 256) {
-    if (!mine[(uint32_t)q / d4 / DM_BM]) continue;
     float4 a = p4[q];
     for (int sp = 1; sp < S; ++sp) {
       const float4 v = p4[(size_t)sp * n4 + q];
@@ -422,7 +415,8 @@ __global__ __launch_bounds__(256) void down_reduce_kernel(Dims d, const float* _
 
 template <int K, int W>
 static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                              const void* Wd, void* y, const DownChoice& ch, hipStream_t s) {
+                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                              hipStream_t s, const DownHint& hint) {
   const int nd = (d.D + DM_BN - 1) / DM_BN;
   const int ntb = (d.T + DM_BM - 1) / DM_BM;
   const int S = down_split(d);
@@ -432,33 +426,33 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
                      static_cast<const uint16_t*>(b.vals), b.cols,
                      static_cast<const uint16_t*>(b.bk_vals), ws.grp_first,
                      static_cast<const uint16_t*>(Wd), static_cast<uint16_t*>(y), ws.dpart, S,
-                     ch);
+                     blk_nnz, thr, hint);
   if (S > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_down_reduce(d, ws, y, S, ch, s);
+    return launch_down_reduce(d, ws, y, S, blk_nnz, thr, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
-                              const DownChoice& ch, hipStream_t s) {
-  if ((d.T + DM_BM - 1) / DM_BM > DM_SPLIT_MAX_BLOCKS) return hipErrorInvalidValue;  // not split
+                              const int32_t* blk_nnz, long long thr, hipStream_t s) {
   const size_t n4 = (size_t)d.T * d.D / 4;
   const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 2048);
   hipLaunchKernelGGL(down_reduce_kernel, dim3(blocks), dim3(256), 0, s, d, ws.dpart, S,
-                     static_cast<uint16_t*>(y), ch);
+                     static_cast<uint16_t*>(y), blk_nnz, thr);
   return hipGetLastError();
 }
 
 template <int K>
 static hipError_t launch_dm_k(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                              const void* Wd, void* y, const DownChoice& ch, hipStream_t s) {
+                              const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                              hipStream_t s, const DownHint& hint) {
   switch (d.W) {
-    case 16: return launch_dm_t<K, 16>(d, b, ws, Wd, y, ch, s);
-    case 32: return launch_dm_t<K, 32>(d, b, ws, Wd, y, ch, s);
-    case 48: return launch_dm_t<K, 48>(d, b, ws, Wd, y, ch, s);
-    case 64: return launch_dm_t<K, 64>(d, b, ws, Wd, y, ch, s);
+    case 16: return launch_dm_t<K, 16>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+    case 32: return launch_dm_t<K, 32>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+    case 48: return launch_dm_t<K, 48>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+    case 64: return launch_dm_t<K, 64>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
   }
   return hipErrorInvalidValue;
 }
@@ -468,11 +462,12 @@ bool down_mfma_supported(const Dims& d) {
 }
 
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                            const void* Wd, void* y, const DownChoice& ch, hipStream_t s) {
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                            hipStream_t s, const DownHint& hint) {
   if (!down_mfma_supported(d)) return hipErrorInvalidValue;
-  if (d.K == 64) return launch_dm_k<64>(d, b, ws, Wd, y, ch, s);
-  if (d.K == 128) return launch_dm_k<128>(d, b, ws, Wd, y, ch, s);
-  return launch_dm_k<256>(d, b, ws, Wd, y, ch, s);
+  if (d.K == 64) return launch_dm_k<64>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+  if (d.K == 128) return launch_dm_k<128>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
+  return launch_dm_k<256>(d, b, ws, Wd, y, blk_nnz, thr, s, hint);
 }
 
 }  // namespace sffn

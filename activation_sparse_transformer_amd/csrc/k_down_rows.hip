@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
     Dims d, const uint16_t* __restrict__ counts, const uint16_t* __restrict__ vals,
     const uint8_t* __restrict__ cols, const uint16_t* __restrict__ bk_vals,
     const int32_t* __restrict__ grp_first, const uint16_t* __restrict__ Wd,
-    uint16_t* __restrict__ y, DownChoice ch) {
+    uint16_t* __restrict__ y, const int32_t* __restrict__ blk_nnz, long long thr, DownHint hint) {
   static_assert(EPL == 8 || EPL == 4 || EPL == 2, "8, 4 or 2 output columns per lane");
   constexpr int CW = 64 * EPL;                 // columns of one wave load of a row
   // rows in flight per wave (registers: NQ EPL / 2 each; at most 64, one lane per slot)
@@ -41,22 +41,10 @@ __global__ __launch_bounds__(64 * ROWS_WAVES) void down_rows_kernel(
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int T = d.T, D = d.D, K = d.K, W = d.W;
   const int cb = blockIdx.y * NQ * CW;  // first output column of this workgroup
-  note_choice(ch, T, d.F, blockIdx.x == 0 && blockIdx.y == 0);
-  // the 256-token blocks the kernel choice gives this kernel, 64 blocks at a time (bit b of
-  // `mine` for block mine_base + b; the token loop only moves forward)
-  const int nblk = (T + DK_BLOCK - 1) / DK_BLOCK;
-  uint64_t mine = 0;
-  int mine_base = -64;
+  // the layer goes to this kernel only when its stored-nonzero count is at most thr
+  if (blk_nnz != nullptr && layer_nnz(blk_nnz, (T + 255) / 256) > thr) return;
+  note_choice(hint, (T + 255) / 256, blockIdx.x == 0 && blockIdx.y == 0);
   for (int t = blockIdx.x; t < T; t += gridDim.x) {  // workgroup-uniform token loop
-  if (ch.mask != 0) {
-    const int bt = t / DK_BLOCK;
-    if (bt - mine_base >= 64) {
-      mine_base = bt & ~63;
-      const int bl = mine_base + lane;
-      mine = ballot64(bl < nblk && dk_takes(ch, DK_GATHER, bl, T, d.F));
-    }
-    if (!((mine >> (bt - mine_base)) & 1ull)) continue;
-  }
   float acc[NQ][EPL];
 #pragma unroll
   for (int q = 0; q < NQ; ++q)
@@ -232,7 +220,8 @@ bool down_rows_supported(const Dims& d) {
 }
 
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                            const void* Wd, void* y, const DownChoice& ch, hipStream_t s) {
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                            hipStream_t s, const DownHint& hint) {
   if (!down_rows_supported(d)) return hipErrorInvalidValue;
   // from ROWS_FEW_T tokens at most 2048 workgroups (x), each looping over tokens: a skipped
   // launch (the layer went to the matrix cores) then costs little
@@ -248,7 +237,7 @@ hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Works
     // launched
     const dim3 grid(d.T, (d.D + 255) / 256), block(64 * 16);
     hipLaunchKernelGGL((down_rows_kernel<1, 16, 4>), grid, block, 0, s, d, c, v, b.cols, bk,
-                       ws.grp_first, w, yy, ch);
+                       ws.grp_first, w, yy, blk_nnz, thr, hint);
     return hipGetLastError();
   }
   // many tokens: 4-wave workgroups over whole tokens
@@ -257,7 +246,7 @@ hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Works
 #define SFFN_ROWS(NQ)                                                                      \
   case NQ:                                                                                 \
     hipLaunchKernelGGL((down_rows_kernel<NQ, 4>), grid, block, 0, s, d, c, v, b.cols, bk,   \
-                       ws.grp_first, w, yy, ch);                                           \
+                       ws.grp_first, w, yy, blk_nnz, thr, hint);                           \
     break;
     SFFN_ROWS(1) SFFN_ROWS(2) SFFN_ROWS(3) SFFN_ROWS(4)
     SFFN_ROWS(5) SFFN_ROWS(6) SFFN_ROWS(7) SFFN_ROWS(8)

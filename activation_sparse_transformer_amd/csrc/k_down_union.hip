@@ -454,7 +454,7 @@ static hipError_t launch_du_t(const Dims& d, const twell_buffers_t& b, const Wor
   if (S > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_down_reduce(d, ws, y, S, DownChoice(), s);
+    return launch_down_reduce(d, ws, y, S, blk_nnz, thr, s);
   }
   return hipGetLastError();
 }

@@ -259,11 +259,10 @@ sffn_status_t twell_pack(const sffn_config_t* cfg, const float* h, int32_t T,
 }
 
 // The down-projection's kernel choice.  Forced policies name one kernel (an unsupported one
-// falls back to the next one down).  Under the auto policy the kernels the layer allows are
-// fixed here (at layer scale, thr_g and thr_m: gather up to thr_g, tiles up to thr_m, mfma
-// above; an unsupported kernel's range goes to the next one down), and each 256-token block
-// is then given to one of them on the device by the same rule at block scale (DownChoice);
-// with a single allowed kernel no count is needed.
+// falls back to the next one down).  Under the auto policy the layer's stored nonzeros n
+// decide: gather for n <= thr_g, tiles for thr_g < n <= thr_m, mfma for n > thr_m; an
+// unsupported kernel's range goes to the next one down, and with a single candidate no count
+// is needed.
 struct DownPlan {
   int32_t policy;
   long long thr_g, thr_m, all;
@@ -289,8 +288,8 @@ static DownPlan plan_down(const sparse_ffn* hd, const Dims& d) {
 
 // Down-projection of a packed activation.  The gather kernel is the per-token row gather
 // for bf16 layers (the staged-tile gather for fp32 layers and d_model > 4096); under the auto
-// policy each 256-token block goes to the kernel its stored nonzeros select, counted and
-// compared on the device by every launched kernel.
+// policy the kernel is chosen by the layer's stored nonzeros, counted and compared on the
+// device: every candidate is launched with its range and all but one return at once.
 // blk_ready: ws.blk_nnz already holds this TwELL's per-block counts (written by the ordering
 // pass of the same call).
 // Hint words come from pages of pinned host memory that the library keeps until the process
@@ -352,61 +351,55 @@ static sffn_status_t down_impl(sparse_ffn* hd, const Dims& d, const twell_buffer
                                const Workspace& ws, void* y, hipStream_t s, bool blk_ready,
                                bool may_alloc) {
   const bool rows_ok = down_rows_supported(d);
-  auto gather = [&](const DownChoice& ch) {
+  DownHint hint;  // where the kernel that runs records its choice (auto policy only)
+  auto gather = [&](const int32_t* blk, long long thr) {
     if (rows_ok)
-      return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, ch, s); });
-    if (down_rows_f32_supported(d) && ch.cnt == nullptr)
+      return run("down", s, [&] { return launch_down_rows(d, act, ws, hd->W_down, y, blk, thr, s, hint); });
+    if (down_rows_f32_supported(d) && blk == nullptr)
       return run("down", s, [&] { return launch_down_rows_f32(d, act, ws, hd->W_down, y, s); });
-    return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, ch, s); });
+    return run("down", s, [&] { return launch_down(d, act, hd->W_down, y, blk, thr, s); });
   };
-  auto tiles = [&](const DownChoice& ch) {
+  auto tiles = [&](const int32_t* blk, long long lo, long long hi) {
     return run("down_tiles", s,
-               [&] { return launch_down_lds(d, act, ws, hd->W_down, y, ch, s); });
+               [&] { return launch_down_lds(d, act, ws, hd->W_down, y, blk, lo, hi, s, hint); });
   };
-  auto mfma = [&](const DownChoice& ch) {
+  auto mfma = [&](const int32_t* blk, long long thr) {
     return run("down_mfma", s,
-               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, ch, s); });
+               [&] { return launch_down_mfma(d, act, ws, hd->W_down, y, blk, thr, s, hint); });
   };
-  auto unionk = [&]() {
+  auto unionk = [&](const int32_t* blk, long long thr) {
     return run("down_union", s,
-               [&] { return launch_down_union(d, act, ws, hd->W_down, y, nullptr, 0, s); });
+               [&] { return launch_down_union(d, act, ws, hd->W_down, y, blk, thr, s); });
   };
-  auto sparse = [&]() {
+  auto sparse = [&](const int32_t* blk, long long thr) {
     return run("down_sparse", s,
-               [&] { return launch_down_sparse(d, act, ws, hd->W_down, y, nullptr, 0, s); });
+               [&] { return launch_down_sparse(d, act, ws, hd->W_down, y, blk, thr, s); });
   };
   const DownPlan p = plan_down(hd, d);
-  const DownChoice all;  // the launched kernel takes every block
-  if (p.policy == SFFN_DOWN_SPARSE) return sparse();
-  if (p.policy == SFFN_DOWN_UNION) return unionk();
-  if (p.policy == SFFN_DOWN_GATHER) return gather(all);
-  if (p.policy == SFFN_DOWN_TILES) return tiles(all);
-  if (p.policy == SFFN_DOWN_MFMA) return mfma(all);
-  if (!p.needs_count) return gather(all);
+  if (p.policy == SFFN_DOWN_SPARSE) return sparse(nullptr, 0);
+  if (p.policy == SFFN_DOWN_UNION) return unionk(nullptr, 0);
+  if (p.policy == SFFN_DOWN_GATHER) return gather(nullptr, 0);
+  if (p.policy == SFFN_DOWN_TILES) return tiles(nullptr, 0, 0);
+  if (p.policy == SFFN_DOWN_MFMA) return mfma(nullptr, 0);
+  if (!p.needs_count) return gather(nullptr, 0);
   if (!blk_ready)
     SFFN_TRY_INNER(run("block_nnz", s, [&] { return launch_block_nnz(d, act, ws.blk_nnz, s); }));
-  // The choice is made per 256-token block on the device from the block's stored nonzeros,
-  // by every launched kernel alike (DownChoice).  Each kernel gives its blocks' result at any
-  // density (the choice is speed only), so a call launches only the kernels the previous
-  // call's blocks selected (a block whose kernel is not among them goes to one that is) and
-  // records the kernels its own blocks select for the call after it.  The first call, a
-  // record naming a kernel this call's shape does not allow, or no hint word: every allowed
-  // kernel is launched.
-  DownChoice ch;
-  ch.cnt = ws.blk_nnz;
-  ch.dg = hd->down_gather_density;
-  ch.dm = hd->down_mfma_density;
-  ch.allowed = DK_GATHER | (p.thr_m > p.thr_g ? DK_TILES : 0) | (p.thr_m < p.all ? DK_MFMA : 0);
-  int launch = ch.allowed;
-  if (int* hw = hint_word(hd, s, may_alloc)) {
-    ch.hint = hw;
+  // Every candidate gives the layer's result at any density (the choice is speed only), so
+  // once a call has recorded the kernel its count selects, the next call launches that one
+  // alone (and records its own count's choice for the call after it).  The first call, a
+  // recorded kernel that is no candidate for this call's shape, or no hint word: every
+  // candidate is launched and the count decides on the device.
+  int* hw = rows_ok ? hint_word(hd, s, may_alloc) : nullptr;
+  if (hw) {
+    hint = DownHint{hw, ws.blk_nnz, p.thr_g, p.thr_m};
     const int h = __atomic_load_n(hd->hint_host, __ATOMIC_RELAXED);
-    if (h > 0 && (h & ~ch.allowed) == 0) launch = h;
+    if (h == 0) return gather(nullptr, 0);
+    if (h == 1 && p.thr_m > p.thr_g) return tiles(nullptr, 0, 0);
+    if (h == 2 && p.thr_m < p.all) return mfma(nullptr, 0);
   }
-  ch.mask = (launch & (launch - 1)) ? launch : 0;  // one kernel: it takes every block
-  if (launch & DK_GATHER) SFFN_TRY_INNER(gather(ch));
-  if (launch & DK_TILES) SFFN_TRY_INNER(tiles(ch));
-  if (launch & DK_MFMA) SFFN_TRY_INNER(mfma(ch));
+  SFFN_TRY_INNER(gather(ws.blk_nnz, p.thr_g));
+  if (p.thr_m > p.thr_g) SFFN_TRY_INNER(tiles(ws.blk_nnz, p.thr_g, p.thr_m));
+  if (p.thr_m < p.all) SFFN_TRY_INNER(mfma(ws.blk_nnz, p.thr_m));
   return SFFN_OK;
 }
 
@@ -527,7 +520,7 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t hd, const void* x, const void* dy
   dact.vals = dh_vals;
   dact.bk_vals = dh_bk_vals;
   return run("bwd_dx", s,
-             [&] { return launch_down_mfma(d, dact, ws, hd->W_up, dx, DownChoice(), s); });
+             [&] { return launch_down_mfma(d, dact, ws, hd->W_up, dx, nullptr, 0, s); });
 }
 
 sffn_status_t sparse_ffn_set_down_policy(sparse_ffn_t hd, int32_t policy, float gather_density,

@@ -182,51 +182,24 @@ __device__ __forceinline__ long long layer_nnz(const int32_t* blk_nnz, int n) {
 }
 #endif
 
-// The auto policy's choice of down-projection kernel, made per 256-token block on the device
-// from the block's stored nonzeros n (the rules of the host plan, with the thresholds scaled
-// to the block's tokens x d_ff cells): gather for n <= gather_density cells, tiles up to
-// mfma_density cells, matrix cores above; a kernel the layer does not allow hands its range
-// to the next one down.  Every kernel launched for a call evaluates the same rule and takes
-// only its own blocks; a block whose kernel was not launched (the call launched the kernels
-// the previous call's blocks selected) goes to the first launched one of mfma, tiles, gather.
-constexpr int DK_GATHER = 1, DK_TILES = 2, DK_MFMA = 4;
-constexpr int DK_BLOCK = 256;  // tokens per block (the per-block counts of the workspace)
-struct DownChoice {
-  const int32_t* cnt = nullptr;  // per-block stored nonzeros (ws.blk_nnz)
-  float dg = 0.0f, dm = 0.0f;    // the handle's density thresholds
-  int allowed = 0;               // kernels the layer allows (DK_* bits)
-  int mask = 0;                  // kernels launched for this call; 0: the kernel takes every block
-  int* hint = nullptr;           // pinned host word: the kernels this call's blocks select
+// Where a down kernel records the kernel the layer's count selects for the next call of the
+// auto policy: dst (a word of pinned host memory, or null) gets 0 (gather, count <= thr_g),
+// 1 (tiles, count <= thr_m) or 2 (matrix cores) from the per-block counts blk.
+struct DownHint {
+  int* dst = nullptr;
+  const int32_t* blk = nullptr;
+  long long thr_g = 0, thr_m = 0;
 };
 #if defined(__HIPCC__)
-__device__ __forceinline__ int dk_preferred(const DownChoice& c, int b, int T, int F) {
-  const int nb = T - DK_BLOCK * b < DK_BLOCK ? T - DK_BLOCK * b : DK_BLOCK;
-  const double cells = (double)nb * (double)F;
-  const long long n = c.cnt[b];
-  const long long tm = (c.allowed & DK_MFMA) ? (long long)((double)c.dm * cells) : (1ll << 62);
-  const long long tg = (c.allowed & DK_TILES) ? (long long)((double)c.dg * cells) : tm;
-  return n <= tg ? DK_GATHER : (n <= tm ? DK_TILES : DK_MFMA);
-}
-// Whether the kernel `self` takes block b (wave-uniform when b is).
-__device__ __forceinline__ bool dk_takes(const DownChoice& c, int self, int b, int T, int F) {
-  if (c.mask == 0) return true;
-  const int p = dk_preferred(c, b, T, F);
-  const int k = (c.mask & p) ? p
-              : (c.mask & DK_MFMA) ? DK_MFMA
-              : (c.mask & DK_TILES) ? DK_TILES : DK_GATHER;
-  return k == self;
-}
-// Called by every thread of a launch that runs; wave 0 of the workgroup for which `first`
-// holds (wave-uniform) records the kernels the blocks select (system scope: the host reads
-// the word).
-__device__ __forceinline__ void note_choice(const DownChoice& c, int T, int F, bool first) {
-  if (c.hint == nullptr || !first || threadIdx.x >= 64) return;
-  const int nblk = (T + DK_BLOCK - 1) / DK_BLOCK;
-  int bits = 0;
-  for (int b = (int)threadIdx.x; b < nblk; b += 64) bits |= dk_preferred(c, b, T, F);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) bits |= __shfl_xor(bits, o);
-  if (threadIdx.x == 0) __hip_atomic_store(c.hint, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+// Called by every thread of a kernel that runs; wave 0 of the workgroup for which `first`
+// holds (wave-uniform) reads the counts and one lane stores the choice (system scope: the
+// host reads it).
+__device__ __forceinline__ void note_choice(const DownHint& h, int n_blocks, bool first) {
+  if (h.dst == nullptr || !first || threadIdx.x >= 64) return;
+  const long long n = layer_nnz(h.blk, n_blocks);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(h.dst, n <= h.thr_g ? 0 : (n <= h.thr_m ? 1 : 2), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
 }
 #endif
 
@@ -256,17 +229,21 @@ hipError_t launch_up_pack_bf16(const Dims& d, const uint16_t* x, const uint16_t*
                                const uint16_t* bu, const twell_buffers_t& b,
                                const Workspace& ws, float* zdump, hipStream_t s);
 // Down-projection.  Three kernels: the per-token gather, the LDS-tile vector kernel and the
-// matrix-core kernel.  Each takes the blocks DownChoice assigns it (every block when its mask
-// is 0) and, with a hint word, records the kernels the blocks select.
+// matrix-core kernel.  With blk_nnz (per-256-token-block stored-nonzero counts from
+// launch_block_nnz) each is launched with its range of the layer's total and reads the
+// total at entry: the one whose range holds it runs, the others return at once.
+// blk_nnz == nullptr runs the kernel launched.  The kernel that runs records, through `hint`,
+// the kernel the count selects (the next auto call launches only that one).
 hipError_t launch_block_nnz(const Dims& d, const twell_buffers_t& b, int32_t* blk_nnz,
                             hipStream_t s);
 hipError_t launch_down(const Dims& d, const twell_buffers_t& b, const void* Wd, void* y,
-                       const DownChoice& ch, hipStream_t s);
+                       const int32_t* blk_nnz, long long thr, hipStream_t s);
 bool down_mfma_supported(const Dims& d);
 // One wave per token over the W_down rows its nonzeros select (bf16, d_model <= 4096).
 bool down_rows_supported(const Dims& d);
 hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                            const void* Wd, void* y, const DownChoice& ch, hipStream_t s);
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                            hipStream_t s, const DownHint& hint = DownHint());
 // One workgroup per (token, 256 output columns) over the W_down rows its nonzeros select
 // (fp32 layers, T <= UP_SMALL_T).
 bool down_rows_f32_supported(const Dims& d);
@@ -276,7 +253,8 @@ hipError_t launch_down_rows_f32(const Dims& d, const twell_buffers_t& b, const W
 // W <= 128).  With blk_nnz it runs only when the layer's stored nonzeros are in (lo, hi].
 bool down_lds_supported(const Dims& d);
 hipError_t launch_down_lds(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                           const void* Wd, void* y, const DownChoice& ch, hipStream_t s);
+                           const void* Wd, void* y, const int32_t* blk_nnz, long long lo,
+                           long long hi, hipStream_t s, const DownHint& hint = DownHint());
 bool backward_supported(const Dims& d);
 // One part of the backward weights pass: which = 0: dh at the stored positions of `act`
 // (into dh_vals / dh_bk); 1: dW_down = H^T g; 2: dW_up = dH^T x and, if db is not null,
@@ -286,7 +264,8 @@ hipError_t launch_backward_part(int which, const Dims& d, const twell_buffers_t&
                                 const void* Wd, void* dh_vals, void* dh_bk, float* dW_up,
                                 float* dW_down, float* db, hipStream_t s);
 hipError_t launch_down_mfma(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
-                            const void* Wd, void* y, const DownChoice& ch, hipStream_t s);
+                            const void* Wd, void* y, const int32_t* blk_nnz, long long thr,
+                            hipStream_t s, const DownHint& hint = DownHint());
 // The matrix-core down-projection over the column unions of 64-token blocks (the same
 // shapes as launch_down_mfma; reads ws.umask, written by the kernel that produced the TwELL).
 hipError_t launch_down_union(const Dims& d, const twell_buffers_t& b, const Workspace& ws,
@@ -304,6 +283,6 @@ hipError_t launch_gather_fma_probe(const void* W, int F, int D, const int32_t* r
 hipError_t launch_hist(const Dims& d, const twell_buffers_t& b, const Workspace& ws, hipStream_t s);
 // y = bf16 of the sum of the S fp32 parts in ws.dpart (split matrix-core kernels).
 hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
-                              const DownChoice& ch, hipStream_t s);
+                              const int32_t* blk_nnz, long long thr, hipStream_t s);
 
 }  // namespace sffn

@@ -231,29 +231,27 @@ sffn_status_t sparse_ffn_backward(sparse_ffn_t h, const void *x, const void *dy,
  *           2-3 in a second that is contracted only where it holds a value, so a step costs
  *           half a dense one where no group has three nonzeros (same shapes as mfma).
  * Policies:
- *   SFFN_DOWN_AUTO:   every 256-token block by its own stored density (its stored nonzeros /
- *                     (its tokens x d_ff)): gather up to gather_density, tiles up to
- *                     mfma_density, mfma above; the counts are taken on the device and every
- *                     launched kernel takes only its own blocks, so the choice costs no host
- *                     synchronisation (the default, with the *_DEFAULT thresholds).  A kernel
- *                     the layer does not support hands its range to the next one down (mfma ->
- *                     tiles -> gather), and so do tiles below SFFN_DOWN_TILES_MIN_T tokens (its
- *                     256-token workgroups walk every tile in turn and need many tokens to fill
- *                     the GPU) and mfma below SFFN_DOWN_MFMA_MIN_T (a handful of tokens: it
- *                     contracts whole 256-token blocks and reads all of W_down, where the
- *                     gather reads only the rows in use).  With few tokens the mfma kernel
- *                     splits the tiles over more workgroups and adds the parts' fp32 sums in a
- *                     fixed order.  Every kernel is correct at any density, so the choice is
- *                     one of speed: the first auto call on a handle (and the first after any
- *                     sparse_ffn_set_down_policy) launches every kernel the layer allows; the
- *                     kernels also write which kernels the call's blocks select into a 4-byte
- *                     word of pinned host memory that the handle takes from pages the library
- *                     keeps until the process ends (by the first auto forward or down call,
- *                     never by sparse_ffn_forward_noalloc or under stream capture), and each
- *                     later call launches only those kernels (a block whose kernel is not
- *                     launched goes to the first launched of mfma, tiles, gather).  A change of
- *                     density thus changes the launched kernels one call later; the result is
- *                     that of the kernels that ran.
+ *   SFFN_DOWN_AUTO:   by the layer's stored density (stored nonzeros / (T d_ff)): gather up to
+ *                     gather_density, tiles up to mfma_density, mfma above; the count is taken
+ *                     on the device, so the choice costs no host synchronisation (the default,
+ *                     with the *_DEFAULT thresholds).  A kernel the layer does not support
+ *                     hands its range to the next one down (mfma -> tiles -> gather), and so
+ *                     do tiles below SFFN_DOWN_TILES_MIN_T tokens (its 256-token workgroups
+ *                     walk every tile in turn and need many tokens to fill the GPU) and mfma
+ *                     below SFFN_DOWN_MFMA_MIN_T (a handful of tokens: it contracts whole
+ *                     256-token blocks and reads all of W_down, where the gather reads only
+ *                     the rows in use).  With few tokens the mfma kernel splits the tiles
+ *                     over more workgroups and adds the parts' fp32 sums in a fixed order.
+ *                     Every candidate is correct at any density, so the choice is one of
+ *                     speed: the first auto call on a handle (and the first after any
+ *                     sparse_ffn_set_down_policy) launches every candidate and the count
+ *                     decides on the device; the kernel that runs also writes which kernel its
+ *                     count selects into a 4-byte word of pinned host memory that the handle
+ *                     takes from pages the library keeps until the process ends (by the first
+ *                     auto forward or down call, never by sparse_ffn_forward_noalloc or under
+ *                     stream capture), and each later call launches that kernel alone.  A
+ *                     change of density thus changes the kernel one call later; the result is
+ *                     the kernel's that ran.
  *   SFFN_DOWN_GATHER, SFFN_DOWN_TILES, SFFN_DOWN_MFMA, SFFN_DOWN_UNION, SFFN_DOWN_SPARSE:
  *                     always that kernel (tiles, mfma, union and sparse fall back as above
  *                     when the layer does not support them).

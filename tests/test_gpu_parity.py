@@ -188,21 +188,20 @@ def test_down_from_pack(T, D, F, K, W, dtype, density, policy):
 
 
 def test_down_auto_policy_choice():
-    """Token blocks with very different densities (0.1%, 4%, 0.3%, 2%, 1024 tokens each, the
-    last part ragged): the auto policy chooses the kernel of every 256-token block on the
-    device from the block's own count.  Every row is written, the result matches the oracle,
-    and the rows of each part equal bit for bit the forced result of the kernel its density
-    selects; the first call after a policy change launches every kernel the layer allows, the
-    next one only those its blocks selected.  Below DOWN_TILES_MIN_T tokens the tiles range
-    goes to the gather kernel."""
+    """Token blocks with very different densities (0.1%, 4%, 0.3%, 2%; the last one ragged):
+    the auto policy hands the whole layer to one kernel by its total stored density (about
+    1.6% here), decided on the device.  Every row is written, the result matches the oracle,
+    and it equals bit for bit the single-kernel result the thresholds select.  Below
+    DOWN_TILES_MIN_T tokens the tiles range goes to the gather kernel."""
     torch, sffn = need_gpu()
     from gen import f32_to_bf16_bits, bf16_bits_to_f32
     T, D, F, K, W = 4200, 256, 2048, 128, 32
     assert T >= sffn.DOWN_TILES_MIN_T
     parts = [make_hidden(1024, F, 0.001, seed=11), make_hidden(1024, F, 0.04, seed=12),
              make_hidden(1024, F, 0.003, seed=13), make_hidden(1128, F, 0.02, seed=14)]
-    bounds = [(0, 1024), (1024, 2048), (2048, 3072), (3072, T)]  # whole 256-token blocks
     h = np.concatenate(parts, axis=0)
+    dens = np.count_nonzero(h) / h.size
+    assert 0.01 < dens < 0.02
     rng = np.random.default_rng(5)
     Wd_bits = f32_to_bf16_bits((rng.standard_normal((F, D)) / np.sqrt(F)).astype(np.float32))
     Wd64 = bf16_bits_to_f32(Wd_bits).astype(np.float64)
@@ -213,43 +212,33 @@ def test_down_auto_policy_choice():
     layer = sffn.SparseFFN(cfg, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
                            torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
     buf = sffn.twell_pack(cfg, to_dev_f32(torch, h))
-    names = {"gather": "down", "tiles": "down_tiles", "mfma": "down_mfma"}
-
-    def run(policy, tg=sffn.DOWN_GATHER_DENSITY_DEFAULT, tm=sffn.DOWN_MFMA_DENSITY_DEFAULT,
-            reset=True):
-        if reset:
-            layer.set_down_policy(policy, tg, tm)
+    # (policy, gather_density, mfma_density) -> the kernel that must run
+    cases = [("gather", 0.0, 0.0, "gather"), ("tiles", 0.0, 0.0, "tiles"),
+             ("mfma", 0.0, 0.0, "mfma"), ("auto", 0.0, 0.0, "mfma"),
+             ("auto", 1.0, 1.0, "gather"), ("auto", 0.0, 1.0, "tiles"),
+             ("auto", 0.005, 0.03, "tiles"), ("auto", 0.02, 0.03, "gather"),
+             ("auto", 0.002, 0.01, "mfma")]
+    ys = {}
+    for policy, tg, tm, expect in cases:
+        layer.set_down_policy(policy, tg, tm)
         y = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
         sffn.profile_reset()
         sffn.profile_enable(True)
-        try:
-            layer.down(buf, y=y)
-            launched = {k for k, n in names.items() if sffn.profile_read(n)[1]}
-        finally:
-            sffn.profile_enable(False)
-            sffn.profile_reset()
+        layer.down(buf, y=y)
+        sffn.profile_enable(False)
         yh = y_to_host(torch, y)
         assert not np.isnan(yh).any(), f"{policy}/{tg}/{tm}: rows not written"
         assert_y_close(yh, y_ref, "bf16", f"{policy}/{tg}/{tm}")
-        return yh, launched
-
-    forced = {}
-    for k in names:
-        forced[k], launched = run(k)
-        assert launched == {k}, launched
-    # (gather_density, mfma_density) -> the kernel of each part, and the kernels the layer
-    # allows (tiles only when its range is not empty)
-    cases = [((0.0, 0.0), ("mfma",) * 4, {"gather", "mfma"}),
-             ((1.0, 1.0), ("gather",) * 4, {"gather", "mfma"}),
-             ((0.0, 1.0), ("tiles",) * 4, {"gather", "tiles", "mfma"}),
-             ((0.002, 0.01), ("gather", "mfma", "tiles", "mfma"), {"gather", "tiles", "mfma"}),
-             ((0.005, 0.03), ("gather", "mfma", "gather", "tiles"), {"gather", "tiles", "mfma"})]
-    for (tg, tm), per_part, allowed in cases:
-        for call in range(2):
-            yh, launched = run("auto", tg, tm, reset=call == 0)
-            assert launched == (allowed if call == 0 else set(per_part)), (tg, tm, call, launched)
-            for (t0, t1), k in zip(bounds, per_part):
-                assert np.array_equal(yh[t0:t1], forced[k][t0:t1]), (tg, tm, call, t0, k)
+        if policy != "auto":
+            ys[expect] = yh
+        else:
+            assert np.array_equal(yh, ys[expect]), f"auto {tg}/{tm} should run {expect}"
+        launched = {k: sffn.profile_read(n)[1] for k, n in
+                    (("gather", "down"), ("tiles", "down_tiles"), ("mfma", "down_mfma"))}
+        if policy == "auto":
+            assert all(v == 1 for v in launched.values() if v) and launched[expect] == 1
+        else:
+            assert launched == {k: int(k == expect) for k in launched}, launched
     sffn.profile_reset()
     # a short activation (the first 48 tokens): the tiles range goes to the gather kernel,
     # and below DOWN_MFMA_MIN_T the matrix-core range too
@@ -329,9 +318,8 @@ def test_down_auto_policy_follows_the_last_count():
     layer = sffn.SparseFFN(cfg, torch.zeros((F, D), dtype=torch.bfloat16, device="cuda"),
                            torch.zeros(F, dtype=torch.bfloat16, device="cuda"), Wd_dev)
     dense = make_hidden(T, F, 0.05, seed=21)
-    sparse = make_hidden(T, F, 0.0002, seed=22)   # below the gather's 0.05% in both blocks
-    assert 0 < np.count_nonzero(sparse[:256]) <= 0.0005 * 256 * F
-    assert np.count_nonzero(sparse[256:]) <= 0.0005 * (T - 256) * F
+    sparse = make_hidden(T, F, 0.0003, seed=22)   # below the gather's 0.05% of T x F
+    assert 0 < np.count_nonzero(sparse) <= 0.0005 * T * F < np.count_nonzero(dense)
     bufs = {k: sffn.twell_pack(cfg, to_dev_f32(torch, h)) for k, h in (("dense", dense), ("sparse", sparse))}
     refs = {}
     for k, h in (("dense", dense), ("sparse", sparse)):
