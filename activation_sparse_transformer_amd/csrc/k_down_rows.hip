@@ -11,15 +11,16 @@
 //
 // One workgroup per token at a time (NW waves; for few tokens, when the gather is the call's
 // only down kernel, NW = 16 and the workgroups of a token also split its columns into 256-wide
-// chunks, so a short batch still spreads over many CUs); wave w takes a contiguous 1/NW of the
+// chunks, 128-wide for a handful of tokens, so a short batch still spreads over many CUs);
+// wave w takes a contiguous 1/NW of the
 // tiles, lane l of it tile k = k0 + l: its count, then its slots 8 at a time (16 B values +
 // 8 B columns).  The (row, value) pairs of the lanes are gathered with readlane into batches
 // (slot i in lane i;
-// 32 pairs for the 256-column chunks, 8 up to d_model 2048 and 4 above otherwise) whose
+// 32 pairs for the 256- and 128-column chunks, 8 up to d_model 2048 and 4 above otherwise) whose
 // W_down row loads are all issued before any is used, so a token with many nonzeros (heavy
 // tokens run at 10-20x the mean density) is not a chain of single-row latencies.  Lane L owns
 // the EPL output columns c0 + 64 EPL q + EPL L (q < NQ; c0 = the workgroup's column chunk;
-// EPL = 8, or 4 for the 256-column chunks): every row is read as NQ coalesced wave loads of
+// EPL = 8, or 4 / 2 for the 256- / 128-column chunks): every row is read as NQ coalesced wave loads of
 // 128 EPL bytes.  The waves' partial rows are summed in LDS and y is written as 4 EPL-byte
 // stores.
 #include "sffn_common.hpp"
@@ -235,6 +236,14 @@ hipError_t launch_down_rows(const Dims& d, const twell_buffers_t& b, const Works
     // choice (the auto policy launches the candidates only until a call has recorded the
     // kernel its count selects), so that the gather's sums do not depend on how it was
     // launched
+    if ((long long)d.T * ((d.D + 255) / 256) < 128) {
+      // a handful of tokens: 128-column chunks, twice the workgroups (each CU's share of the
+      // gathered rows bounds these)
+      const dim3 grid(d.T, (d.D + 127) / 128), block(64 * 16);
+      hipLaunchKernelGGL((down_rows_kernel<1, 16, 2>), grid, block, 0, s, d, c, v, b.cols, bk,
+                         ws.grp_first, w, yy, blk_nnz, thr, hint);
+      return hipGetLastError();
+    }
     const dim3 grid(d.T, (d.D + 255) / 256), block(64 * 16);
     hipLaunchKernelGGL((down_rows_kernel<1, 16, 4>), grid, block, 0, s, d, c, v, b.cols, bk,
                        ws.grp_first, w, yy, blk_nnz, thr, hint);
