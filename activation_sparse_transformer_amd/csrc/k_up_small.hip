@@ -13,19 +13,22 @@
 // row and not written.
 //
 // Two forms, by measurement on MI355X at d_model 2048:
-//  * up to 64 tokens (one or two token blocks): 4 waves, each over a quarter of d_model in
-//    batches of 8 (4) steps whose loads are in flight together.  Where the quarters fit LDS
+//  * fewer than 8 tokens (one token block): 4 waves, each over a quarter of d_model in
+//    batches of 8 steps whose loads are in flight together.  Where the quarters fit LDS
 //    (d_model <= 2048, a multiple of 512), each wave first copies its 32 W_up rows x D/4
 //    columns into its own LDS region with contiguous 1 KB direct loads (16-byte piece s of row
 //    rr at slot s ^ (rr % 16), so the fragment reads of 16 rows hit distinct banks): read in
 //    the MFMA layout straight from memory, each load used 32 bytes of 32 lines, and W_up
 //    streamed at 6.3 TB/s against 11.3 TB/s for whole-row loads (a probe over the 1.5B-like
 //    layer's W_up, cache-resident as in the forward);
-//  * 65 to 128 tokens (four token blocks, four times the token-row bytes per W_up piece):
-//    8 waves, each over an eighth of d_model in groups of four steps, with the W_up pieces of
-//    two groups in flight at once and the token rows of the next group loaded as whole
-//    128-byte lines and staged through the wave's own LDS (a token row's 32 bytes per step,
-//    loaded straight into the MFMA layout, would cost a line fetch from L2 each).
+//  * 8 to 128 tokens (one, two or four token blocks; d_model a multiple of 64): 8 waves, each
+//    over an eighth of d_model in groups of four steps, with the W_up pieces of four groups
+//    (two for four token blocks, whose token rows take the registers) in flight at once and
+//    the token rows of the next group loaded as whole 128-byte lines and staged through the
+//    wave's own LDS (a token row's 32 bytes per step, loaded straight into the MFMA layout,
+//    cost a line fetch from L2 each: the 4-wave form took 17.8 us at 64 tokens against
+//    10.5 us at 32, and this form 12-13 us).
+// Other shapes run the 4-wave form with direct loads.
 #include "sffn_common.hpp"
 
 namespace sffn {
@@ -163,19 +166,21 @@ __global__ __launch_bounds__(256) void up_small_kernel(Dims d, const uint16_t* _
 
 constexpr int US8_NW = 8;  // waves of the 8-wave form
 
-// groups of four steps per chunk (two: the 8 W_up pieces, two sets of token-row lines and the
-// accumulators fill the 256 registers of a wave at two waves per SIMD)
+// groups of four steps per chunk for four token blocks (two: the 8 W_up pieces, two sets of
+// token-row lines and the accumulators fill the 256 registers of a wave at two waves per SIMD)
 constexpr int US8_NGC = 2;
+// the same for one and two token blocks (fewer token-row registers: more W_up pieces in flight)
+constexpr int US8_NGC12 = 4;
 
 // Groups g0 .. g0 + n - 1 (1 <= n <= NGC) of one wave of the 8-wave form.  A group is
 // four 16-column steps: 64 columns, one 128-byte line of every token row.  The W_up pieces of
-// the whole chunk are loaded first.  The 128 token rows of a group are loaded as whole lines
-// (8 lanes per row, 8 rows per load), one group ahead of the MFMAs, and written to the wave's
-// own 16 KB of LDS (row t at t * 128 bytes, 16-byte piece p at (p ^ (t & 7)) * 16), from
-// which each step reads its MFMA operand (lane l: row 32 tb + l % 32, piece 2 j + l / 32).
+// the whole chunk are loaded first.  The 32 NTB token rows of a group are loaded as whole
+// lines (8 lanes per row, 8 rows per load), one group ahead of the MFMAs, and written to the
+// wave's own 4 NTB KB of LDS (row t at t * 128 bytes, 16-byte piece p at (p ^ (t & 7)) * 16),
+// from which each step reads its MFMA operand (lane l: row 32 tb + l % 32, piece 2 j + l / 32).
 // Groups past n repeat a valid address and multiply a zero A.
-template <int NGC>
-__device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[4], const uint16_t* wrow,
+template <int NGC, int NTB>
+__device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[NTB], const uint16_t* wrow,
                                                 const uint16_t* xl, const int* toff, char* xs,
                                                 int g0, int n, int lane) {
   bf16x8_s a[4 * NGC];
@@ -184,26 +189,27 @@ __device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[4], const uint
     const int g = st >> 2, gc = g < n ? g : n - 1;
     a[st] = *reinterpret_cast<const bf16x8_s*>(wrow + ((g0 + gc) * 4 + (st & 3)) * 16);
   }
-  u32x4_s xr0[16], xr1[16];  // token-row lines of even and odd groups
+  constexpr int NL = 4 * NTB;  // token-row loads per group
+  u32x4_s xr0[NL], xr1[NL];    // token-row lines of even and odd groups
 #pragma unroll
-  for (int i = 0; i < 16; ++i) xr0[i] = *reinterpret_cast<const u32x4_s*>(xl + toff[i] + g0 * 64);
+  for (int i = 0; i < NL; ++i) xr0[i] = *reinterpret_cast<const u32x4_s*>(xl + toff[i] + g0 * 64);
   // keep the scheduler from sinking these loads back next to their uses
   __builtin_amdgcn_sched_barrier(0);
   const bf16x8_s zero = {};
   const int wp = lane & 7;
 #pragma unroll
   for (int g = 0; g < NGC; ++g) {
-    u32x4_s(&cur)[16] = (g & 1) ? xr1 : xr0;
-    u32x4_s(&nxt)[16] = (g & 1) ? xr0 : xr1;
+    u32x4_s(&cur)[NL] = (g & 1) ? xr1 : xr0;
+    u32x4_s(&nxt)[NL] = (g & 1) ? xr0 : xr1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NL; ++i) {
       const int t = 8 * i + (lane >> 3);
       *reinterpret_cast<u32x4_s*>(xs + t * 128 + ((wp ^ (t & 7)) << 4)) = cur[i];
     }
     if (g + 1 < NGC) {
       const int gc = g + 1 < n ? g + 1 : n - 1;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < NL; ++i)
         nxt[i] = *reinterpret_cast<const u32x4_s*>(xl + toff[i] + (g0 + gc) * 64);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -211,7 +217,7 @@ __device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[4], const uint
     for (int j = 0; j < 4; ++j) {
       const bf16x8_s av = g < n ? a[4 * g + j] : zero;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0; tb < NTB; ++tb) {
         const int R = 32 * tb + (lane & 31), P = 2 * j + (lane >> 5);
         const bf16x8_s b =
             *reinterpret_cast<const bf16x8_s*>(xs + R * 128 + ((P ^ (R & 7)) << 4));
@@ -221,13 +227,13 @@ __device__ __forceinline__ void up_small8_chunk(floatx16_s (&acc)[4], const uint
   }
 }
 
-template <int NTB>
+template <int NTB, int NGC>
 __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
     Dims d, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wu,
     const uint16_t* __restrict__ bu, float* __restrict__ h, float* __restrict__ zdump) {
-  static_assert(NTB == 4, "the 8-wave form stages 128 token rows");
+  static_assert(NTB == 1 || NTB == 2 || NTB == 4, "the 8-wave form stages 32, 64 or 128 token rows");
   constexpr int US_NW = US8_NW;
-  // wave w's 16 KB: first its staged token rows, then its partial sums
+  // wave w's 4 NTB KB: first its staged token rows, then its partial sums
   // [wave][token block][element][lane] (the same bytes, after its last MFMA)
   __shared__ __attribute__((aligned(16))) float red[US_NW * NTB * 16 * 64];
   const int lane = threadIdx.x & 63;
@@ -241,13 +247,13 @@ __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
   // token-row loads: load i of lane l reads row 8 i + l / 8 (rows past T repeat row T - 1),
   // 16-byte piece l % 8 of the group's line
   const uint16_t* xl = x + 8 * (lane & 7);
-  int toff[16];
+  int toff[4 * NTB];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 4 * NTB; ++i) {
     const int t = 8 * i + (lane >> 3);
     toff[i] = (t < T ? t : T - 1) * D;
   }
-  char* xs = reinterpret_cast<char*>(red) + wave * 16384;
+  char* xs = reinterpret_cast<char*>(red) + wave * NTB * 4096;
 
   floatx16_s acc[NTB];
 #pragma unroll
@@ -255,9 +261,8 @@ __global__ __launch_bounds__(US8_NW * 64) void up_small8_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[tb][e] = 0.0f;
   int g = g0;
-  for (; g + US8_NGC <= g1; g += US8_NGC)
-    up_small8_chunk<US8_NGC>(acc, wrow, xl, toff, xs, g, US8_NGC, lane);
-  if (g < g1) up_small8_chunk<US8_NGC>(acc, wrow, xl, toff, xs, g, g1 - g, lane);
+  for (; g + NGC <= g1; g += NGC) up_small8_chunk<NGC, NTB>(acc, wrow, xl, toff, xs, g, NGC, lane);
+  if (g < g1) up_small8_chunk<NGC, NTB>(acc, wrow, xl, toff, xs, g, g1 - g, lane);
 
   // element e of lane l is neuron 8(e/4) + 4(l/32) + e%4 of the block and token l % 32 of
   // the token block
@@ -309,19 +314,19 @@ hipError_t launch_up_small(const Dims& d, const uint16_t* x, const uint16_t* Wu,
                            const uint16_t* bu, float* h, float* zdump,
                            hipStream_t s) {
   if (!up_small_supported(d)) return hipErrorInvalidValue;
-  const dim3 grid(d.F / US_NB);
-  const bool stg = up_small_staged(d);
-  if (d.T <= 32 && stg)
+  const dim3 grid(d.F / US_NB), g8(US8_NW * 64);
+  if (d.T < 8 && up_small_staged(d))
     hipLaunchKernelGGL((up_small_kernel<1, true>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
+  else if (d.D % 64 == 0 && d.T <= 32)
+    hipLaunchKernelGGL((up_small8_kernel<1, US8_NGC12>), grid, g8, 0, s, d, x, Wu, bu, h, zdump);
+  else if (d.D % 64 == 0 && d.T <= 64)
+    hipLaunchKernelGGL((up_small8_kernel<2, US8_NGC12>), grid, g8, 0, s, d, x, Wu, bu, h, zdump);
+  else if (d.D % 64 == 0)
+    hipLaunchKernelGGL((up_small8_kernel<4, US8_NGC>), grid, g8, 0, s, d, x, Wu, bu, h, zdump);
   else if (d.T <= 32)
     hipLaunchKernelGGL((up_small_kernel<1, false>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
-  else if (d.T <= 64 && stg)
-    hipLaunchKernelGGL((up_small_kernel<2, true>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   else if (d.T <= 64)
     hipLaunchKernelGGL((up_small_kernel<2, false>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
-  else if (d.D % 64 == 0)
-    hipLaunchKernelGGL(up_small8_kernel<4>, grid, dim3(US8_NW * 64), 0, s, d, x, Wu, bu, h,
-                       zdump);
   else
     hipLaunchKernelGGL((up_small_kernel<4, false>), grid, dim3(256), 0, s, d, x, Wu, bu, h, zdump);
   return hipGetLastError();

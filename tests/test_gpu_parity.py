@@ -434,6 +434,7 @@ def _forward_case(torch, sffn, L, cap=None, check_pattern=True, policy="auto"):
     # one to four 32-token blocks per workgroup, the last one ragged)
     ("C3", 1, 0.05), ("C3", 7, 0.01), ("C3", 32, 0.05), ("C2", 3, None), ("C4", 5, None),
     ("C3", 64, 0.05), ("C3", 100, 0.05), ("C2", 128, None), ("C4", 97, None),
+    ("C3", 45, 0.05), ("C4", 33, None),
 ])
 def test_forward_parity(name, T, rho, policy):
     torch, sffn = need_gpu()
