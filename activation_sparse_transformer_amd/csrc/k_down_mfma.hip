@@ -399,13 +399,20 @@ __global__ __launch_bounds__(256) void down_reduce_kernel(Dims d, const float* _
   const size_t n4 = (size_t)d.T * d.D / 4;
   const float4* p4 = reinterpret_cast<const float4*>(part);
   for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n4; q += (size_t)gridDim.x * 256) {
-    float4 a = p4[q];
-    for (int sp = 1; sp < S; ++sp) {
-      const float4 v = p4[(size_t)sp * n4 + q];
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
+    // every part's load in flight before the first add (S <= DM_MAX_SPLIT)
+    float4 v[DM_MAX_SPLIT];
+#pragma unroll
+    for (int sp = 0; sp < DM_MAX_SPLIT; ++sp)
+      v[sp] = sp < S ? p4[(size_t)sp * n4 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 a = v[0];
+#pragma unroll
+    for (int sp = 1; sp < DM_MAX_SPLIT; ++sp) {
+      if (sp < S) {
+        a.x += v[sp].x;
+        a.y += v[sp].y;
+        a.z += v[sp].z;
+        a.w += v[sp].w;
+      }
     }
     const uint32_t lo = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
@@ -437,6 +444,7 @@ static hipError_t launch_dm_t(const Dims& d, const twell_buffers_t& b, const Wor
 
 hipError_t launch_down_reduce(const Dims& d, const Workspace& ws, void* y, int S,
                               const int32_t* blk_nnz, long long thr, hipStream_t s) {
+  if (S < 1 || S > DM_MAX_SPLIT) return hipErrorInvalidValue;  // down_split keeps S in range
   const size_t n4 = (size_t)d.T * d.D / 4;
   const int blocks = (int)std::min<size_t>((n4 + 255) / 256, 2048);
   hipLaunchKernelGGL(down_reduce_kernel, dim3(blocks), dim3(256), 0, s, d, ws.dpart, S,
