@@ -13,22 +13,22 @@
 // row and not written.
 //
 // Two forms, by measurement on MI355X at d_model 2048:
-//  * fewer than 8 tokens (one token block): 4 waves, each over a quarter of d_model in
-//    batches of 8 steps whose loads are in flight together.  Where the quarters fit LDS
-//    (d_model <= 2048, a multiple of 512), each wave first copies its 32 W_up rows x D/4
+//  * fewer than 8 tokens (one token block) where W_up's quarters fit LDS (d_model <= 2048, a
+//    multiple of 512): 4 waves, each over a quarter of d_model in batches of 8 steps whose
+//    loads are in flight together.  Each wave first copies its 32 W_up rows x D/4
 //    columns into its own LDS region with contiguous 1 KB direct loads (16-byte piece s of row
 //    rr at slot s ^ (rr % 16), so the fragment reads of 16 rows hit distinct banks): read in
 //    the MFMA layout straight from memory, each load used 32 bytes of 32 lines, and W_up
 //    streamed at 6.3 TB/s against 11.3 TB/s for whole-row loads (a probe over the 1.5B-like
 //    layer's W_up, cache-resident as in the forward);
-//  * 8 to 128 tokens (one, two or four token blocks; d_model a multiple of 64): 8 waves, each
+//  * otherwise, for d_model a multiple of 64 (one, two or four token blocks): 8 waves, each
 //    over an eighth of d_model in groups of four steps, with the W_up pieces of four groups
 //    (two for four token blocks, whose token rows take the registers) in flight at once and
 //    the token rows of the next group loaded as whole 128-byte lines and staged through the
 //    wave's own LDS (a token row's 32 bytes per step, loaded straight into the MFMA layout,
 //    cost a line fetch from L2 each: the 4-wave form took 17.8 us at 64 tokens against
 //    10.5 us at 32, and this form 12-13 us).
-// Other shapes run the 4-wave form with direct loads.
+// Other shapes run the 4-wave form with W_up and the token rows loaded straight from memory.
 #include "sffn_common.hpp"
 
 namespace sffn {
